@@ -1,0 +1,84 @@
+"""Number formats used by the oracle (test infrastructure).
+
+bf16: a bfloat16 value is the float32 whose upper 16 bits are the stored bits
+and whose lower 16 bits are zero, so widening is exact.
+
+fp8 e4m3fn (the OCP 8-bit float with 4 exponent bits, bias 7, 3 mantissa bits,
+no infinities, a single NaN mantissa pattern per sign, largest finite 448): the
+pages quantise activations to FP8 before dispatch ("MoE: what it costs to train
+and serve", worked example "how many bytes does one token send?", where FP8
+halves the payload).  The encoder rounds to nearest with ties to even.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen a stored tensor ("f32" values or "bf16" bits) to float64."""
+    if dtype == "bf16":
+        return bf16_to_f64(a)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of e4m3fn codes (uint8) as float64; the NaN codes 0x7F/0xFF give NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = c & 0x7
+    sub = man / 8.0 * 2.0 ** -6                       # exponent field 0: subnormal
+    nor = (1.0 + man / 8.0) * np.exp2(ex - 7.0)
+    v = np.where(ex == 0, sub, nor)
+    v = np.where((ex == 15) & (man == 7), np.nan, v)
+    return sign * v
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Round float32 values with |v| < 464 to e4m3fn codes, nearest, ties to even.
+
+    Values in [448, 464) round to 448 (464 is the midpoint to 480, which the
+    format does not have); the per-token scaling can land a hair above 448.
+
+    The quantum in the binade [2^e, 2^(e+1)) is 2^(e-3); below 2^-6 the format
+    is subnormal with quantum 2^-9.  |v| / quantum is exact in float64, so
+    ``np.rint`` (ties to even) gives the rounded significand; a carry into the
+    next binade is handled by re-deriving the code from the rounded value.
+    A negative zero keeps its sign (code 0x80)."""
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(v)) or np.any(np.abs(v) >= 464.0):
+        raise ValueError("e4m3_encode: input outside the finite e4m3fn range")
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    # guard against log2 rounding at exact powers of two
+    e = np.where(np.exp2(e) > a, e - 1, e)
+    e = np.where(np.exp2(e + 1) <= a, e + 1, e)
+    e = np.maximum(e, -6.0)
+    q = np.exp2(e - 3.0)
+    r = np.rint(a / q) * q                              # rounded magnitude
+    # encode the rounded magnitude
+    with np.errstate(divide="ignore"):
+        er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    er = np.where(np.exp2(er) > r, er - 1, er)
+    er = np.where(np.exp2(er + 1) <= r, er + 1, er)
+    normal = r >= 2.0 ** -6
+    ex_field = np.where(normal, er + 7.0, 0.0)
+    man = np.where(normal, r / np.exp2(er) * 8.0 - 8.0, r / 2.0 ** -9)
+    code = (ex_field.astype(np.int64) << 3) | np.rint(man).astype(np.int64)
+    code = np.where(r == 0, 0, code)
+    sign = np.signbit(v)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
+def f32(a) -> np.ndarray:
+    """Round to float32 (IEEE, nearest even)."""
+    return np.asarray(a, dtype=np.float32)

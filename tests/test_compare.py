@@ -1,0 +1,62 @@
+"""The tie-band adoption procedure used by the GPU parity tests (CPU only)."""
+import numpy as np
+
+import synthetic_inputs as si
+from oracle import compare, moe
+
+
+def wl(**kw):
+    base = dict(T=4, d=4, N=8, k=2, F=8, act="silu", dtype="f32", buf="f32")
+    base.update(kw)
+    return si.Workload("cmp", **base)
+
+
+def test_identical_selection_needs_no_adoption():
+    w = wl()
+    l = np.array([[3.0, 1.0, 2.0, 0.0, -1.0, 0.5, 0.2, 0.1]])
+    idx = moe.top_k(l, np.ones_like(l, bool), 2)
+    r = compare.adopt(w, l, idx, idx)
+    assert r["adopted"] == [] and r["bad"] == []
+
+
+def test_near_tie_at_kth_is_adopted():
+    w = wl()
+    l = np.array([[3.0, 1.0, 2.0, 2.0 + 1e-9, -1.0, 0.5, 0.2, 0.1]])
+    o = moe.top_k(l, np.ones_like(l, bool), 2)
+    assert o.tolist() == [[0, 3]]
+    r = compare.adopt(w, l, o, np.array([[0, 2]]))
+    assert r["adopted"] == [0] and r["bad"] == []
+    assert np.allclose(r["w"][0], moe.sparse_softmax(l, np.array([[0, 2]]))[0])
+
+
+def test_clear_gap_is_rejected():
+    w = wl()
+    l = np.array([[3.0, 1.0, 2.0, 2.1, -1.0, 0.5, 0.2, 0.1]])
+    o = moe.top_k(l, np.ones_like(l, bool), 2)
+    r = compare.adopt(w, l, o, np.array([[0, 2]]))
+    assert r["bad"] == [0]
+    # wrong slot order outside the band is also rejected
+    r = compare.adopt(w, l, o, np.array([[3, 0]]))
+    assert r["bad"] == [0]
+    # duplicates are never admissible
+    r = compare.adopt(w, l, o, np.array([[0, 0]]))
+    assert r["bad"] == [0]
+
+
+def test_group_level_near_tie():
+    w = wl(N=8, k=2, n_groups=4, topk_groups=1, group_score_k=2)
+    # group scores: g0 = 3, g1 = 3 + 1e-9 -> oracle keeps g1; the GPU may keep g0
+    l = np.array([[2.0, 1.0, 1.5, 1.5 + 1e-9, 0.0, 0.0, -1.0, -1.0]])
+    mask = moe.group_mask(l, 4, 1, 2)
+    o = moe.top_k(l, mask, 2)
+    assert o.tolist() == [[3, 2]]
+    r = compare.adopt(w, l, o, np.array([[0, 1]]))
+    assert r["adopted"] == [0]
+    r = compare.adopt(w, l, o, np.array([[0, 4]]))         # mixes groups: never admissible
+    assert r["bad"] == [0]
+
+
+def test_rel_l2():
+    a = np.array([1.0, 2.0, 2.0])
+    assert compare.rel_l2(a, a) == 0.0
+    assert abs(compare.rel_l2(a * 1.01, a) - 0.01) < 1e-12
