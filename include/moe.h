@@ -1,0 +1,209 @@
+/*
+ * moe.h — C ABI of the sparse Mixture-of-Experts layer forward for AMD MI355X (gfx950).
+ *
+ * The layer, for T tokens x[t] of width d, N routed experts and k experts per token:
+ *   route     l[t][e] = W_g[e] . x[t] (+ b[e]); optional group limit; the k largest
+ *             logits (ties to the lower expert index); weights = softmax over only
+ *             those k logits; load statistics f, p and L_aux.
+ *   dispatch  permute the (token, slot) assignments into expert-contiguous order
+ *             (histogram, prefix scan, stable rank, capacity drop, row copy or
+ *             fp8 quantise).
+ *   experts   per expert segment: h = act(W1 x, W3 x), o = W2 h (grouped GEMMs).
+ *   combine   y[t] = sum_j w[t][j] * (o of slot j, or x[t] / 0 when dropped)
+ *             (+ the shared expert's output).
+ *
+ * Sources (web pages, cited by title and section):
+ *   "Advanced GPU Optimization: How to tech an LLM with CUDA and ROCm? - Part 5":
+ *       "The Math"; "1.1 The Router Kernel (Top-k Gating)"; "1.2 Expert Parallelism
+ *       with All-to-All Communication".
+ *   "MoE: what it costs to train and serve": "Expert parallelism and two
+ *       all-to-alls"; "Worked example: how many bytes does one token send?";
+ *       "Limit how many machines a token touches"; "Numerical precision".
+ *   "moe communication costs": "Router design"; "Load balancing - the critical
+ *       auxiliary loss"; "Capacity factor and token dropping".
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by
+ *     the caller.  The library never allocates, frees, or keeps state between
+ *     calls.  Scratch memory comes from the caller through `ws`/`ws_bytes`
+ *     (size from moe_workspace_bytes).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues kernels on it: no host synchronisation, no device-to-host read.
+ *     Outputs are valid once the stream has reached that point.
+ *   - Element types: `dtype` is the storage of x, W_g, the expert weights, the
+ *     intermediate h, the expert outputs and y: MOE_F32 or MOE_BF16 (bit patterns
+ *     of bfloat16).  Router logits, weights and statistics are always float32;
+ *     all products accumulate in float32.
+ *   - Errors are returned as moe_status; nothing is thrown.  Argument checks run
+ *     on the host before any launch: MOE_ERR_ARG for invalid sizes or NULL
+ *     required pointers, MOE_ERR_UNSUPPORTED for valid but unimplemented
+ *     combinations, MOE_ERR_WORKSPACE when ws_bytes is too small, MOE_ERR_HIP
+ *     when a launch fails.  T == 0 is a no-op returning MOE_OK.
+ *   - Inputs must be finite; NaN/Inf inputs give undefined (but memory-safe)
+ *     results.
+ *   - Results are deterministic: repeated calls with the same inputs give
+ *     bit-identical outputs (no floating-point atomics; fixed reduction orders).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act;
+typedef enum { MOE_DROP_PASSTHROUGH = 0, MOE_DROP_ZERO = 1 } moe_drop;
+
+/* Shape and options of one layer.  Enumerations are stored as int32_t so that
+ * the struct layout is fixed: 8 + 14 * 4 = 64 bytes, alpha at offset 60. */
+typedef struct moe_shape {
+  int64_t T;             /* tokens, >= 0 */
+  int32_t d;             /* hidden size */
+  int32_t N;             /* routed experts, 1..256 */
+  int32_t k;             /* experts per token, 1..min(N, 8) ("1.1 The Router Kernel": top-2;
+                            "moe communication costs" table: k from 1 to 6) */
+  int32_t F;             /* expert FFN width */
+  int32_t capacity;      /* max kept assignments per expert; <= 0: unlimited
+                            ("Capacity factor and token dropping": C = factor * T / N,
+                            rounded by the caller) */
+  int32_t n_groups;      /* 0 or 1: no group limit; else G contiguous groups of N/G
+                            experts ("Limit how many machines a token touches") */
+  int32_t topk_groups;   /* groups kept per token (G > 1) */
+  int32_t group_score_k; /* a group's score is the sum of its group_score_k largest
+                            logits, 1..8 */
+  int32_t has_shared;    /* 1: one always-on shared expert (weight 1, unquantised x) */
+  int32_t dtype;         /* moe_dtype: MOE_F32 or MOE_BF16 */
+  int32_t buf_dtype;     /* dispatch buffer: == dtype, or MOE_FP8_E4M3 when dtype is bf16 */
+  int32_t act;           /* moe_act */
+  int32_t drop;          /* moe_drop: what a dropped slot contributes */
+  float alpha;           /* L_aux coefficient ("Load balancing": typically 0.01-0.1) */
+} moe_shape;
+
+/* Bytes of device scratch needed by moe_route, moe_dispatch and moe_experts for
+ * this shape (one buffer serves all of them; 256-byte aligned).  The largest
+ * part is the expert intermediate h: T*k rows of F elements (+ T rows for the
+ * shared expert).  Returns 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape* s);
+
+/* Checks a shape; MOE_OK when every call supports it. */
+moe_status moe_check_shape(const moe_shape* s);
+
+/* Router.  "moe communication costs" / "Router design" (logits W_g x, no noise at
+ * inference); "Part 5" / "1.1 The Router Kernel" (top-k scan with strict >, so
+ * ties go to the lower index; softmax over only the selected logits, max
+ * subtracted); "Load balancing" (f_i, p_i, L_aux = alpha N sum f_i p_i).
+ *   x       [T][d] dtype          W_g [N][d] dtype (stored like x)
+ *   bias    [N] float32 or NULL   added to the logits before every use
+ *   idx     [T][k] int32 out      expert ids, slot 0 = largest logit
+ *   w       [T][k] float32 out    sparse-softmax weights (each row sums to 1)
+ *   counts  [N] int32 out         assignments per expert before capacity drops
+ *   kept_counts [N] int32 out     min(counts, capacity) (= counts if unlimited)
+ *   p, f    [N] float32 out or NULL   mean full-softmax probability; counts/(T k)
+ *   l_aux   [1] float32 out or NULL   alpha * N * sum(f * p)
+ *   logits  [T][N] float32 out or NULL (debug: the biased logits)
+ */
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                     int32_t* idx, float* w, int32_t* counts, int32_t* kept_counts,
+                     float* p, float* f, float* l_aux, float* logits,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: the single-GPU form of the dispatch all-to-all ("Part 5" / "1.2
+ * Expert Parallelism", step 1; "MoE: what it costs to train and serve" / "Expert
+ * parallelism and two all-to-alls").  Assignment a = t*k + j goes to expert
+ * e = idx[t][j]; its rank is the number of earlier assignments (smaller a) to e;
+ * it is kept when capacity <= 0 or rank < capacity.
+ *   idx       [T][k] int32 in (each row holds k distinct ids in [0, N))
+ *   offsets   [N+1] int32 out   exclusive scan of the kept counts; R = offsets[N]
+ *   pos       [T][k] int32 out  offsets[e] + rank, or -1 when dropped
+ *   src       [T*k] int32 out   src[pos] = t for the R kept rows (rest untouched)
+ *   drop      [T][k] uint8 out  1 when dropped
+ *   x_perm    [T*k][d] out      row pos = x[t] (dtype), or fp8 e4m3 codes when
+ *                               buf_dtype is FP8 ("Worked example: how many bytes
+ *                               does one token send?": FP8 before dispatch);
+ *                               rows >= R untouched.  Bytes written = R*d*s.
+ *   row_scale [T*k] float32 out (FP8 only, else may be NULL): per-row scale;
+ *             value = code * scale.  Per token: amax = max|x|, inv = 448/amax,
+ *             code = e4m3(x*inv) rounded to nearest even, scale = amax/448
+ *             (float32 IEEE arithmetic; amax < 2^-100, zero included, gives
+ *             inv = scale = 1).
+ */
+moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx,
+                        int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                        void* x_perm, float* row_scale,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Expert up-projection over the expert segments of x_perm (grouped GEMM 1 with
+ * the activation fused): for row r of expert e, h[r] = act(W1[e] x_r, W3[e] x_r)
+ * with x_r the (dequantised) dispatch row.  act: SiLU, ReLU, or SwiGLU
+ * silu(W1 x) * (W3 x).  "moe communication costs" / "The core idea" (expert FFNs).
+ *   x_perm [T*k][d] buf_dtype, row_scale [T*k] (FP8 only), offsets [N+1] from dispatch
+ *   w1, w3 [N][F][d] dtype (w3 NULL unless SwiGLU)
+ *   h      [T*k][F] dtype out (rows >= R untouched)
+ */
+moe_status moe_expert_up(const moe_shape* s, const void* x_perm, const float* row_scale,
+                         const int32_t* offsets, const void* w1, const void* w3, void* h,
+                         void* stream);
+
+/* Expert down-projection (grouped GEMM 2): out[r] = W2[e] h[r].
+ *   h [T*k][F] dtype, offsets [N+1], w2 [N][d][F] dtype, out [T*k][d] dtype. */
+moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* offsets,
+                           const void* w2, void* out, void* stream);
+
+/* The always-on shared expert on the unquantised input ("moe communication
+ * costs" / "Capacity factor and token dropping": a shared expert every token
+ * passes through): h_shared = act(Ws1 x, Ws3 x), out_shared = Ws2 h_shared.
+ *   x [T][d]; ws1, ws3 [F][d] (ws3 NULL unless SwiGLU); ws2 [d][F];
+ *   h_shared [T][F] scratch; out_shared [T][d] out.  All dtype. */
+moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1,
+                             const void* ws3, const void* ws2, void* h_shared,
+                             void* out_shared, void* stream);
+
+/* All experts: moe_expert_up + moe_expert_down, plus moe_shared_expert when
+ * has_shared (x, ws1, ws3, ws2, out_shared required then, else ignored).  The
+ * intermediates live in the workspace.  out [T*k][d], out_shared [T][d]. */
+moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_scale,
+                       const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                       const void* x, const void* ws1, const void* ws3, const void* ws2,
+                       void* out, void* out_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: the single-GPU form of the return all-to-all ("Part 5" / "1.2", step 3)
+ * and the mixture y = sum over the top-k of weight * expert output ("moe
+ * communication costs" / "Router design").  Accumulates in float32 in slot order
+ * j = 0..k-1, adds out_shared last, rounds once to dtype.
+ *   out [T*k][d], out_shared [T][d] or NULL, x [T][d], pos [T][k], w [T][k] f32,
+ *   y [T][d] dtype out.  A dropped slot contributes w * x[t] (pass-through) or 0. */
+moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shared,
+                       const void* x, const int32_t* pos, const float* w, void* y,
+                       void* stream);
+
+/* The whole layer: route, dispatch, experts, combine, enqueued on one stream.
+ * Every output buffer of the four calls is required except p, f, l_aux, logits
+ * (may be NULL) and the shared-expert buffers (ignored unless has_shared). */
+moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                       const void* w1, const void* w3, const void* w2,
+                       const void* ws1, const void* ws3, const void* ws2,
+                       int32_t* idx, float* w, int32_t* counts, int32_t* kept_counts,
+                       float* p, float* f, float* l_aux,
+                       int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                       void* x_perm, float* row_scale, void* out, void* out_shared, void* y,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

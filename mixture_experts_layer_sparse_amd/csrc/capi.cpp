@@ -1,0 +1,244 @@
+// C ABI: argument checks, workspace layout and kernel launches.  Every entry
+// point validates on the host before touching the device, so the error
+// conventions of include/moe.h hold without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t elem_size(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
+}  // namespace
+
+WsLayout ws_layout(const moe_shape& s) {
+  WsLayout L{};
+  const size_t T = static_cast<size_t>(s.T), N = static_cast<size_t>(s.N);
+  const size_t nb_route = static_cast<size_t>(ceil_div(s.T, kRouteTile));
+  const size_t nb_disp = static_cast<size_t>(ceil_div(s.T, kDispatchBlock));
+  size_t off = 0;
+  L.route_psum = off;
+  off = align_up(off + nb_route * N * 4);
+  L.route_hist = off;
+  off = align_up(off + nb_route * N * 4);
+  L.disp_hist = off;
+  off = align_up(off + nb_disp * N * 4);
+  L.h = off;
+  off = align_up(off + T * static_cast<size_t>(s.k) * static_cast<size_t>(s.F) * elem_size(s.dtype));
+  L.h_shared = off;
+  if (s.has_shared) off = align_up(off + T * static_cast<size_t>(s.F) * elem_size(s.dtype));
+  L.total = off;
+  return L;
+}
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace moe
+
+using moe::WsLayout;
+
+namespace {
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_ARG;
+  if (s->T < 0 || s->d < 8 || s->d % 8 != 0 || s->N < 1 || s->N > moe::kMaxExperts || s->k < 1 ||
+      s->k > s->N || s->F < 1)
+    return MOE_ERR_ARG;
+  if (s->k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_ARG;
+  if (s->buf_dtype != s->dtype && !(s->buf_dtype == MOE_FP8_E4M3 && s->dtype == MOE_BF16))
+    return s->buf_dtype == MOE_FP8_E4M3 ? MOE_ERR_UNSUPPORTED : MOE_ERR_ARG;
+  if (s->act < MOE_ACT_SILU || s->act > MOE_ACT_SWIGLU) return MOE_ERR_ARG;
+  if (s->drop != MOE_DROP_PASSTHROUGH && s->drop != MOE_DROP_ZERO) return MOE_ERR_ARG;
+  if (s->n_groups > 1) {
+    const int G = s->n_groups;
+    if (G > 64 || s->N % G != 0) return MOE_ERR_ARG;
+    if (s->topk_groups < 1 || s->topk_groups > G) return MOE_ERR_ARG;
+    if (static_cast<int64_t>(s->topk_groups) * (s->N / G) < s->k) return MOE_ERR_ARG;
+    if (s->group_score_k < 1 || s->group_score_k > s->N / G) return MOE_ERR_ARG;
+    if (s->group_score_k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  } else if (s->n_groups < 0) {
+    return MOE_ERR_ARG;
+  }
+  if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_ARG;
+  // positions and row indices are int32
+  if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype == MOE_BF16 && (s->d % 64 != 0 || s->F % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return moe::ws_layout(*s).total;
+}
+
+moe_status moe_check_shape(const moe_shape* s) { return check_shape(s); }
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or type combination";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                     int32_t* idx, float* w, int32_t* counts, int32_t* kept_counts, float* p,
+                     float* f, float* l_aux, float* logits, void* ws, size_t ws_bytes,
+                     void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !w_g || !idx || !w || !counts || !kept_counts || !ws) return MOE_ERR_ARG;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.disp_hist) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* psum = reinterpret_cast<float*>(base + L.route_psum);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux, st));
+}
+
+moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* offsets,
+                        int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm, float* row_scale,
+                        void* ws, size_t ws_bytes, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !idx || !offsets || !pos || !src || !drop || !x_perm || !ws) return MOE_ERR_ARG;
+  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.h) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.disp_hist);
+  hipError_t e = moe::launch_dispatch_hist(*s, idx, hist, st);
+  if (e == hipSuccess) e = moe::launch_dispatch_plan(*s, idx, hist, offsets, pos, src, drop, st);
+  if (e == hipSuccess) e = moe::launch_dispatch_copy(*s, x, pos, x_perm, row_scale, st);
+  return hip_status(e);
+}
+
+moe_status moe_expert_up(const moe_shape* s, const void* x_perm, const float* row_scale,
+                         const int32_t* offsets, const void* w1, const void* w3, void* h,
+                         void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!x_perm || !offsets || !w1 || !h) return MOE_ERR_ARG;
+  if (s->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
+  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  return hip_status(moe::launch_expert_up(*s, x_perm, row_scale, offsets, s->T * s->k, s->N, w1,
+                                          w3, h, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* offsets,
+                           const void* w2, void* out, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!h || !offsets || !w2 || !out) return MOE_ERR_ARG;
+  return hip_status(moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1, const void* ws3,
+                             const void* ws2, void* h_shared, void* out_shared, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !ws1 || !ws2 || !h_shared || !out_shared) return MOE_ERR_ARG;
+  if (s->act == MOE_ACT_SWIGLU && !ws3) return MOE_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the shared expert sees the unquantised input: same dtype as x
+  moe_shape sd = *s;
+  sd.buf_dtype = sd.dtype;
+  hipError_t e = moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared, st);
+  if (e == hipSuccess) e = moe::launch_expert_down(sd, h_shared, nullptr, s->T, 1, ws2, out_shared, st);
+  return hip_status(e);
+}
+
+moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_scale,
+                       const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                       const void* x, const void* ws1, const void* ws3, const void* ws2,
+                       void* out, void* out_shared, void* ws, size_t ws_bytes, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!ws || !out) return MOE_ERR_ARG;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  moe_status r = moe_expert_up(s, x_perm, row_scale, offsets, w1, w3, base + L.h, stream);
+  if (r != MOE_OK) return r;
+  r = moe_expert_down(s, base + L.h, offsets, w2, out, stream);
+  if (r != MOE_OK || !s->has_shared) return r;
+  return moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, stream);
+}
+
+moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shared, const void* x,
+                       const int32_t* pos, const float* w, void* y, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!out || !x || !pos || !w || !y) return MOE_ERR_ARG;
+  if (s->has_shared && !out_shared) return MOE_ERR_ARG;
+  return hip_status(moe::launch_combine(*s, out, s->has_shared ? out_shared : nullptr, x, pos, w, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                       const void* w1, const void* w3, const void* w2, const void* ws1,
+                       const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
+                       int32_t* kept_counts, float* p, float* f, float* l_aux, int32_t* offsets,
+                       int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm, float* row_scale,
+                       void* out, void* out_shared, void* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  moe_status r = check_shape(s);
+  if (r != MOE_OK) return r;
+  if (s->T == 0) return MOE_OK;
+  // every check of the four calls up front, so that nothing is launched on error
+  if (!x || !w_g || !w1 || !w2 || !idx || !w || !counts || !kept_counts || !offsets || !pos ||
+      !src || !drop || !x_perm || !out || !y || !ws)
+    return MOE_ERR_ARG;
+  if (s->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
+  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  if (s->has_shared && (!ws1 || !ws2 || !out_shared || (s->act == MOE_ACT_SWIGLU && !ws3)))
+    return MOE_ERR_ARG;
+  if (ws_bytes < moe::ws_layout(*s).total) return MOE_ERR_WORKSPACE;
+  r = moe_route(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, nullptr, ws, ws_bytes,
+                stream);
+  if (r != MOE_OK) return r;
+  r = moe_dispatch(s, x, idx, offsets, pos, src, drop, x_perm, row_scale, ws, ws_bytes, stream);
+  if (r != MOE_OK) return r;
+  r = moe_experts(s, x_perm, row_scale, offsets, w1, w3, w2, x, ws1, ws3, ws2, out, out_shared, ws,
+                  ws_bytes, stream);
+  if (r != MOE_OK) return r;
+  return moe_combine(s, out, out_shared, x, pos, w, y, stream);
+}
+
+}  // extern "C"

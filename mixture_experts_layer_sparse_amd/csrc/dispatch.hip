@@ -1,0 +1,296 @@
+// Dispatch: the single-GPU form of the dispatch all-to-all.  "Part 5" / "1.2
+// Expert Parallelism with All-to-All Communication" builds one send buffer per
+// destination from the routing decisions; "MoE: what it costs to train and
+// serve" / "Expert parallelism and two all-to-alls" describes the same step.
+// With every expert local, the send buffer becomes one expert-contiguous
+// buffer: a histogram, a prefix scan, a stable rank, and a row copy.
+// "Capacity factor and token dropping" ("moe communication costs") bounds each
+// expert's rows; "Worked example: how many bytes does one token send?" gives
+// the payload k*d*s per token and FP8 (s = 1) before dispatch.
+//
+// Kernels
+//   disp_hist  per block of 256 tokens, an LDS histogram of the block's
+//              assignments (integer atomics: the counts do not depend on order).
+//   disp_plan  per block: the block's base per expert (sum over earlier
+//              blocks), the kept counts and their exclusive scan (offsets), and
+//              the stable in-block rank of every assignment from wave ballots
+//              (match on the expert-id bits) plus a wave-ordered LDS prefix.
+//              No atomics decide a position, so the permutation is unique.
+//   disp_copy  one wave per token: read the row once, write it to each kept
+//              slot's position (bf16/f32 copy, or fp8 e4m3 with a per-token scale).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int TB = kDispatchBlock;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t* __restrict__ idx, int64_t T,
+                                                        int k, int N, int32_t* __restrict__ hist) {
+  __shared__ int h[kMaxExperts];
+  for (int e = threadIdx.x; e < kMaxExperts; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * TB + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = idx[t * k + j];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256) hist[static_cast<int64_t>(blockIdx.x) * N + e] = h[e];
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(256) void disp_plan_kernel(const int32_t* __restrict__ idx, int64_t T,
+                                                        int k, int N, int cap,
+                                                        const int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ src,
+                                                        uint8_t* __restrict__ drop) {
+  __shared__ int base[kMaxExperts];       // assignments to e in earlier blocks
+  __shared__ int scan[2][kMaxExperts + 1];
+  __shared__ int wh[4][kMaxExperts];      // per-wave counts inside this block
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = blockIdx.x, nb = gridDim.x;
+
+  // 1. totals and this block's base, kept counts
+  for (int e = tid; e < kMaxExperts; e += 256) {
+    int tot = 0, bb = 0;
+    if (e < N) {
+      for (int b = 0; b < nb; ++b) {
+        int h = hist[static_cast<int64_t>(b) * N + e];
+        if (b < blk) bb += h;
+        tot += h;
+      }
+    }
+    base[e] = bb;
+    int kept = cap > 0 ? (tot < cap ? tot : cap) : tot;
+    scan[0][e] = e < N ? kept : 0;
+    wh[0][e] = wh[1][e] = wh[2][e] = wh[3][e] = 0;
+  }
+  __syncthreads();
+  // 2. inclusive scan over experts (Hillis-Steele, ping-pong buffers)
+  int cur = 0;
+  for (int off = 1; off < kMaxExperts; off <<= 1) {
+    for (int e = tid; e < kMaxExperts; e += 256)
+      scan[cur ^ 1][e] = scan[cur][e] + (e >= off ? scan[cur][e - off] : 0);
+    cur ^= 1;
+    __syncthreads();
+  }
+  // exclusive offset of e = inclusive[e - 1]
+  if (blk == 0) {
+    for (int e = tid; e <= N; e += 256) offsets[e] = e == 0 ? 0 : scan[cur][e - 1];
+  }
+
+  // 3. in-block stable ranks
+  const int64_t t = static_cast<int64_t>(blk) * TB + tid;
+  const bool valid = t < T;
+  int ej[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    int e = -1;
+    if (j < k && valid) {
+      e = idx[t * k + j];
+      if (static_cast<unsigned>(e) >= static_cast<unsigned>(N)) e = -1;
+    }
+    ej[j] = e;
+    if (e >= 0) atomicAdd(&wh[wave][e], 1);
+  }
+  int nbits = 1;
+  while ((1 << nbits) < N) ++nbits;
+  int rank[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) rank[j] = 0;
+  const uint64_t lt = lanemask_lt(lane);
+#pragma unroll
+  for (int jp = 0; jp < kMaxTopK; ++jp) {
+    if (jp < k) {
+      const uint64_t vb = __ballot(ej[jp] >= 0);
+      uint64_t bal[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) bal[b] = b < nbits ? __ballot((ej[jp] >> b) & 1) : 0ull;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          uint64_t m = vb & lt;
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            if (b < nbits) m &= ((ej[j] >> b) & 1) ? bal[b] : ~bal[b];
+          rank[j] += __popcll(m);
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k && valid) {
+      const int e = ej[j];
+      int p = -1;
+      if (e >= 0) {
+        int r = base[e] + rank[j];
+        for (int w = 0; w < wave; ++w) r += wh[w][e];
+        if (cap <= 0 || r < cap) {
+          p = (e == 0 ? 0 : scan[cur][e - 1]) + r;
+          src[p] = static_cast<int32_t>(t);
+        }
+      }
+      pos[t * k + j] = p;
+      drop[t * k + j] = p < 0 ? 1 : 0;
+    }
+  }
+}
+
+// One wave per token; 16-byte chunks.  Row bytes must be a multiple of 16.
+__global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restrict__ x, int64_t T,
+                                                        int k, int row_bytes,
+                                                        const int32_t* __restrict__ pos,
+                                                        uint8_t* __restrict__ xp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int pj[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
+  const int nch = row_bytes / 16;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + t * row_bytes);
+#pragma unroll 4
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr) + c);
+    const uint4 v = make_uint4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (pj[j] >= 0)
+        reinterpret_cast<uint4*>(xp + static_cast<int64_t>(pj[j]) * row_bytes)[c] = v;
+  }
+}
+
+__device__ __forceinline__ uint2 quant8(uint4 v, float inv) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16) * inv;
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * inv;
+  }
+  // two floats -> two e4m3 codes (nearest even) into the low / high half-word
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+}
+
+__device__ __forceinline__ float absmax8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+  }
+  return m;
+}
+
+// fp8 dispatch: one wave per token.  Rows up to 64*MAXC chunks of 8 bf16 stay in
+// registers; longer rows are read twice.
+template <int MAXC>
+__global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                       int k, int d,
+                                                       const int32_t* __restrict__ pos,
+                                                       uint8_t* __restrict__ xp,
+                                                       float* __restrict__ row_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int pj[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
+  const int nch = d / 8;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
+  const bool in_regs = nch <= 64 * MAXC;
+  uint4 buf[MAXC];
+  float amax = 0.f;
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) {
+      int c = lane + 64 * q;
+      buf[q] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
+      amax = fmaxf(amax, absmax8(buf[q]));
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) amax = fmaxf(amax, absmax8(xr[c]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  // rows below 2^-100 (zero included) count as zero rows: 448/amax would overflow
+  const bool tiny = amax < 0x1p-100f;
+  const float inv = tiny ? 1.f : __fdiv_rn(448.0f, amax);
+  const float scale = tiny ? 1.f : __fdiv_rn(amax, 448.0f);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (pj[j] >= 0) row_scale[pj[j]] = scale;
+  }
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) {
+      int c = lane + 64 * q;
+      if (c < nch) {
+        uint2 code = quant8(buf[q], inv);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+          if (pj[j] >= 0) reinterpret_cast<uint2*>(xp + static_cast<int64_t>(pj[j]) * d)[c] = code;
+      }
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) {
+      uint2 code = quant8(xr[c], inv);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (pj[j] >= 0) reinterpret_cast<uint2*>(xp + static_cast<int64_t>(pj[j]) * d)[c] = code;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_hist(const moe_shape& s, const int32_t* idx, int32_t* hist,
+                                hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(ceil_div(s.T, TB)));
+  hipLaunchKernelGGL(disp_hist_kernel, grid, dim3(256), 0, st, idx, s.T, s.k, s.N, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_plan(const moe_shape& s, const int32_t* idx, const int32_t* hist,
+                                int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                                hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(ceil_div(s.T, TB)));
+  hipLaunchKernelGGL(disp_plan_kernel, grid, dim3(256), 0, st, idx, s.T, s.k, s.N, s.capacity,
+                     hist, offsets, pos, src, drop);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_copy(const moe_shape& s, const void* x, const int32_t* pos,
+                                void* x_perm, float* row_scale, hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(ceil_div(s.T, 4)));
+  if (s.buf_dtype == MOE_FP8_E4M3) {
+    hipLaunchKernelGGL(disp_fp8_kernel<16>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
+                       static_cast<uint8_t*>(x_perm), row_scale);
+  } else {
+    int es = s.dtype == MOE_BF16 ? 2 : 4;
+    hipLaunchKernelGGL(disp_copy_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
+                       static_cast<uint8_t*>(x_perm));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+constexpr int kRouteTile = 16;     // tokens per router workgroup
+constexpr int kDispatchBlock = 256;  // tokens per dispatch-plan block
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) {
+  return (a + b - 1) / b;
+}
+
+// Workspace carving: offsets (bytes) of each region for one shape.
+struct WsLayout {
+  size_t route_psum;    // float   [nb_route][N]
+  size_t route_hist;    // int32   [nb_route][N]
+  size_t disp_hist;     // int32   [nb_disp][N]
+  size_t h;             // dtype   [T*k][F]
+  size_t h_shared;      // dtype   [T][F]
+  size_t total;
+};
+WsLayout ws_layout(const moe_shape& s);
+
+// ---------------------------------------------------------------- launchers --
+// Each returns hipSuccess or the launch error; shapes are already validated.
+
+hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                        int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
+                        hipStream_t st);
+hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
+                                 int32_t* counts, int32_t* kept, float* p, float* f,
+                                 float* l_aux, hipStream_t st);
+
+hipError_t launch_dispatch_hist(const moe_shape& s, const int32_t* idx, int32_t* hist,
+                                hipStream_t st);
+hipError_t launch_dispatch_plan(const moe_shape& s, const int32_t* idx, const int32_t* hist,
+                                int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                                hipStream_t st);
+hipError_t launch_dispatch_copy(const moe_shape& s, const void* x, const int32_t* pos,
+                                void* x_perm, float* row_scale, hipStream_t st);
+
+// Grouped GEMMs.  `offsets` == nullptr means one dense segment of `rows` rows.
+hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
+                            const int32_t* offsets, int64_t rows, int n_seg,
+                            const void* w1, const void* w3, void* h, hipStream_t st);
+hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
+                              int64_t rows, int n_seg, const void* w2, void* out,
+                              hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_shared,
+                          const void* x, const int32_t* pos, const float* w, void* y,
+                          hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,352 @@
+// Router: logits (skinny GEMM), group limit, top-k, sparse softmax and the
+// per-block load statistics, fused in one kernel; plus a one-workgroup
+// finalisation of counts, f, p and L_aux.
+//
+// What it computes follows "moe communication costs" / "Router design" (logits
+// W_g x; the top-k entries pick the experts), "Part 5" / "1.1 The Router Kernel"
+// (strict > while scanning experts in index order, so equal logits go to the
+// lower index; softmax over only the selected logits, max subtracted) and
+// "Load balancing" (f_i, p_i, L_aux).  The group limit follows "MoE: what it
+// costs to train and serve" / "Limit how many machines a token touches".
+//
+// Design (differs from the page's one-thread-per-token kernel): a workgroup of
+// 4 waves owns 16 tokens.  For bf16 the logits come from 16x16x32 bf16 MFMAs
+// reading x and W_g straight from global memory (each x element is read once;
+// W_g is small and stays in L2); when N < 64 the waves split the d-loop and
+// their partial sums are added in a fixed order.  Then one wave per token does
+// the selection with 64-bit wave max-reductions on keys (logit, ~index), so
+// the result is independent of thread timing.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TM = kRouteTile;
+
+struct RouteArgs {
+  const void* x;
+  const void* wg;
+  const float* bias;
+  int32_t* idx;
+  float* w;
+  float* logits;
+  float* psum;
+  int32_t* hist;
+  int64_t T;
+  int d, N, k, n_groups, topk_groups, gsk;
+};
+
+// Key ordering "larger logit first, then lower expert index"; 0 = no candidate.
+__device__ __forceinline__ uint64_t sel_key(float v, int e) {
+  v = v + 0.0f;                                   // -0 -> +0 so that zeros tie
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(0xFFFF - e);
+}
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return 0xFFFF - static_cast<int>(key & 0xFFFFFFFFu);
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t u = static_cast<uint32_t>(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+// Butterfly sum: every lane ends with the same value (a + b == b + a exactly).
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Logit tile [TM][ldl] in LDS, computed by the bf16 MFMA path.
+__device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* lt, int ldl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = a.N, d = a.d;
+  const int NB = (N + 15) / 16;                       // 16-expert column blocks
+  const int KS = NB >= 3 ? 1 : 4 / NB;                // d-splits across waves
+  const int CG = 4 / KS;                              // column groups
+  const int ks = wave / CG, cg = wave % CG;
+  const int nsteps = d / 32;
+  const int s0 = ks * nsteps / KS, s1 = (ks + 1) * nsteps / KS;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* wg = static_cast<const uint16_t*>(a.wg);
+  int64_t t = t0 + lr;
+  if (t > a.T - 1) t = a.T - 1;
+  const uint16_t* xrow = x + t * d + lk;
+  const uint16_t* wrow[4];
+  bool wok[4];
+  int nblk = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int cb = cg + i * CG;
+    int e = cb * 16 + lr;
+    wok[i] = cb < NB && e < N;
+    wrow[i] = wg + static_cast<int64_t>(wok[i] ? e : 0) * d + lk;
+    if (cb < NB) nblk = i + 1;
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero = {};
+#pragma unroll 2
+  for (int s = s0; s < s1; ++s) {
+    const int k0 = s * 32;
+    bf16x8 av = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < nblk) {
+        bf16x8 bv = wok[i] ? *reinterpret_cast<const bf16x8*>(wrow[i] + k0) : zero;
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+      }
+    }
+  }
+  // acc[i][r] = partial logit of token 4*(lane/16)+r, expert (cg+i*CG)*16 + lane%16
+  const int NP = NB * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < nblk) {
+      int col = (cg + i * CG) * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(ks * TM + (lane >> 4) * 4 + r) * NP + col] = acc[i][r];
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < TM * N; q += 256) {
+    int m = q / N, e = q % N;
+    float v = 0.f;
+    for (int kk = 0; kk < KS; ++kk) v += part[(kk * TM + m) * NP + e];
+    if (a.bias) v += a.bias[e];
+    lt[m * ldl + e] = v;
+  }
+}
+
+// fp32 path: plain dot products, one (token, expert) pair per thread at a time.
+__device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
+  const float* x = static_cast<const float*>(a.x);
+  const float* wg = static_cast<const float*>(a.wg);
+  for (int q = threadIdx.x; q < TM * a.N; q += 256) {
+    int m = q / a.N, e = q % a.N;
+    int64_t t = t0 + m;
+    if (t > a.T - 1) t = a.T - 1;
+    const float* xr = x + t * a.d;
+    const float* wr = wg + static_cast<int64_t>(e) * a.d;
+    float v = 0.f;
+    for (int j = 0; j < a.d; ++j) v = fmaf(xr[j], wr[j], v);
+    if (a.bias) v += a.bias[e];
+    lt[m * ldl + e] = v;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  __shared__ float part[4096];           // d-split partials [KS][TM][NP]
+  __shared__ float lt[TM * (kMaxExperts + 1)];
+  __shared__ float ps[4][kMaxExperts];
+  __shared__ int hl[kMaxExperts];
+  const int ldl = kMaxExperts + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = a.N, k = a.k;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TM;
+
+  for (int e = threadIdx.x; e < kMaxExperts; e += 256) hl[e] = 0;
+  if (BF16) logits_bf16(a, t0, part, lt, ldl);
+  else logits_f32(a, t0, lt, ldl);
+  __syncthreads();
+
+  if (a.logits) {
+    for (int q = threadIdx.x; q < TM * N; q += 256) {
+      int m = q / N, e = q % N;
+      if (t0 + m < a.T) a.logits[(t0 + m) * N + e] = lt[m * ldl + e];
+    }
+  }
+
+  float psr[4] = {0.f, 0.f, 0.f, 0.f};    // this wave's sum of p over its tokens
+  const int G = a.n_groups > 1 ? a.n_groups : 1;
+  const int gsz = N / G;
+  for (int m = wave; m < TM; m += 4) {
+    const int64_t t = t0 + m;
+    if (t >= a.T) break;
+    const float* row = lt + m * ldl;
+    float v[4];
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = lane + 64 * i;
+      ok[i] = e < N;
+      v[i] = ok[i] ? row[e] : -INFINITY;
+    }
+    // full softmax over all N (bias included, no group mask) for p
+    float mx = wave_max_f(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    float z[4], zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = ok[i] ? expf(v[i] - mx) : 0.f;
+      zs += z[i];
+    }
+    zs = wave_sum_f(zs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) psr[i] += z[i] / zs;
+
+    // group limit: lane g scores group g by the sum of its gsk largest logits
+    uint64_t gmask = ~0ull;
+    if (G > 1) {
+      float gs = 0.f;
+      if (lane < G) {
+        float top[kMaxTopK];
+#pragma unroll
+        for (int q = 0; q < kMaxTopK; ++q) top[q] = -INFINITY;
+        for (int e = lane * gsz; e < (lane + 1) * gsz; ++e) {
+          float val = row[e];
+          // insert into the descending list top[0..gsk)
+#pragma unroll
+          for (int q = 0; q < kMaxTopK; ++q) {
+            if (q < a.gsk && val > top[q]) {
+              float tmp = top[q];
+              top[q] = val;
+              val = tmp;
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kMaxTopK; ++q)
+          if (q < a.gsk) gs += top[q];
+      }
+      uint64_t gkey = lane < G ? sel_key(gs, lane) : 0ull;
+      gmask = 0ull;
+      for (int q = 0; q < a.topk_groups; ++q) {
+        uint64_t best = wave_max_u64(gkey);
+        int g = key_index(best);
+        g = g < G ? g : G - 1;
+        gmask |= 1ull << g;
+        if (lane == g) gkey = 0ull;
+      }
+    }
+    // top-k by repeated wave max over (logit, ~index)
+    bool cand[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = lane + 64 * i;
+      cand[i] = ok[i] && ((gmask >> (e / gsz)) & 1ull);
+    }
+    int sel_e[kMaxTopK];
+    float sel_v[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        uint64_t kb = 0ull;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint64_t kk = cand[i] ? sel_key(v[i], lane + 64 * i) : 0ull;
+          kb = kk > kb ? kk : kb;
+        }
+        uint64_t best = wave_max_u64(kb);
+        int e = key_index(best);
+        e = e < N ? e : N - 1;                    // unreachable guard (k <= candidates)
+        sel_e[j] = e;
+        sel_v[j] = row[e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e == lane + 64 * i) cand[i] = false;
+      }
+    }
+    // softmax over the k selected logits, summed in slot order
+    float den = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) den += expf(sel_v[j] - sel_v[0]);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k && lane == j) {
+        a.idx[t * k + j] = sel_e[j];
+        a.w[t * k + j] = expf(sel_v[j] - sel_v[0]) / den;
+        atomicAdd(&hl[sel_e[j]], 1);
+      }
+    }
+  }
+  // per-block partial statistics, combined over waves in wave order
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = lane + 64 * i;
+    if (e < N) ps[wave][e] = psr[i];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256) {
+    float s = ((ps[0][e] + ps[1][e]) + ps[2][e]) + ps[3][e];
+    a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = s;
+    a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void route_finalize_kernel(const float* psum, const int32_t* hist,
+                                                             int nb, int64_t T, int N, int k,
+                                                             int cap, float alpha, int32_t* counts,
+                                                             int32_t* kept, float* p, float* f,
+                                                             float* l_aux) {
+  __shared__ double prod[kMaxExperts];
+  const int e = threadIdx.x;
+  if (e < N) {
+    int64_t c = 0;
+    double s = 0.0;
+    for (int b = 0; b < nb; ++b) {
+      c += hist[static_cast<int64_t>(b) * N + e];
+      s += static_cast<double>(psum[static_cast<int64_t>(b) * N + e]);
+    }
+    double pe = s / static_cast<double>(T);
+    double fe = static_cast<double>(c) / (static_cast<double>(T) * k);
+    counts[e] = static_cast<int32_t>(c);
+    kept[e] = cap > 0 ? static_cast<int32_t>(c < cap ? c : cap) : static_cast<int32_t>(c);
+    if (p) p[e] = static_cast<float>(pe);
+    if (f) f[e] = static_cast<float>(fe);
+    prod[e] = fe * pe;
+  }
+  __syncthreads();
+  if (e == 0 && l_aux) {
+    double acc = 0.0;
+    for (int q = 0; q < N; ++q) acc += prod[q];
+    l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                        int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
+                        hipStream_t st) {
+  RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
+              s.n_groups, s.topk_groups, s.group_score_k};
+  dim3 grid(static_cast<unsigned>(ceil_div(s.T, TM)));
+  if (s.dtype == MOE_BF16)
+    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
+                                 int32_t* counts, int32_t* kept, float* p, float* f,
+                                 float* l_aux, hipStream_t st) {
+  int nb = static_cast<int>(ceil_div(s.T, TM));
+  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(256), 0, st, psum, hist, nb, s.T, s.N,
+                     s.k, s.capacity, s.alpha, counts, kept, p, f, l_aux);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,353 @@
+"""Python binding of the C ABI in include/moe.h (ctypes over libmoe.so).
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity) and their device pointers are passed with the current HIP stream.
+Every step of the layer runs in the library's HIP kernels; there is no other
+code path.  The library must be built (``python -m
+mixture_experts_layer_sparse_amd.build``); importing works without it, but the
+first call raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_ACT_SILU, MOE_ACT_RELU, MOE_ACT_SWIGLU = range(3)
+MOE_DROP_PASSTHROUGH, MOE_DROP_ZERO = range(2)
+
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+_ACT = {"silu": MOE_ACT_SILU, "relu": MOE_ACT_RELU, "swiglu": MOE_ACT_SWIGLU}
+_DROP = {"passthrough": MOE_DROP_PASSTHROUGH, "zero": MOE_DROP_ZERO}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``moe_shape``."""
+    _fields_ = [("T", c_int64), ("d", c_int32), ("N", c_int32), ("k", c_int32), ("F", c_int32),
+                ("capacity", c_int32), ("n_groups", c_int32), ("topk_groups", c_int32),
+                ("group_score_k", c_int32), ("has_shared", c_int32), ("dtype", c_int32),
+                ("buf_dtype", c_int32), ("act", c_int32), ("drop", c_int32), ("alpha", c_float)]
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == MOE_BF16 else torch.float32
+
+    @property
+    def buf_torch_dtype(self) -> torch.dtype:
+        if self.buf_dtype == MOE_FP8_E4M3:
+            return torch.uint8
+        return self.torch_dtype
+
+    def replace(self, **kw) -> "Shape":
+        s = Shape()
+        ctypes.pointer(s)[0] = self
+        for key, val in kw.items():
+            setattr(s, key, val)
+        return s
+
+
+def make_shape(T, d, N, k, F, act="swiglu", dtype="bf16", buf=None, capacity=0,
+               drop="passthrough", n_groups=0, topk_groups=0, group_score_k=2, shared=False,
+               alpha=0.01) -> Shape:
+    return Shape(T=T, d=d, N=N, k=k, F=F, capacity=capacity, n_groups=n_groups,
+                 topk_groups=topk_groups, group_score_k=group_score_k,
+                 has_shared=1 if shared else 0, dtype=_DT[dtype], buf_dtype=_DT[buf or dtype],
+                 act=_ACT[act], drop=_DROP[drop], alpha=alpha)
+
+
+def shape_of(wl) -> Shape:
+    """Shape from any object with the workload attributes (T, d, N, k, F, act,
+    dtype, buf, capacity, drop, n_groups, topk_groups, group_score_k, shared, alpha)."""
+    return make_shape(wl.T, wl.d, wl.N, wl.k, wl.F, act=wl.act, dtype=wl.dtype, buf=wl.buf,
+                      capacity=wl.capacity, drop=wl.drop, n_groups=wl.n_groups,
+                      topk_groups=wl.topk_groups, group_score_k=wl.group_score_k,
+                      shared=wl.shared, alpha=wl.alpha)
+
+
+_lib = None
+_P = c_void_p
+_SIGS = {
+    "moe_workspace_bytes": (c_size_t, [POINTER(Shape)]),
+    "moe_check_shape": (c_int32, [POINTER(Shape)]),
+    "moe_route": (c_int32, [POINTER(Shape)] + [_P] * 11 + [_P, c_size_t, _P]),
+    "moe_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 8 + [_P, c_size_t, _P]),
+    "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
+    "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P]),
+    "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
+    "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
+    "moe_combine": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
+    "moe_forward": (c_int32, [POINTER(Shape)] + [_P] * 25 + [_P, c_size_t, _P]),
+    "moe_status_string": (ctypes.c_char_p, [c_int32]),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_sparse_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().moe_status_string(st).decode()
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != MOE_OK:
+        raise MoeError(name, st)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(t: torch.Tensor | None, name: str, shape: tuple, dtype: torch.dtype,
+           required: bool = True) -> None:
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(s: Shape) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(s)))
+
+
+def check_shape(s: Shape) -> int:
+    return int(lib().moe_check_shape(ctypes.byref(s)))
+
+
+def alloc_workspace(s: Shape, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(s)
+    if n == 0:
+        raise MoeError("moe_workspace_bytes", check_shape(s) or MOE_ERR_ARG)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ calls --
+
+def route(s: Shape, x, wg, bias=None, ws=None, logits=False, out=None) -> dict:
+    T, N, k = s.T, s.N, s.k
+    dev = x.device
+    _check(x, "x", (T, s.d), s.torch_dtype)
+    _check(wg, "wg", (N, s.d), s.torch_dtype)
+    _check(bias, "bias", (N,), torch.float32, required=False)
+    o = out if out is not None else {
+        "idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "counts": torch.empty(N, dtype=torch.int32, device=dev),
+        "kept_counts": torch.empty(N, dtype=torch.int32, device=dev),
+        "p": torch.empty(N, dtype=torch.float32, device=dev),
+        "f": torch.empty(N, dtype=torch.float32, device=dev),
+        "l_aux": torch.empty(1, dtype=torch.float32, device=dev),
+    }
+    if logits and "logits" not in o:
+        o["logits"] = torch.empty((T, N), dtype=torch.float32, device=dev)
+    ws = ws if ws is not None else alloc_workspace(s, dev)
+    _call("moe_route", ctypes.byref(s), _ptr(x), _ptr(wg), _ptr(bias), _ptr(o["idx"]),
+          _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["kept_counts"]), _ptr(o.get("p")),
+          _ptr(o.get("f")), _ptr(o.get("l_aux")), _ptr(o.get("logits")), _ptr(ws), ws.numel(),
+          _stream())
+    return o
+
+
+def dispatch(s: Shape, x, idx, ws=None, out=None) -> dict:
+    T, N, k, d = s.T, s.N, s.k, s.d
+    dev = x.device
+    _check(x, "x", (T, d), s.torch_dtype)
+    _check(idx, "idx", (T, k), torch.int32)
+    fp8 = s.buf_dtype == MOE_FP8_E4M3
+    o = out if out is not None else {
+        "offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+        "pos": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "src": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "drop": torch.empty((T, k), dtype=torch.uint8, device=dev),
+        "x_perm": torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=dev),
+        "row_scale": torch.empty(T * k, dtype=torch.float32, device=dev) if fp8 else None,
+    }
+    ws = ws if ws is not None else alloc_workspace(s, dev)
+    _call("moe_dispatch", ctypes.byref(s), _ptr(x), _ptr(idx), _ptr(o["offsets"]), _ptr(o["pos"]),
+          _ptr(o["src"]), _ptr(o["drop"]), _ptr(o["x_perm"]), _ptr(o.get("row_scale")), _ptr(ws),
+          ws.numel(), _stream())
+    return o
+
+
+def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None):
+    R, F = s.T * s.k, s.F
+    _check(x_perm, "x_perm", (R, s.d), s.buf_torch_dtype)
+    _check(offsets, "offsets", (s.N + 1,), torch.int32)
+    _check(w1, "w1", (s.N, F, s.d), s.torch_dtype)
+    _check(w3, "w3", (s.N, F, s.d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
+    if h is None:
+        h = torch.empty((R, F), dtype=s.torch_dtype, device=x_perm.device)
+    _call("moe_expert_up", ctypes.byref(s), _ptr(x_perm), _ptr(row_scale), _ptr(offsets), _ptr(w1),
+          _ptr(w3), _ptr(h), _stream())
+    return h
+
+
+def expert_down(s: Shape, h, offsets, w2, out=None):
+    R = s.T * s.k
+    _check(h, "h", (R, s.F), s.torch_dtype)
+    _check(w2, "w2", (s.N, s.d, s.F), s.torch_dtype)
+    if out is None:
+        out = torch.empty((R, s.d), dtype=s.torch_dtype, device=h.device)
+    _call("moe_expert_down", ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(out), _stream())
+    return out
+
+
+def shared_expert(s: Shape, x, ws1, ws3, ws2, h_shared=None, out_shared=None):
+    T, d, F = s.T, s.d, s.F
+    _check(ws1, "ws1", (F, d), s.torch_dtype)
+    _check(ws3, "ws3", (F, d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
+    _check(ws2, "ws2", (d, F), s.torch_dtype)
+    if h_shared is None:
+        h_shared = torch.empty((T, F), dtype=s.torch_dtype, device=x.device)
+    if out_shared is None:
+        out_shared = torch.empty((T, d), dtype=s.torch_dtype, device=x.device)
+    _call("moe_shared_expert", ctypes.byref(s), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(ws2),
+          _ptr(h_shared), _ptr(out_shared), _stream())
+    return out_shared
+
+
+def experts(s: Shape, x_perm, row_scale, offsets, w1, w3, w2, x=None, ws1=None, ws3=None,
+            ws2=None, ws=None, out=None, out_shared=None):
+    R, d = s.T * s.k, s.d
+    dev = x_perm.device
+    if out is None:
+        out = torch.empty((R, d), dtype=s.torch_dtype, device=dev)
+    if s.has_shared and out_shared is None:
+        out_shared = torch.empty((s.T, d), dtype=s.torch_dtype, device=dev)
+    ws = ws if ws is not None else alloc_workspace(s, dev)
+    _call("moe_experts", ctypes.byref(s), _ptr(x_perm), _ptr(row_scale), _ptr(offsets), _ptr(w1),
+          _ptr(w3), _ptr(w2), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out),
+          _ptr(out_shared), _ptr(ws), ws.numel(), _stream())
+    return out, out_shared
+
+
+def combine(s: Shape, out, out_shared, x, pos, w, y=None):
+    T, d = s.T, s.d
+    _check(out, "out", (T * s.k, d), s.torch_dtype)
+    _check(out_shared, "out_shared", (T, d), s.torch_dtype, required=bool(s.has_shared))
+    _check(pos, "pos", (T, s.k), torch.int32)
+    _check(w, "w", (T, s.k), torch.float32)
+    if y is None:
+        y = torch.empty((T, d), dtype=s.torch_dtype, device=x.device)
+    _call("moe_combine", ctypes.byref(s), _ptr(out), _ptr(out_shared), _ptr(x), _ptr(pos), _ptr(w),
+          _ptr(y), _stream())
+    return y
+
+
+class Layer:
+    """One MoE layer with every output and scratch buffer allocated once, so
+    that ``forward()`` only enqueues the library's kernels (what a timed loop or
+    a captured graph needs).  Buffers are exposed as attributes."""
+
+    def __init__(self, s: Shape, wg, w1, w3, w2, bias=None, ws1=None, ws3=None, ws2=None,
+                 device="cuda"):
+        st = check_shape(s)
+        if st != MOE_OK:
+            raise MoeError("moe_check_shape", st)
+        self.s = s
+        T, N, k, d, F = s.T, s.N, s.k, s.d, s.F
+        dt = s.torch_dtype
+        _check(wg, "wg", (N, d), dt)
+        _check(w1, "w1", (N, F, d), dt)
+        _check(w3, "w3", (N, F, d), dt, required=s.act == MOE_ACT_SWIGLU)
+        _check(w2, "w2", (N, d, F), dt)
+        _check(bias, "bias", (N,), torch.float32, required=False)
+        if s.has_shared:
+            _check(ws1, "ws1", (F, d), dt)
+            _check(ws3, "ws3", (F, d), dt, required=s.act == MOE_ACT_SWIGLU)
+            _check(ws2, "ws2", (d, F), dt)
+        self.wg, self.w1, self.w3, self.w2, self.bias = wg, w1, w3, w2, bias
+        self.ws1, self.ws3, self.ws2 = ws1, ws3, ws2
+        e = dict(dtype=torch.int32, device=device)
+        f = dict(dtype=torch.float32, device=device)
+        self.idx = torch.empty((T, k), **e)
+        self.w = torch.empty((T, k), **f)
+        self.counts = torch.empty(N, **e)
+        self.kept_counts = torch.empty(N, **e)
+        self.p = torch.empty(N, **f)
+        self.f = torch.empty(N, **f)
+        self.l_aux = torch.empty(1, **f)
+        self.offsets = torch.empty(N + 1, **e)
+        self.pos = torch.empty((T, k), **e)
+        self.src = torch.empty(T * k, **e)
+        self.drop = torch.empty((T, k), dtype=torch.uint8, device=device)
+        self.x_perm = torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=device)
+        self.row_scale = torch.empty(T * k, **f) if s.buf_dtype == MOE_FP8_E4M3 else None
+        self.out = torch.empty((T * k, d), dtype=dt, device=device)
+        self.out_shared = torch.empty((T, d), dtype=dt, device=device) if s.has_shared else None
+        self.y = torch.empty((T, d), dtype=dt, device=device)
+        self.ws = alloc_workspace(s, device)
+
+    def forward(self, x) -> torch.Tensor:
+        s = self.s
+        _check(x, "x", (s.T, s.d), s.torch_dtype)
+        _call("moe_forward", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias),
+              _ptr(self.w1), _ptr(self.w3), _ptr(self.w2), _ptr(self.ws1), _ptr(self.ws3),
+              _ptr(self.ws2), _ptr(self.idx), _ptr(self.w), _ptr(self.counts),
+              _ptr(self.kept_counts), _ptr(self.p), _ptr(self.f), _ptr(self.l_aux),
+              _ptr(self.offsets), _ptr(self.pos), _ptr(self.src), _ptr(self.drop),
+              _ptr(self.x_perm), _ptr(self.row_scale), _ptr(self.out), _ptr(self.out_shared),
+              _ptr(self.y), _ptr(self.ws), self.ws.numel(), _stream())
+        return self.y
+
+    # the four phases separately (same kernels as forward)
+    def route(self, x):
+        s = self.s
+        _call("moe_route", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias), _ptr(self.idx),
+              _ptr(self.w), _ptr(self.counts), _ptr(self.kept_counts), _ptr(self.p), _ptr(self.f),
+              _ptr(self.l_aux), None, _ptr(self.ws), self.ws.numel(), _stream())
+
+    def dispatch(self, x):
+        s = self.s
+        _call("moe_dispatch", ctypes.byref(s), _ptr(x), _ptr(self.idx), _ptr(self.offsets),
+              _ptr(self.pos), _ptr(self.src), _ptr(self.drop), _ptr(self.x_perm),
+              _ptr(self.row_scale), _ptr(self.ws), self.ws.numel(), _stream())
+
+    def experts(self, x):
+        s = self.s
+        _call("moe_experts", ctypes.byref(s), _ptr(self.x_perm), _ptr(self.row_scale),
+              _ptr(self.offsets), _ptr(self.w1), _ptr(self.w3), _ptr(self.w2), _ptr(x),
+              _ptr(self.ws1), _ptr(self.ws3), _ptr(self.ws2), _ptr(self.out),
+              _ptr(self.out_shared), _ptr(self.ws), self.ws.numel(), _stream())
+
+    def combine(self, x):
+        s = self.s
+        _call("moe_combine", ctypes.byref(s), _ptr(self.out), _ptr(self.out_shared), _ptr(x),
+              _ptr(self.pos), _ptr(self.w), _ptr(self.y), _stream())

@@ -32,8 +32,8 @@ the design notes):
   * a router bias, when present, is added to the logits before every use;
   * the shared expert runs on the unquantised input with weight 1;
   * fp8 dispatch: per token, amax = max|x|, inv = fl32(448 / amax),
-    code = e4m3(fl32(x * inv)), scale = fl32(amax / 448); amax = 0 gives
-    inv = scale = 1.
+    code = e4m3(fl32(x * inv)), scale = fl32(amax / 448); amax < 2^-100
+    (zero included) gives inv = scale = 1, so every code is +-0.
 """
 from __future__ import annotations
 
@@ -164,12 +164,15 @@ def quantize_fp8_rows(x_bits_or_vals: np.ndarray, dtype: str) -> tuple:
     example on bytes per token: FP8 before dispatch, s = 1).  The scale is one
     float32 per token; every step is float32 arithmetic on the stored values:
     amax = max|x| (exact), inv = fl32(448/amax), code = e4m3(fl32(x*inv)),
-    scale = fl32(amax/448).  Returns (codes uint8 [T][d], scale float32 [T])."""
+    scale = fl32(amax/448); a row with amax < 2^-100 gets inv = scale = 1.
+    Returns (codes uint8 [T][d], scale float32 [T])."""
     xv = f32(as_f64(x_bits_or_vals, dtype))
     T = xv.shape[0]
     amax = np.abs(xv).max(axis=1) if xv.shape[1] else np.zeros(T, np.float32)
     amax = f32(amax)
-    zero = amax == 0
+    # a row whose largest magnitude is below 2^-100 (zero included) is treated
+    # as a zero row: 448/amax would overflow float32 below about 1.3e-36
+    zero = amax < np.float32(2.0 ** -100)
     safe = np.where(zero, np.float32(1), amax)
     inv = np.where(zero, np.float32(1), f32(np.float32(E4M3_MAX) / safe))
     scale = np.where(zero, np.float32(1), f32(safe / np.float32(E4M3_MAX)))

@@ -1,0 +1,133 @@
+"""Helpers shared by the GPU parity tests: upload the seeded inputs, run the
+HIP path through the binding (C ABI), and compare every output with the
+oracle under the acceptance rules:
+
+  * routing (idx), counts, kept counts, offsets, pos, src, drop: bit-exact
+    after tie-band adoption (tokens whose k-th/(k+1)-th logits differ by at most
+    1e-5 * max|l| may be routed either way; see oracle.compare);
+  * the dispatch buffer: bit-exact (a copy, or fp8 codes and scales that both
+    sides compute with the same float32 operations);
+  * w, p, f, L_aux (float32): relative L2 <= 1e-5;
+  * y: relative L2 <= 1e-5 for float32 layers, <= 2e-2 for bf16 layers,
+    against the float64 oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synthetic_inputs as si
+from mixture_experts_layer_sparse_amd import moe as M
+from oracle import compare, moe as om
+from oracle.numerics import e4m3_decode
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def dev(arr, dtype: str | None = None):
+    """numpy array -> device tensor (uint16 bf16 bits -> torch.bfloat16)."""
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def host(t):
+    if t is None:
+        return None
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bf16_bits_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def as_values(arr, dtype):
+    return bf16_bits_to_f64(arr) if dtype == "bf16" else np.asarray(arr, np.float64)
+
+
+def upload(wl, inp):
+    d = {k: dev(v) for k, v in inp.items() if v is not None}
+    return d
+
+
+def run_gpu(wl, inp, logits=True):
+    """Run the four phases through the C ABI; returns host copies of everything."""
+    s = M.shape_of(wl)
+    g = upload(wl, inp)
+    ws = M.alloc_workspace(s)
+    r = M.route(s, g["x"], g["wg"], g.get("bias"), ws=ws, logits=logits)
+    dsp = M.dispatch(s, g["x"], r["idx"], ws=ws)
+    out, out_shared = M.experts(s, dsp["x_perm"], dsp["row_scale"], dsp["offsets"], g["w1"],
+                                g.get("w3"), g["w2"], x=g["x"], ws1=g.get("ws1"),
+                                ws3=g.get("ws3"), ws2=g.get("ws2"), ws=ws)
+    y = M.combine(s, out, out_shared, g["x"], dsp["pos"], r["w"])
+    torch.cuda.synchronize()
+    res = {k: host(v) for k, v in r.items()}
+    res.update({k: host(v) for k, v in dsp.items()})
+    res["out"] = host(out)
+    res["out_shared"] = host(out_shared)
+    res["y"] = host(y)
+    return res
+
+
+def check_layer(wl, inp, gpu, y_tokens=None, max_adopted=None):
+    """Compare a GPU run with the oracle; returns a dict of measured errors."""
+    from oracle.numerics import as_f64
+    r0 = om.route(wl, as_f64(inp["x"], wl.dtype), as_f64(inp["wg"], wl.dtype), inp.get("bias"))
+    ad = compare.adopt(wl, r0["logits"], r0["idx"], gpu["idx"])
+    assert ad["bad"] == [], f"{wl.name}: non-admissible routing at tokens {ad['bad'][:10]}"
+    if max_adopted is not None:
+        assert len(ad["adopted"]) <= max_adopted, f"{wl.name}: {len(ad['adopted'])} tokens adopted"
+    routed = {"idx": ad["idx"], "w": ad["w"]}
+    full = om.forward(wl, inp, ffn_tokens=y_tokens, routed=routed)
+    errs = {"adopted": len(ad["adopted"])}
+    assert np.array_equal(gpu["idx"], full["idx"]), "idx"
+    errs["w"] = compare.rel_l2(gpu["w"], full["w"])
+    assert errs["w"] <= TOL_F32, errs
+    assert np.array_equal(gpu["counts"], full["counts"]), "counts"
+    assert np.array_equal(gpu["kept_counts"], full["kept_counts"]), "kept_counts"
+    errs["p"] = compare.rel_l2(gpu["p"], full["p"])
+    errs["f"] = compare.rel_l2(gpu["f"], full["f"])
+    errs["l_aux"] = abs(float(gpu["l_aux"][0]) - full["l_aux"]) / max(abs(full["l_aux"]), 1e-30)
+    assert errs["p"] <= TOL_F32 and errs["f"] <= TOL_F32 and errs["l_aux"] <= TOL_F32, errs
+    if "logits" in gpu and gpu["logits"] is not None:
+        errs["logits"] = compare.rel_l2(gpu["logits"], full["logits"])
+        assert errs["logits"] <= TOL_F32, errs
+    # dispatch plan: bit-exact
+    R = int(full["offsets"][-1])
+    assert np.array_equal(gpu["offsets"], full["offsets"]), "offsets"
+    assert np.array_equal(gpu["pos"], full["pos"]), "pos"
+    assert np.array_equal(gpu["src"][:R], full["src"]), "src"
+    assert np.array_equal(gpu["drop"].astype(bool), full["drop"]), "drop"
+    # dispatch buffer: bit-exact
+    if wl.buf == "fp8":
+        assert np.array_equal(gpu["x_perm"][:R], full["xperm"]), "fp8 codes"
+        assert np.array_equal(gpu["row_scale"][:R], full["row_scale"]), "fp8 scales"
+    else:
+        assert np.array_equal(gpu["x_perm"][:R], full["xperm"]), "x_perm"
+    # expert outputs and y
+    tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16
+    toks = full["y_tokens"]
+    rows = full["pos"][toks]
+    rows = rows[rows >= 0]
+    if rows.size:
+        errs["out"] = compare.rel_l2(as_values(gpu["out"][rows], wl.dtype), full["o_rows"][rows])
+        assert errs["out"] <= tol, errs
+    if wl.shared:
+        errs["shared"] = compare.rel_l2(as_values(gpu["out_shared"][toks], wl.dtype), full["shared"])
+        assert errs["shared"] <= tol, errs
+    errs["y"] = compare.rel_l2(as_values(gpu["y"][toks], wl.dtype), full["y"])
+    assert errs["y"] <= tol, errs
+    return errs
+
+
+def sample_tokens(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(T, size=min(n, T), replace=False)
+    return np.unique(np.concatenate([pick, [0, T - 1]]))

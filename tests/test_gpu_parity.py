@@ -1,0 +1,163 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small cases span several tiles of every kernel with ragged tails; full-size
+cases run the workloads at their real shapes (all of routing, the plan and the
+dispatch buffer compared; y on sampled tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic_inputs as si
+from mixture_experts_layer_sparse_amd import moe as M
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from moe_gpu_util import check_layer, run_gpu, sample_tokens
+
+
+def _run_and_check(wl, inp=None, y_tokens=None, max_adopted=None):
+    print(f"case {wl.name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} F={wl.F}", flush=True)
+    inp = inp if inp is not None else si.generate(wl)
+    gpu = run_gpu(wl, inp)
+    errs = check_layer(wl, inp, gpu, y_tokens=y_tokens, max_adopted=max_adopted)
+    print(f"  {errs}", flush=True)
+    return gpu, errs
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "switch", "deepseek_v3", "dbrx"])
+def test_small_parity(name):
+    wl = si.WORKLOADS["tiny"] if name == "tiny" else si.small(name)
+    _run_and_check(wl, max_adopted=2)
+
+
+def test_tiny_full_config_f32_tolerance():
+    gpu, errs = _run_and_check(si.WORKLOADS["tiny"], max_adopted=0)
+    assert errs["y"] <= 1e-5
+
+
+# ------------------------------------------------------------- edge cases --
+
+def test_single_token():
+    _run_and_check(si.small("mixtral", T=1))
+
+
+def test_t_zero_is_noop():
+    wl = si.small("mixtral", T=0)
+    s = M.shape_of(wl)
+    x = torch.empty((0, wl.d), dtype=torch.bfloat16, device="cuda")
+    wg = torch.zeros((wl.N, wl.d), dtype=torch.bfloat16, device="cuda")
+    r = M.route(s, x, wg, ws=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert r["idx"].shape == (0, wl.k)
+
+
+def test_all_tokens_one_expert_and_empty_segments():
+    """A large bias sends every token to expert 3 first: one huge segment,
+    several empty ones; with a capacity the overflow is dropped."""
+    wl = si.small("switch", T=700, N=16, k=2, capacity=0)
+    inp = si.generate(wl)
+    b = np.zeros(wl.N, np.float32)
+    b[3] = 50.0
+    b[5] = 40.0
+    inp["bias"] = b
+    _run_and_check(wl, inp)
+    wlc = wl.replace(capacity=100)
+    gpu, _ = _run_and_check(wlc, inp)
+    assert gpu["drop"].sum() == 2 * (700 - 100)
+
+
+def test_exact_ties_go_to_lower_index():
+    """Duplicated router rows give bit-identical logits: the lower expert wins."""
+    wl = si.small("mixtral", T=300, N=8, k=2)
+    inp = si.generate(wl)
+    wg = inp["wg"].copy()
+    wg[5] = wg[1]
+    wg[6] = wg[2]
+    inp["wg"] = wg
+    gpu, _ = _run_and_check(wl, inp, max_adopted=0)
+    assert not np.any(gpu["idx"] == 5) or np.all(np.any(gpu["idx"] == 1, axis=1)[np.any(gpu["idx"] == 5, axis=1)])
+    for t in range(wl.T):
+        sel = list(gpu["idx"][t])
+        if 5 in sel:
+            assert 1 in sel and sel.index(1) < sel.index(5)
+        if 6 in sel:
+            assert 2 in sel and sel.index(2) < sel.index(6)
+
+
+def test_zero_rows_and_k_equals_n():
+    wl = si.Workload("kN", T=130, d=128, N=4, k=4, F=128, act="swiglu", dtype="bf16", buf="fp8")
+    inp = si.generate(wl)
+    x = inp["x"].copy()
+    x[7] = 0
+    x[64] = 0x8000      # -0.0 everywhere
+    inp["x"] = x
+    gpu, _ = _run_and_check(wl, inp)
+    assert np.all(gpu["row_scale"][gpu["pos"][7]] == 1.0)
+
+
+def test_capacity_one_and_drop_zero():
+    wl = si.small("switch", T=400, N=8, k=2, capacity=1, drop="zero")
+    gpu, _ = _run_and_check(wl)
+    assert gpu["offsets"][-1] == 8
+
+
+def test_groups_k_le_group_span():
+    wl = si.small("deepseek_v3", T=333, N=32, k=3, n_groups=4, topk_groups=1, F=128)
+    _run_and_check(wl)
+
+
+def test_fp8_quantiser_exhaustive_bf16_patterns():
+    """Every finite bf16 pattern goes through the fp8 dispatch quantiser at
+    four relative scales: rows of 255 neighbouring patterns plus one anchor
+    element A times the row's largest magnitude (A = 1, 2^6, 2^12, 2^19), so
+    each pattern lands near the top, the middle, the subnormal range and below
+    the smallest code.  Codes and scales must equal the oracle's bit for bit
+    (rows below 2^-100 are zero rows on both sides)."""
+    from moe_gpu_util import dev, host
+    from oracle import moe as om
+    from oracle.numerics import bf16_to_f64
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits.astype(np.uint32) >> 7) & 0xFF) != 0xFF
+    vals = bits[finite]
+    vals = np.concatenate([vals, np.zeros((-vals.size) % 255, np.uint16)]).reshape(-1, 255)
+    mags = np.abs(bf16_to_f64(vals)).max(axis=1)
+    rows = []
+    for A in (1.0, 2.0 ** 6, 2.0 ** 12, 2.0 ** 19):
+        anchor = mags * A
+        ok = anchor < 3.3e38
+        a_bits = si.f32_to_bf16_bits(anchor[ok].astype(np.float32))
+        assert np.array_equal(bf16_to_f64(a_bits), anchor[ok])       # exact anchors
+        rows.append(np.concatenate([vals[ok], a_bits[:, None]], axis=1))
+    x = np.concatenate(rows)
+    x = np.concatenate([x, np.zeros((x.shape[0], 1), np.uint16)], axis=1)   # d = 256
+    T, d = x.shape
+    wl = si.Workload("q", T=T, d=d, N=4, k=1, F=64, act="swiglu", dtype="bf16", buf="fp8")
+    s = M.shape_of(wl)
+    idx = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+    dsp = M.dispatch(s, dev(x), idx)
+    torch.cuda.synchronize()
+    codes, scale = om.quantize_fp8_rows(x, "bf16")
+    got_c, got_s = host(dsp["x_perm"]), host(dsp["row_scale"])
+    bad = np.flatnonzero(np.any(got_c != codes, axis=1))
+    assert bad.size == 0, (bad[:5], x[bad[0]][:8], got_c[bad[0]][:8], codes[bad[0]][:8])
+    assert np.array_equal(got_s, scale)
+
+
+def test_determinism_bitwise():
+    wl = si.small("deepseek_v3")
+    inp = si.generate(wl)
+    a = run_gpu(wl, inp)
+    b = run_gpu(wl, inp)
+    for key in a:
+        if a[key] is not None:
+            assert np.array_equal(a[key], b[key]), key
+
+
+# -------------------------------------------------------------- full sizes --
+
+@pytest.mark.parametrize("name", ["mixtral", "switch", "deepseek_v3", "dbrx"])
+def test_full_size_parity(name):
+    wl = si.WORKLOADS[name]
+    inp = si.generate(wl)
+    toks = sample_tokens(wl.T, 40)
+    _run_and_check(wl, inp, y_tokens=toks)

@@ -176,6 +176,10 @@ def test_fp8_quantiser_definition():
     assert scale[1] == 1.0 and np.array_equal(codes[1], np.array([0, 0, 0x80, 0], np.uint8))
     # the row maximum always maps to the largest code
     assert codes[0, 3] == 0x7E and codes[2, 2] == 0xFE
+    # a row below 2^-100 is a zero row: scale 1, every code +-0
+    tiny = np.array([[1e-35, -2e-36, 0.0, 1e-38]], np.float32)
+    c, sc = moe.quantize_fp8_rows(tiny, "f32")
+    assert sc[0] == 1.0 and c.tolist() == [[0x00, 0x80, 0x00, 0x00]]
     # dequantised error within half an e4m3 step (relative 2^-4) of the row max scale
     dq = e4m3_decode(codes) * scale[:, None]
     assert np.all(np.abs(dq - x) <= np.abs(x) * 2.0 ** -4 + scale[:, None] * 2.0 ** -9)
