@@ -1,0 +1,215 @@
+"""Benchmark of the sparse MoE-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+                    [--no-cpu-baseline] [--mode bench|copy]
+
+One step = one whole layer forward (route, dispatch, grouped GEMM up, grouped
+GEMM down, shared expert if any, combine) over one batch of seeded synthetic
+inputs already resident in HBM.  The timed region is bracketed by
+torch.cuda.synchronize() on both sides; inside it, HIP events on the launch
+stream separate the phases, so each kernel's average duration is measured on
+the same launches that are timed.
+
+Prints one JSON line: tokens/s (whole job), ms per step, per-phase times, the
+dominant kernel's roofline (grouped GEMM up: algorithmic FLOPs per launch /
+its measured duration, against the bf16 dense MFMA peak), the dispatch and
+memory-phase bandwidths, and the float64 CPU oracle timed on a bounded sample.
+
+--mode copy runs a plain device copy of a known size (the calibration kernel
+for the hardware byte counters) and exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at Mixtral shape; grouped-GEMM % MFMA peak; dispatch GB/s"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
+    return ap.parse_args()
+
+
+def alg_bytes(wl, R):
+    """Algorithmic (minimum) HBM bytes of the memory phases; R kept rows."""
+    sx = 2 if wl.dtype == "bf16" else 4
+    sb = 1 if wl.buf == "fp8" else sx
+    T, d, N, k = wl.T, wl.d, wl.N, wl.k
+    route = T * d * sx + N * d * sx + 8 * T * k + 4 * N
+    dispatch = T * d * sx + R * d * sb + (4 * R if wl.buf == "fp8" else 0) + 8 * T * k + 4 * R
+    combine = R * d * sx + T * d * sx + (T * d * sx if wl.shared else 0) + 8 * T * k
+    return route, dispatch, combine
+
+
+def gemm_flops(wl, R):
+    m = 2 if wl.act == "swiglu" else 1
+    up = 2 * R * wl.d * wl.F * m
+    down = 2 * R * wl.F * wl.d
+    shared = (2 * wl.T * wl.d * wl.F * (m + 1)) if wl.shared else 0
+    return up, down, shared
+
+
+def cpu_baseline(wl, inp, n_tok):
+    """The float64 oracle as it stands, on a bounded sample: routing, statistics
+    and the dispatch plan for all T tokens, the expert FFNs and combine for
+    ``n_tok`` sampled tokens.  Returns a tokens/s figure for the whole layer:
+    1 / (routing time per token + FFN time per sampled token)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import moe as om
+    toks = np.linspace(0, wl.T - 1, n_tok).astype(np.int64)
+    t0 = time.perf_counter()
+    om.forward(wl, {**inp, "w1": None})
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    om.forward(wl, inp, ffn_tokens=toks)
+    t_all = time.perf_counter() - t0
+    t_ffn = max(t_all - t_route, 1e-9)
+    per_tok = t_route / wl.T + t_ffn / n_tok
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"routing + plan for all {wl.T} tokens ({t_route:.2f} s); expert FFNs + "
+                      f"combine for {n_tok} evenly spaced tokens ({t_ffn:.2f} s); float64 NumPy"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synthetic_inputs as si
+    from mixture_experts_layer_sparse_amd import moe as M
+
+    torch.cuda.set_device(0)
+    if a.mode == "copy":
+        n = 1 << 28                         # 256 MiB
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 10}))
+        return
+
+    wl = si.WORKLOADS[a.workload]
+    inp = si.generate(wl)
+
+    def dev(arr):
+        if arr is None:
+            return None
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+    g = {k: dev(v) for k, v in inp.items()}
+    s = M.shape_of(wl)
+    L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
+                ws3=g["ws3"], ws2=g["ws2"])
+    x = g["x"]
+    dt = s.torch_dtype
+    h = torch.empty((wl.T * wl.k, wl.F), dtype=dt, device="cuda")
+    hs = torch.empty((wl.T, wl.F), dtype=dt, device="cuda") if wl.shared else None
+
+    def step(ev=None):
+        # the same kernels as moe_forward, phase by phase
+        L.route(x)
+        ev and ev[0].record()
+        L.dispatch(x)
+        ev and ev[1].record()
+        M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h)
+        ev and ev[2].record()
+        M.expert_down(s, h, L.offsets, L.w2, L.out)
+        ev and ev[3].record()
+        if wl.shared:
+            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
+        ev and ev[4].record()
+        L.combine(x)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    E = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        E[i][5].record()
+        step(E[i])
+        E[i][6].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = {"route": [], "dispatch": [], "gemm_up": [], "gemm_down": [], "shared": [], "combine": []}
+    for e in E:
+        ph["route"].append(e[5].elapsed_time(e[0]))
+        ph["dispatch"].append(e[0].elapsed_time(e[1]))
+        ph["gemm_up"].append(e[1].elapsed_time(e[2]))
+        ph["gemm_down"].append(e[2].elapsed_time(e[3]))
+        ph["shared"].append(e[3].elapsed_time(e[4]))
+        ph["combine"].append(e[4].elapsed_time(e[6]))
+    ph_ms = {k: float(np.mean(v)) for k, v in ph.items()}
+    ms = wall * 1e3 / a.steps
+    R = int(L.offsets[-1].item())
+
+    # the same result as the fused entry point
+    y_split = L.y.clone()
+    L.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_split, L.y), "phase-by-phase and moe_forward results differ"
+
+    up, down, shared = gemm_flops(wl, R)
+    rb, db, cb = alg_bytes(wl, R)
+    t_up = ph_ms["gemm_up"] * 1e-3
+    achieved = up / t_up / 1e12
+    gemm_t = (ph_ms["gemm_up"] + ph_ms["gemm_down"] + ph_ms["shared"]) * 1e-3
+    mem_t = (ph_ms["route"] + ph_ms["dispatch"] + ph_ms["combine"]) * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": wl.T * a.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "N": wl.N, "k": wl.k, "F": wl.F,
+                   "act": wl.act, "dispatch_buffer": wl.buf, "capacity": wl.capacity,
+                   "groups": [wl.n_groups, wl.topk_groups], "shared_expert": wl.shared,
+                   "kept_rows": R},
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM up (gate/up + activation)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "grouped_gemm_pct_mfma_peak": 100.0 * (up + down + shared) / gemm_t / 1e12 / PEAK_BF16_TFLOPS,
+        "dispatch_GBps": db / (ph_ms["dispatch"] * 1e-3) / 1e9,
+        "memory_phases": {"bytes": rb + db + cb, "us": mem_t * 1e6,
+                          "GBps": (rb + db + cb) / mem_t / 1e9,
+                          "frac_hbm": (rb + db + cb) / mem_t / 1e9 / PEAK_HBM_GBPS},
+        "phases_us": {k: v * 1e3 for k, v in ph_ms.items()},
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

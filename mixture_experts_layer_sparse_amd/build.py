@@ -48,6 +48,12 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every kernel launched from host code needs its host-side stub: a device-only
+    # construct in a kernel body can make the host pass drop it silently
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel stubs missing from the host code:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -54,8 +54,6 @@ struct GemmArgs {
 
 constexpr int GM = 4;      // m-tiles sharing one n-tile in the tile order
 
-__device__ __forceinline__ int swz(int row) { return row & 7; }
-
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
 
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
@@ -73,32 +71,60 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from a buffer straight into LDS (lane i writes lds + 16*i).
+// Kept in a device function: the host compilation pass only needs the kernel stub.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                          uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)lds, 16, voff, soff, 0, 0);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
+}
+
+// 16-byte chunk swizzle inside a 128-byte LDS row (bf16 rows of 64 elements).
+__device__ __forceinline__ int swz128(int row) { return row & 7; }
+// inside a 64-byte LDS row (fp8 rows of 64 codes): 4 chunks
+__device__ __forceinline__ int swz64(int row) { return (row >> 1) & 3; }
+
 template <int BM, int BN, int EPI, bool FP8A>
 __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
   constexpr int BK = 64;
+  constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
+  constexpr int ROWA = BK * SA, ROWB = BK * 2;     // bytes per tile row per stage
+  constexpr int A_BYTES = BM * ROWA, B_BYTES = BN * ROWB;
+  constexpr int A_PW = A_BYTES / 1024 / 4;         // 1 KB wave-loads per wave per stage
+  constexpr int B_PW = B_BYTES / 1024 / 4;
+  constexpr int A_RPI = 1024 / ROWA;               // tile rows per wave-load
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TMI = WM / 32, TNI = WN / 32;
-  constexpr int AR = BM / 32, BR = BN / 32;      // rows per thread per stage
   constexpr bool GATED = EPI == EPI_SWIGLU;
   static_assert(!GATED || (TNI % 2 == 0), "gated tile needs an even number of n-subtiles");
+  static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for the load split");
 
-  __shared__ uint4 As[2][BM * 8];
-  __shared__ uint4 Bs[2][BN * 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[A_BYTES + B_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[A_BYTES + B_BYTES];
   __shared__ int mt_start[kMaxExperts + 2];
   __shared__ int seg_off[kMaxExperts + 2];
   __shared__ int scan_tmp[2][kMaxExperts + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int n_seg = g.offsets ? g.n_seg : 1;
   const int K = g.K, KT = K / BK;
 
   // m-tiles per segment and their exclusive scan (segments <= 256)
   {
-    int ntile = 0, so = 0;
+    int ntile = 0;
     if (tid < n_seg) {
-      so = g.offsets ? g.offsets[tid] : 0;
-      int eo = g.offsets ? g.offsets[tid + 1] : static_cast<int>(g.rows);
+      const int so = g.offsets ? g.offsets[tid] : 0;
+      const int eo = g.offsets ? g.offsets[tid + 1] : static_cast<int>(g.rows);
       ntile = (eo - so + BM - 1) / BM;
       seg_off[tid] = so;
       if (tid == n_seg - 1) seg_off[n_seg] = eo;
@@ -116,12 +142,13 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
     if (tid < n_seg) mt_start[tid + 1] = scan_tmp[cur][tid];
     __syncthreads();
   }
-  const int MT = mt_start[n_seg];
+  const int MT = __builtin_amdgcn_readfirstlane(mt_start[n_seg]);
   const int NT = g.nt;
   const int total = MT * NT;
-
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, S = gridDim.x >> 3;
-  const int lc = tid & 7, lr = tid >> 3;         // load chunk / base row
+
+  // per-lane LDS fragment offsets (rows i*32 + lane%32 share the swizzle)
+  const int fr = lane & 31, fk = lane >> 5;
 
   for (int round = 0;; ++round) {
     const int L = (round * 8 + xcd) * S + slot;
@@ -132,43 +159,68 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
     const int gmn = min(GM, MT - m_base);
     const int mt = m_base + rem % gmn;
     const int ntile = rem / gmn;
-    // expert of this m-tile: last e with mt_start[e] <= mt
-    int lo = 0, hi = n_seg;                      // invariant: mt_start[lo] <= mt < mt_start[hi]
+    int lo = 0, hi = n_seg;                      // mt_start[lo] <= mt < mt_start[hi]
     while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
+      const int mid = (lo + hi) >> 1;
       if (mt_start[mid] <= mt) lo = mid; else hi = mid;
     }
-    const int e = lo;
-    const int row0 = seg_off[e] + (mt - mt_start[e]) * BM;
-    const int row_end = seg_off[e + 1];
+    // values read from LDS are the same in every lane: make that explicit so
+    // that the buffer descriptors below live in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int row0 = __builtin_amdgcn_readfirstlane(seg_off[e] + (mt - mt_start[e]) * BM);
+    const int row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
 
-    // global row pointers for this thread's loads
-    const uint8_t* a_base = static_cast<const uint8_t*>(g.a);
-    const int64_t a_es = FP8A ? 1 : 2;
-    const uint8_t* ap[AR];
+    // buffer resources: A from this tile's first row (reads past the buffer
+    // return zero), B per expert matrix
+    const uint8_t* a_tile = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(row0) * K * SA;
+    const __amdgpu_buffer_rsrc_t rsA =
+        make_rsrc(a_tile, static_cast<uint64_t>(g.rows - row0) * K * SA);
+    const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
+    const __amdgpu_buffer_rsrc_t rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
+    const __amdgpu_buffer_rsrc_t rsB1 = GATED ? make_rsrc(g.b1 + e * g.b_stride, b_bytes) : rsB0;
+
+    // per-lane source offsets of this wave's loads (the K step is added as soffset)
+    uint32_t a_off[A_PW], b_off[B_PW];
 #pragma unroll
-    for (int i = 0; i < AR; ++i) {
-      int r = row0 + lr + 32 * i;
-      r = r < row_end ? r : row_end - 1;
-      ap[i] = a_base + (static_cast<int64_t>(r) * K + lc * 8) * a_es;
+    for (int j = 0; j < A_PW; ++j) {
+      const int gi = wave * A_PW + j;
+      if (FP8A) {
+        const int r = gi * A_RPI + (lane >> 2);
+        const int c = (lane & 3) ^ swz64(r);
+        a_off[j] = static_cast<uint32_t>(r * K + c * 16);
+      } else {
+        const int r = gi * A_RPI + (lane >> 3);
+        const int c = (lane & 7) ^ swz128(r);
+        a_off[j] = static_cast<uint32_t>((r * K + c * 8) * 2);
+      }
     }
-    const uint16_t* bp[BR];
 #pragma unroll
-    for (int i = 0; i < BR; ++i) {
-      const int n = lr + 32 * i;
+    for (int j = 0; j < B_PW; ++j) {
+      const int gi = wave * B_PW + j;
+      const int n = gi * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz128(n);
       int f;
-      const uint16_t* base;
       if (GATED) {
         const int wn_ = n / WN, q = n % WN, half = WN / 2;
         f = ntile * (BN / 2) + wn_ * half + (q % half);
-        base = q < half ? g.b0 : g.b1;
       } else {
         f = ntile * BN + n;
-        base = g.b0;
       }
-      f = f < g.n_out ? f : g.n_out - 1;
-      bp[i] = base + e * g.b_stride + static_cast<int64_t>(f) * K + lc * 8;
+      b_off[j] = static_cast<uint32_t>((f * K + c * 8) * 2);
     }
+    auto issue = [&](int kt, uint8_t* stg) {
+      const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j)
+        lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j) {
+        const int gi = wave * B_PW + j;
+        // gated: B rows q < WN/2 of each wave half come from W1, the rest from W3
+        const bool w3 = GATED && ((gi * 8) % WN) >= WN / 2;
+        lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
+      }
+    };
 
     f32x16 acc[TMI][TNI];
 #pragma unroll
@@ -178,51 +230,33 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 ra[AR];
-    uint2 ra8[AR];
-    uint4 rb[BR];
-    auto gload = [&](int kt) {
-      const int64_t ko = static_cast<int64_t>(kt) * BK;
-#pragma unroll
-      for (int i = 0; i < AR; ++i) {
-        if (FP8A) ra8[i] = *reinterpret_cast<const uint2*>(ap[i] + ko);
-        else ra[i] = *reinterpret_cast<const uint4*>(ap[i] + ko * 2);
-      }
-#pragma unroll
-      for (int i = 0; i < BR; ++i) rb[i] = *reinterpret_cast<const uint4*>(bp[i] + ko);
-    };
-    auto sstore = [&](int st) {
-#pragma unroll
-      for (int i = 0; i < AR; ++i) {
-        const int r = lr + 32 * i;
-        As[st][r * 8 + (lc ^ swz(r))] = FP8A ? fp8x8_to_bf16x8(ra8[i]) : ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < BR; ++i) {
-        const int r = lr + 32 * i;
-        Bs[st][r * 8 + (lc ^ swz(r))] = rb[i];
-      }
-    };
-
-    gload(0);
-    sstore(0);
+    issue(0, st0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < KT) gload(kt + 1);
+      uint8_t* cur = (kt & 1) ? st1 : st0;
+      if (kt + 1 < KT) issue(kt + 1, (kt & 1) ? st0 : st1);
+      const uint8_t* sA = cur;
+      const uint8_t* sB = cur + A_BYTES;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cc = kk * 2 + (lane >> 5);
+        const int cc = kk * 2 + fk;               // 8-element k chunk of this lane
         bf16x8 af[TMI], bfr[TNI];
 #pragma unroll
         for (int i = 0; i < TMI; ++i) {
-          const int r = wm * WM + i * 32 + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8*>(&As[st][r * 8 + (cc ^ swz(r))]);
+          const int r = wm * WM + i * 32 + fr;
+          if (FP8A) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                sA + r * ROWA + (((cc >> 1) ^ swz64(r)) << 4) + ((cc & 1) << 3));
+            const uint4 w = fp8x8_to_bf16x8(v);
+            af[i] = *reinterpret_cast<const bf16x8*>(&w);
+          } else {
+            af[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz128(r)) << 4));
+          }
         }
 #pragma unroll
         for (int j = 0; j < TNI; ++j) {
-          const int r = wn * WN + j * 32 + (lane & 31);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[st][r * 8 + (cc ^ swz(r))]);
+          const int n = wn * WN + j * 32 + fr;
+          bfr[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz128(n)) << 4));
         }
 #pragma unroll
         for (int i = 0; i < TMI; ++i)
@@ -230,8 +264,7 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
           for (int j = 0; j < TNI; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < KT) sstore(st ^ 1);
-      __syncthreads();
+      __syncthreads();                             // this step's loads landed; stage free
     }
 
     // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32

@@ -106,7 +106,7 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
-#pragma unroll 2
+#pragma unroll 8
   for (int s = s0; s < s1; ++s) {
     const int k0 = s * 32;
     bf16x8 av = *reinterpret_cast<const bf16x8*>(xrow + k0);
@@ -295,30 +295,52 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void route_finalize_kernel(const float* psum, const int32_t* hist,
-                                                             int nb, int64_t T, int N, int k,
-                                                             int cap, float alpha, int32_t* counts,
-                                                             int32_t* kept, float* p, float* f,
-                                                             float* l_aux) {
+// One workgroup of 1024 threads: thread (part, e) sums the per-block partials of
+// expert e over the blocks b = part, part + P, ... in increasing order, then the
+// P parts are added in a fixed tree order, so the result does not depend on timing.
+__global__ __launch_bounds__(1024) void route_finalize_kernel(const float* psum, const int32_t* hist,
+                                                              int nb, int64_t T, int N, int k,
+                                                              int cap, float alpha, int32_t* counts,
+                                                              int32_t* kept, float* p, float* f,
+                                                              float* l_aux) {
+  __shared__ double sp[1024];
+  __shared__ int sc[1024];
   __shared__ double prod[kMaxExperts];
-  const int e = threadIdx.x;
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  const int P = 1024 / NP;
+  const int e = threadIdx.x % NP, part = threadIdx.x / NP;
+  double s = 0.0;
+  int c = 0;
   if (e < N) {
-    int64_t c = 0;
-    double s = 0.0;
-    for (int b = 0; b < nb; ++b) {
-      c += hist[static_cast<int64_t>(b) * N + e];
+#pragma unroll 4
+    for (int b = part; b < nb; b += P) {
       s += static_cast<double>(psum[static_cast<int64_t>(b) * N + e]);
+      c += hist[static_cast<int64_t>(b) * N + e];
     }
-    double pe = s / static_cast<double>(T);
-    double fe = static_cast<double>(c) / (static_cast<double>(T) * k);
-    counts[e] = static_cast<int32_t>(c);
-    kept[e] = cap > 0 ? static_cast<int32_t>(c < cap ? c : cap) : static_cast<int32_t>(c);
+  }
+  sp[threadIdx.x] = s;
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int half = P / 2; half >= 1; half >>= 1) {
+    if (part < half) {
+      sp[threadIdx.x] += sp[threadIdx.x + half * NP];
+      sc[threadIdx.x] += sc[threadIdx.x + half * NP];
+    }
+    __syncthreads();
+  }
+  if (part == 0 && e < N) {
+    const int64_t cnt = sc[e];
+    const double pe = sp[e] / static_cast<double>(T);
+    const double fe = static_cast<double>(cnt) / (static_cast<double>(T) * k);
+    counts[e] = static_cast<int32_t>(cnt);
+    kept[e] = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
     if (p) p[e] = static_cast<float>(pe);
     if (f) f[e] = static_cast<float>(fe);
     prod[e] = fe * pe;
   }
   __syncthreads();
-  if (e == 0 && l_aux) {
+  if (threadIdx.x == 0 && l_aux) {
     double acc = 0.0;
     for (int q = 0; q < N; ++q) acc += prod[q];
     l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
@@ -344,7 +366,7 @@ hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const in
                                  int32_t* counts, int32_t* kept, float* p, float* f,
                                  float* l_aux, hipStream_t st) {
   int nb = static_cast<int>(ceil_div(s.T, TM));
-  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(256), 0, st, psum, hist, nb, s.T, s.N,
+  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(1024), 0, st, psum, hist, nb, s.T, s.N,
                      s.k, s.capacity, s.alpha, counts, kept, p, f, l_aux);
   return hipGetLastError();
 }

@@ -129,7 +129,6 @@ def test_fp8_quantiser_exhaustive_bf16_patterns():
         assert np.array_equal(bf16_to_f64(a_bits), anchor[ok])       # exact anchors
         rows.append(np.concatenate([vals[ok], a_bits[:, None]], axis=1))
     x = np.concatenate(rows)
-    x = np.concatenate([x, np.zeros((x.shape[0], 1), np.uint16)], axis=1)   # d = 256
     T, d = x.shape
     wl = si.Workload("q", T=T, d=d, N=4, k=1, F=64, act="swiglu", dtype="bf16", buf="fp8")
     s = M.shape_of(wl)
