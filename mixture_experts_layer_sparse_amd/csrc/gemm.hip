@@ -17,12 +17,15 @@
 //     weight and activation tiles from that XCD's L2;
 //   * 4 waves in a 2x2 grid, each computing a (BM/2)x(BN/2) block with
 //     v_mfma_f32_32x32x16_bf16, float32 accumulation;
-//   * K is streamed in 64-wide steps through two LDS stages (global -> registers
-//     -> LDS, next step's loads in flight during this step's MFMAs); the 16-byte
-//     chunks of each 128-byte LDS row are XOR-swizzled by the row index so that
-//     fragment reads and tile writes are free of bank conflicts;
-//   * fp8 activations (e4m3 codes) are widened to bf16 exactly on their way into
-//     LDS and the per-row scale multiplies the float32 accumulator;
+//   * K is streamed in 64-wide steps through two LDS stages, loaded straight
+//     from memory into LDS by buffer loads (no staging registers), the next
+//     step's loads in flight during this step's MFMAs; the 16-byte
+//     chunks of each LDS row are XOR-swizzled by the row index so that fragment
+//     reads are free of bank conflicts (the loads pick swizzled source chunks,
+//     so each 1 KB wave-load still lands contiguously);
+//   * fp8 activations (e4m3 codes) stay fp8 in LDS and are widened to bf16
+//     exactly as fragments are read; the per-row scale multiplies the float32
+//     accumulator;
 //   * SwiGLU: the B tile interleaves W1 and W3 rows of the same output columns
 //     so that each wave holds both halves of its outputs; the activation runs
 //     on the accumulators and h is written once, in bf16.
@@ -87,25 +90,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            static_cast<int>(n), 0x00020000);
 }
 
-// 16-byte chunk swizzle inside a 128-byte LDS row (bf16 rows of 64 elements).
-__device__ __forceinline__ int swz128(int row) { return row & 7; }
-// inside a 64-byte LDS row (fp8 rows of 64 codes): 4 chunks
-__device__ __forceinline__ int swz64(int row) { return (row >> 1) & 3; }
+// LDS holds 64 banks of 4 bytes and a 16-byte-per-lane read is served 16 lanes
+// (256 bytes) at a time.  Fragment reads hit 16 consecutive rows at the same
+// logical chunk, so the chunk is XOR-swizzled by the row: in 128-byte rows
+// (bf16, 8 chunks) the row parity picks the bank half and (row/2)%8 the chunk;
+// in 64-byte rows (fp8, 4 chunks) row%4 picks the quarter and (row/4)%4 the chunk.
+__device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
 
-template <int BM, int BN, int EPI, bool FP8A>
-__global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
+  constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
   constexpr int BK = 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
   constexpr int ROWA = BK * SA, ROWB = BK * 2;     // bytes per tile row per stage
   constexpr int A_BYTES = BM * ROWA, B_BYTES = BN * ROWB;
-  constexpr int A_PW = A_BYTES / 1024 / 4;         // 1 KB wave-loads per wave per stage
-  constexpr int B_PW = B_BYTES / 1024 / 4;
+  constexpr int A_PW = A_BYTES / 1024 / NW;        // 1 KB wave-loads per wave per stage
+  constexpr int B_PW = B_BYTES / 1024 / NW;
   constexpr int A_RPI = 1024 / ROWA;               // tile rows per wave-load
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TMI = WM / 32, TNI = WN / 32;
   constexpr bool GATED = EPI == EPI_SWIGLU;
   static_assert(!GATED || (TNI % 2 == 0), "gated tile needs an even number of n-subtiles");
   static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for the load split");
+  static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "load split");
+  static_assert(!GATED || (WN / 2) % 8 == 0, "a wave-load must not straddle W1 and W3 rows");
 
   __shared__ __attribute__((aligned(1024))) uint8_t st0[A_BYTES + B_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[A_BYTES + B_BYTES];
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int n_seg = g.offsets ? g.n_seg : 1;
   const int K = g.K, KT = K / BK;
 
@@ -129,12 +138,13 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GemmArgs g) {
       seg_off[tid] = so;
       if (tid == n_seg - 1) seg_off[n_seg] = eo;
     }
-    scan_tmp[0][tid] = ntile;
+    if (tid < 256) scan_tmp[0][tid] = ntile;
     __syncthreads();
     int cur = 0;
 #pragma unroll
     for (int off = 1; off < 256; off <<= 1) {
-      scan_tmp[cur ^ 1][tid] = scan_tmp[cur][tid] + (tid >= off ? scan_tmp[cur][tid - off] : 0);
+      if (tid < 256)
+        scan_tmp[cur ^ 1][tid] = scan_tmp[cur][tid] + (tid >= off ? scan_tmp[cur][tid - off] : 0);
       cur ^= 1;
       __syncthreads();
     }
@@ -360,14 +370,15 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------- launch --
 
-template <int BM, int BN, int EPI, bool FP8A>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, EPI, FP8A>), dim3(grid), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A>), dim3(grid), dim3(64 * WGM * WGN), 0,
+                     st, g);
   return hipGetLastError();
 }
 
@@ -376,16 +387,18 @@ int pick_bm(int64_t rows, int n_seg) {
   return avg >= 384 ? 256 : 128;
 }
 
+// 8 waves (two per SIMD, so one wave's MFMAs cover the other's waits) in a
+// 2 x 4 grid: 128x64 per wave at BM = 256, 64x64 at BM = 128.
 template <int EPI, bool FP8A>
 hipError_t dispatch_up(int bm, const GemmArgs& g, int64_t rows, int n_seg, bool dense,
                        hipStream_t st) {
   const int nt = g.nt;
   if (bm == 256) {
     int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
-    return launch_gg_on<256, 256, EPI, FP8A>(g, mtu * nt, st);
+    return launch_gg_on<256, 256, 2, 4, EPI, FP8A>(g, mtu * nt, st);
   }
   int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
-  return launch_gg_on<128, 256, EPI, FP8A>(g, mtu * nt, st);
+  return launch_gg_on<128, 256, 2, 4, EPI, FP8A>(g, mtu * nt, st);
 }
 
 }  // namespace
