@@ -11,12 +11,13 @@
 // bf16 design (gfx950):
 //   * one persistent workgroup per CU walks a device-side tile list: m-tiles of
 //     every expert segment (counted from `offsets` on the device, so the host
-//     never reads the routing) times n-tiles.  Consecutive tile ids share the
-//     weight n-tile (GM m-tiles per n-tile) and each XCD owns contiguous runs
-//     of tile ids, so the tiles running together on one XCD reuse the same
-//     weight and activation tiles from that XCD's L2;
-//   * 4 waves in a 2x2 grid, each computing a (BM/2)x(BN/2) block with
-//     v_mfma_f32_32x32x16_bf16, float32 accumulation;
+//     never reads the routing) times n-tiles, expert-major and n-tile-major, so
+//     that an expert's m-tiles consume each weight n-tile back to back; each XCD
+//     owns runs of consecutive tile ids, so the tiles running together on one
+//     XCD reuse the same weight and activation tiles from that XCD's L2;
+//   * 8 waves (two per SIMD) in a WGM x WGN grid, each computing a block of
+//     the tile with v_mfma_f32_32x32x16_bf16, float32 accumulation; a wave whose
+//     rows all lie past the segment end skips its MFMAs;
 //   * K is streamed in 64-wide steps through two LDS stages, loaded straight
 //     from memory into LDS by buffer loads (no staging registers), the next
 //     step's loads in flight during this step's MFMAs; the 16-byte
@@ -30,7 +31,20 @@
 //     so that each wave holds both halves of its outputs; the activation runs
 //     on the accumulators and h is written once, in bf16.
 // The float32 path (small correctness shapes) is a plain dot-product kernel.
+#include <type_traits>
+
 #include "moe_internal.h"
+
+// Pipeline settings (compile-time tuning knobs; the defaults are the measured best).
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_NS
+#define MOE_GEMM_NS 2
+#endif
+#ifndef MOE_GEMM_INTERLEAVE
+#define MOE_GEMM_INTERLEAVE 0
+#endif
 
 namespace moe {
 namespace {
@@ -54,8 +68,6 @@ struct GemmArgs {
   uint16_t* out;           // [rows][n_out]
   int nt;                  // n-tiles
 };
-
-constexpr int GM = 4;      // m-tiles sharing one n-tile in the tile order
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
 
@@ -92,32 +104,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // LDS holds 64 banks of 4 bytes and a 16-byte-per-lane read is served 16 lanes
 // (256 bytes) at a time.  Fragment reads hit 16 consecutive rows at the same
-// logical chunk, so the chunk is XOR-swizzled by the row: in 128-byte rows
-// (bf16, 8 chunks) the row parity picks the bank half and (row/2)%8 the chunk;
-// in 64-byte rows (fp8, 4 chunks) row%4 picks the quarter and (row/4)%4 the chunk.
-__device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
+// logical 16-byte chunk, so the chunk is XOR-swizzled by the row: with RB-byte
+// rows, 256/RB rows share one 256-byte bank line (the row's place in the line
+// picks the bank group) and (row / (256/RB)) % (RB/16) picks the chunk.
+template <int RB>
+__device__ __forceinline__ int swz(int row) {
+  return (row / (256 / RB)) % (RB / 16);
+}
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A>
+// s_waitcnt on the vector-memory counter only: vmcnt <= n (n < 64).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int EPI, bool FP8A>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
-  constexpr int BK = 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
   constexpr int ROWA = BK * SA, ROWB = BK * 2;     // bytes per tile row per stage
   constexpr int A_BYTES = BM * ROWA, B_BYTES = BN * ROWB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_PW = A_BYTES / 1024 / NW;        // 1 KB wave-loads per wave per stage
   constexpr int B_PW = B_BYTES / 1024 / NW;
-  constexpr int A_RPI = 1024 / ROWA;               // tile rows per wave-load
+  constexpr int LPW = A_PW + B_PW;                 // loads per wave per stage
+  constexpr int A_CPR = ROWA / 16, B_CPR = ROWB / 16;   // 16-byte chunks per row
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TMI = WM / 32, TNI = WN / 32;
   constexpr bool GATED = EPI == EPI_SWIGLU;
   static_assert(!GATED || (TNI % 2 == 0), "gated tile needs an even number of n-subtiles");
   static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for the load split");
   static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "load split");
-  static_assert(!GATED || (WN / 2) % 8 == 0, "a wave-load must not straddle W1 and W3 rows");
+  static_assert(!GATED || (WN / 2) % (1024 / ROWB) == 0, "a wave-load must not straddle W1 and W3");
+  static_assert(LPW * (NS - 2) < 64, "vmcnt range");
+  static_assert(NS * STAGE <= 144 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[A_BYTES + B_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[A_BYTES + B_BYTES];
+  // one array per stage: every LDS access below names its stage's array, so the
+  // compiler can tell the stage being read from the stages the DMA is filling
+  // (with a single array it conservatively waits for all loads before any read)
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[NS > 2 ? STAGE : 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[NS > 3 ? STAGE : 1024];
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   __shared__ int mt_start[kMaxExperts + 2];
   __shared__ int seg_off[kMaxExperts + 2];
   __shared__ int scan_tmp[2][kMaxExperts + 1];
@@ -161,24 +191,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   const int fr = lane & 31, fk = lane >> 5;
 
   for (int round = 0;; ++round) {
+    // tile order: expert-major, then n-tile, then the expert's m-tiles, so the
+    // m-tiles of an expert consume each weight n-tile back to back (one HBM
+    // read, the rest from L2); each XCD takes S consecutive tile ids per round
     const int L = (round * 8 + xcd) * S + slot;
     if (L >= total) break;
-    const int per_group = GM * NT;
-    const int grp = L / per_group, rem = L - grp * per_group;
-    const int m_base = grp * GM;
-    const int gmn = min(GM, MT - m_base);
-    const int mt = m_base + rem % gmn;
-    const int ntile = rem / gmn;
-    int lo = 0, hi = n_seg;                      // mt_start[lo] <= mt < mt_start[hi]
+    int lo = 0, hi = n_seg;                      // mt_start[lo]*NT <= L < mt_start[hi]*NT
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (mt_start[mid] <= mt) lo = mid; else hi = mid;
+      if (mt_start[mid] * NT <= L) lo = mid; else hi = mid;
     }
     // values read from LDS are the same in every lane: make that explicit so
     // that the buffer descriptors below live in scalar registers
     const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int row0 = __builtin_amdgcn_readfirstlane(seg_off[e] + (mt - mt_start[e]) * BM);
+    const int mte = __builtin_amdgcn_readfirstlane(mt_start[e + 1] - mt_start[e]);
+    const int local = L - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
+    const int ntile = local / mte;
+    const int mloc = local - ntile * mte;
+    const int row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * BM;
     const int row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
+    // a wave whose rows all lie past the segment end skips its MFMAs
+    const bool wave_rows = row0 + wm * WM < row_end;
 
     // buffer resources: A from this tile's first row (reads past the buffer
     // return zero), B per expert matrix
@@ -193,22 +226,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     uint32_t a_off[A_PW], b_off[B_PW];
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) {
-      const int gi = wave * A_PW + j;
-      if (FP8A) {
-        const int r = gi * A_RPI + (lane >> 2);
-        const int c = (lane & 3) ^ swz64(r);
-        a_off[j] = static_cast<uint32_t>(r * K + c * 16);
-      } else {
-        const int r = gi * A_RPI + (lane >> 3);
-        const int c = (lane & 7) ^ swz128(r);
-        a_off[j] = static_cast<uint32_t>((r * K + c * 8) * 2);
-      }
+      const int r = (wave * A_PW + j) * (1024 / ROWA) + lane / A_CPR;
+      const int c = (lane % A_CPR) ^ swz<ROWA>(r);
+      a_off[j] = static_cast<uint32_t>(r * K * SA + c * 16);
     }
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
-      const int gi = wave * B_PW + j;
-      const int n = gi * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz128(n);
+      const int n = (wave * B_PW + j) * (1024 / ROWB) + lane / B_CPR;
+      const int c = (lane % B_CPR) ^ swz<ROWB>(n);
       int f;
       if (GATED) {
         const int wn_ = n / WN, q = n % WN, half = WN / 2;
@@ -216,18 +241,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       } else {
         f = ntile * BN + n;
       }
-      b_off[j] = static_cast<uint32_t>((f * K + c * 8) * 2);
+      b_off[j] = static_cast<uint32_t>((f * K) * 2 + c * 16);
     }
-    auto issue = [&](int kt, uint8_t* stg) {
+    auto stage_ptr = [&](auto S) -> uint8_t* {
+      constexpr int q = decltype(S)::value;
+      if constexpr (q == 0) return sm0;
+      else if constexpr (q == 1) return sm1;
+      else if constexpr (q == 2) return sm2;
+      else return sm3;
+    };
+    auto issue_to = [&](int kt, uint8_t* stg) {
       const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
-      for (int j = 0; j < A_PW; ++j)
-        lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
+      for (int j = 0; j < A_PW; ++j) lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
 #pragma unroll
       for (int j = 0; j < B_PW; ++j) {
         const int gi = wave * B_PW + j;
-        // gated: B rows q < WN/2 of each wave half come from W1, the rest from W3
-        const bool w3 = GATED && ((gi * 8) % WN) >= WN / 2;
+        // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
+        const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
         lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
       }
     };
@@ -240,42 +271,83 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    issue(0, st0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      uint8_t* cur = (kt & 1) ? st1 : st0;
-      if (kt + 1 < KT) issue(kt + 1, (kt & 1) ? st0 : st1);
-      const uint8_t* sA = cur;
-      const uint8_t* sB = cur + A_BYTES;
+    // NS-stage pipeline: the loads of step kt + NS - 1 are issued while step kt
+    // computes.  Each wave waits only for its own loads of step kt (vmcnt), then
+    // a barrier makes every wave's loads visible and marks the stage of step
+    // kt - 1 free for reuse.  The loop is unrolled by NS so that each step's
+    // stage is a compile-time choice.
+    auto step = [&](int kt, auto S) {
+      constexpr int q = decltype(S)::value;
+      const int ahead = KT - 1 - kt;             // steps after kt already issued (<= NS - 2)
+      if (ahead >= NS - 2) wait_vmcnt<LPW * (NS - 2)>();
+      else if (NS > 3 && ahead == 2) wait_vmcnt<LPW * 2>();
+      else if (NS > 2 && ahead == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + NS - 1 < KT)
+        issue_to(kt + NS - 1, stage_ptr(std::integral_constant<int, (q + NS - 1) % NS>{}));
+      const uint8_t* sA = stage_ptr(S);
+      const uint8_t* sB = sA + A_BYTES;
+      if (wave_rows) {
+        // fragments of k-substep kk + 1 are read while substep kk's MFMAs run
+        bf16x8 af[2][TMI], bfr[2][TNI];
+        auto read_frags = [&](int kk, bf16x8* a, bf16x8* b) {
+          const int cc = kk * 2 + fk;             // 8-element k chunk of this lane
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cc = kk * 2 + fk;               // 8-element k chunk of this lane
-        bf16x8 af[TMI], bfr[TNI];
-#pragma unroll
-        for (int i = 0; i < TMI; ++i) {
-          const int r = wm * WM + i * 32 + fr;
-          if (FP8A) {
-            const uint2 v = *reinterpret_cast<const uint2*>(
-                sA + r * ROWA + (((cc >> 1) ^ swz64(r)) << 4) + ((cc & 1) << 3));
-            const uint4 w = fp8x8_to_bf16x8(v);
-            af[i] = *reinterpret_cast<const bf16x8*>(&w);
-          } else {
-            af[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz128(r)) << 4));
+          for (int i = 0; i < TMI; ++i) {
+            const int r = wm * WM + i * 32 + fr;
+            if (FP8A) {
+              const uint2 v = *reinterpret_cast<const uint2*>(
+                  sA + r * ROWA + (((cc >> 1) ^ swz<ROWA>(r)) << 4) + ((cc & 1) << 3));
+              const uint4 w = fp8x8_to_bf16x8(v);
+              a[i] = *reinterpret_cast<const bf16x8*>(&w);
+            } else {
+              a[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz<ROWA>(r)) << 4));
+            }
           }
+#pragma unroll
+          for (int j = 0; j < TNI; ++j) {
+            const int n = wn * WN + j * 32 + fr;
+            b[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
+          }
+        };
+        read_frags(0, af[0], bfr[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const int cb = kk & 1;
+          if (kk + 1 < BK / 16) read_frags(kk + 1, af[cb ^ 1], bfr[cb ^ 1]);
+#pragma unroll
+          for (int i = 0; i < TMI; ++i)
+#pragma unroll
+            for (int j = 0; j < TNI; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+#if MOE_GEMM_INTERLEAVE
+          if (kk + 1 < BK / 16) {
+            // one fragment read between consecutive MFMAs
+#pragma unroll
+            for (int q = 0; q < TMI + TNI; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, TMI * TNI - (TMI + TNI), 0);
+          }
+#endif
         }
-#pragma unroll
-        for (int j = 0; j < TNI; ++j) {
-          const int n = wn * WN + j * 32 + fr;
-          bfr[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz128(n)) << 4));
-        }
-#pragma unroll
-        for (int i = 0; i < TMI; ++i)
-#pragma unroll
-          for (int j = 0; j < TNI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      __syncthreads();                             // this step's loads landed; stage free
+    };
+
+    wait_vmcnt<0>();                              // the previous tile's stores are out:
+                                                  // vmcnt now counts only this tile's loads
+    issue_to(0, sm0);
+    if (1 < KT) issue_to(1, sm1);
+    if (NS > 2 && 2 < KT) issue_to(2, stage_ptr(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}));
+    for (int kt0 = 0; kt0 < KT; kt0 += NS) {
+      step(kt0, std::integral_constant<int, 0>{});
+      if (kt0 + 1 < KT) step(kt0 + 1, std::integral_constant<int, 1>{});
+      if (NS > 2 && kt0 + 2 < KT) step(kt0 + 2, std::integral_constant<int, (NS > 2 ? 2 : 0)>{});
+      if (NS > 3 && kt0 + 3 < KT) step(kt0 + 3, std::integral_constant<int, (NS > 3 ? 3 : 0)>{});
     }
+    __builtin_amdgcn_s_barrier();                 // every wave is done with the stages
 
     // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32
 #pragma unroll
@@ -370,15 +442,15 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------- launch --
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A>
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int EPI, bool FP8A>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A>), dim3(grid), dim3(64 * WGM * WGN), 0,
-                     st, g);
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, BK, NS, EPI, FP8A>), dim3(grid),
+                     dim3(64 * WGM * WGN), 0, st, g);
   return hipGetLastError();
 }
 
@@ -387,18 +459,23 @@ int pick_bm(int64_t rows, int n_seg) {
   return avg >= 384 ? 256 : 128;
 }
 
+
 // 8 waves (two per SIMD, so one wave's MFMAs cover the other's waits) in a
-// 2 x 4 grid: 128x64 per wave at BM = 256, 64x64 at BM = 128.
+// 2 x 4 grid: 128x64 per wave at BM = 256, 64x64 at BM = 128.  Operands stream
+// through 2 LDS stages of 64-wide K steps (measured: 4 stages of 32 are slower,
+// the extra barriers cost more than the longer prefetch gains).
 template <int EPI, bool FP8A>
 hipError_t dispatch_up(int bm, const GemmArgs& g, int64_t rows, int n_seg, bool dense,
                        hipStream_t st) {
+  constexpr int BK = FP8A ? 64 : MOE_GEMM_BK;
+  constexpr int NS = FP8A ? 2 : MOE_GEMM_NS;
   const int nt = g.nt;
   if (bm == 256) {
     int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
-    return launch_gg_on<256, 256, 2, 4, EPI, FP8A>(g, mtu * nt, st);
+    return launch_gg_on<256, 256, 2, 4, BK, NS, EPI, FP8A>(g, mtu * nt, st);
   }
   int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
-  return launch_gg_on<128, 256, 2, 4, EPI, FP8A>(g, mtu * nt, st);
+  return launch_gg_on<128, 256, 2, 4, BK, NS, EPI, FP8A>(g, mtu * nt, st);
 }
 
 }  // namespace
