@@ -30,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s at Mixtral shape; grouped-GEMM % MFMA peak; dispatch GB/s"
+# the gate/up grouped-GEMM kernel instance each workload runs (key in the counter summary)
+UP_KERNEL = {"mixtral": "gg_kernel<256,256,2,4,64,2,3,false>"}
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
 
@@ -41,8 +43,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens whose expert FFNs the CPU oracle runs (0: all T)")
+    ap.add_argument("--mode", choices=["bench", "copy", "summarize"], default="bench")
+    ap.add_argument("--prof", default=None,
+                    help="summarize: directory holding trace/ fetch/ write/ cfetch/ cwrite/ "
+                         "rocprofv3 csv output")
+    ap.add_argument("--out", default=None, help="summarize: markdown file to write")
     return ap.parse_args()
 
 
@@ -73,7 +80,7 @@ def cpu_baseline(wl, inp, n_tok):
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import moe as om
-    toks = np.linspace(0, wl.T - 1, n_tok).astype(np.int64)
+    toks = np.linspace(0, wl.T - 1, min(n_tok, wl.T)).astype(np.int64)
     t0 = time.perf_counter()
     om.forward(wl, {**inp, "w1": None})
     t_route = time.perf_counter() - t0
@@ -88,8 +95,124 @@ def cpu_baseline(wl, inp, n_tok):
                       f"combine for {n_tok} evenly spaced tokens ({t_ffn:.2f} s); float64 NumPy"}
 
 
+COUNTER_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_mixtral_counters.md")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sparse_amd", "csrc", "gemm.hip")
+PROFILE_CMDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
+    "python3 bench.py --no-cpu-baseline --steps 10 --warmup 3",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
+    "python3 bench.py --no-cpu-baseline --steps 3 --warmup 1",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
+    "python3 bench.py --no-cpu-baseline --steps 3 --warmup 1",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/cfetch -o run -- python3 bench.py --mode copy",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/cwrite -o run -- python3 bench.py --mode copy",
+]
+
+
+def _src_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _short(name):
+    for key in ("gg_kernel", "route_kernel", "route_finalize_kernel", "disp_hist_kernel",
+                "disp_plan_kernel", "disp_copy_kernel", "disp_fp8_kernel", "combine_bf16_kernel",
+                "combine_f32_kernel", "__amd_rocclr_copyBuffer"):
+        if key in name:
+            i = name.find(key)
+            j = name.find("(", i)
+            return name[i:j if j > 0 else None].replace(" ", "")
+    return None
+
+
+def summarize(prof, out):
+    """Markdown summary of a rocprofv3 session of this benchmark: average
+    kernel durations, HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE scaled
+    by what the same counters read for a plain copy of known size."""
+    import csv
+    from collections import defaultdict
+
+    def counters(sub, name):
+        agg = defaultdict(list)
+        with open(os.path.join(prof, sub, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == name:
+                    k = _short(r["Kernel_Name"])
+                    if k:
+                        agg[k].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    stats = {}
+    with open(os.path.join(prof, "trace", "run_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            k = _short(r["Name"])
+            if k:
+                stats[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    fetch, write = counters("fetch", "FETCH_SIZE"), counters("write", "WRITE_SIZE")
+    cf = counters("cfetch", "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    cw = counters("cwrite", "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    copy_kib = (1 << 28) / 1024
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    rows, table = {}, []
+    for k, (calls, us) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        if k.startswith("__amd"):
+            continue
+        fb = fetch.get(k, 0.0) * 1024 * f_scale
+        wb = write.get(k, 0.0) * 1024 * w_scale
+        rows[k] = {"avg_us": us, "fetch_bytes": fb, "write_bytes": wb}
+        table.append(f"| `{k}` | {calls} | {us:.1f} | {fb / 2**20:.1f} | {wb / 2**20:.1f} |")
+    data = {"gemm_src_sha256_16": _src_hash(GEMM_SRC), "fetch_scale": f_scale,
+            "write_scale": w_scale, "kernels": rows}
+    text = "\n".join([
+        "# Grouped GEMM and memory kernels, Mixtral-shaped layer (T=4096, d=4096, N=8, k=2, F=14336, bf16)",
+        "",
+        "rocprofv3 on one MI355X; commands (run from the repository root, `<dir>` a scratch directory):",
+        "",
+        *[f"    {c}" for c in PROFILE_CMDS],
+        "",
+        "Summarised with `python3 bench.py --mode summarize --prof <dir> --out <this file>`.",
+        "",
+        f"Counter scale factors from the 256 MiB copy: FETCH_SIZE x {f_scale:.3f}, "
+        f"WRITE_SIZE x {w_scale:.3f} (the copy reads and writes 256 MiB each).",
+        "",
+        "| kernel | calls | avg us | HBM read MiB/dispatch | HBM write MiB/dispatch |",
+        "|---|---|---|---|---|",
+        *table,
+        "",
+        "Machine-readable (bench.py reads this to fill `roofline.traffic` while `gemm.hip` is unchanged):",
+        "",
+        "```json",
+        json.dumps(data),
+        "```",
+        "",
+    ])
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def profiled_traffic(kernel_key):
+    """HBM bytes per launch of a kernel from the committed counter summary, or
+    None when there is none or gemm.hip has changed since it was taken."""
+    try:
+        with open(COUNTER_FILE) as f:
+            text = f.read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(blob)
+        if data.get("gemm_src_sha256_16") != _src_hash(GEMM_SRC):
+            return None
+        k = data["kernels"].get(kernel_key)
+        return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+    except (OSError, IndexError, ValueError, KeyError):
+        return None
+
+
 def main():
     a = parse()
+    if a.mode == "summarize":
+        summarize(a.prof, a.out or COUNTER_FILE)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
@@ -198,7 +321,9 @@ def main():
                    "kept_rows": R},
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM up (gate/up + activation)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": profiled_traffic(UP_KERNEL.get(wl.name)),
+                     "traffic_unit": "bytes per launch (HBM read + write)"},
         "grouped_gemm_pct_mfma_peak": 100.0 * (up + down + shared) / gemm_t / 1e12 / PEAK_BF16_TFLOPS,
         "dispatch_GBps": db / (ph_ms["dispatch"] * 1e-3) / 1e9,
         "memory_phases": {"bytes": rb + db + cb, "us": mem_t * 1e6,
@@ -207,7 +332,7 @@ def main():
         "phases_us": {k: v * 1e3 for k, v in ph_ms.items()},
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_sample_tokens or wl.T)
     print(json.dumps(out), flush=True)
 
 
