@@ -10,6 +10,10 @@
 // in slot order 0..k-1, then the shared expert, with one rounding at the end.
 #include "moe_internal.h"
 
+#ifndef MOE_COMBINE_UNROLL
+#define MOE_COMBINE_UNROLL 2
+#endif
+
 namespace moe {
 namespace {
 
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
     wj[j] = j < k ? w[t * k + j] : 0.f;
   }
   const int nch = d / 8;
-#pragma unroll 2
+#pragma unroll MOE_COMBINE_UNROLL
   for (int c = lane; c < nch; c += 64) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -10,12 +10,14 @@
 // costs to train and serve" / "Limit how many machines a token touches".
 //
 // Design (differs from the page's one-thread-per-token kernel): a workgroup of
-// 4 waves owns 16 tokens.  For bf16 the logits come from 16x16x32 bf16 MFMAs
+// 8 waves owns 16 tokens.  For bf16 the logits come from 16x16x32 bf16 MFMAs
 // reading x and W_g straight from global memory (each x element is read once;
-// W_g is small and stays in L2); when N < 64 the waves split the d-loop and
-// their partial sums are added in a fixed order.  Then one wave per token does
-// the selection with 64-bit wave max-reductions on keys (logit, ~index), so
-// the result is independent of thread timing.
+// W_g is small and stays in L2); the waves split the experts and the d-loop and
+// their partial sums are added in a fixed order.  Selection: with at most 32
+// experts one lane handles one token, scanning experts in index order in
+// registers; with more, one wave handles one token with 64-bit wave
+// max-reductions on keys (logit, ~index).  Either way the result does not
+// depend on thread timing.
 #include "moe_internal.h"
 
 namespace moe {
@@ -75,13 +77,20 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
-// Logit tile [TM][ldl] in LDS, computed by the bf16 MFMA path.
+constexpr int RW = 8;                  // waves per router workgroup
+constexpr int SMALL_N = 32;            // up to this many experts one lane selects for one token
+
+// Logit tile [TM][ldl] in LDS, computed by the bf16 MFMA path.  The 8 waves
+// split the experts into CG column groups of 16-expert blocks and d into KS
+// slices (CG * KS = 8); each wave issues the loads of 8 k-steps before their
+// MFMAs, so that about 32 KB per wave are in flight.
 __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* lt, int ldl) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = a.N, d = a.d;
   const int NB = (N + 15) / 16;                       // 16-expert column blocks
-  const int KS = NB >= 3 ? 1 : 4 / NB;                // d-splits across waves
-  const int CG = 4 / KS;                              // column groups
+  const int CG = NB >= 8 ? 8 : (NB >= 3 ? 4 : NB);    // column groups
+  const int KS = RW / CG;                             // d-slices
   const int ks = wave / CG, cg = wave % CG;
   const int nsteps = d / 32;
   const int s0 = ks * nsteps / KS, s1 = (ks + 1) * nsteps / KS;
@@ -91,29 +100,44 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
   int64_t t = t0 + lr;
   if (t > a.T - 1) t = a.T - 1;
   const uint16_t* xrow = x + t * d + lk;
-  const uint16_t* wrow[4];
-  bool wok[4];
+  const uint16_t* wrow[2];
+  bool wok[2];
   int nblk = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int cb = cg + i * CG;
-    int e = cb * 16 + lr;
+  for (int i = 0; i < 2; ++i) {
+    const int cb = cg + i * CG;
+    const int e = cb * 16 + lr;
     wok[i] = cb < NB && e < N;
     wrow[i] = wg + static_cast<int64_t>(wok[i] ? e : 0) * d + lk;
     if (cb < NB) nblk = i + 1;
   }
-  f32x4 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const bf16x8 zero = {};
-#pragma unroll 8
-  for (int s = s0; s < s1; ++s) {
-    const int k0 = s * 32;
-    bf16x8 av = *reinterpret_cast<const bf16x8*>(xrow + k0);
+  constexpr int U = 8;
+  int s = s0;
+  for (; s + U <= s1; s += U) {
+    bf16x8 av[U], bv[U][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int u = 0; u < U; ++u) {
+      const int k0 = (s + u) * 32;
+      av[u] = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        bv[u][i] = (i < nblk && wok[i]) ? *reinterpret_cast<const bf16x8*>(wrow[i] + k0) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (i < nblk) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][i], acc[i], 0, 0, 0);
+  }
+  for (; s < s1; ++s) {
+    const int k0 = s * 32;
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       if (i < nblk) {
-        bf16x8 bv = wok[i] ? *reinterpret_cast<const bf16x8*>(wrow[i] + k0) : zero;
+        const bf16x8 bv = wok[i] ? *reinterpret_cast<const bf16x8*>(wrow[i] + k0) : zero;
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
       }
     }
@@ -121,16 +145,16 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
   // acc[i][r] = partial logit of token 4*(lane/16)+r, expert (cg+i*CG)*16 + lane%16
   const int NP = NB * 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     if (i < nblk) {
-      int col = (cg + i * CG) * 16 + lr;
+      const int col = (cg + i * CG) * 16 + lr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[(ks * TM + (lane >> 4) * 4 + r) * NP + col] = acc[i][r];
     }
   }
   __syncthreads();
-  for (int q = threadIdx.x; q < TM * N; q += 256) {
-    int m = q / N, e = q % N;
+  for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
+    const int m = q / N, e = q % N;
     float v = 0.f;
     for (int kk = 0; kk < KS; ++kk) v += part[(kk * TM + m) * NP + e];
     if (a.bias) v += a.bias[e];
@@ -142,8 +166,8 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
 __device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
   const float* x = static_cast<const float*>(a.x);
   const float* wg = static_cast<const float*>(a.wg);
-  for (int q = threadIdx.x; q < TM * a.N; q += 256) {
-    int m = q / a.N, e = q % a.N;
+  for (int q = threadIdx.x; q < TM * a.N; q += RW * 64) {
+    const int m = q / a.N, e = q % a.N;
     int64_t t = t0 + m;
     if (t > a.T - 1) t = a.T - 1;
     const float* xr = x + t * a.d;
@@ -155,33 +179,134 @@ __device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
   }
 }
 
+// Selection for one token by one lane (N <= SMALL_N): everything in order over
+// the expert index, so a strictly larger value is needed to replace the
+// current best and equal logits keep the lower index.  Writes the token's full
+// softmax to prow (for p) and its k picks; counts go to the block histogram.
+__device__ void select_lane(const RouteArgs& a, const float* row, float* prow, int64_t t, int* hl) {
+  const int N = a.N, k = a.k;
+  float mx = -INFINITY;
+  for (int e = 0; e < N; ++e) mx = fmaxf(mx, row[e]);
+  float zs = 0.f;
+  for (int e = 0; e < N; ++e) zs += expf(row[e] - mx);
+  for (int e = 0; e < N; ++e) prow[e] = expf(row[e] - mx) / zs;
+  uint32_t allowed = N >= 32 ? 0xFFFFFFFFu : ((1u << N) - 1u);
+  if (a.n_groups > 1) {
+    const int G = a.n_groups, gsz = N / G;
+    float gs[SMALL_N];
+    for (int g = 0; g < G; ++g) {
+      float top[kMaxTopK];
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q) top[q] = -INFINITY;
+      for (int e = g * gsz; e < (g + 1) * gsz; ++e) {
+        float val = row[e];
+#pragma unroll
+        for (int q = 0; q < kMaxTopK; ++q) {
+          if (q < a.gsk && val > top[q]) {
+            const float tmp = top[q];
+            top[q] = val;
+            val = tmp;
+          }
+        }
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q)
+        if (q < a.gsk) sum += top[q];
+      gs[g] = sum + 0.0f;
+    }
+    uint32_t gsel = 0u;
+    for (int q = 0; q < a.topk_groups; ++q) {
+      int best = -1;
+      float bv = 0.f;
+      for (int g = 0; g < G; ++g)
+        if (!((gsel >> g) & 1u) && (best < 0 || gs[g] > bv)) { best = g; bv = gs[g]; }
+      gsel |= 1u << best;
+    }
+    allowed = 0u;
+    for (int e = 0; e < N; ++e)
+      if ((gsel >> (e / gsz)) & 1u) allowed |= 1u << e;
+  }
+  int sel_e[kMaxTopK];
+  float sel_v[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      int best = -1;
+      float bv = 0.f;
+      for (int e = 0; e < N; ++e) {
+        const float v = row[e];
+        if (((allowed >> e) & 1u) && (best < 0 || v > bv)) { best = e; bv = v; }
+      }
+      best = best < 0 ? 0 : best;                 // unreachable guard (k <= candidates)
+      allowed &= ~(1u << best);
+      sel_e[j] = best;
+      sel_v[j] = row[best];
+    }
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) den += expf(sel_v[j] - sel_v[0]);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      a.idx[t * k + j] = sel_e[j];
+      a.w[t * k + j] = expf(sel_v[j] - sel_v[0]) / den;
+      atomicAdd(&hl[sel_e[j]], 1);
+    }
+  }
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   __shared__ float part[4096];           // d-split partials [KS][TM][NP]
   __shared__ float lt[TM * (kMaxExperts + 1)];
-  __shared__ float ps[4][kMaxExperts];
+  __shared__ float ps[RW][kMaxExperts];  // wave partial sums of p (large N)
+  __shared__ float pl[TM][SMALL_N + 1];  // per-token p (small N)
   __shared__ int hl[kMaxExperts];
   const int ldl = kMaxExperts + 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = a.N, k = a.k;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TM;
 
-  for (int e = threadIdx.x; e < kMaxExperts; e += 256) hl[e] = 0;
+  for (int e = threadIdx.x; e < kMaxExperts; e += RW * 64) hl[e] = 0;
   if (BF16) logits_bf16(a, t0, part, lt, ldl);
   else logits_f32(a, t0, lt, ldl);
   __syncthreads();
 
   if (a.logits) {
-    for (int q = threadIdx.x; q < TM * N; q += 256) {
-      int m = q / N, e = q % N;
+    for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
+      const int m = q / N, e = q % N;
       if (t0 + m < a.T) a.logits[(t0 + m) * N + e] = lt[m * ldl + e];
     }
   }
 
+  if (N <= SMALL_N) {
+    // one lane per token
+    const int m = threadIdx.x;
+    if (m < TM) {
+      if (t0 + m < a.T) {
+        select_lane(a, lt + m * ldl, pl[m], t0 + m, hl);
+      } else {
+        for (int e = 0; e < N; ++e) pl[m][e] = 0.f;
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += RW * 64) {
+      float sum = 0.f;
+      for (int m2 = 0; m2 < TM; ++m2) sum += pl[m2][e];
+      a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
+      a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
+    }
+    return;
+  }
+
+  // one wave per token
   float psr[4] = {0.f, 0.f, 0.f, 0.f};    // this wave's sum of p over its tokens
   const int G = a.n_groups > 1 ? a.n_groups : 1;
   const int gsz = N / G;
-  for (int m = wave; m < TM; m += 4) {
+  for (int m = wave; m < TM; m += RW) {
     const int64_t t = t0 + m;
     if (t >= a.T) break;
     const float* row = lt + m * ldl;
@@ -189,12 +314,12 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     bool ok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = lane + 64 * i;
+      const int e = lane + 64 * i;
       ok[i] = e < N;
       v[i] = ok[i] ? row[e] : -INFINITY;
     }
     // full softmax over all N (bias included, no group mask) for p
-    float mx = wave_max_f(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    const float mx = wave_max_f(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
     float z[4], zs = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -219,7 +344,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 #pragma unroll
           for (int q = 0; q < kMaxTopK; ++q) {
             if (q < a.gsk && val > top[q]) {
-              float tmp = top[q];
+              const float tmp = top[q];
               top[q] = val;
               val = tmp;
             }
@@ -232,7 +357,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       uint64_t gkey = lane < G ? sel_key(gs, lane) : 0ull;
       gmask = 0ull;
       for (int q = 0; q < a.topk_groups; ++q) {
-        uint64_t best = wave_max_u64(gkey);
+        const uint64_t best = wave_max_u64(gkey);
         int g = key_index(best);
         g = g < G ? g : G - 1;
         gmask |= 1ull << g;
@@ -243,7 +368,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     bool cand[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = lane + 64 * i;
+      const int e = lane + 64 * i;
       cand[i] = ok[i] && ((gmask >> (e / gsz)) & 1ull);
     }
     int sel_e[kMaxTopK];
@@ -254,10 +379,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         uint64_t kb = 0ull;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint64_t kk = cand[i] ? sel_key(v[i], lane + 64 * i) : 0ull;
+          const uint64_t kk = cand[i] ? sel_key(v[i], lane + 64 * i) : 0ull;
           kb = kk > kb ? kk : kb;
         }
-        uint64_t best = wave_max_u64(kb);
+        const uint64_t best = wave_max_u64(kb);
         int e = key_index(best);
         e = e < N ? e : N - 1;                    // unreachable guard (k <= candidates)
         sel_e[j] = e;
@@ -284,13 +409,14 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   // per-block partial statistics, combined over waves in wave order
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int e = lane + 64 * i;
+    const int e = lane + 64 * i;
     if (e < N) ps[wave][e] = psr[i];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += 256) {
-    float s = ((ps[0][e] + ps[1][e]) + ps[2][e]) + ps[3][e];
-    a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = s;
+  for (int e = threadIdx.x; e < N; e += RW * 64) {
+    float sum = 0.f;
+    for (int w = 0; w < RW; ++w) sum += ps[w][e];
+    a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
     a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
   }
 }
@@ -356,9 +482,9 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
               s.n_groups, s.topk_groups, s.group_score_k};
   dim3 grid(static_cast<unsigned>(ceil_div(s.T, TM)));
   if (s.dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(RW * 64), 0, st, a);
   else
-    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(RW * 64), 0, st, a);
   return hipGetLastError();
 }
 

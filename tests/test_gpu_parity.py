@@ -101,6 +101,15 @@ def test_capacity_one_and_drop_zero():
     assert gpu["offsets"][-1] == 8
 
 
+def test_many_tokens_with_capacity():
+    """80 dispatch blocks with a capacity that drops a few percent of the
+    assignments, on a cheap layer width."""
+    wl = si.Workload("mb", T=20011, d=64, N=16, k=2, F=128, act="swiglu", dtype="bf16",
+                     buf="bf16", capacity=2300)
+    gpu, _ = _run_and_check(wl)
+    assert gpu["drop"].sum() > 0
+
+
 def test_groups_k_le_group_span():
     wl = si.small("deepseek_v3", T=333, N=32, k=3, n_groups=4, topk_groups=1, F=128)
     _run_and_check(wl)
