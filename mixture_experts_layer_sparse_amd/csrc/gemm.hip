@@ -18,12 +18,14 @@
 //   * 8 waves (two per SIMD) in a WGM x WGN grid, each computing a block of
 //     the tile with v_mfma_f32_32x32x16_bf16, float32 accumulation; a wave whose
 //     rows all lie past the segment end skips its MFMAs;
-//   * K is streamed in 64-wide steps through two LDS stages, loaded straight
-//     from memory into LDS by buffer loads (no staging registers), the next
-//     step's loads in flight during this step's MFMAs; the 16-byte
-//     chunks of each LDS row are XOR-swizzled by the row index so that fragment
-//     reads are free of bank conflicts (the loads pick swizzled source chunks,
-//     so each 1 KB wave-load still lands contiguously);
+//   * K is streamed in 64-wide steps through two LDS stages, by one of two
+//     pipelines: (a) buffer loads straight into LDS (buffer_load ... lds), the
+//     next step's loads in flight during this step's MFMAs; (b) buffer loads
+//     into registers holding the next two steps, written to the free stage
+//     halfway through each step (more bytes in flight).  (a) is faster on the
+//     MFMA-bound 256-row tiles, (b) on the weight-streaming 128-row tiles;
+//     the 16-byte chunks of each LDS row are XOR-swizzled by the row index so
+//     that fragment reads are free of bank conflicts;
 //   * fp8 activations (e4m3 codes) stay fp8 in LDS and are widened to bf16
 //     exactly as fragments are read; the per-row scale multiplies the float32
 //     accumulator;
@@ -35,15 +37,13 @@
 
 #include "moe_internal.h"
 
-// Pipeline settings (compile-time tuning knobs; the defaults are the measured best).
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
+// register buffers of staged loads: 1 or 2 K steps in flight beyond the LDS stages
+#ifndef MOE_GEMM_RBUF
+#define MOE_GEMM_RBUF 2
 #endif
-#ifndef MOE_GEMM_NS
-#define MOE_GEMM_NS 2
-#endif
-#ifndef MOE_GEMM_INTERLEAVE
-#define MOE_GEMM_INTERLEAVE 0
+// 1: each XCD owns runs of consecutive tile ids; 0: tile id = round * grid + block
+#ifndef MOE_GEMM_XCD_MAP
+#define MOE_GEMM_XCD_MAP 1
 #endif
 
 namespace moe {
@@ -86,14 +86,25 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 16 bytes per lane from a buffer straight into LDS (lane i writes lds + 16*i).
+// 16 bytes per lane from a buffer into registers (reads past the end return zero).
 // Kept in a device function: the host compilation pass only needs the kernel stub.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (lane i writes lds + 16 * i).
+typedef __attribute__((address_space(3))) void* lds_ptr;
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
                                           uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)lds, 16, voff, soff, 0, 0);
 }
+
+// s_waitcnt on the LDS counter only (lgkmcnt = 0), leaving vector loads in flight.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_waitcnt on the vector-memory counter only (vmcnt = 0).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Buffer resource over [base, base + bytes): loads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
@@ -112,16 +123,10 @@ __device__ __forceinline__ int swz(int row) {
   return (row / (256 / RB)) % (RB / 16);
 }
 
-// s_waitcnt on the vector-memory counter only: vmcnt <= n (n < 64).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int EPI, bool FP8A>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
+  constexpr int BK = 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
   constexpr int ROWA = BK * SA, ROWB = BK * 2;     // bytes per tile row per stage
   constexpr int A_BYTES = BM * ROWA, B_BYTES = BN * ROWB;
@@ -137,17 +142,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for the load split");
   static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "load split");
   static_assert(!GATED || (WN / 2) % (1024 / ROWB) == 0, "a wave-load must not straddle W1 and W3");
-  static_assert(LPW * (NS - 2) < 64, "vmcnt range");
-  static_assert(NS * STAGE <= 144 * 1024, "LDS budget");
+  static_assert(2 * STAGE <= 144 * 1024, "LDS budget");
 
-  // one array per stage: every LDS access below names its stage's array, so the
-  // compiler can tell the stage being read from the stages the DMA is filling
-  // (with a single array it conservatively waits for all loads before any read)
+  // two LDS stages: step kt computes from one while step kt + 1 is written to the other
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm2[NS > 2 ? STAGE : 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm3[NS > 3 ? STAGE : 1024];
-  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   __shared__ int mt_start[kMaxExperts + 2];
   __shared__ int seg_off[kMaxExperts + 2];
   __shared__ int scan_tmp[2][kMaxExperts + 1];
@@ -194,7 +193,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     // tile order: expert-major, then n-tile, then the expert's m-tiles, so the
     // m-tiles of an expert consume each weight n-tile back to back (one HBM
     // read, the rest from L2); each XCD takes S consecutive tile ids per round
-    const int L = (round * 8 + xcd) * S + slot;
+    const int L = MOE_GEMM_XCD_MAP ? (round * 8 + xcd) * S + slot
+                                   : round * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
     if (L >= total) break;
     int lo = 0, hi = n_seg;                      // mt_start[lo]*NT <= L < mt_start[hi]*NT
     while (hi - lo > 1) {
@@ -243,26 +243,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       }
       b_off[j] = static_cast<uint32_t>((f * K) * 2 + c * 16);
     }
-    auto stage_ptr = [&](auto S) -> uint8_t* {
-      constexpr int q = decltype(S)::value;
-      if constexpr (q == 0) return sm0;
-      else if constexpr (q == 1) return sm1;
-      else if constexpr (q == 2) return sm2;
-      else return sm3;
-    };
-    auto issue_to = [&](int kt, uint8_t* stg) {
-      const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
-#pragma unroll
-      for (int j = 0; j < A_PW; ++j) lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
-#pragma unroll
-      for (int j = 0; j < B_PW; ++j) {
-        const int gi = wave * B_PW + j;
-        // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
-        const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
-        lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
-      }
-    };
-
     f32x16 acc[TMI][TNI];
 #pragma unroll
     for (int i = 0; i < TMI; ++i)
@@ -271,83 +251,128 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // NS-stage pipeline: the loads of step kt + NS - 1 are issued while step kt
-    // computes.  Each wave waits only for its own loads of step kt (vmcnt), then
-    // a barrier makes every wave's loads visible and marks the stage of step
-    // kt - 1 free for reuse.  The loop is unrolled by NS so that each step's
-    // stage is a compile-time choice.
-    auto step = [&](int kt, auto S) {
-      constexpr int q = decltype(S)::value;
-      const int ahead = KT - 1 - kt;             // steps after kt already issued (<= NS - 2)
-      if (ahead >= NS - 2) wait_vmcnt<LPW * (NS - 2)>();
-      else if (NS > 3 && ahead == 2) wait_vmcnt<LPW * 2>();
-      else if (NS > 2 && ahead == 1) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      if (kt + NS - 1 < KT)
-        issue_to(kt + NS - 1, stage_ptr(std::integral_constant<int, (q + NS - 1) % NS>{}));
-      const uint8_t* sA = stage_ptr(S);
-      const uint8_t* sB = sA + A_BYTES;
-      if (wave_rows) {
-        // fragments of k-substep kk + 1 are read while substep kk's MFMAs run
-        bf16x8 af[2][TMI], bfr[2][TNI];
-        auto read_frags = [&](int kk, bf16x8* a, bf16x8* b) {
-          const int cc = kk * 2 + fk;             // 8-element k chunk of this lane
+    // K steps of this wave's loads, staged in registers: A_PW + B_PW pieces of
+    // 16 bytes per lane, each landing at lane * 16 of its 1 KB block in LDS.
+    // RB register buffers keep RB steps of loads in flight.
+    constexpr int RB = REG ? MOE_GEMM_RBUF : 1;
+    u32x4 ra[RB][A_PW], rb[RB][B_PW];
+    auto load_regs = [&](int kt, auto Q) {
+      constexpr int q = decltype(Q)::value;
+      const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
-          for (int i = 0; i < TMI; ++i) {
-            const int r = wm * WM + i * 32 + fr;
-            if (FP8A) {
-              const uint2 v = *reinterpret_cast<const uint2*>(
-                  sA + r * ROWA + (((cc >> 1) ^ swz<ROWA>(r)) << 4) + ((cc & 1) << 3));
-              const uint4 w = fp8x8_to_bf16x8(v);
-              a[i] = *reinterpret_cast<const bf16x8*>(&w);
-            } else {
-              a[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz<ROWA>(r)) << 4));
-            }
-          }
+      for (int j = 0; j < A_PW; ++j) ra[q][j] = buf_load16(rsA, a_off[j], ka);
 #pragma unroll
-          for (int j = 0; j < TNI; ++j) {
-            const int n = wn * WN + j * 32 + fr;
-            b[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
-          }
-        };
-        read_frags(0, af[0], bfr[0]);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          const int cb = kk & 1;
-          if (kk + 1 < BK / 16) read_frags(kk + 1, af[cb ^ 1], bfr[cb ^ 1]);
-#pragma unroll
-          for (int i = 0; i < TMI; ++i)
-#pragma unroll
-            for (int j = 0; j < TNI; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
-#if MOE_GEMM_INTERLEAVE
-          if (kk + 1 < BK / 16) {
-            // one fragment read between consecutive MFMAs
-#pragma unroll
-            for (int q = 0; q < TMI + TNI; ++q) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, TMI * TNI - (TMI + TNI), 0);
-          }
-#endif
-        }
+      for (int j = 0; j < B_PW; ++j) {
+        const int gi = wave * B_PW + j;
+        // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
+        const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
+        rb[q][j] = buf_load16(w3 ? rsB1 : rsB0, b_off[j], kb);
       }
     };
+    auto store_regs = [&](uint8_t* stg, auto Q) {
+      constexpr int q = decltype(Q)::value;
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j)
+        *reinterpret_cast<u32x4*>(stg + (wave * A_PW + j) * 1024 + lane * 16) = ra[q][j];
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j)
+        *reinterpret_cast<u32x4*>(stg + A_BYTES + (wave * B_PW + j) * 1024 + lane * 16) = rb[q][j];
+    };
+    auto compute = [&](const uint8_t* sA, int kk) {
+      const uint8_t* sB = sA + A_BYTES;
+      const int cc = kk * 2 + fk;                 // 8-element k chunk of this lane
+      bf16x8 af[TMI], bfr[TNI];
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const int r = wm * WM + i * 32 + fr;
+        if (FP8A) {
+          const uint2 v = *reinterpret_cast<const uint2*>(
+              sA + r * ROWA + (((cc >> 1) ^ swz<ROWA>(r)) << 4) + ((cc & 1) << 3));
+          const uint4 w = fp8x8_to_bf16x8(v);
+          af[i] = *reinterpret_cast<const bf16x8*>(&w);
+        } else {
+          af[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz<ROWA>(r)) << 4));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TNI; ++j) {
+        const int n = wn * WN + j * 32 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
 
-    wait_vmcnt<0>();                              // the previous tile's stores are out:
-                                                  // vmcnt now counts only this tile's loads
-    issue_to(0, sm0);
-    if (1 < KT) issue_to(1, sm1);
-    if (NS > 2 && 2 < KT) issue_to(2, stage_ptr(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}));
-    for (int kt0 = 0; kt0 < KT; kt0 += NS) {
-      step(kt0, std::integral_constant<int, 0>{});
-      if (kt0 + 1 < KT) step(kt0 + 1, std::integral_constant<int, 1>{});
-      if (NS > 2 && kt0 + 2 < KT) step(kt0 + 2, std::integral_constant<int, (NS > 2 ? 2 : 0)>{});
-      if (NS > 3 && kt0 + 3 < KT) step(kt0 + 3, std::integral_constant<int, (NS > 3 ? 3 : 0)>{});
+    if constexpr (REG) {
+      // Register-staged pipeline: while step kt computes from one LDS stage,
+      // registers hold the loads of the next RB steps; halfway through step kt
+      // the registers of step kt + 1 are written to the other stage and refilled
+      // with the loads of step kt + 1 + RB, so RB steps of global loads stay in
+      // flight.  One barrier per step publishes the written stage and frees the
+      // one just read.  Register buffer q holds steps congruent to q mod RB.
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, (RB > 1 ? 1 : 0)>;
+      auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, auto Q) {
+        if (wave_rows) {
+#pragma unroll
+          for (int kk = 0; kk < BK / 32; ++kk) compute(cur, kk);
+        }
+        if (kt + 1 < KT) store_regs(nxt, Q);
+        if (kt + 1 + RB < KT) load_regs(kt + 1 + RB, Q);
+        if (wave_rows) {
+#pragma unroll
+          for (int kk = BK / 32; kk < BK / 16; ++kk) compute(cur, kk);
+        }
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      };
+      load_regs(0, I0{});
+      store_regs(sm0, I0{});
+      if (KT > 1) load_regs(1, I1{});
+      if (RB > 1 && KT > 2) load_regs(2, I0{});
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      // step kt stores the registers of step kt + 1: buffer (kt + 1) % RB
+      for (int kt = 0; kt < KT; kt += 2) {
+        step(kt, sm0, sm1, I1{});
+        if (kt + 1 < KT) step(kt + 1, sm1, sm0, I0{});
+      }
+    } else {
+      // LDS-DMA pipeline: buffer loads write straight into LDS (no registers);
+      // the loads of step kt + 1 go to the other stage while step kt computes.
+      // Each stage is its own array, so the compiler can tell the stage being
+      // read from the one being filled and does not wait for the DMA before
+      // fragment reads; each wave waits for its own loads, then one barrier.
+      auto dma = [&](int kt, uint8_t* stg) {
+        const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+        for (int j = 0; j < A_PW; ++j) lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
+#pragma unroll
+        for (int j = 0; j < B_PW; ++j) {
+          const int gi = wave * B_PW + j;
+          const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
+          lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
+        }
+      };
+      auto dstep = [&](int kt, const uint8_t* cur, uint8_t* nxt) {
+        wait_vm0();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < KT) dma(kt + 1, nxt);
+        if (wave_rows) {
+#pragma unroll
+          for (int kk = 0; kk < BK / 16; ++kk) compute(cur, kk);
+        }
+      };
+      dma(0, sm0);
+      for (int kt = 0; kt < KT; kt += 2) {
+        dstep(kt, sm0, sm1);
+        if (kt + 1 < KT) dstep(kt + 1, sm1, sm0);
+      }
+      __builtin_amdgcn_s_barrier();               // every wave is done with the stages
     }
-    __builtin_amdgcn_s_barrier();                 // every wave is done with the stages
 
     // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32
 #pragma unroll
@@ -442,14 +467,14 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------- launch --
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int EPI, bool FP8A>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, BK, NS, EPI, FP8A>), dim3(grid),
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, st, g);
   return hipGetLastError();
 }
@@ -461,21 +486,19 @@ int pick_bm(int64_t rows, int n_seg) {
 
 
 // 8 waves (two per SIMD, so one wave's MFMAs cover the other's waits) in a
-// 2 x 4 grid: 128x64 per wave at BM = 256, 64x64 at BM = 128.  Operands stream
-// through 2 LDS stages of 64-wide K steps (measured: 4 stages of 32 are slower,
-// the extra barriers cost more than the longer prefetch gains).
+// 2 x 4 grid: 128x64 per wave at BM = 256, 64x64 at BM = 128.  Measured choice of
+// load path: LDS-DMA for the MFMA-bound 256-row tiles, the register-staged
+// pipeline (more bytes in flight) for the weight-streaming 128-row tiles.
 template <int EPI, bool FP8A>
 hipError_t dispatch_up(int bm, const GemmArgs& g, int64_t rows, int n_seg, bool dense,
                        hipStream_t st) {
-  constexpr int BK = FP8A ? 64 : MOE_GEMM_BK;
-  constexpr int NS = FP8A ? 2 : MOE_GEMM_NS;
   const int nt = g.nt;
   if (bm == 256) {
     int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
-    return launch_gg_on<256, 256, 2, 4, BK, NS, EPI, FP8A>(g, mtu * nt, st);
+    return launch_gg_on<256, 256, 2, 4, EPI, FP8A, false>(g, mtu * nt, st);
   }
   int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
-  return launch_gg_on<128, 256, 2, 4, BK, NS, EPI, FP8A>(g, mtu * nt, st);
+  return launch_gg_on<128, 256, 2, 4, EPI, FP8A, true>(g, mtu * nt, st);
 }
 
 }  // namespace
