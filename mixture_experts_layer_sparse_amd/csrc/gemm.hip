@@ -66,7 +66,8 @@ struct GemmArgs {
   const uint16_t* b1;      // [n_seg][n_out][K]  (W3, SwiGLU only)
   int64_t b_stride;        // n_out * K
   uint16_t* out;           // [rows][n_out]
-  int nt;                  // n-tiles
+  int nt;                  // n-tiles of the tile list
+  int split_slots;         // > 0: tail split over this many workgroup slots (see below)
 };
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
@@ -123,7 +124,15 @@ __device__ __forceinline__ int swz(int row) {
   return (row / (256 / RB)) % (RB / 16);
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG>
+// Tail split.  With split_slots = S > 0 the tile list (m-tiles of height MBM,
+// n-tiles of g.nt) is cut at total - r, r = total % S, when 0 < r <= S / 2: the
+// main launch (TAIL = false, tile BM x BN = MBM x BN) runs the tiles before the
+// cut, whole rounds of S workgroups; the tail launch (TAIL = true, tile of half
+// height and half width) runs each of the r remaining tiles as four quarters,
+// so that the last round is not left mostly idle.  Both launches count the
+// same tile list from `offsets`; every output element is still computed by one
+// workgroup over the whole K.
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
   constexpr int BK = 64;
@@ -156,6 +165,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   const int wm = wave / WGN, wn = wave % WGN;
   const int n_seg = g.offsets ? g.n_seg : 1;
   const int K = g.K, KT = K / BK;
+  constexpr int MBM = TAIL ? 2 * BM : BM;        // m-tile height of the tile list
 
   // m-tiles per segment and their exclusive scan (segments <= 256)
   {
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     if (tid < n_seg) {
       const int so = g.offsets ? g.offsets[tid] : 0;
       const int eo = g.offsets ? g.offsets[tid + 1] : static_cast<int>(g.rows);
-      ntile = (eo - so + BM - 1) / BM;
+      ntile = (eo - so + MBM - 1) / MBM;
       seg_off[tid] = so;
       if (tid == n_seg - 1) seg_off[n_seg] = eo;
     }
@@ -184,6 +194,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   const int MT = __builtin_amdgcn_readfirstlane(mt_start[n_seg]);
   const int NT = g.nt;
   const int total = MT * NT;
+  int cut = total;                               // main tiles [0, cut), tail tiles [cut, total)
+  if (g.split_slots > 0) {
+    const int r = total % g.split_slots;
+    if (r > 0 && 2 * r <= g.split_slots) cut = total - r;
+  }
+  const int items = TAIL ? 4 * (total - cut) : cut;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, S = gridDim.x >> 3;
 
   // per-lane LDS fragment offsets (rows i*32 + lane%32 share the swizzle)
@@ -195,21 +211,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     // read, the rest from L2); each XCD takes S consecutive tile ids per round
     const int L = MOE_GEMM_XCD_MAP ? (round * 8 + xcd) * S + slot
                                    : round * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
-    if (L >= total) break;
-    int lo = 0, hi = n_seg;                      // mt_start[lo]*NT <= L < mt_start[hi]*NT
+    if (L >= items) break;
+    const int Lm = TAIL ? cut + (L >> 2) : L;    // tile of the list (quarter L & 3 in the tail)
+    int lo = 0, hi = n_seg;                      // mt_start[lo]*NT <= Lm < mt_start[hi]*NT
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (mt_start[mid] * NT <= L) lo = mid; else hi = mid;
+      if (mt_start[mid] * NT <= Lm) lo = mid; else hi = mid;
     }
     // values read from LDS are the same in every lane: make that explicit so
     // that the buffer descriptors below live in scalar registers
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int mte = __builtin_amdgcn_readfirstlane(mt_start[e + 1] - mt_start[e]);
-    const int local = L - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
-    const int ntile = local / mte;
-    const int mloc = local - ntile * mte;
-    const int row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * BM;
+    const int local = Lm - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
+    const int nt_list = local / mte;
+    const int mloc = local - nt_list * mte;
+    const int row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * MBM + (TAIL ? ((L >> 1) & 1) * BM : 0);
     const int row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
+    const int ntile = TAIL ? 2 * nt_list + (L & 1) : nt_list;
+    // a tail quarter wholly past the segment end or the last column has no work
+    if (TAIL && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
     // a wave whose rows all lie past the segment end skips its MFMAs
     const bool wave_rows = row0 + wm * WM < row_end;
 
@@ -467,14 +487,14 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------- launch --
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG>), dim3(grid),
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, st, g);
   return hipGetLastError();
 }
@@ -488,17 +508,22 @@ int pick_bm(int64_t rows, int n_seg) {
 // 8 waves (two per SIMD, so one wave's MFMAs cover the other's waits) in a
 // 2 x 4 grid: 128x64 per wave at BM = 256, 64x64 at BM = 128.  Measured choice of
 // load path: LDS-DMA for the MFMA-bound 256-row tiles, the register-staged
-// pipeline (more bytes in flight) for the weight-streaming 128-row tiles.
+// pipeline (more bytes in flight) for the weight-streaming 128-row tiles.  The
+// 256-row tile list is tail-split; its 128x128 quarters run on 4 waves of 64x64.
 template <int EPI, bool FP8A>
-hipError_t dispatch_up(int bm, const GemmArgs& g, int64_t rows, int n_seg, bool dense,
+hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense,
                        hipStream_t st) {
   const int nt = g.nt;
   if (bm == 256) {
-    int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
-    return launch_gg_on<256, 256, 2, 4, EPI, FP8A, false>(g, mtu * nt, st);
+    const int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
+    g.split_slots = (device_cu_count() / 8) * 8;
+    hipError_t err = launch_gg_on<256, 256, 2, 4, EPI, FP8A, false, false>(g, mtu * nt, st);
+    if (err != hipSuccess) return err;
+    return launch_gg_on<128, 128, 2, 2, EPI, FP8A, false, true>(g, 4 * mtu * nt, st);
   }
-  int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
-  return launch_gg_on<128, 256, 2, 4, EPI, FP8A, true>(g, mtu * nt, st);
+  const int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
+  g.split_slots = 0;
+  return launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
 }
 
 }  // namespace

@@ -117,14 +117,32 @@ def check_layer(wl, inp, gpu, y_tokens=None, max_adopted=None):
     rows = full["pos"][toks]
     rows = rows[rows >= 0]
     if rows.size:
-        errs["out"] = compare.rel_l2(as_values(gpu["out"][rows], wl.dtype), full["o_rows"][rows])
-        assert errs["out"] <= tol, errs
+        got, want = as_values(gpu["out"][rows], wl.dtype), full["o_rows"][rows]
+        errs["out"] = compare.rel_l2(got, want)
+        # every row on its own too, so that one wrong tile cannot hide in the mean
+        num = np.sqrt(np.sum((got - want) ** 2, axis=1))
+        den = np.maximum(np.sqrt(np.sum(want ** 2, axis=1)), 1e-300)
+        errs["out_row_max"] = float(np.max(np.where(np.any(want != 0, axis=1), num / den, num)))
+        assert errs["out"] <= tol and errs["out_row_max"] <= tol, errs
     if wl.shared:
         errs["shared"] = compare.rel_l2(as_values(gpu["out_shared"][toks], wl.dtype), full["shared"])
         assert errs["shared"] <= tol, errs
     errs["y"] = compare.rel_l2(as_values(gpu["y"][toks], wl.dtype), full["y"])
     assert errs["y"] <= tol, errs
     return errs
+
+
+def gemm_tail_split(counts, bm, nt):
+    """The grouped GEMMs' tail split, restated on the host: m-tiles of height bm
+    per expert segment times nt n-tiles, cut at total - r, r = total % slots,
+    when 0 < r <= slots / 2 (slots: the device's CUs, rounded down to a
+    multiple of 8).  Returns (total, tiles before the cut, slots)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slots = (cus // 8) * 8
+    total = int(np.sum((np.asarray(counts) + bm - 1) // bm)) * nt
+    r = total % slots
+    cut = total - r if 0 < r <= slots // 2 else total
+    return total, cut, slots
 
 
 def sample_tokens(T, n, seed=0):

@@ -110,6 +110,32 @@ def test_many_tokens_with_capacity():
     assert gpu["drop"].sum() > 0
 
 
+@pytest.mark.parametrize("act,buf", [("swiglu", "bf16"), ("relu", "fp8")])
+def test_gemm_tail_quarters_only(act, buf):
+    """Fewer 256-row tiles than half the CUs: every tile runs as 128x128
+    quarters, including quarters wholly past a segment end or past the last
+    output column (d = 320, and F = 384 with ReLU)."""
+    from moe_gpu_util import gemm_tail_split
+    wl = si.Workload("tq", T=2000, d=320, N=8, k=2, F=384, act=act, dtype="bf16", buf=buf)
+    gpu, errs = _run_and_check(wl)
+    nt_up = -(-wl.F // 128) if act == "swiglu" else -(-wl.F // 256)
+    for nt in (nt_up, -(-wl.d // 256)):
+        total, cut, _ = gemm_tail_split(gpu["kept_counts"], 256, nt)
+        assert cut == 0 and total > 0, (total, cut)
+
+
+def test_gemm_main_and_tail():
+    """Whole rounds of 256x256 tiles plus a tail of quarters in both GEMMs;
+    every token's y is compared."""
+    from moe_gpu_util import gemm_tail_split
+    wl = si.Workload("tm", T=36000, d=256, N=16, k=2, F=256, act="swiglu", dtype="bf16",
+                     buf="bf16")
+    gpu, errs = _run_and_check(wl)
+    for nt in (wl.F // 128, 1):
+        total, cut, slots = gemm_tail_split(gpu["kept_counts"], 256, nt)
+        assert slots <= cut < total, (total, cut, slots)
+
+
 def test_groups_k_le_group_span():
     wl = si.small("deepseek_v3", T=333, N=32, k=3, n_groups=4, topk_groups=1, F=128)
     _run_and_check(wl)
