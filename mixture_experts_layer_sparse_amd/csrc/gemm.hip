@@ -19,11 +19,12 @@
 //     the tile with v_mfma_f32_32x32x16_bf16, float32 accumulation; a wave whose
 //     rows all lie past the segment end skips its MFMAs;
 //   * K is streamed in 64-wide steps through two LDS stages, by one of two
-//     pipelines: (a) buffer loads straight into LDS (buffer_load ... lds), the
-//     next step's loads in flight during this step's MFMAs; (b) buffer loads
+//     pipelines: (a) buffer loads straight into LDS (buffer_load ... lds),
+//     double-buffered fragments, and the loads of step kt + 2 issued one per
+//     MFMA right after the barrier that frees their stage; (b) buffer loads
 //     into registers holding the next two steps, written to the free stage
 //     halfway through each step (more bytes in flight).  (a) is faster on the
-//     MFMA-bound 256-row tiles, (b) on the weight-streaming 128-row tiles;
+//     256-row tiles, (b) on the weight-streaming 128-row tiles;
 //     the 16-byte chunks of each LDS row are XOR-swizzled by the row index so
 //     that fragment reads are free of bank conflicts;
 //   * fp8 activations (e4m3 codes) stay fp8 in LDS and are widened to bf16
@@ -34,6 +35,7 @@
 //     on the accumulators and h is written once, in bf16.
 // The float32 path (small correctness shapes) is a plain dot-product kernel.
 #include <type_traits>
+#include <utility>
 
 #include "moe_internal.h"
 
@@ -70,7 +72,15 @@ struct GemmArgs {
   int split_slots;         // > 0: tail split over this many workgroup slots (see below)
 };
 
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+// silu(u) = u / (1 + e^-u) with the hardware reciprocal (about 1 ulp): the result is rounded to
+// bf16 (8 significant bits) right after, so the exact quotient buys nothing
+__device__ __forceinline__ float silu_fast(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
+// float32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
 
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
   // e4m3 -> float32 is exact, and every e4m3 value is a bf16 value, so the
@@ -106,6 +116,21 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // s_waitcnt on the vector-memory counter only (vmcnt = 0).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+
+
+// Scheduling pattern for the machine scheduler: for q = 0 .. NMM - 1, one MFMA
+// followed by the vector-memory loads that fall to it when LPW loads are spread
+// evenly over NMM MFMAs.
+template <int CNT>
+__device__ __forceinline__ void sched_mfma_then_loads() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+  if constexpr (CNT > 0) __builtin_amdgcn_sched_group_barrier(0x020, CNT, 0);   // VMEM read
+}
+template <int NMM, int LPW, int... Q>
+__device__ __forceinline__ void sched_mfma_loads(std::integer_sequence<int, Q...>) {
+  (sched_mfma_then_loads<(Q + 1) * LPW / NMM - Q * LPW / NMM>(), ...);
+}
 
 // Buffer resource over [base, base + bytes): loads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
@@ -153,7 +178,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   static_assert(!GATED || (WN / 2) % (1024 / ROWB) == 0, "a wave-load must not straddle W1 and W3");
   static_assert(2 * STAGE <= 144 * 1024, "LDS budget");
 
-  // two LDS stages: step kt computes from one while step kt + 1 is written to the other
+  // two LDS stages, each its own array: step kt computes from one while step
+  // kt + 1 is written to the other
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
   __shared__ int mt_start[kMaxExperts + 2];
@@ -205,51 +231,60 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // per-lane LDS fragment offsets (rows i*32 + lane%32 share the swizzle)
   const int fr = lane & 31, fk = lane >> 5;
 
-  for (int round = 0;; ++round) {
-    // tile order: expert-major, then n-tile, then the expert's m-tiles, so the
-    // m-tiles of an expert consume each weight n-tile back to back (one HBM
-    // read, the rest from L2); each XCD takes S consecutive tile ids per round
-    const int L = MOE_GEMM_XCD_MAP ? (round * 8 + xcd) * S + slot
-                                   : round * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
-    if (L >= items) break;
-    const int Lm = TAIL ? cut + (L >> 2) : L;    // tile of the list (quarter L & 3 in the tail)
-    int lo = 0, hi = n_seg;                      // mt_start[lo]*NT <= Lm < mt_start[hi]*NT
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (mt_start[mid] * NT <= Lm) lo = mid; else hi = mid;
-    }
-    // values read from LDS are the same in every lane: make that explicit so
-    // that the buffer descriptors below live in scalar registers
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int mte = __builtin_amdgcn_readfirstlane(mt_start[e + 1] - mt_start[e]);
-    const int local = Lm - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
-    const int nt_list = local / mte;
-    const int mloc = local - nt_list * mte;
-    const int row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * MBM + (TAIL ? ((L >> 1) & 1) * BM : 0);
-    const int row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
-    const int ntile = TAIL ? 2 * nt_list + (L & 1) : nt_list;
-    // a tail quarter wholly past the segment end or the last column has no work
-    if (TAIL && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
-    // a wave whose rows all lie past the segment end skips its MFMAs
-    const bool wave_rows = row0 + wm * WM < row_end;
-
-    // buffer resources: A from this tile's first row (reads past the buffer
-    // return zero), B per expert matrix
-    const uint8_t* a_tile = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(row0) * K * SA;
-    const __amdgpu_buffer_rsrc_t rsA =
-        make_rsrc(a_tile, static_cast<uint64_t>(g.rows - row0) * K * SA);
-    const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
-    const __amdgpu_buffer_rsrc_t rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
-    const __amdgpu_buffer_rsrc_t rsB1 = GATED ? make_rsrc(g.b1 + e * g.b_stride, b_bytes) : rsB0;
-
-    // per-lane source offsets of this wave's loads (the K step is added as soffset)
-    uint32_t a_off[A_PW], b_off[B_PW];
+  // per-lane source offsets of this wave's A loads (the K step is added as
+  // soffset); relative to the tile's first row, so the same for every tile
+  uint32_t a_off[A_PW];
 #pragma unroll
-    for (int j = 0; j < A_PW; ++j) {
-      const int r = (wave * A_PW + j) * (1024 / ROWA) + lane / A_CPR;
-      const int c = (lane % A_CPR) ^ swz<ROWA>(r);
-      a_off[j] = static_cast<uint32_t>(r * K * SA + c * 16);
+  for (int j = 0; j < A_PW; ++j) {
+    const int r = (wave * A_PW + j) * (1024 / ROWA) + lane / A_CPR;
+    const int c = (lane % A_CPR) ^ swz<ROWA>(r);
+    a_off[j] = static_cast<uint32_t>(r * K * SA + c * 16);
+  }
+
+  // The current tile (wave-uniform values).  Tile order: expert-major, then
+  // n-tile, then the expert's m-tiles, so the m-tiles of an expert consume
+  // each weight n-tile back to back (one HBM read, the rest from L2); each XCD
+  // takes S consecutive tile ids per round.
+  int round = -1, row0 = 0, row_end = 0, ntile = 0, e = 0;
+  auto next_tile = [&]() -> bool {
+    for (;;) {
+      ++round;
+      const int L = MOE_GEMM_XCD_MAP ? (round * 8 + xcd) * S + slot
+                                     : round * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
+      if (L >= items) return false;
+      const int Lm = TAIL ? cut + (L >> 2) : L;  // tile of the list (quarter L & 3 in the tail)
+      int lo = 0, hi = n_seg;                    // mt_start[lo]*NT <= Lm < mt_start[hi]*NT
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (mt_start[mid] * NT <= Lm) lo = mid; else hi = mid;
+      }
+      // values read from LDS are the same in every lane: make that explicit so
+      // that the buffer descriptors live in scalar registers
+      e = __builtin_amdgcn_readfirstlane(lo);
+      const int mte = __builtin_amdgcn_readfirstlane(mt_start[e + 1] - mt_start[e]);
+      const int local = Lm - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
+      const int nt_list = local / mte;
+      const int mloc = local - nt_list * mte;
+      row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * MBM + (TAIL ? ((L >> 1) & 1) * BM : 0);
+      row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
+      ntile = TAIL ? 2 * nt_list + (L & 1) : nt_list;
+      // a tail quarter wholly past the segment end or the last column has no work
+      if (TAIL && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
+      return true;
     }
+  };
+
+  // buffer resources of the current tile: A from its first row (reads past
+  // the buffer return zero), B per expert matrix; per-lane B offsets
+  __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.a, 0), rsB0 = rsA, rsB1 = rsA;
+  uint32_t b_off[B_PW];
+  bool wave_rows = false;                        // a wave whose rows all lie past the segment end skips its MFMAs
+  auto bind_tile = [&]() {
+    const uint8_t* a_tile = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(row0) * K * SA;
+    rsA = make_rsrc(a_tile, static_cast<uint64_t>(g.rows - row0) * K * SA);
+    const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
+    rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
+    rsB1 = GATED ? make_rsrc(g.b1 + e * g.b_stride, b_bytes) : rsB0;
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
       const int n = (wave * B_PW + j) * (1024 / ROWB) + lane / B_CPR;
@@ -263,7 +298,200 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       }
       b_off[j] = static_cast<uint32_t>((f * K) * 2 + c * 16);
     }
-    f32x16 acc[TMI][TNI];
+    wave_rows = row0 + wm * WM < row_end;
+  };
+
+  f32x16 acc[TMI][TNI];
+
+  // K steps of this wave's loads, staged in registers: A_PW + B_PW pieces of
+  // 16 bytes per lane, each landing at lane * 16 of its 1 KB block in LDS.
+  // RB register buffers keep RB steps of loads in flight.
+  constexpr int RB = REG ? MOE_GEMM_RBUF : 1;
+  u32x4 ra[RB][A_PW], rb[RB][B_PW];
+  auto load_regs = [&](int kt, auto Q) {
+    constexpr int q = decltype(Q)::value;
+    const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j) ra[q][j] = buf_load16(rsA, a_off[j], ka);
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+      const int gi = wave * B_PW + j;
+      // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
+      const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
+      rb[q][j] = buf_load16(w3 ? rsB1 : rsB0, b_off[j], kb);
+    }
+  };
+  auto store_regs = [&](uint8_t* stg, auto Q) {
+    constexpr int q = decltype(Q)::value;
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j)
+      *reinterpret_cast<u32x4*>(stg + (wave * A_PW + j) * 1024 + lane * 16) = ra[q][j];
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j)
+      *reinterpret_cast<u32x4*>(stg + A_BYTES + (wave * B_PW + j) * 1024 + lane * 16) = rb[q][j];
+  };
+  auto compute = [&](const uint8_t* sA, int kk) {
+    const uint8_t* sB = sA + A_BYTES;
+    const int cc = kk * 2 + fk;                 // 8-element k chunk of this lane
+    bf16x8 af[TMI], bfr[TNI];
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int r = wm * WM + i * 32 + fr;
+      if (FP8A) {
+        const uint2 v = *reinterpret_cast<const uint2*>(
+            sA + r * ROWA + (((cc >> 1) ^ swz<ROWA>(r)) << 4) + ((cc & 1) << 3));
+        const uint4 w = fp8x8_to_bf16x8(v);
+        af[i] = *reinterpret_cast<const bf16x8*>(&w);
+      } else {
+        af[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz<ROWA>(r)) << 4));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+      const int n = wn * WN + j * 32 + fr;
+      bfr[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Register-staged pipeline: while step kt computes from one LDS stage,
+  // registers hold the loads of the next RB steps; halfway through step kt
+  // the registers of step kt + 1 are written to the other stage and refilled
+  // with the loads of step kt + 1 + RB, so RB steps of global loads stay in
+  // flight.  One barrier per step publishes the written stage and frees the
+  // one just read.  Register buffer q holds steps congruent to q mod RB.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, (RB > 1 ? 1 : 0)>;
+  auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, auto Q) {
+    if (wave_rows) {
+#pragma unroll
+      for (int kk = 0; kk < BK / 32; ++kk) compute(cur, kk);
+    }
+    if (kt + 1 < KT) store_regs(nxt, Q);
+    if (kt + 1 + RB < KT) load_regs(kt + 1 + RB, Q);
+    if (wave_rows) {
+#pragma unroll
+      for (int kk = BK / 32; kk < BK / 16; ++kk) compute(cur, kk);
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  // LDS-DMA pipeline: buffer loads write straight into LDS (no registers),
+  // each stage its own array so that the compiler can tell the stage being
+  // read from the one being filled and adds no wait before fragment reads.
+  // Fragments are double-buffered in registers: the reads of slice kk + 1
+  // are in flight while slice kk's MFMAs run.  The last slice's fragments
+  // are read before the step barrier, so its MFMAs run after it, with the
+  // loads of step kt + 2 (into the stage just freed) issued one after each
+  // MFMA: a wave that issues them all at once stalls on the full load
+  // queue with its MFMAs unissued.
+  auto dma = [&](int kt, uint8_t* stg) {
+    const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j) lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+      const int gi = wave * B_PW + j;
+      const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
+      lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
+    }
+  };
+  bf16x8 fa[2][TMI], fb[2][TNI];
+  auto ldfr = [&](const uint8_t* sA, int kk, auto P) {
+    constexpr int p = decltype(P)::value;
+    const uint8_t* sB = sA + A_BYTES;
+    const int cc = kk * 2 + fk;
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int r = wm * WM + i * 32 + fr;
+      if (FP8A) {
+        const uint2 v = *reinterpret_cast<const uint2*>(
+            sA + r * ROWA + (((cc >> 1) ^ swz<ROWA>(r)) << 4) + ((cc & 1) << 3));
+        const uint4 w = fp8x8_to_bf16x8(v);
+        fa[p][i] = *reinterpret_cast<const bf16x8*>(&w);
+      } else {
+        fa[p][i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz<ROWA>(r)) << 4));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+      const int n = wn * WN + j * 32 + fr;
+      fb[p][j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
+    }
+  };
+  auto mm = [&](auto P) {
+    constexpr int p = decltype(P)::value;
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+  };
+  // MFMAs of fragment buffer P with the loads of step kt2 into stg spread
+  // between them.  Every wave runs these MFMAs, also one whose rows all lie
+  // past the segment end (its results are never stored): a branch here
+  // would duplicate the loads, and the compiler then no longer tells the
+  // two stages apart and waits for all loads before every fragment read.
+  // Past the last step the loads go through an empty descriptor (every
+  // lane out of range: no memory access), which keeps this a single block.
+  const __amdgpu_buffer_rsrc_t rs_null = make_rsrc(g.b0, 0);
+  auto mm_dma = [&](auto P, int kt2, uint8_t* stg) {
+    constexpr int p = decltype(P)::value;
+    constexpr int NMM = TMI * TNI;
+    const bool live = kt2 < KT;
+    const __amdgpu_buffer_rsrc_t ra = live ? rsA : rs_null;
+    const __amdgpu_buffer_rsrc_t rb0 = live ? rsB0 : rs_null;
+    const __amdgpu_buffer_rsrc_t rb1 = live ? rsB1 : rs_null;
+    const uint32_t ka = live ? static_cast<uint32_t>(kt2 * BK * SA) : 0u;
+    const uint32_t kb = live ? static_cast<uint32_t>(kt2 * BK * 2) : 0u;
+    auto issue = [&](int u) {
+      if (u < A_PW) {
+        lds_dma16(ra, stg + (wave * A_PW + u) * 1024, a_off[u], ka);
+      } else {
+        const int j = u - A_PW, gi = wave * B_PW + j;
+        const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
+        lds_dma16(w3 ? rb1 : rb0, stg + A_BYTES + gi * 1024, b_off[j], kb);
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < NMM; ++q) {
+      acc[q / TNI][q % TNI] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          fa[p][q / TNI], fb[p][q % TNI], acc[q / TNI][q % TNI], 0, 0, 0);
+#pragma unroll
+      for (int u = q * LPW / NMM; u < (q + 1) * LPW / NMM; ++u) issue(u);
+    }
+    // keep that order through scheduling: one MFMA, then its loads
+    sched_mfma_loads<NMM, LPW>(std::make_integer_sequence<int, NMM>{});
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  static_assert(BK / 16 == 4, "four K slices per step");
+  // invariant at step entry: fragments of (cur, slice 0) issued into buffer 0
+  auto fstep = [&](int kt, uint8_t* cur, uint8_t* nxt) {
+    ldfr(cur, 1, P1{});
+    if (wave_rows) mm(P0{});
+    ldfr(cur, 2, P0{});
+    if (wave_rows) mm(P1{});
+    ldfr(cur, 3, P1{});
+    if (wave_rows) mm(P0{});
+    wait_vm0();                               // own loads of step kt + 1 landed
+    wait_lgkm0();                             // own reads of cur done
+    __builtin_amdgcn_s_barrier();
+    ldfr(nxt, 0, P0{});
+    mm_dma(P1{}, kt + 2, cur);
+  };
+
+  if (!next_tile()) return;
+  bind_tile();
+  if constexpr (!REG) {
+    dma(0, sm0);
+    dma(1, sm1);                                 // (with K = 64 this reads unused bytes, in range)
+  }
+  for (;;) {
 #pragma unroll
     for (int i = 0; i < TMI; ++i)
 #pragma unroll
@@ -271,84 +499,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // K steps of this wave's loads, staged in registers: A_PW + B_PW pieces of
-    // 16 bytes per lane, each landing at lane * 16 of its 1 KB block in LDS.
-    // RB register buffers keep RB steps of loads in flight.
-    constexpr int RB = REG ? MOE_GEMM_RBUF : 1;
-    u32x4 ra[RB][A_PW], rb[RB][B_PW];
-    auto load_regs = [&](int kt, auto Q) {
-      constexpr int q = decltype(Q)::value;
-      const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
-#pragma unroll
-      for (int j = 0; j < A_PW; ++j) ra[q][j] = buf_load16(rsA, a_off[j], ka);
-#pragma unroll
-      for (int j = 0; j < B_PW; ++j) {
-        const int gi = wave * B_PW + j;
-        // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
-        const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
-        rb[q][j] = buf_load16(w3 ? rsB1 : rsB0, b_off[j], kb);
-      }
-    };
-    auto store_regs = [&](uint8_t* stg, auto Q) {
-      constexpr int q = decltype(Q)::value;
-#pragma unroll
-      for (int j = 0; j < A_PW; ++j)
-        *reinterpret_cast<u32x4*>(stg + (wave * A_PW + j) * 1024 + lane * 16) = ra[q][j];
-#pragma unroll
-      for (int j = 0; j < B_PW; ++j)
-        *reinterpret_cast<u32x4*>(stg + A_BYTES + (wave * B_PW + j) * 1024 + lane * 16) = rb[q][j];
-    };
-    auto compute = [&](const uint8_t* sA, int kk) {
-      const uint8_t* sB = sA + A_BYTES;
-      const int cc = kk * 2 + fk;                 // 8-element k chunk of this lane
-      bf16x8 af[TMI], bfr[TNI];
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) {
-        const int r = wm * WM + i * 32 + fr;
-        if (FP8A) {
-          const uint2 v = *reinterpret_cast<const uint2*>(
-              sA + r * ROWA + (((cc >> 1) ^ swz<ROWA>(r)) << 4) + ((cc & 1) << 3));
-          const uint4 w = fp8x8_to_bf16x8(v);
-          af[i] = *reinterpret_cast<const bf16x8*>(&w);
-        } else {
-          af[i] = *reinterpret_cast<const bf16x8*>(sA + r * ROWA + ((cc ^ swz<ROWA>(r)) << 4));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < TNI; ++j) {
-        const int n = wn * WN + j * 32 + fr;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-#pragma unroll
-        for (int j = 0; j < TNI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    };
-
     if constexpr (REG) {
-      // Register-staged pipeline: while step kt computes from one LDS stage,
-      // registers hold the loads of the next RB steps; halfway through step kt
-      // the registers of step kt + 1 are written to the other stage and refilled
-      // with the loads of step kt + 1 + RB, so RB steps of global loads stay in
-      // flight.  One barrier per step publishes the written stage and frees the
-      // one just read.  Register buffer q holds steps congruent to q mod RB.
-      using I0 = std::integral_constant<int, 0>;
-      using I1 = std::integral_constant<int, (RB > 1 ? 1 : 0)>;
-      auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, auto Q) {
-        if (wave_rows) {
-#pragma unroll
-          for (int kk = 0; kk < BK / 32; ++kk) compute(cur, kk);
-        }
-        if (kt + 1 < KT) store_regs(nxt, Q);
-        if (kt + 1 + RB < KT) load_regs(kt + 1 + RB, Q);
-        if (wave_rows) {
-#pragma unroll
-          for (int kk = BK / 32; kk < BK / 16; ++kk) compute(cur, kk);
-        }
-        wait_lgkm0();
-        __builtin_amdgcn_s_barrier();
-      };
       load_regs(0, I0{});
       store_regs(sm0, I0{});
       if (KT > 1) load_regs(1, I1{});
@@ -361,37 +512,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         if (kt + 1 < KT) step(kt + 1, sm1, sm0, I0{});
       }
     } else {
-      // LDS-DMA pipeline: buffer loads write straight into LDS (no registers);
-      // the loads of step kt + 1 go to the other stage while step kt computes.
-      // Each stage is its own array, so the compiler can tell the stage being
-      // read from the one being filled and does not wait for the DMA before
-      // fragment reads; each wave waits for its own loads, then one barrier.
-      auto dma = [&](int kt, uint8_t* stg) {
-        const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
-#pragma unroll
-        for (int j = 0; j < A_PW; ++j) lds_dma16(rsA, stg + (wave * A_PW + j) * 1024, a_off[j], ka);
-#pragma unroll
-        for (int j = 0; j < B_PW; ++j) {
-          const int gi = wave * B_PW + j;
-          const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
-          lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
-        }
-      };
-      auto dstep = [&](int kt, const uint8_t* cur, uint8_t* nxt) {
-        wait_vm0();
-        __builtin_amdgcn_s_barrier();
-        if (kt + 1 < KT) dma(kt + 1, nxt);
-        if (wave_rows) {
-#pragma unroll
-          for (int kk = 0; kk < BK / 16; ++kk) compute(cur, kk);
-        }
-      };
-      dma(0, sm0);
+      // the tile's first two steps were issued before the previous epilogue
+      wait_vm0();
+      __builtin_amdgcn_s_barrier();
+      ldfr(sm0, 0, P0{});
       for (int kt = 0; kt < KT; kt += 2) {
-        dstep(kt, sm0, sm1);
-        if (kt + 1 < KT) dstep(kt + 1, sm1, sm0);
+        fstep(kt, sm0, sm1);
+        if (kt + 1 < KT) fstep(kt + 1, sm1, sm0);
       }
+      wait_vm0();                                 // (the last steps' empty loads included)
       __builtin_amdgcn_s_barrier();               // every wave is done with the stages
+    }
+
+    // Next tile first: its first two steps load while this tile's epilogue
+    // runs (the stages are free, the epilogue does not use LDS).
+    const int erow0 = row0, erow_end = row_end, entile = ntile;
+    const bool more = next_tile();
+    if (more) {
+      bind_tile();
+      if constexpr (!REG) {
+        dma(0, sm0);
+        dma(1, sm1);
+      }
     }
 
     // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32
@@ -399,33 +541,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     for (int i = 0; i < TMI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= row_end) continue;
+        const int row = erow0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= erow_end) continue;
         const float sc = FP8A ? g.a_scale[row] : 1.0f;
         uint16_t* orow = g.out + static_cast<int64_t>(row) * g.n_out;
         if (GATED) {
 #pragma unroll
           for (int j = 0; j < TNI / 2; ++j) {
-            const int col = ntile * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
+            const int col = entile * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
             if (col < g.n_out) {
               const float u = acc[i][j][r] * sc, gt = acc[i][j + TNI / 2][r] * sc;
-              orow[col] = f32_to_bf16(silu(u) * gt);
+              orow[col] = to_bf16(silu_fast(u) * gt);
             }
           }
         } else {
 #pragma unroll
           for (int j = 0; j < TNI; ++j) {
-            const int col = ntile * BN + wn * WN + j * 32 + (lane & 31);
+            const int col = entile * BN + wn * WN + j * 32 + (lane & 31);
             if (col < g.n_out) {
               float v = acc[i][j][r] * sc;
-              if (EPI == EPI_SILU) v = silu(v);
+              if (EPI == EPI_SILU) v = silu_fast(v);
               if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-              orow[col] = f32_to_bf16(v);
+              orow[col] = to_bf16(v);
             }
           }
         }
       }
     }
+    if (!more) break;
   }
 }
 
