@@ -188,9 +188,25 @@ moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shar
                        const void* x, const int32_t* pos, const float* w, void* y,
                        void* stream);
 
-/* The whole layer: route, dispatch, experts, combine, enqueued on one stream.
- * Every output buffer of the four calls is required except p, f, l_aux, logits
- * (may be NULL) and the shared-expert buffers (ignored unless has_shared). */
+/* Route then dispatch in one call, enqueued on one stream: the outputs of
+ * moe_route (idx, w, counts, kept_counts, p, f, l_aux; no logits) and of
+ * moe_dispatch (offsets, pos, src, drop, x_perm, row_scale), equal to those of
+ * the two calls made one after the other.  The dispatch plan is folded into
+ * the row copy: the router's per-tile expert counts give each 16-token tile's
+ * base and the copy ranks its token inside its tile ("Part 5" / "1.2", step 1,
+ * with every expert local), which saves two kernel launches.  Arguments,
+ * layouts and errors as for the two calls; p, f, l_aux may be NULL. */
+moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g,
+                              const float* bias, int32_t* idx, float* w, int32_t* counts,
+                              int32_t* kept_counts, float* p, float* f, float* l_aux,
+                              int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                              void* x_perm, float* row_scale, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* The whole layer: moe_route_dispatch, moe_experts, moe_combine, enqueued on
+ * one stream; results equal those of the four single-phase calls.  Every
+ * output buffer is required except p, f, l_aux (may be NULL) and the
+ * shared-expert buffers (ignored unless has_shared). */
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
                        const void* w1, const void* w3, const void* w2,
                        const void* ws1, const void* ws3, const void* ws2,

@@ -25,6 +25,8 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align_up(off + nb_route * N * 4);
   L.route_hist = off;
   off = align_up(off + nb_route * N * 4);
+  L.route_base = off;
+  off = align_up(off + nb_route * N * 4);
   L.disp_hist = off;
   off = align_up(off + nb_disp * N * 4);
   L.h = off;
@@ -122,7 +124,8 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_g, const f
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
   hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux, st));
+  return hip_status(moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux,
+                                               nullptr, nullptr, st));
 }
 
 moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* offsets,
@@ -211,6 +214,38 @@ moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shar
                                         static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g,
+                              const float* bias, int32_t* idx, float* w, int32_t* counts,
+                              int32_t* kept_counts, float* p, float* f, float* l_aux,
+                              int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                              void* x_perm, float* row_scale, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status r = check_shape(s);
+  if (r != MOE_OK) return r;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !w_g || !idx || !w || !counts || !kept_counts || !offsets || !pos || !src || !drop ||
+      !x_perm || !ws)
+    return MOE_ERR_ARG;
+  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.disp_hist) return MOE_ERR_WORKSPACE;
+  // the router's per-tile counts give every tile's base, so the row copy
+  // places its token itself; the results equal moe_route then moe_dispatch
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* psum = reinterpret_cast<float*>(base + L.route_psum);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
+  int32_t* tbase = reinterpret_cast<int32_t*>(base + L.route_base);
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, st);
+  if (e == hipSuccess)
+    e = moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux, offsets,
+                                   tbase, st);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch_copy_planned(*s, x, idx, tbase, offsets, pos, src, drop, x_perm,
+                                          row_scale, st);
+  return hip_status(e);
+}
+
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
                        const void* w1, const void* w3, const void* w2, const void* ws1,
                        const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
@@ -221,7 +256,7 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
   moe_status r = check_shape(s);
   if (r != MOE_OK) return r;
   if (s->T == 0) return MOE_OK;
-  // every check of the four calls up front, so that nothing is launched on error
+  // every check of the three calls up front, so that nothing is launched on error
   if (!x || !w_g || !w1 || !w2 || !idx || !w || !counts || !kept_counts || !offsets || !pos ||
       !src || !drop || !x_perm || !out || !y || !ws)
     return MOE_ERR_ARG;
@@ -230,10 +265,8 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
   if (s->has_shared && (!ws1 || !ws2 || !out_shared || (s->act == MOE_ACT_SWIGLU && !ws3)))
     return MOE_ERR_ARG;
   if (ws_bytes < moe::ws_layout(*s).total) return MOE_ERR_WORKSPACE;
-  r = moe_route(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, nullptr, ws, ws_bytes,
-                stream);
-  if (r != MOE_OK) return r;
-  r = moe_dispatch(s, x, idx, offsets, pos, src, drop, x_perm, row_scale, ws, ws_bytes, stream);
+  r = moe_route_dispatch(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets, pos,
+                         src, drop, x_perm, row_scale, ws, ws_bytes, stream);
   if (r != MOE_OK) return r;
   r = moe_experts(s, x_perm, row_scale, offsets, w1, w3, w2, x, ws1, ws3, ws2, out, out_shared, ws,
                   ws_bytes, stream);

@@ -18,6 +18,12 @@
 //              No atomics decide a position, so the permutation is unique.
 //   disp_copy  one wave per token: read the row once, write it to each kept
 //              slot's position (bf16/f32 copy, or fp8 e4m3 with a per-token scale).
+// Within a whole layer the router has already counted each expert's
+// assignments per tile of 16 tokens, and its finalisation turns them into
+// per-tile bases; the copy then places its token itself (the tile's base plus
+// the earlier tokens of the same tile that chose the expert), so the layer
+// needs neither disp_hist nor disp_plan.  The order is the same token order, so
+// the permutation is the same.
 #include "moe_internal.h"
 
 namespace moe {
@@ -147,17 +153,65 @@ __global__ __launch_bounds__(256) void disp_plan_kernel(const int32_t* __restric
   }
 }
 
+// Slot positions of token t when the copy does the planning (see above):
+// for slot j with expert e, r = base[tile][e] + (earlier tokens of t's tile
+// that chose e); kept when there is no capacity or r < cap, at offsets[e] + r.
+// Lane 0 writes pos, drop and src.  pj[] is the same in every lane.
+struct PlanArgs {
+  const int32_t* idx;
+  const int32_t* base;     // [tiles][N]
+  const int32_t* offsets;  // [N + 1]
+  int32_t* pos;
+  int32_t* src;
+  uint8_t* drop;
+  int N, cap;
+};
+
+__device__ __forceinline__ void plan_token(const PlanArgs& pa, int64_t T, int k, int64_t t, int lane,
+                                           int pj[kMaxTopK]) {
+  constexpr int TM = kRouteTile;
+  const int64_t tile = t / TM, t0 = tile * TM;
+  const int before = static_cast<int>(t - t0) * k;        // idx entries of earlier tokens in the tile
+  // lane l holds entries l and l + 64 of the tile (TM * k <= 128)
+  const int v0 = (lane < before) ? pa.idx[t0 * k + lane] : -1;
+  const int v1 = (lane + 64 < before) ? pa.idx[t0 * k + lane + 64] : -1;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    pj[j] = -1;
+    if (j < k) {
+      const int e = pa.idx[t * k + j];
+      int p = -1;
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(pa.N)) {
+        const int r = pa.base[tile * pa.N + e] + __popcll(__ballot(v0 == e)) + __popcll(__ballot(v1 == e));
+        if (pa.cap <= 0 || r < pa.cap) p = pa.offsets[e] + r;
+      }
+      pj[j] = p;
+      if (lane == 0) {
+        pa.pos[t * k + j] = p;
+        pa.drop[t * k + j] = p < 0 ? 1 : 0;
+        if (p >= 0) pa.src[p] = static_cast<int32_t>(t);
+      }
+    }
+  }
+}
+
 // One wave per token; 16-byte chunks.  Row bytes must be a multiple of 16.
+// PLANNED: positions from plan_token, else read from pos.
+template <bool PLANNED>
 __global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restrict__ x, int64_t T,
                                                         int k, int row_bytes,
                                                         const int32_t* __restrict__ pos,
-                                                        uint8_t* __restrict__ xp) {
+                                                        uint8_t* __restrict__ xp, PlanArgs pa) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int pj[kMaxTopK];
+  if (PLANNED) {
+    plan_token(pa, T, k, t, lane, pj);
+  } else {
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
+    for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
+  }
   const int nch = row_bytes / 16;
   const uint4* xr = reinterpret_cast<const uint4*>(x + t * row_bytes);
 #pragma unroll 4
@@ -200,18 +254,22 @@ __device__ __forceinline__ float absmax8(uint4 v) {
 
 // fp8 dispatch: one wave per token.  Rows up to 64*MAXC chunks of 8 bf16 stay in
 // registers; longer rows are read twice.
-template <int MAXC>
+template <int MAXC, bool PLANNED>
 __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restrict__ x, int64_t T,
                                                        int k, int d,
                                                        const int32_t* __restrict__ pos,
                                                        uint8_t* __restrict__ xp,
-                                                       float* __restrict__ row_scale) {
+                                                       float* __restrict__ row_scale, PlanArgs pa) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int pj[kMaxTopK];
+  if (PLANNED) {
+    plan_token(pa, T, k, t, lane, pj);
+  } else {
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
+    for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
+  }
   const int nch = d / 8;
   const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
   const bool in_regs = nch <= 64 * MAXC;
@@ -277,20 +335,46 @@ hipError_t launch_dispatch_plan(const moe_shape& s, const int32_t* idx, const in
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_copy(const moe_shape& s, const void* x, const int32_t* pos,
-                                void* x_perm, float* row_scale, hipStream_t st) {
+namespace {
+hipError_t launch_copy(const moe_shape& s, const void* x, const int32_t* pos, void* x_perm,
+                       float* row_scale, const PlanArgs* pa, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(ceil_div(s.T, 4)));
+  const PlanArgs none{};
   if (s.buf_dtype == MOE_FP8_E4M3) {
-    hipLaunchKernelGGL(disp_fp8_kernel<16>, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
-                       static_cast<uint8_t*>(x_perm), row_scale);
+    if (pa)
+      hipLaunchKernelGGL((disp_fp8_kernel<16, true>), grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
+                         static_cast<uint8_t*>(x_perm), row_scale, *pa);
+    else
+      hipLaunchKernelGGL((disp_fp8_kernel<16, false>), grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
+                         static_cast<uint8_t*>(x_perm), row_scale, none);
   } else {
     int es = s.dtype == MOE_BF16 ? 2 : 4;
-    hipLaunchKernelGGL(disp_copy_kernel, grid, dim3(256), 0, st,
-                       static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
-                       static_cast<uint8_t*>(x_perm));
+    if (pa)
+      hipLaunchKernelGGL(disp_copy_kernel<true>, grid, dim3(256), 0, st,
+                         static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
+                         static_cast<uint8_t*>(x_perm), *pa);
+    else
+      hipLaunchKernelGGL(disp_copy_kernel<false>, grid, dim3(256), 0, st,
+                         static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
+                         static_cast<uint8_t*>(x_perm), none);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_dispatch_copy(const moe_shape& s, const void* x, const int32_t* pos,
+                                void* x_perm, float* row_scale, hipStream_t st) {
+  return launch_copy(s, x, pos, x_perm, row_scale, nullptr, st);
+}
+
+hipError_t launch_dispatch_copy_planned(const moe_shape& s, const void* x, const int32_t* idx,
+                                        const int32_t* base, const int32_t* offsets,
+                                        int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm,
+                                        float* row_scale, hipStream_t st) {
+  const PlanArgs pa{idx, base, offsets, pos, src, drop, s.N, s.capacity};
+  return launch_copy(s, x, pos, x_perm, row_scale, &pa, st);
 }
 
 }  // namespace moe

@@ -35,6 +35,7 @@ __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) {
 struct WsLayout {
   size_t route_psum;    // float   [nb_route][N]
   size_t route_hist;    // int32   [nb_route][N]
+  size_t route_base;    // int32   [nb_route][N]
   size_t disp_hist;     // int32   [nb_disp][N]
   size_t h;             // dtype   [T*k][F]
   size_t h_shared;      // dtype   [T][F]
@@ -48,9 +49,11 @@ WsLayout ws_layout(const moe_shape& s);
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
                         hipStream_t st);
+// offsets (may be null): exclusive scan of the kept counts, N + 1 entries.
+// base (may be null): [nb_route][N] assignments to each expert in earlier tiles.
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
                                  int32_t* counts, int32_t* kept, float* p, float* f,
-                                 float* l_aux, hipStream_t st);
+                                 float* l_aux, int32_t* offsets, int32_t* base, hipStream_t st);
 
 hipError_t launch_dispatch_hist(const moe_shape& s, const int32_t* idx, int32_t* hist,
                                 hipStream_t st);
@@ -59,6 +62,12 @@ hipError_t launch_dispatch_plan(const moe_shape& s, const int32_t* idx, const in
                                 hipStream_t st);
 hipError_t launch_dispatch_copy(const moe_shape& s, const void* x, const int32_t* pos,
                                 void* x_perm, float* row_scale, hipStream_t st);
+// The copy with the plan folded in: positions from the router's per-tile
+// counts (base, offsets from launch_route_finalize); writes pos, src, drop too.
+hipError_t launch_dispatch_copy_planned(const moe_shape& s, const void* x, const int32_t* idx,
+                                        const int32_t* base, const int32_t* offsets,
+                                        int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm,
+                                        float* row_scale, hipStream_t st);
 
 // Grouped GEMMs.  `offsets` == nullptr means one dense segment of `rows` rows.
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,

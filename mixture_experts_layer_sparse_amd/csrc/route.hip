@@ -20,6 +20,11 @@
 // depend on thread timing.
 #include "moe_internal.h"
 
+// k-steps of loads each wave issues before their MFMAs
+#ifndef MOE_ROUTE_U
+#define MOE_ROUTE_U 8
+#endif
+
 namespace moe {
 namespace {
 
@@ -113,7 +118,7 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
   }
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const bf16x8 zero = {};
-  constexpr int U = 8;
+  constexpr int U = MOE_ROUTE_U;
   int s = s0;
   for (; s + U <= s1; s += U) {
     bf16x8 av[U], bv[U][2];
@@ -421,32 +426,42 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   }
 }
 
-// One workgroup of 1024 threads: thread (part, e) sums the per-block partials of
-// expert e over the blocks b = part, part + P, ... in increasing order, then the
-// P parts are added in a fixed tree order, so the result does not depend on timing.
+// One workgroup of 1024 threads.  Thread (part, e) covers a contiguous range of
+// tiles for expert e and sums its p partials and counts in increasing tile
+// order; the P parts are combined in a fixed tree order, so the result does not
+// depend on timing.  With `offsets`, the exclusive scan of the kept counts over
+// experts is written; with `base`, a second pass writes for every tile and
+// expert the number of assignments to the expert in earlier tiles, from which
+// the dispatch copy places each token without a separate plan step.
 __global__ __launch_bounds__(1024) void route_finalize_kernel(const float* psum, const int32_t* hist,
                                                               int nb, int64_t T, int N, int k,
                                                               int cap, float alpha, int32_t* counts,
                                                               int32_t* kept, float* p, float* f,
-                                                              float* l_aux) {
+                                                              float* l_aux, int32_t* offsets,
+                                                              int32_t* base) {
   __shared__ double sp[1024];
   __shared__ int sc[1024];
+  __shared__ int pc[1024];               // per-part counts, kept for the tile prefix
   __shared__ double prod[kMaxExperts];
+  __shared__ int kc[kMaxExperts];
   int NP = 1;
   while (NP < N) NP <<= 1;
   const int P = 1024 / NP;
   const int e = threadIdx.x % NP, part = threadIdx.x / NP;
+  const int b0 = static_cast<int>(static_cast<int64_t>(part) * nb / P);
+  const int b1 = static_cast<int>(static_cast<int64_t>(part + 1) * nb / P);
   double s = 0.0;
   int c = 0;
   if (e < N) {
 #pragma unroll 4
-    for (int b = part; b < nb; b += P) {
+    for (int b = b0; b < b1; ++b) {
       s += static_cast<double>(psum[static_cast<int64_t>(b) * N + e]);
       c += hist[static_cast<int64_t>(b) * N + e];
     }
   }
   sp[threadIdx.x] = s;
   sc[threadIdx.x] = c;
+  pc[threadIdx.x] = c;
   __syncthreads();
   for (int half = P / 2; half >= 1; half >>= 1) {
     if (part < half) {
@@ -459,17 +474,37 @@ __global__ __launch_bounds__(1024) void route_finalize_kernel(const float* psum,
     const int64_t cnt = sc[e];
     const double pe = sp[e] / static_cast<double>(T);
     const double fe = static_cast<double>(cnt) / (static_cast<double>(T) * k);
+    const int32_t kp = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
     counts[e] = static_cast<int32_t>(cnt);
-    kept[e] = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
+    kept[e] = kp;
+    kc[e] = kp;
     if (p) p[e] = static_cast<float>(pe);
     if (f) f[e] = static_cast<float>(fe);
     prod[e] = fe * pe;
   }
   __syncthreads();
-  if (threadIdx.x == 0 && l_aux) {
-    double acc = 0.0;
-    for (int q = 0; q < N; ++q) acc += prod[q];
-    l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
+  if (threadIdx.x == 0) {
+    if (l_aux) {
+      double acc = 0.0;
+      for (int q = 0; q < N; ++q) acc += prod[q];
+      l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
+    }
+    if (offsets) {
+      int run = 0;
+      for (int q = 0; q < N; ++q) {
+        offsets[q] = run;
+        run += kc[q];
+      }
+      offsets[N] = run;
+    }
+  }
+  if (base && e < N) {
+    int run = 0;
+    for (int q = 0; q < part; ++q) run += pc[q * NP + e];
+    for (int b = b0; b < b1; ++b) {
+      base[static_cast<int64_t>(b) * N + e] = run;
+      run += hist[static_cast<int64_t>(b) * N + e];
+    }
   }
 }
 
@@ -490,10 +525,10 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
 
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
                                  int32_t* counts, int32_t* kept, float* p, float* f,
-                                 float* l_aux, hipStream_t st) {
+                                 float* l_aux, int32_t* offsets, int32_t* base, hipStream_t st) {
   int nb = static_cast<int>(ceil_div(s.T, TM));
   hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(1024), 0, st, psum, hist, nb, s.T, s.N,
-                     s.k, s.capacity, s.alpha, counts, kept, p, f, l_aux);
+                     s.k, s.capacity, s.alpha, counts, kept, p, f, l_aux, offsets, base);
   return hipGetLastError();
 }
 

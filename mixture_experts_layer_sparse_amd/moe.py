@@ -83,6 +83,7 @@ _SIGS = {
     "moe_check_shape": (c_int32, [POINTER(Shape)]),
     "moe_route": (c_int32, [POINTER(Shape)] + [_P] * 11 + [_P, c_size_t, _P]),
     "moe_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 8 + [_P, c_size_t, _P]),
+    "moe_route_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P, c_size_t, _P]),
     "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
     "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P]),
     "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
@@ -203,6 +204,38 @@ def dispatch(s: Shape, x, idx, ws=None, out=None) -> dict:
     _call("moe_dispatch", ctypes.byref(s), _ptr(x), _ptr(idx), _ptr(o["offsets"]), _ptr(o["pos"]),
           _ptr(o["src"]), _ptr(o["drop"]), _ptr(o["x_perm"]), _ptr(o.get("row_scale")), _ptr(ws),
           ws.numel(), _stream())
+    return o
+
+
+def route_dispatch(s: Shape, x, wg, bias=None, ws=None) -> dict:
+    """moe_route_dispatch: the outputs of route() and dispatch() (no logits)
+    from one call, with the dispatch plan folded into the row copy."""
+    T, N, k, d = s.T, s.N, s.k, s.d
+    dev = x.device
+    _check(x, "x", (T, d), s.torch_dtype)
+    _check(wg, "wg", (N, d), s.torch_dtype)
+    _check(bias, "bias", (N,), torch.float32, required=False)
+    fp8 = s.buf_dtype == MOE_FP8_E4M3
+    o = {
+        "idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "counts": torch.empty(N, dtype=torch.int32, device=dev),
+        "kept_counts": torch.empty(N, dtype=torch.int32, device=dev),
+        "p": torch.empty(N, dtype=torch.float32, device=dev),
+        "f": torch.empty(N, dtype=torch.float32, device=dev),
+        "l_aux": torch.empty(1, dtype=torch.float32, device=dev),
+        "offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+        "pos": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "src": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "drop": torch.empty((T, k), dtype=torch.uint8, device=dev),
+        "x_perm": torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=dev),
+        "row_scale": torch.empty(T * k, dtype=torch.float32, device=dev) if fp8 else None,
+    }
+    ws = ws if ws is not None else alloc_workspace(s, dev)
+    _call("moe_route_dispatch", ctypes.byref(s), _ptr(x), _ptr(wg), _ptr(bias), _ptr(o["idx"]),
+          _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["kept_counts"]), _ptr(o["p"]), _ptr(o["f"]),
+          _ptr(o["l_aux"]), _ptr(o["offsets"]), _ptr(o["pos"]), _ptr(o["src"]), _ptr(o["drop"]),
+          _ptr(o["x_perm"]), _ptr(o.get("row_scale")), _ptr(ws), ws.numel(), _stream())
     return o
 
 
@@ -327,7 +360,16 @@ class Layer:
               _ptr(self.y), _ptr(self.ws), self.ws.numel(), _stream())
         return self.y
 
-    # the four phases separately (same kernels as forward)
+    # forward in three calls (the same kernels): route + dispatch, experts, combine
+    def route_dispatch(self, x):
+        s = self.s
+        _call("moe_route_dispatch", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias),
+              _ptr(self.idx), _ptr(self.w), _ptr(self.counts), _ptr(self.kept_counts),
+              _ptr(self.p), _ptr(self.f), _ptr(self.l_aux), _ptr(self.offsets), _ptr(self.pos),
+              _ptr(self.src), _ptr(self.drop), _ptr(self.x_perm), _ptr(self.row_scale),
+              _ptr(self.ws), self.ws.numel(), _stream())
+
+    # the single phases (route and dispatch as separate calls)
     def route(self, x):
         s = self.s
         _call("moe_route", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias), _ptr(self.idx),

@@ -76,6 +76,20 @@ def run_gpu(wl, inp, logits=True):
     return res
 
 
+def run_gpu_forward(wl, inp):
+    """The whole layer in one call (moe_forward); host copies of its outputs
+    under the same names as run_gpu."""
+    s = M.shape_of(wl)
+    g = upload(wl, inp)
+    L = M.Layer(s, g["wg"], g["w1"], g.get("w3"), g["w2"], bias=g.get("bias"), ws1=g.get("ws1"),
+                ws3=g.get("ws3"), ws2=g.get("ws2"))
+    L.forward(g["x"])
+    torch.cuda.synchronize()
+    names = ["idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "src",
+             "drop", "x_perm", "row_scale", "out", "out_shared", "y"]
+    return {n: host(getattr(L, n)) for n in names}
+
+
 def check_layer(wl, inp, gpu, y_tokens=None, max_adopted=None):
     """Compare a GPU run with the oracle; returns a dict of measured errors."""
     from oracle.numerics import as_f64

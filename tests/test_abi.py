@@ -90,6 +90,13 @@ def test_null_pointers_and_workspace_rejected_on_host(M):
     st = L.moe_experts(ctypes.byref(s), p, None, p, p, None, p, None, None, None, None, p, None,
                        p, 16, None)
     assert st == M.MOE_ERR_WORKSPACE
+    # route + dispatch in one call: missing x_perm, then too small a workspace
+    st = L.moe_route_dispatch(ctypes.byref(s), p, p, None, p, p, p, p, None, None, None, p, p, p,
+                              p, None, None, p, M.workspace_bytes(s), None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_route_dispatch(ctypes.byref(s), p, p, None, p, p, p, p, None, None, None, p, p, p,
+                              p, p, None, p, 8, None)
+    assert st == M.MOE_ERR_WORKSPACE
     # SwiGLU without W3
     s2 = _s(M, act="swiglu")
     st = L.moe_expert_up(ctypes.byref(s2), p, None, p, p, None, p, None)

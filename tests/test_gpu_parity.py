@@ -187,6 +187,44 @@ def test_determinism_bitwise():
             assert np.array_equal(a[key], b[key]), key
 
 
+# ------------------------------------------------------ the one-call layer --
+
+FORWARD_CASES = {
+    "mixtral_ragged": lambda: si.small("mixtral", T=1001),
+    "switch_capacity": lambda: si.small("switch"),
+    "switch_drop_zero": lambda: si.small("switch", T=999, capacity=20, drop="zero"),
+    "deepseek_fp8_groups_shared": lambda: si.small("deepseek_v3"),
+    "dbrx_skew": lambda: si.small("dbrx"),
+    "single_token": lambda: si.small("mixtral", T=1),
+    "many_tiles_capacity": lambda: si.Workload("mbf", T=20011, d=64, N=16, k=2, F=128,
+                                               act="swiglu", dtype="bf16", buf="bf16",
+                                               capacity=2300),
+}
+
+
+@pytest.mark.parametrize("name", list(FORWARD_CASES))
+def test_forward_matches_oracle_and_phases(name):
+    """moe_forward places tokens inside the row copy (from the router's
+    per-tile counts); its outputs must pass the oracle checks and equal, bit
+    for bit, those of moe_route, moe_dispatch, moe_experts and moe_combine
+    called one after the other."""
+    from moe_gpu_util import run_gpu_forward
+    wl = FORWARD_CASES[name]()
+    print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} cap={wl.capacity}", flush=True)
+    inp = si.generate(wl)
+    fwd = run_gpu_forward(wl, inp)
+    errs = check_layer(wl, inp, fwd, max_adopted=2)
+    print(f"  {errs}", flush=True)
+    ph = run_gpu(wl, inp)
+    R = int(fwd["offsets"][-1])
+    for key in ("idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "drop", "y"):
+        assert np.array_equal(fwd[key], ph[key]), key
+    for key in ("src", "x_perm", "out"):
+        assert np.array_equal(fwd[key][:R], ph[key][:R]), key
+    if wl.buf == "fp8":
+        assert np.array_equal(fwd["row_scale"][:R], ph["row_scale"][:R])
+
+
 # -------------------------------------------------------------- full sizes --
 
 @pytest.mark.parametrize("name", ["mixtral", "switch", "deepseek_v3", "dbrx"])
