@@ -150,11 +150,13 @@ __device__ __forceinline__ int swz(int row) {
 }
 
 // Tail split.  With split_slots = S > 0 the tile list (m-tiles of height MBM,
-// n-tiles of g.nt) is cut at total - r, r = total % S, when 0 < r <= S / 2: the
+// n-tiles of g.nt) is cut at total - r, r = total % S, when 0 < r <= S / 4: the
 // main launch (TAIL = false, tile BM x BN = MBM x BN) runs the tiles before the
 // cut, whole rounds of S workgroups; the tail launch (TAIL = true, tile of half
 // height and half width) runs each of the r remaining tiles as four quarters,
-// so that the last round is not left mostly idle.  Both launches count the
+// so that the last round is not left mostly idle.  A quarter streams twice
+// the bytes per FLOP of a whole tile and runs at about half its rate, so the
+// split pays only while all quarters fit in one round (4 r <= S).  Both launches count the
 // same tile list from `offsets`; every output element is still computed by one
 // workgroup over the whole K.
 template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL>
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   int cut = total;                               // main tiles [0, cut), tail tiles [cut, total)
   if (g.split_slots > 0) {
     const int r = total % g.split_slots;
-    if (r > 0 && 2 * r <= g.split_slots) cut = total - r;
+    if (r > 0 && 4 * r <= g.split_slots) cut = total - r;
   }
   const int items = TAIL ? 4 * (total - cut) : cut;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, S = gridDim.x >> 3;

@@ -167,6 +167,117 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
   }
 }
 
+// 16 bytes per lane from a buffer straight into LDS (lane i writes lds + 16 * i).
+typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)lds, 16, voff, 0, 0, 0);
+}
+
+constexpr int SCH = 512;               // staged chunk: 512 elements (1 KB) of each token row
+constexpr int SPH = 8;                 // chunks per staging phase (8 x 16 rows x 1 KB = 128 KB)
+
+// The same logits with x staged through LDS (d a multiple of 512): every
+// load is one token row's contiguous 1 KB, all of a phase's loads are issued
+// at once (up to 128 KB in flight per workgroup), and the MFMA fragments are
+// read from LDS.  Chunk ch of row r sits at buf + (ch * 16 + r) KB with its
+// 16-byte pieces q stored at (q & ~15) | ((q & 15) ^ r): a fragment read (16
+// rows, one piece each) then touches 16 different bank groups.  Rows past T
+// read as zeros (buffer range).  part / lt live in buf once the loads are done.
+__device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf, float* part,
+                                   float* lt, int ldl) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int N = a.N, d = a.d;
+  const int NB = (N + 15) / 16;
+  const int CG = NB >= 8 ? 8 : (NB >= 3 ? 4 : NB);
+  const int KS = RW / CG;
+  const int ks = wave / CG, cg = wave % CG;
+  const int lr = lane & 15, kc = lane >> 4;
+  const uint16_t* wg = static_cast<const uint16_t*>(a.wg);
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.x) + t0 * d), static_cast<short>(0),
+      static_cast<int>((a.T - t0 < TM ? a.T - t0 : TM) * d * 2), 0x00020000);
+  const uint16_t* wrow[2];
+  bool wok[2];
+  int nblk = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cb = cg + i * CG;
+    const int e = cb * 16 + lr;
+    wok[i] = cb < NB && e < N;
+    wrow[i] = wg + static_cast<int64_t>(wok[i] ? e : 0) * d + kc * 8;
+    if (cb < NB) nblk = i + 1;
+  }
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const bf16x8 zero = {};
+  const int nch_all = d / SCH;
+  for (int c0 = 0; c0 < nch_all; c0 += SPH) {
+    const int nch = nch_all - c0 < SPH ? nch_all - c0 : SPH;
+    // loads: row-chunk i = ch * 16 + r, taken by the waves in turn
+    for (int i = wave; i < nch * TM; i += RW) {
+      const int ch = i / TM, r = i % TM;
+      const int q = (lane & ~15) | ((lane & 15) ^ r);  // the piece this lane writes at lane * 16
+      lds_dma16(rsx, buf + i * 1024,
+                static_cast<uint32_t>(r * d * 2 + (c0 + ch) * 1024 + q * 16));
+    }
+    // this wave's k-steps (of 32) among the phase's nch * 16
+    const int S = nch * (SCH / 32);
+    const int s0 = ks * S / KS, s1 = (ks + 1) * S / KS;
+    constexpr int U = 8;
+    // W_g fragments of the first batch are loaded while x is still arriving
+    bf16x8 bv[U][2];
+    auto load_w = [&](int s) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int st = s + u < s1 ? s + u : s1 - 1;    // (repeats are not accumulated)
+        const int k0 = (c0 * SCH) + st * 32;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          bv[u][i] = (i < nblk && wok[i]) ? *reinterpret_cast<const bf16x8*>(wrow[i] + k0) : zero;
+      }
+    };
+    if (s0 < s1) load_w(s0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): own loads landed
+    __syncthreads();
+    for (int s = s0; s < s1; s += U) {
+      bf16x8 av[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int st = s + u < s1 ? s + u : s1 - 1;
+        const int ch = st / (SCH / 32), q = (st % (SCH / 32)) * 4 + kc;
+        av[u] = *reinterpret_cast<const bf16x8*>(buf + (ch * TM + lr) * 1024 +
+                                                 (((q & ~15) | ((q & 15) ^ lr)) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (s + u < s1) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            if (i < nblk) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][i], acc[i], 0, 0, 0);
+        }
+      if (s + U < s1) load_w(s + U);
+    }
+    __syncthreads();                                 // buf free for the next phase
+  }
+  const int NP = NB * 16;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i < nblk) {
+      const int col = (cg + i * CG) * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(ks * TM + kc * 4 + r) * NP + col] = acc[i][r];
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
+    const int m = q / N, e = q % N;
+    float v = 0.f;
+    for (int kk = 0; kk < KS; ++kk) v += part[(kk * TM + m) * NP + e];
+    if (a.bias) v += a.bias[e];
+    lt[m * ldl + e] = v;
+  }
+}
+
 // fp32 path: plain dot products, one (token, expert) pair per thread at a time.
 __device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
   const float* x = static_cast<const float*>(a.x);
@@ -265,8 +376,13 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
 
 template <bool BF16>
 __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
-  __shared__ float part[4096];           // d-split partials [KS][TM][NP]
-  __shared__ float lt[TM * (kMaxExperts + 1)];
+  // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
+  // on the other paths, it holds the d-split partials [KS][TM][NP] (16 KB) and
+  // the logit tile [TM][kMaxExperts + 1]
+  __shared__ __attribute__((aligned(1024))) uint8_t sbuf[SPH * TM * 1024];
+  float* part = reinterpret_cast<float*>(sbuf);
+  float* lt = reinterpret_cast<float*>(sbuf + 16384);
+  static_assert(16384 + TM * (kMaxExperts + 1) * 4 <= SPH * TM * 1024, "partials and logits fit");
   __shared__ float ps[RW][kMaxExperts];  // wave partial sums of p (large N)
   __shared__ float pl[TM][SMALL_N + 1];  // per-token p (small N)
   __shared__ int hl[kMaxExperts];
@@ -276,8 +392,12 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TM;
 
   for (int e = threadIdx.x; e < kMaxExperts; e += RW * 64) hl[e] = 0;
-  if (BF16) logits_bf16(a, t0, part, lt, ldl);
-  else logits_f32(a, t0, lt, ldl);
+  if (BF16) {
+    if (a.d % SCH == 0) logits_bf16_staged(a, t0, sbuf, part, lt, ldl);
+    else logits_bf16(a, t0, part, lt, ldl);
+  } else {
+    logits_f32(a, t0, lt, ldl);
+  }
   __syncthreads();
 
   if (a.logits) {
@@ -498,9 +618,17 @@ __global__ __launch_bounds__(1024) void route_finalize_kernel(const float* psum,
       offsets[N] = run;
     }
   }
+  if (base) {
+    // exclusive prefix of the part counts over parts (Hillis-Steele, then shift)
+    for (int off = 1; off < P; off <<= 1) {
+      const int v = part >= off ? pc[threadIdx.x - off * NP] : 0;
+      __syncthreads();
+      pc[threadIdx.x] += v;
+      __syncthreads();
+    }
+  }
   if (base && e < N) {
-    int run = 0;
-    for (int q = 0; q < part; ++q) run += pc[q * NP + e];
+    int run = part > 0 ? pc[threadIdx.x - NP] : 0;
     for (int b = b0; b < b1; ++b) {
       base[static_cast<int64_t>(b) * N + e] = run;
       run += hist[static_cast<int64_t>(b) * N + e];

@@ -149,13 +149,13 @@ def check_layer(wl, inp, gpu, y_tokens=None, max_adopted=None):
 def gemm_tail_split(counts, bm, nt):
     """The grouped GEMMs' tail split, restated on the host: m-tiles of height bm
     per expert segment times nt n-tiles, cut at total - r, r = total % slots,
-    when 0 < r <= slots / 2 (slots: the device's CUs, rounded down to a
+    when 0 < r <= slots / 4 (slots: the device's CUs, rounded down to a
     multiple of 8).  Returns (total, tiles before the cut, slots)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     slots = (cus // 8) * 8
     total = int(np.sum((np.asarray(counts) + bm - 1) // bm)) * nt
     r = total % slots
-    cut = total - r if 0 < r <= slots // 2 else total
+    cut = total - r if 0 < r <= slots // 4 else total
     return total, cut, slots
 
 
