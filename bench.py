@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s at Mixtral shape; grouped-GEMM % MFMA peak; dispatch GB/s"
 # the gate/up grouped-GEMM kernel instance each workload runs (key in the counter summary)
-UP_KERNEL = {"mixtral": "gg_kernel<256,256,2,4,3,false,false>"}
+UP_KERNEL = {"mixtral": "gg_kernel<256,256,2,4,3,false,false,false>"}
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
 
