@@ -16,7 +16,8 @@ its measured duration, against the bf16 dense MFMA peak), the dispatch and
 memory-phase bandwidths, and the float64 CPU oracle timed on a bounded sample.
 
 --mode copy runs a plain device copy of a known size (the calibration kernel
-for the hardware byte counters) and exits.
+for the hardware byte counters) and exits.  --mode sweep times every workload
+family at full size, phase by phase, and prints a markdown table.
 """
 from __future__ import annotations
 
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens whose expert FFNs the CPU oracle runs (0: all T)")
-    ap.add_argument("--mode", choices=["bench", "copy", "summarize"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep"], default="bench")
     ap.add_argument("--prof", default=None,
                     help="summarize: directory holding trace/ fetch/ write/ cfetch/ cwrite/ "
                          "rocprofv3 csv output")
@@ -208,10 +209,90 @@ def profiled_traffic(kernel_key):
         return None
 
 
+def expert_weight_bytes(wl):
+    """Bytes of the expert weights one layer reads (routed + shared)."""
+    m = 3 if wl.act == "swiglu" else 2
+    s = 2 if wl.dtype == "bf16" else 4
+    return (wl.N + (1 if wl.shared else 0)) * m * wl.F * wl.d * s
+
+
+def sweep(steps, warmup):
+    """Every workload family at its full size, phase by phase (the kernels of
+    moe_forward); prints a markdown table."""
+    import numpy as np
+    import torch
+    import synthetic_inputs as si
+    from mixture_experts_layer_sparse_amd import moe as M
+
+    def dev(arr):
+        if arr is None:
+            return None
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+    print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | GEMM down us | shared us | "
+          "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx"):
+        wl = si.WORKLOADS[name]
+        inp = si.generate(wl)
+        g = {k: dev(v) for k, v in inp.items()}
+        del inp
+        s = M.shape_of(wl)
+        L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
+                    ws3=g["ws3"], ws2=g["ws2"])
+        x = g["x"]
+        h = torch.empty((wl.T * wl.k, wl.F), dtype=s.torch_dtype, device="cuda")
+        hs = torch.empty((wl.T, wl.F), dtype=s.torch_dtype, device="cuda") if wl.shared else None
+
+        def step(ev):
+            ev[0].record()
+            L.route_dispatch(x)
+            ev[1].record()
+            M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h)
+            ev[2].record()
+            M.expert_down(s, h, L.offsets, L.w2, L.out)
+            ev[3].record()
+            if wl.shared:
+                M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
+            ev[4].record()
+            L.combine(x)
+            ev[5].record()
+
+        E = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps + warmup)]
+        for i in range(warmup):
+            step(E[i])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warmup, warmup + steps):
+            step(E[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in E[warmup:]]).mean(0) * 1e3
+        R = int(L.offsets[-1].item())
+        up, down, shared = gemm_flops(wl, R)
+        rb, db, cb = alg_bytes(wl, R)
+        gemm_us = ph[1] + ph[2] + ph[3]
+        tf = (up + down + shared) / (gemm_us * 1e-6) / 1e12
+        wgb = expert_weight_bytes(wl) / (gemm_us * 1e-6) / 1e9
+        mem_us = ph[0] + ph[4]
+        mgb = (rb + db + cb) / (mem_us * 1e-6) / 1e9
+        print(f"| {name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k}, F={wl.F}) | {wl.T / wall:,.0f} | "
+              f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | "
+              f"{tf:.0f} ({100 * tf / PEAK_BF16_TFLOPS:.1f}%) | {wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) | "
+              f"{mgb:.0f} ({100 * mgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
+        del L, g, x, h, hs
+        torch.cuda.empty_cache()
+
+
 def main():
     a = parse()
     if a.mode == "summarize":
         summarize(a.prof, a.out or COUNTER_FILE)
+        return
+    if a.mode == "sweep":
+        sweep(a.steps, a.warmup)
         return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
