@@ -644,9 +644,14 @@ hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   return hipGetLastError();
 }
 
-int pick_bm(int64_t rows, int n_seg) {
+// Tile height: 256 rows read each weight n-tile once per 256 rows of an
+// expert, 128 rows waste less on short segments.  With fp8 activations the A
+// rows cost half as much, so the taller tile pays from shorter segments
+// (measured: DeepSeek-V3-shaped gate/up, ~128 rows per expert, 4.18 -> 3.96
+// ms; with bf16 activations the same change loses 6%).
+int pick_bm(int64_t rows, int n_seg, bool fp8_a) {
   const int64_t avg = n_seg > 0 ? rows / n_seg : rows;
-  return avg >= 384 ? 256 : 128;
+  return avg >= (fp8_a ? 96 : 384) ? 256 : 128;
 }
 
 
@@ -700,7 +705,7 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
   g.out = static_cast<uint16_t*>(h);
   const bool gated = s.act == MOE_ACT_SWIGLU;
   g.nt = static_cast<int>(gated ? ceil_div(s.F, 128) : ceil_div(s.F, 256));
-  const int bm = pick_bm(rows, dense ? 1 : n_seg);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8);
   if (gated) return fp8 ? dispatch_up<EPI_SWIGLU, true>(bm, g, rows, n_seg, dense, st)
                         : dispatch_up<EPI_SWIGLU, false>(bm, g, rows, n_seg, dense, st);
   if (s.act == MOE_ACT_RELU) return fp8 ? dispatch_up<EPI_RELU, true>(bm, g, rows, n_seg, dense, st)
@@ -734,7 +739,7 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.b_stride = static_cast<int64_t>(s.d) * s.F;
   g.out = static_cast<uint16_t*>(out);
   g.nt = static_cast<int>(ceil_div(s.d, 256));
-  const int bm = pick_bm(rows, dense ? 1 : n_seg);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, false);
   return dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, st);
 }
 

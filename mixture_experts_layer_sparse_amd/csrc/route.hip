@@ -378,8 +378,10 @@ template <bool BF16>
 __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
   // on the other paths, it holds the d-split partials [KS][TM][NP] (16 KB) and
-  // the logit tile [TM][kMaxExperts + 1]
-  __shared__ __attribute__((aligned(1024))) uint8_t sbuf[SPH * TM * 1024];
+  // the logit tile [TM][kMaxExperts + 1].  Sized at launch (route_lds_bytes):
+  // no larger than the shape needs, so that small d leaves room for more
+  // workgroups per CU.
+  extern __shared__ __attribute__((aligned(1024))) uint8_t sbuf[];
   float* part = reinterpret_cast<float*>(sbuf);
   float* lt = reinterpret_cast<float*>(sbuf + 16384);
   static_assert(16384 + TM * (kMaxExperts + 1) * 4 <= SPH * TM * 1024, "partials and logits fit");
@@ -638,16 +640,40 @@ __global__ __launch_bounds__(1024) void route_finalize_kernel(const float* psum,
 
 }  // namespace
 
+namespace {
+// dynamic LDS of route_kernel: the staged x chunks of one phase, at least the
+// partials and the logit tile
+size_t route_lds_bytes(const moe_shape& s) {
+  const size_t minimum = 16384 + static_cast<size_t>(TM) * (kMaxExperts + 1) * 4;
+  size_t staged = 0;
+  if (s.dtype == MOE_BF16 && s.d % SCH == 0) {
+    const int nch = s.d / SCH;
+    staged = static_cast<size_t>(nch < SPH ? nch : SPH) * TM * 1024;
+  }
+  return staged > minimum ? staged : minimum;
+}
+}  // namespace
+
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
                         hipStream_t st) {
   RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
               s.n_groups, s.topk_groups, s.group_score_k};
   dim3 grid(static_cast<unsigned>(ceil_div(s.T, TM)));
+  const size_t lds = route_lds_bytes(s);
+  // allow dynamic LDS above the default limit (the largest staging buffer)
+  static const bool attr_set = [] {
+    const int most = SPH * TM * 1024;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<true>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
+           hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<false>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
+  }();
+  if (!attr_set) return hipErrorInvalidValue;
   if (s.dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(RW * 64), 0, st, a);
+    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(RW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(RW * 64), 0, st, a);
+    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(RW * 64), lds, st, a);
   return hipGetLastError();
 }
 
