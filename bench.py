@@ -250,9 +250,9 @@ def sweep(steps, warmup):
             ev[0].record()
             L.route_dispatch(x)
             ev[1].record()
-            M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h)
+            M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
             ev[2].record()
-            M.expert_down(s, h, L.offsets, L.w2, L.out)
+            M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
             ev[3].record()
             if wl.shared:
                 M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
@@ -337,9 +337,9 @@ def main():
         # one call: the dispatch plan is folded into the row copy)
         L.route_dispatch(x)
         ev and ev[1].record()
-        M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h)
+        M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
         ev and ev[2].record()
-        M.expert_down(s, h, L.offsets, L.w2, L.out)
+        M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
         ev and ev[3].record()
         if wl.shared:
             M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)

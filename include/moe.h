@@ -151,15 +151,21 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx,
  *   x_perm [T*k][d] buf_dtype, row_scale [T*k] (FP8 only), offsets [N+1] from dispatch
  *   w1, w3 [N][F][d] dtype (w3 NULL unless SwiGLU)
  *   h      [T*k][F] dtype out (rows >= R untouched)
+ *   ws     NULL, or a workspace of moe_workspace_bytes(s) bytes: with it, when the
+ *          last round of 256x256 output tiles would leave most CUs idle, those
+ *          tiles are split along K and their float32 partials added in a fixed
+ *          order (deterministic); without it they run as 128x128 quarter tiles.
+ *          The two give results that differ only in float32 rounding order.
  */
 moe_status moe_expert_up(const moe_shape* s, const void* x_perm, const float* row_scale,
                          const int32_t* offsets, const void* w1, const void* w3, void* h,
-                         void* stream);
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Expert down-projection (grouped GEMM 2): out[r] = W2[e] h[r].
- *   h [T*k][F] dtype, offsets [N+1], w2 [N][d][F] dtype, out [T*k][d] dtype. */
+ *   h [T*k][F] dtype, offsets [N+1], w2 [N][d][F] dtype, out [T*k][d] dtype;
+ *   ws as for moe_expert_up. */
 moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* offsets,
-                           const void* w2, void* out, void* stream);
+                           const void* w2, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* The always-on shared expert on the unquantised input ("moe communication
  * costs" / "Capacity factor and token dropping": a shared expert every token

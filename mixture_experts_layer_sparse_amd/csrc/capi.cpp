@@ -29,6 +29,8 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align_up(off + nb_route * N * 4);
   L.disp_hist = off;
   off = align_up(off + nb_disp * N * 4);
+  L.gemm_split = off;
+  off = align_up(off + moe::gemm_split_bytes(s));
   L.h = off;
   off = align_up(off + T * static_cast<size_t>(s.k) * static_cast<size_t>(s.F) * elem_size(s.dtype));
   L.h_shared = off;
@@ -146,26 +148,44 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, i
   return hip_status(e);
 }
 
+namespace {
+// the split-K scratch inside a caller's workspace, or null (quarter-tile tail)
+void* split_scratch(const moe_shape& s, void* ws, size_t ws_bytes, moe_status* err) {
+  *err = MOE_OK;
+  if (!ws || moe::gemm_split_bytes(s) == 0) return nullptr;
+  const WsLayout L = moe::ws_layout(s);
+  if (ws_bytes < L.gemm_split + moe::gemm_split_bytes(s)) {
+    *err = MOE_ERR_WORKSPACE;
+    return nullptr;
+  }
+  return static_cast<char*>(ws) + L.gemm_split;
+}
+}  // namespace
+
 moe_status moe_expert_up(const moe_shape* s, const void* x_perm, const float* row_scale,
                          const int32_t* offsets, const void* w1, const void* w3, void* h,
-                         void* stream) {
+                         void* ws, size_t ws_bytes, void* stream) {
   moe_status c = check_shape(s);
   if (c != MOE_OK) return c;
   if (s->T == 0) return MOE_OK;
   if (!x_perm || !offsets || !w1 || !h) return MOE_ERR_ARG;
   if (s->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
   if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
   return hip_status(moe::launch_expert_up(*s, x_perm, row_scale, offsets, s->T * s->k, s->N, w1,
-                                          w3, h, static_cast<hipStream_t>(stream)));
+                                          w3, h, split, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* offsets,
-                           const void* w2, void* out, void* stream) {
+                           const void* w2, void* out, void* ws, size_t ws_bytes, void* stream) {
   moe_status c = check_shape(s);
   if (c != MOE_OK) return c;
   if (s->T == 0) return MOE_OK;
   if (!h || !offsets || !w2 || !out) return MOE_ERR_ARG;
-  return hip_status(moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out,
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
+  return hip_status(moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out, split,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -180,8 +200,10 @@ moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1,
   // the shared expert sees the unquantised input: same dtype as x
   moe_shape sd = *s;
   sd.buf_dtype = sd.dtype;
-  hipError_t e = moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared, st);
-  if (e == hipSuccess) e = moe::launch_expert_down(sd, h_shared, nullptr, s->T, 1, ws2, out_shared, st);
+  hipError_t e = moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared,
+                                       nullptr, st);
+  if (e == hipSuccess)
+    e = moe::launch_expert_down(sd, h_shared, nullptr, s->T, 1, ws2, out_shared, nullptr, st);
   return hip_status(e);
 }
 
@@ -196,9 +218,10 @@ moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_
   const WsLayout L = moe::ws_layout(*s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
-  moe_status r = moe_expert_up(s, x_perm, row_scale, offsets, w1, w3, base + L.h, stream);
+  moe_status r = moe_expert_up(s, x_perm, row_scale, offsets, w1, w3, base + L.h, ws, ws_bytes,
+                               stream);
   if (r != MOE_OK) return r;
-  r = moe_expert_down(s, base + L.h, offsets, w2, out, stream);
+  r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
   if (r != MOE_OK || !s->has_shared) return r;
   return moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, stream);
 }

@@ -34,6 +34,7 @@
 //     so that each wave holds both halves of its outputs; the activation runs
 //     on the accumulators and h is written once, in bf16.
 // The float32 path (small correctness shapes) is a plain dot-product kernel.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -70,6 +71,9 @@ struct GemmArgs {
   uint16_t* out;           // [rows][n_out]
   int nt;                  // n-tiles of the tile list
   int split_slots;         // > 0: tail split over this many workgroup slots (see below)
+  float* part;             // split-K tail: [units][256][256] float32 partial tiles
+  int32_t* part_meta;      // split-K tail: [0] = tail tiles, then (row0, row_end, ntile) per tile
+  int ksplit;              // split-K tail: K ranges per tail tile
 };
 
 // silu(u) = u / (1 + e^-u) with the hardware reciprocal (about 1 ulp): the result is rounded to
@@ -156,11 +160,16 @@ __device__ __forceinline__ int swz(int row) {
 // height and half width) runs each of the r remaining tiles as four quarters,
 // so that the last round is not left mostly idle.  A quarter streams twice
 // the bytes per FLOP of a whole tile and runs at about half its rate, so the
-// split pays only while all quarters fit in one round (4 r <= S).  Both launches count the
+// split pays only while all quarters fit in one round (4 r <= S).  When the
+// caller provides scratch (part), the tail launch instead splits each of the r
+// tiles along K into ksplit ranges (SPLITK = true, whole 256x256 tiles, so at
+// the main kernel's rate); the float32 partial tiles are then added in range
+// order by gg_splitk_reduce, which applies the epilogue.  Both launches count the
 // same tile list from `offsets`; every output element is still computed by one
 // workgroup over the whole K.
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
+  static_assert(!SPLITK || (TAIL && !REG), "split-K is a tail mode of the LDS-DMA pipeline");
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
   constexpr int BK = 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
@@ -193,7 +202,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   const int wm = wave / WGN, wn = wave % WGN;
   const int n_seg = g.offsets ? g.n_seg : 1;
   const int K = g.K, KT = K / BK;
-  constexpr int MBM = TAIL ? 2 * BM : BM;        // m-tile height of the tile list
+  constexpr bool QUARTERS = TAIL && !SPLITK;
+  constexpr int MBM = QUARTERS ? 2 * BM : BM;    // m-tile height of the tile list
 
   // m-tiles per segment and their exclusive scan (segments <= 256)
   {
@@ -227,7 +237,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     const int r = total % g.split_slots;
     if (r > 0 && 4 * r <= g.split_slots) cut = total - r;
   }
-  const int items = TAIL ? 4 * (total - cut) : cut;
+  const int items = TAIL ? (SPLITK ? g.ksplit : 4) * (total - cut) : cut;
+  if (SPLITK && blockIdx.x == 0 && tid == 0) g.part_meta[0] = total - cut;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, S = gridDim.x >> 3;
 
   // per-lane LDS fragment offsets (rows i*32 + lane%32 share the swizzle)
@@ -248,13 +259,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // each weight n-tile back to back (one HBM read, the rest from L2); each XCD
   // takes S consecutive tile ids per round.
   int round = -1, row0 = 0, row_end = 0, ntile = 0, e = 0;
+  int kbeg = 0, kend = KT, unit = 0;             // K steps of the current tile (a range for split-K)
   auto next_tile = [&]() -> bool {
     for (;;) {
       ++round;
       const int L = MOE_GEMM_XCD_MAP ? (round * 8 + xcd) * S + slot
                                      : round * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
       if (L >= items) return false;
-      const int Lm = TAIL ? cut + (L >> 2) : L;  // tile of the list (quarter L & 3 in the tail)
+      // tile of the list (quarter L & 3, or K range L / r, in the tail; the
+      // split-K units are range-major, so that the units running together on
+      // an XCD share A and B ranges through its L2 as whole tiles do)
+      const int Lm = TAIL ? cut + (SPLITK ? L % (total - cut) : (L >> 2)) : L;
       int lo = 0, hi = n_seg;                    // mt_start[lo]*NT <= Lm < mt_start[hi]*NT
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -267,11 +282,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const int local = Lm - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
       const int nt_list = local / mte;
       const int mloc = local - nt_list * mte;
-      row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * MBM + (TAIL ? ((L >> 1) & 1) * BM : 0);
+      row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * MBM + (QUARTERS ? ((L >> 1) & 1) * BM : 0);
       row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
-      ntile = TAIL ? 2 * nt_list + (L & 1) : nt_list;
+      ntile = QUARTERS ? 2 * nt_list + (L & 1) : nt_list;
       // a tail quarter wholly past the segment end or the last column has no work
-      if (TAIL && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
+      if (QUARTERS && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
+      if (SPLITK) {
+        const int sp = L / (total - cut);
+        kbeg = sp * KT / g.ksplit;
+        kend = (sp + 1) * KT / g.ksplit;
+        unit = L;
+        if (sp == 0 && tid == 0) {
+          int32_t* m = g.part_meta + 1 + 3 * (Lm - cut);
+          m[0] = row0;
+          m[1] = row_end;
+          m[2] = ntile;
+        }
+      }
       return true;
     }
   };
@@ -444,7 +471,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   auto mm_dma = [&](auto P, int kt2, uint8_t* stg) {
     constexpr int p = decltype(P)::value;
     constexpr int NMM = TMI * TNI;
-    const bool live = kt2 < KT;
+    const bool live = kt2 < kend;
     const __amdgpu_buffer_rsrc_t ra = live ? rsA : rs_null;
     const __amdgpu_buffer_rsrc_t rb0 = live ? rsB0 : rs_null;
     const __amdgpu_buffer_rsrc_t rb1 = live ? rsB1 : rs_null;
@@ -490,8 +517,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   if (!next_tile()) return;
   bind_tile();
   if constexpr (!REG) {
-    dma(0, sm0);
-    dma(1, sm1);                                 // (with K = 64 this reads unused bytes, in range)
+    dma(kbeg, sm0);
+    dma(kbeg + 1, sm1);                          // (past the range: unused bytes, in range or zero)
   }
   for (;;) {
 #pragma unroll
@@ -518,9 +545,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       wait_vm0();
       __builtin_amdgcn_s_barrier();
       ldfr(sm0, 0, P0{});
-      for (int kt = 0; kt < KT; kt += 2) {
+      for (int kt = kbeg; kt < kend; kt += 2) {
         fstep(kt, sm0, sm1);
-        if (kt + 1 < KT) fstep(kt + 1, sm1, sm0);
+        if (kt + 1 < kend) fstep(kt + 1, sm1, sm0);
       }
       wait_vm0();                                 // (the last steps' empty loads included)
       __builtin_amdgcn_s_barrier();               // every wave is done with the stages
@@ -528,14 +555,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 
     // Next tile first: its first two steps load while this tile's epilogue
     // runs (the stages are free, the epilogue does not use LDS).
-    const int erow0 = row0, erow_end = row_end, entile = ntile;
+    const int erow0 = row0, erow_end = row_end, entile = ntile, eunit = unit;
     const bool more = next_tile();
     if (more) {
       bind_tile();
       if constexpr (!REG) {
-        dma(0, sm0);
-        dma(1, sm1);
+        dma(kbeg, sm0);
+        dma(kbeg + 1, sm1);
       }
+    }
+
+    if constexpr (SPLITK) {
+      // the raw float32 partial tile, rows and columns in tile order
+      float* pt = g.part + static_cast<int64_t>(eunit) * (BM * BN);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+#pragma unroll
+          for (int j = 0; j < TNI; ++j) pt[lr * BN + wn * WN + j * 32 + (lane & 31)] = acc[i][j][r];
+        }
+      if (!more) break;
+      continue;
     }
 
     // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32
@@ -571,6 +613,50 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       }
     }
     if (!more) break;
+  }
+}
+
+// Split-K tail: adds the ksplit float32 partials of each tail tile in range
+// order (fixed, so the result does not depend on timing) and applies the
+// epilogue.  Unit sp * tiles + t holds range sp of tail tile t.  Grid (tail tiles at most, 16): block y covers 16 of the tile's
+// 256 rows, thread c one tile column (SwiGLU: c < 128 pairs the W1 column
+// (c / 32) * 64 + c % 32 with the W3 column 32 further).
+template <int EPI, bool FP8A>
+__global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
+  constexpr int TB = 256;                        // tile rows and columns
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  const int t = blockIdx.x, ntail = g.part_meta[0];
+  if (t >= ntail) return;
+  const int32_t* m = g.part_meta + 1 + 3 * t;
+  const int row0 = m[0], row_end = m[1], ntile = m[2];
+  const int c = threadIdx.x;
+  if (GATED && c >= TB / 2) return;
+  const float* pt = g.part + static_cast<int64_t>(t) * (TB * TB);
+  const int64_t range_stride = static_cast<int64_t>(ntail) * (TB * TB);
+  for (int rr = 0; rr < 16; ++rr) {
+    const int lr = blockIdx.y * 16 + rr;
+    const int row = row0 + lr;
+    if (row >= row_end) break;
+    const float sc = FP8A ? g.a_scale[row] : 1.0f;
+    if (GATED) {
+      const int pu = (c >> 5) * 64 + (c & 31);
+      float u = 0.f, gt = 0.f;
+      for (int sp = 0; sp < g.ksplit; ++sp) {
+        u += pt[sp * range_stride + lr * TB + pu];
+        gt += pt[sp * range_stride + lr * TB + pu + 32];
+      }
+      const int col = ntile * (TB / 2) + c;
+      if (col < g.n_out)
+        g.out[static_cast<int64_t>(row) * g.n_out + col] = to_bf16(silu_fast(u * sc) * (gt * sc));
+    } else {
+      float v = 0.f;
+      for (int sp = 0; sp < g.ksplit; ++sp) v += pt[sp * range_stride + lr * TB + c];
+      v *= sc;
+      if (EPI == EPI_SILU) v = silu_fast(v);
+      if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+      const int col = ntile * TB + c;
+      if (col < g.n_out) g.out[static_cast<int64_t>(row) * g.n_out + col] = to_bf16(v);
+    }
   }
 }
 
@@ -632,14 +718,14 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------- launch --
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK = false>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL>), dim3(grid),
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL, SPLITK>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, st, g);
   return hipGetLastError();
 }
@@ -649,6 +735,8 @@ hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
 // rows cost half as much, so the taller tile pays from shorter segments
 // (measured: DeepSeek-V3-shaped gate/up, ~128 rows per expert, 4.18 -> 3.96
 // ms; with bf16 activations the same change loses 6%).
+int split_slots() { return (device_cu_count() / 8) * 8; }
+
 int pick_bm(int64_t rows, int n_seg, bool fp8_a) {
   const int64_t avg = n_seg > 0 ? rows / n_seg : rows;
   return avg >= (fp8_a ? 96 : 384) ? 256 : 128;
@@ -661,16 +749,27 @@ int pick_bm(int64_t rows, int n_seg, bool fp8_a) {
 // pipeline (more bytes in flight) for the weight-streaming 128-row tiles.  The
 // 256-row tile list is tail-split; its 128x128 quarters run on 4 waves of 64x64.
 template <int EPI, bool FP8A>
-hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense,
+hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, void* split,
                        hipStream_t st) {
   const int nt = g.nt;
   if (bm == 256) {
     const int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
-    g.split_slots = (device_cu_count() / 8) * 8;
+    g.split_slots = split_slots();
     hipError_t err = launch_gg_on<256, 256, 2, 4, EPI, FP8A, false, false>(g, mtu * nt, st);
     if (err != hipSuccess) return err;
-    return launch_gg_on<128, 128, 2, 2, EPI, FP8A, false, true>(g, 4 * mtu * nt, st);
+    if (split == nullptr)
+      return launch_gg_on<128, 128, 2, 2, EPI, FP8A, false, true>(g, 4 * mtu * nt, st);
+    // split-K tail (scratch from the caller): whole tiles, kSplitK ranges each
+    g.ksplit = kSplitK;
+    g.part_meta = static_cast<int32_t*>(split);
+    g.part = reinterpret_cast<float*>(static_cast<char*>(split) + kSplitMetaBytes);
+    err = launch_gg_on<256, 256, 2, 4, EPI, FP8A, false, true, true>(g, kSplitK * mtu * nt, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gg_splitk_reduce<EPI, FP8A>), dim3(g.split_slots / 4, 16), dim3(256), 0,
+                       st, g);
+    return hipGetLastError();
   }
+  (void)split;
   const int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
   g.split_slots = 0;
   return launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
@@ -678,9 +777,26 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense,
 
 }  // namespace
 
+// Scratch of the split-K tail for this shape's grouped GEMMs: none when
+// neither uses 256-row tiles, else kSplitK partial tiles for each of at most
+// min(S / 4, tiles) tail tiles.
+size_t gemm_split_bytes(const moe_shape& s) {
+  if (s.dtype != MOE_BF16) return 0;
+  const int64_t rows = s.T * s.k;
+  const bool up256 = pick_bm(rows, s.N, s.buf_dtype == MOE_FP8_E4M3) == 256;
+  const bool down256 = pick_bm(rows, s.N, false) == 256;
+  if (!up256 && !down256) return 0;
+  const int64_t mtu = ceil_div(rows, 256) + s.N;
+  const int64_t nt_up = s.act == MOE_ACT_SWIGLU ? ceil_div(s.F, 128) : ceil_div(s.F, 256);
+  const int64_t nt_down = ceil_div(s.d, 256);
+  const int64_t tiles = mtu * ((up256 ? nt_up : 0) > (down256 ? nt_down : 0) ? nt_up : nt_down);
+  const int64_t tail = std::min<int64_t>(split_slots() / 4, tiles);
+  return kSplitMetaBytes + static_cast<size_t>(tail) * kSplitK * 256 * 256 * 4;
+}
+
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg, const void* w1,
-                            const void* w3, void* h, hipStream_t st) {
+                            const void* w3, void* h, void* split, hipStream_t st) {
   if (s.dtype == MOE_F32) {
     int64_t n = rows * s.F;
     dim3 grid(static_cast<unsigned>(ceil_div(n, 256)));
@@ -706,16 +822,16 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
   const bool gated = s.act == MOE_ACT_SWIGLU;
   g.nt = static_cast<int>(gated ? ceil_div(s.F, 128) : ceil_div(s.F, 256));
   const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8);
-  if (gated) return fp8 ? dispatch_up<EPI_SWIGLU, true>(bm, g, rows, n_seg, dense, st)
-                        : dispatch_up<EPI_SWIGLU, false>(bm, g, rows, n_seg, dense, st);
-  if (s.act == MOE_ACT_RELU) return fp8 ? dispatch_up<EPI_RELU, true>(bm, g, rows, n_seg, dense, st)
-                                        : dispatch_up<EPI_RELU, false>(bm, g, rows, n_seg, dense, st);
-  return fp8 ? dispatch_up<EPI_SILU, true>(bm, g, rows, n_seg, dense, st)
-             : dispatch_up<EPI_SILU, false>(bm, g, rows, n_seg, dense, st);
+  if (gated) return fp8 ? dispatch_up<EPI_SWIGLU, true>(bm, g, rows, n_seg, dense, split, st)
+                        : dispatch_up<EPI_SWIGLU, false>(bm, g, rows, n_seg, dense, split, st);
+  if (s.act == MOE_ACT_RELU) return fp8 ? dispatch_up<EPI_RELU, true>(bm, g, rows, n_seg, dense, split, st)
+                                        : dispatch_up<EPI_RELU, false>(bm, g, rows, n_seg, dense, split, st);
+  return fp8 ? dispatch_up<EPI_SILU, true>(bm, g, rows, n_seg, dense, split, st)
+             : dispatch_up<EPI_SILU, false>(bm, g, rows, n_seg, dense, split, st);
 }
 
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
-                              int64_t rows, int n_seg, const void* w2, void* out,
+                              int64_t rows, int n_seg, const void* w2, void* out, void* split,
                               hipStream_t st) {
   if (s.dtype == MOE_F32) {
     int64_t n = rows * s.d;
@@ -740,7 +856,7 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.out = static_cast<uint16_t*>(out);
   g.nt = static_cast<int>(ceil_div(s.d, 256));
   const int bm = pick_bm(rows, dense ? 1 : n_seg, false);
-  return dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, st);
+  return dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, split, st);
 }
 
 }  // namespace moe

@@ -13,6 +13,8 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
 constexpr int kRouteTile = 16;     // tokens per router workgroup
 constexpr int kDispatchBlock = 256;  // tokens per dispatch-plan block
+constexpr int kSplitK = 4;           // K ranges per tail tile of a split-K grouped GEMM tail
+constexpr size_t kSplitMetaBytes = 4096;  // header of the split-K scratch (tile count, tile rows)
 
 // ---------------------------------------------------------------- helpers --
 
@@ -37,6 +39,7 @@ struct WsLayout {
   size_t route_hist;    // int32   [nb_route][N]
   size_t route_base;    // int32   [nb_route][N]
   size_t disp_hist;     // int32   [nb_disp][N]
+  size_t gemm_split;    // split-K tail scratch of the grouped GEMMs (gemm_split_bytes(s))
   size_t h;             // dtype   [T*k][F]
   size_t h_shared;      // dtype   [T][F]
   size_t total;
@@ -70,12 +73,15 @@ hipError_t launch_dispatch_copy_planned(const moe_shape& s, const void* x, const
                                         float* row_scale, hipStream_t st);
 
 // Grouped GEMMs.  `offsets` == nullptr means one dense segment of `rows` rows.
+// `split` (may be null): gemm_split_bytes(s) of scratch for a split-K tail;
+// without it a mostly idle last round runs as quarter tiles.
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg,
-                            const void* w1, const void* w3, void* h, hipStream_t st);
+                            const void* w1, const void* w3, void* h, void* split, hipStream_t st);
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
-                              int64_t rows, int n_seg, const void* w2, void* out,
+                              int64_t rows, int n_seg, const void* w2, void* out, void* split,
                               hipStream_t st);
+size_t gemm_split_bytes(const moe_shape& s);
 
 hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_shared,
                           const void* x, const int32_t* pos, const float* w, void* y,

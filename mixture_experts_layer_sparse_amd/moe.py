@@ -84,8 +84,8 @@ _SIGS = {
     "moe_route": (c_int32, [POINTER(Shape)] + [_P] * 11 + [_P, c_size_t, _P]),
     "moe_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 8 + [_P, c_size_t, _P]),
     "moe_route_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P, c_size_t, _P]),
-    "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
-    "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P]),
+    "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
+    "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
     "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
     "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
@@ -239,7 +239,9 @@ def route_dispatch(s: Shape, x, wg, bias=None, ws=None) -> dict:
     return o
 
 
-def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None):
+def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None, ws=None):
+    """ws: None (a mostly idle last tile round runs as quarter tiles) or a
+    workspace from alloc_workspace (that round is split along K instead)."""
     R, F = s.T * s.k, s.F
     _check(x_perm, "x_perm", (R, s.d), s.buf_torch_dtype)
     _check(offsets, "offsets", (s.N + 1,), torch.int32)
@@ -248,17 +250,19 @@ def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None):
     if h is None:
         h = torch.empty((R, F), dtype=s.torch_dtype, device=x_perm.device)
     _call("moe_expert_up", ctypes.byref(s), _ptr(x_perm), _ptr(row_scale), _ptr(offsets), _ptr(w1),
-          _ptr(w3), _ptr(h), _stream())
+          _ptr(w3), _ptr(h), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     return h
 
 
-def expert_down(s: Shape, h, offsets, w2, out=None):
+def expert_down(s: Shape, h, offsets, w2, out=None, ws=None):
+    """ws as for expert_up."""
     R = s.T * s.k
     _check(h, "h", (R, s.F), s.torch_dtype)
     _check(w2, "w2", (s.N, s.d, s.F), s.torch_dtype)
     if out is None:
         out = torch.empty((R, s.d), dtype=s.torch_dtype, device=h.device)
-    _call("moe_expert_down", ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(out), _stream())
+    _call("moe_expert_down", ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(out), _ptr(ws),
+          0 if ws is None else ws.numel(), _stream())
     return out
 
 

@@ -76,6 +76,29 @@ def run_gpu(wl, inp, logits=True):
     return res
 
 
+def run_experts_no_workspace(wl, inp):
+    """Route and dispatch as run_gpu, then the two grouped GEMMs called alone
+    without a workspace (a mostly idle last tile round runs as quarter tiles
+    instead of split-K); host copies of offsets and out."""
+    s = M.shape_of(wl)
+    g = upload(wl, inp)
+    r = M.route(s, g["x"], g["wg"], g.get("bias"))
+    dsp = M.dispatch(s, g["x"], r["idx"])
+    h = M.expert_up(s, dsp["x_perm"], dsp["row_scale"], dsp["offsets"], g["w1"], g.get("w3"))
+    out = M.expert_down(s, h, dsp["offsets"], g["w2"])
+    torch.cuda.synchronize()
+    return {"offsets": host(dsp["offsets"]), "out": host(out)}
+
+
+def rows_rel_err(a, b):
+    """Largest per-row relative L2 difference of two bf16/f32 row blocks."""
+    a = as_values(a, "bf16") if a.dtype == np.uint16 else a.astype(np.float64)
+    b = as_values(b, "bf16") if b.dtype == np.uint16 else b.astype(np.float64)
+    num = np.sqrt(np.sum((a - b) ** 2, axis=1))
+    den = np.maximum(np.sqrt(np.sum(b ** 2, axis=1)), 1e-30)
+    return float(np.max(num / den)) if a.size else 0.0
+
+
 def run_gpu_forward(wl, inp):
     """The whole layer in one call (moe_forward); host copies of its outputs
     under the same names as run_gpu."""

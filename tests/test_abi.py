@@ -99,7 +99,7 @@ def test_null_pointers_and_workspace_rejected_on_host(M):
     assert st == M.MOE_ERR_WORKSPACE
     # SwiGLU without W3
     s2 = _s(M, act="swiglu")
-    st = L.moe_expert_up(ctypes.byref(s2), p, None, p, p, None, p, None)
+    st = L.moe_expert_up(ctypes.byref(s2), p, None, p, p, None, p, None, 0, None)
     assert st == M.MOE_ERR_ARG
     # T == 0 is a no-op even with null buffers
     s0 = _s(M, T=0)
@@ -110,7 +110,9 @@ def test_null_pointers_and_workspace_rejected_on_host(M):
 
 
 def test_workspace_grows_with_h(M):
-    a = M.workspace_bytes(_s(M, T=64))
-    b = M.workspace_bytes(_s(M, T=128))
-    assert b > a
-    assert M.workspace_bytes(_s(M, T=64, dtype="bf16")) < a   # bf16 h is half the bytes
+    for dt, es in (("f32", 4), ("bf16", 2)):
+        a = M.workspace_bytes(_s(M, T=64, dtype=dt))
+        b = M.workspace_bytes(_s(M, T=128, dtype=dt))
+        assert b > a
+        s = _s(M, T=128, dtype=dt)
+        assert b >= s.T * s.k * s.F * es          # the expert intermediate h lives there

@@ -110,11 +110,25 @@ def test_many_tokens_with_capacity():
     assert gpu["drop"].sum() > 0
 
 
+def _check_tail_paths(wl, gpu):
+    """The tail as split-K (moe_experts, with a workspace: gpu, already checked
+    against the oracle) and as quarter tiles (the GEMM calls alone, without a
+    workspace) must agree row by row to rounding."""
+    from moe_gpu_util import rows_rel_err, run_experts_no_workspace
+    q = run_experts_no_workspace(wl, si.generate(wl))
+    assert np.array_equal(q["offsets"], gpu["offsets"])
+    R = int(gpu["offsets"][-1])
+    err = rows_rel_err(q["out"][:R], gpu["out"][:R])
+    print(f"  split-K vs quarter tiles: max row rel err {err:.2e}", flush=True)
+    assert err <= 1e-2
+
+
 @pytest.mark.parametrize("act,buf", [("swiglu", "bf16"), ("relu", "fp8")])
-def test_gemm_tail_quarters_only(act, buf):
-    """Fewer 256-row tiles than half the CUs: every tile runs as 128x128
-    quarters, including quarters wholly past a segment end or past the last
-    output column (d = 320, and F = 384 with ReLU)."""
+def test_gemm_tail_only(act, buf):
+    """Fewer 256-row tiles than a quarter of the CUs: every tile is in the
+    tail, as split-K partials or as 128x128 quarters (including quarters
+    wholly past a segment end or past the last output column: d = 320, and
+    F = 384 with ReLU)."""
     from moe_gpu_util import gemm_tail_split
     wl = si.Workload("tq", T=2000, d=320, N=8, k=2, F=384, act=act, dtype="bf16", buf=buf)
     gpu, errs = _run_and_check(wl)
@@ -122,11 +136,12 @@ def test_gemm_tail_quarters_only(act, buf):
     for nt in (nt_up, -(-wl.d // 256)):
         total, cut, _ = gemm_tail_split(gpu["kept_counts"], 256, nt)
         assert cut == 0 and total > 0, (total, cut)
+    _check_tail_paths(wl, gpu)
 
 
 def test_gemm_main_and_tail():
-    """Whole rounds of 256x256 tiles plus a tail of quarters in both GEMMs;
-    every token's y is compared."""
+    """Whole rounds of 256x256 tiles plus a tail in both GEMMs; every token's
+    y is compared, and both forms of the tail."""
     from moe_gpu_util import gemm_tail_split
     wl = si.Workload("tm", T=34000, d=256, N=16, k=2, F=256, act="swiglu", dtype="bf16",
                      buf="bf16")
@@ -134,6 +149,7 @@ def test_gemm_main_and_tail():
     for nt in (wl.F // 128, 1):
         total, cut, slots = gemm_tail_split(gpu["kept_counts"], 256, nt)
         assert slots <= cut < total, (total, cut, slots)
+    _check_tail_paths(wl, gpu)
 
 
 def test_groups_k_le_group_span():
