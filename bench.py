@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s at Mixtral shape; grouped-GEMM % MFMA peak; dispatch GB/s"
 # the gate/up grouped-GEMM kernel instance each workload runs (key in the counter summary)
-UP_KERNEL = {"mixtral": "gg_kernel<256,256,2,4,3,false,false,false>"}
+UP_KERNEL = {"mixtral": "gg_kernel<256,256,2,4,3,false,false,false,false>"}
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
 
@@ -40,8 +40,8 @@ PEAK_HBM_GBPS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
@@ -99,8 +99,7 @@ def cpu_baseline(wl, inp, n_tok):
 COUNTER_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_mixtral_counters.md")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sparse_amd", "csrc", "gemm.hip")
 PROFILE_CMDS = [
-    "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
-    "python3 bench.py --no-cpu-baseline --steps 10 --warmup 3",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- python3 bench.py",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
     "python3 bench.py --no-cpu-baseline --steps 3 --warmup 1",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
