@@ -136,6 +136,18 @@ __device__ __forceinline__ void sched_mfma_loads(std::integer_sequence<int, Q...
   (sched_mfma_then_loads<(Q + 1) * LPW / NMM - Q * LPW / NMM>(), ...);
 }
 
+// f(integral_constant<int, min(n, N)>) for a wave-uniform 0 <= n: one code
+// path per count of live 32-row blocks.
+template <int N, typename F>
+__device__ __forceinline__ void with_blocks(int n, F&& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N) f(std::integral_constant<int, N>{});
+    else with_blocks<N - 1>(n, f);
+  }
+}
+
 // Buffer resource over [base, base + bytes): loads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
@@ -241,6 +253,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   if (SPLITK && blockIdx.x == 0 && tid == 0) g.part_meta[0] = total - cut;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, S = gridDim.x >> 3;
 
+  // segment of tile-list entry Lm: mt_start[e] * NT <= Lm < mt_start[e + 1] * NT
+  auto seg_of_tile = [&](int Lm) {
+    int lo = 0, hi = n_seg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (mt_start[mid] * NT <= Lm) lo = mid; else hi = mid;
+    }
+    return __builtin_amdgcn_readfirstlane(lo);
+  };
   // per-lane LDS fragment offsets (rows i*32 + lane%32 share the swizzle)
   const int fr = lane & 31, fk = lane >> 5;
 
@@ -270,14 +291,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       // split-K units are range-major, so that the units running together on
       // an XCD share A and B ranges through its L2 as whole tiles do)
       const int Lm = TAIL ? cut + (SPLITK ? L % (total - cut) : (L >> 2)) : L;
-      int lo = 0, hi = n_seg;                    // mt_start[lo]*NT <= Lm < mt_start[hi]*NT
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (mt_start[mid] * NT <= Lm) lo = mid; else hi = mid;
-      }
       // values read from LDS are the same in every lane: make that explicit so
       // that the buffer descriptors live in scalar registers
-      e = __builtin_amdgcn_readfirstlane(lo);
+      e = seg_of_tile(Lm);
       const int mte = __builtin_amdgcn_readfirstlane(mt_start[e + 1] - mt_start[e]);
       const int local = Lm - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
       const int nt_list = local / mte;
@@ -308,6 +324,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   __amdgpu_buffer_rsrc_t rsB0 = make_rsrc(g.b0, 0), rsB1 = rsB0;
   uint32_t b_off[B_PW];
   bool wave_rows = false;                        // a wave whose rows all lie past the segment end skips its MFMAs
+  int wave_blocks = TMI;                         // 32-row blocks of the wave's rows inside the segment
   int a_rows = 0;                                // rows of the tile inside its segment
   const uint8_t* a_tile = static_cast<const uint8_t*>(g.a);
   uint32_t a_nrec = 0;
@@ -348,6 +365,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     wave_rows = row0 + wm * WM < row_end;
     a_rows = __builtin_amdgcn_readfirstlane(row_end - row0);
     rs_a_whole = make_rsrc(a_tile, a_bytes);
+    const int live = a_rows - wm * WM;
+    wave_blocks = live <= 0 ? 0 : (live >= TMI * 32 ? TMI : (live + 31) >> 5);
   };
 
   f32x16 acc[TMI][TNI];
@@ -450,12 +469,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     }
   };
   bf16x8 fa[2][TMI], fb[2][TNI];
-  auto ldfr = [&](const uint8_t* sA, int kk, auto P) {
-    constexpr int p = decltype(P)::value;
+  auto ldfr = [&](const uint8_t* sA, int kk, auto P, auto NI) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value, ni = decltype(NI)::value;
+    if constexpr (ni == 0) return;
     const uint8_t* sB = sA + A_BYTES;
     const int cc = kk * 2 + fk;
 #pragma unroll
-    for (int i = 0; i < TMI; ++i) {
+    for (int i = 0; i < ni; ++i) {
       const int r = wm * WM + i * 32 + fr;
       if (FP8A) {
         const uint2 v = *reinterpret_cast<const uint2*>(
@@ -472,24 +492,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       fb[p][j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
     }
   };
-  auto mm = [&](auto P) {
-    constexpr int p = decltype(P)::value;
+  auto mm = [&](auto P, auto NI) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value, ni = decltype(NI)::value;
 #pragma unroll
-    for (int i = 0; i < TMI; ++i)
+    for (int i = 0; i < ni; ++i)
 #pragma unroll
       for (int j = 0; j < TNI; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
   };
-  // MFMAs of fragment buffer P with the loads of step kt2 into stg spread
-  // between them.  Every wave runs these MFMAs, also one whose rows all lie
-  // past the segment end (its results are never stored): a branch here
-  // would duplicate the loads, and the compiler then no longer tells the
-  // two stages apart and waits for all loads before every fragment read.
-  // Past the last step the loads go through an empty descriptor (every
-  // lane out of range: no memory access), which keeps this a single block.
-  auto mm_dma = [&](auto P, int kt2, uint8_t* stg) {
+  // MFMAs of fragment buffer P (the NI live row blocks) with the loads of
+  // step kt2 into stg spread between them.  Past the last step the loads go
+  // through an empty descriptor (every lane out of range: no memory access)
+  // rather than a branch: a branch would duplicate the loads, and the
+  // compiler then no longer tells the two stages apart and waits for all
+  // loads before every fragment read.
+  auto mm_dma = [&](auto P, auto NI, int kt2, uint8_t* stg) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
-    constexpr int NMM = TMI * TNI;
+    constexpr int NMM = decltype(NI)::value * TNI;
     const bool live = kt2 < kend;
 
     const __amdgpu_buffer_rsrc_t rb0 = live ? rsB0 : rs_null;
@@ -505,32 +524,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         lds_dma16(w3 ? rb1 : rb0, stg + A_BYTES + gi * 1024, b_off[j], kb);
       }
     };
+    if constexpr (NMM == 0) {
 #pragma unroll
-    for (int q = 0; q < NMM; ++q) {
-      acc[q / TNI][q % TNI] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          fa[p][q / TNI], fb[p][q % TNI], acc[q / TNI][q % TNI], 0, 0, 0);
+      for (int u = 0; u < LPW; ++u) issue(u);
+    } else {
 #pragma unroll
-      for (int u = q * LPW / NMM; u < (q + 1) * LPW / NMM; ++u) issue(u);
+      for (int q = 0; q < NMM; ++q) {
+        acc[q / TNI][q % TNI] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fa[p][q / TNI], fb[p][q % TNI], acc[q / TNI][q % TNI], 0, 0, 0);
+#pragma unroll
+        for (int u = q * LPW / NMM; u < (q + 1) * LPW / NMM; ++u) issue(u);
+      }
+      // keep that order through scheduling: one MFMA, then its loads
+      sched_mfma_loads<NMM, LPW>(std::make_integer_sequence<int, NMM>{});
     }
-    // keep that order through scheduling: one MFMA, then its loads
-    sched_mfma_loads<NMM, LPW>(std::make_integer_sequence<int, NMM>{});
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   static_assert(BK / 16 == 4, "four K slices per step");
-  // invariant at step entry: fragments of (cur, slice 0) issued into buffer 0
-  auto fstep = [&](int kt, uint8_t* cur, uint8_t* nxt) {
-    ldfr(cur, 1, P1{});
-    if (wave_rows) mm(P0{});
-    ldfr(cur, 2, P0{});
-    if (wave_rows) mm(P1{});
-    ldfr(cur, 3, P1{});
-    if (wave_rows) mm(P0{});
+  // invariant at step entry: fragments of (cur, slice 0) issued into buffer 0.
+  // NI = the wave's live 32-row blocks: fragment reads and MFMAs of blocks
+  // wholly past the segment end are left out, so that a segment's partial
+  // last m-tile costs about its share of rows; every NI runs the same loads
+  // and barriers.
+  auto fstep = [&](int kt, uint8_t* cur, uint8_t* nxt, auto NI) __attribute__((always_inline)) {
+    ldfr(cur, 1, P1{}, NI);
+    mm(P0{}, NI);
+    ldfr(cur, 2, P0{}, NI);
+    mm(P1{}, NI);
+    ldfr(cur, 3, P1{}, NI);
+    mm(P0{}, NI);
     wait_vm0();                               // own loads of step kt + 1 landed
     wait_lgkm0();                             // own reads of cur done
     __builtin_amdgcn_s_barrier();
-    ldfr(nxt, 0, P0{});
-    mm_dma(P1{}, kt + 2, cur);
+    ldfr(nxt, 0, P0{}, NI);
+    mm_dma(P1{}, NI, kt + 2, cur);
   };
 
   if (!next_tile()) return;
@@ -563,11 +591,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       // the tile's first two steps were issued before the previous epilogue
       wait_vm0();
       __builtin_amdgcn_s_barrier();
-      ldfr(sm0, 0, P0{});
-      for (int kt = kbeg; kt < kend; kt += 2) {
-        fstep(kt, sm0, sm1);
-        if (kt + 1 < kend) fstep(kt + 1, sm1, sm0);
-      }
+      // (steps in pairs, the odd last one after the loop: a conditional step
+      // inside the loop merges a path with loads pending into the stage the
+      // loop head reads, and the compiler then waits for them there)
+      with_blocks<TMI>(wave_blocks, [&](auto NI) __attribute__((always_inline)) {
+        ldfr(sm0, 0, P0{}, NI);
+        int kt = kbeg;
+        for (; kt + 1 < kend; kt += 2) {
+          fstep(kt, sm0, sm1, NI);
+          fstep(kt + 1, sm1, sm0, NI);
+        }
+        if (kt < kend) fstep(kt, sm0, sm1, NI);
+      });
       wait_vm0();                                 // (the last steps' empty loads included)
       __builtin_amdgcn_s_barrier();               // every wave is done with the stages
     }
