@@ -161,7 +161,9 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
   for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
     const int m = q / N, e = q % N;
     float v = 0.f;
-    for (int kk = 0; kk < KS; ++kk) v += part[(kk * TM + m) * NP + e];
+#pragma unroll
+    for (int kk = 0; kk < RW; ++kk)             // (KS <= RW: the reads issued together, added in order)
+      if (kk < KS) v += part[(kk * TM + m) * NP + e];
     if (a.bias) v += a.bias[e];
     lt[m * ldl + e] = v;
   }
@@ -272,7 +274,9 @@ __device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf,
   for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
     const int m = q / N, e = q % N;
     float v = 0.f;
-    for (int kk = 0; kk < KS; ++kk) v += part[(kk * TM + m) * NP + e];
+#pragma unroll
+    for (int kk = 0; kk < RW; ++kk)             // (KS <= RW: the reads issued together, added in order)
+      if (kk < KS) v += part[(kk * TM + m) * NP + e];
     if (a.bias) v += a.bias[e];
     lt[m * ldl + e] = v;
   }
@@ -295,6 +299,10 @@ __device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
   }
 }
 
+// Exponentials of the routing weights and of p use the hardware exp2 (__expf,
+// a few ulp for these arguments): both are float32 results checked to 1e-5
+// relative, and no selection depends on them.
+
 // Selection for one token by one lane (N <= SMALL_N): everything in order over
 // the expert index, so a strictly larger value is needed to replace the
 // current best and equal logits keep the lower index.  Writes the token's full
@@ -304,8 +312,8 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
   float mx = -INFINITY;
   for (int e = 0; e < N; ++e) mx = fmaxf(mx, row[e]);
   float zs = 0.f;
-  for (int e = 0; e < N; ++e) zs += expf(row[e] - mx);
-  for (int e = 0; e < N; ++e) prow[e] = expf(row[e] - mx) / zs;
+  for (int e = 0; e < N; ++e) zs += __expf(row[e] - mx);
+  for (int e = 0; e < N; ++e) prow[e] = __expf(row[e] - mx) / zs;
   uint32_t allowed = N >= 32 ? 0xFFFFFFFFu : ((1u << N) - 1u);
   if (a.n_groups > 1) {
     const int G = a.n_groups, gsz = N / G;
@@ -363,12 +371,12 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
   float den = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k) den += expf(sel_v[j] - sel_v[0]);
+    if (j < k) den += __expf(sel_v[j] - sel_v[0]);
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j < k) {
       a.idx[t * k + j] = sel_e[j];
-      a.w[t * k + j] = expf(sel_v[j] - sel_v[0]) / den;
+      a.w[t * k + j] = __expf(sel_v[j] - sel_v[0]) / den;
       atomicAdd(&hl[sel_e[j]], 1);
     }
   }
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
     float z[4], zs = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = ok[i] ? expf(v[i] - mx) : 0.f;
+      z[i] = ok[i] ? __expf(v[i] - mx) : 0.f;
       zs += z[i];
     }
     zs = wave_sum_f(zs);
@@ -523,12 +531,12 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
     float den = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
-      if (j < k) den += expf(sel_v[j] - sel_v[0]);
+      if (j < k) den += __expf(sel_v[j] - sel_v[0]);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k && lane == j) {
         a.idx[t * k + j] = sel_e[j];
-        a.w[t * k + j] = expf(sel_v[j] - sel_v[0]) / den;
+        a.w[t * k + j] = __expf(sel_v[j] - sel_v[0]) / den;
         atomicAdd(&hl[sel_e[j]], 1);
       }
     }
