@@ -1,7 +1,7 @@
 """Benchmark of the sparse MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--no-cpu-baseline] [--mode bench|copy]
+                    [--no-cpu-baseline] [--mode bench|copy|sweep|decode|summarize]
 
 One step = one whole layer forward (route, dispatch, grouped GEMM up, grouped
 GEMM down, shared expert if any, combine) over one batch of seeded synthetic
@@ -17,7 +17,9 @@ memory-phase bandwidths, and the float64 CPU oracle timed on a bounded sample.
 
 --mode copy runs a plain device copy of a known size (the calibration kernel
 for the hardware byte counters) and exits.  --mode sweep times every workload
-family at full size, phase by phase, and prints a markdown table.
+family at full size, phase by phase, and prints a markdown table.  --mode
+decode times decode steps (B = 1, 32, 128 tokens) at the DeepSeek-V3 shape:
+experts touched and the expert-weight bytes streamed against the HBM peak.
 """
 from __future__ import annotations
 
@@ -46,7 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens whose expert FFNs the CPU oracle runs (0: all T)")
-    ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep", "decode"], default="bench")
     ap.add_argument("--prof", default=None,
                     help="summarize: directory holding trace/ fetch/ write/ cfetch/ cwrite/ "
                          "rocprofv3 csv output")
@@ -215,20 +217,61 @@ def expert_weight_bytes(wl):
     return (wl.N + (1 if wl.shared else 0)) * m * wl.F * wl.d * s
 
 
+def _to_dev(arr):
+    import numpy as np
+    import torch
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def _phases(wl, g, x, steps, warmup):
+    """Runs the kernels of moe_forward phase by phase; returns (layer, mean
+    phase times in us [route+dispatch, up, down, shared, combine], wall time
+    per step in s)."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_sparse_amd import moe as M
+    s = M.shape_of(wl)
+    L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
+                ws3=g["ws3"], ws2=g["ws2"])
+    h = torch.empty((wl.T * wl.k, wl.F), dtype=s.torch_dtype, device="cuda")
+    hs = torch.empty((wl.T, wl.F), dtype=s.torch_dtype, device="cuda") if wl.shared else None
+
+    def step(ev):
+        ev[0].record()
+        L.route_dispatch(x)
+        ev[1].record()
+        M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
+        ev[2].record()
+        M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
+        ev[3].record()
+        if wl.shared:
+            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
+        ev[4].record()
+        L.combine(x)
+        ev[5].record()
+
+    E = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps + warmup)]
+    for i in range(warmup):
+        step(E[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        step(E[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in E[warmup:]]).mean(0) * 1e3
+    return L, ph, wall
+
+
 def sweep(steps, warmup):
     """Every workload family at its full size, phase by phase (the kernels of
     moe_forward); prints a markdown table."""
-    import numpy as np
     import torch
     import synthetic_inputs as si
-    from mixture_experts_layer_sparse_amd import moe as M
-
-    def dev(arr):
-        if arr is None:
-            return None
-        if arr.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
     print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | GEMM down us | shared us | "
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
@@ -236,39 +279,10 @@ def sweep(steps, warmup):
     for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx"):
         wl = si.WORKLOADS[name]
         inp = si.generate(wl)
-        g = {k: dev(v) for k, v in inp.items()}
+        g = {k: _to_dev(v) for k, v in inp.items()}
         del inp
-        s = M.shape_of(wl)
-        L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
-                    ws3=g["ws3"], ws2=g["ws2"])
         x = g["x"]
-        h = torch.empty((wl.T * wl.k, wl.F), dtype=s.torch_dtype, device="cuda")
-        hs = torch.empty((wl.T, wl.F), dtype=s.torch_dtype, device="cuda") if wl.shared else None
-
-        def step(ev):
-            ev[0].record()
-            L.route_dispatch(x)
-            ev[1].record()
-            M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
-            ev[2].record()
-            M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
-            ev[3].record()
-            if wl.shared:
-                M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
-            ev[4].record()
-            L.combine(x)
-            ev[5].record()
-
-        E = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps + warmup)]
-        for i in range(warmup):
-            step(E[i])
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(warmup, warmup + steps):
-            step(E[i])
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / steps
-        ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in E[warmup:]]).mean(0) * 1e3
+        L, ph, wall = _phases(wl, g, x, steps, warmup)
         R = int(L.offsets[-1].item())
         up, down, shared = gemm_flops(wl, R)
         rb, db, cb = alg_bytes(wl, R)
@@ -281,7 +295,41 @@ def sweep(steps, warmup):
               f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | "
               f"{tf:.0f} ({100 * tf / PEAK_BF16_TFLOPS:.1f}%) | {wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) | "
               f"{mgb:.0f} ({100 * mgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
-        del L, g, x, h, hs
+        del L, g, x
+        torch.cuda.empty_cache()
+
+
+def decode(steps, warmup):
+    """Decode steps at the DeepSeek-V3 shape (B = 1, 32, 128 tokens, the
+    prefill batch's first B tokens and the same weights): experts touched
+    against the uniform-routing estimate N (1 - (1 - k/N)^B), and the expert
+    weight bytes the GEMMs must stream (touched routed experts + the shared
+    one) over the GEMM time, against the HBM peak.  Prints a markdown table."""
+    import torch
+    import synthetic_inputs as si
+
+    base = si.WORKLOADS["deepseek_v3"]
+    inp = si.generate(base)
+    g = {k: _to_dev(v) for k, v in inp.items()}
+    del inp
+    m = 3 if base.swiglu else 2
+    per_expert = m * base.F * base.d * 2
+    print("| B | experts touched (uniform estimate) | us/step | tokens/s | route+dispatch us | GEMM up us | "
+          "GEMM down us | shared us | combine us | weight bytes streamed | weight GB/s (% HBM) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for B in (1, 32, 128):
+        wl = si.decode(B)
+        x = g["x"][:B].contiguous()
+        L, ph, wall = _phases(wl, g, x, steps, warmup)
+        touched = int((L.counts > 0).sum().item())
+        est = base.N * (1.0 - (1.0 - base.k / base.N) ** B)
+        wbytes = (touched + (1 if base.shared else 0)) * per_expert
+        gemm_us = ph[1] + ph[2] + ph[3]
+        wgb = wbytes / (gemm_us * 1e-6) / 1e9
+        print(f"| {B} | {touched} ({est:.1f}) | {wall * 1e6:.1f} | {B / wall:,.0f} | {ph[0]:.1f} | {ph[1]:.1f} | "
+              f"{ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | {wbytes / 2**30:.2f} GiB | "
+              f"{wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
+        del L, x
         torch.cuda.empty_cache()
 
 
@@ -292,6 +340,9 @@ def main():
         return
     if a.mode == "sweep":
         sweep(a.steps, a.warmup)
+        return
+    if a.mode == "decode":
+        decode(a.steps, a.warmup)
         return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))

@@ -18,6 +18,7 @@ train and serve"):
                                                     per-token scale, +1 shared expert
     dbrx         T=16384 d=6144 N=16  k=4  F=10752  SwiGLU, bf16, router bias
                                                     b_e = 2 ln(1/(e+1))
+    decode(B)    deepseek_v3 with T = B tokens (B = 1, 32, 128: a decode step)
 
 Recipe (identical bytes go to the GPU and to the oracle):
   * every tensor is filled chunk by chunk; chunk ``c`` of tensor ``tag`` is
@@ -84,6 +85,15 @@ WORKLOADS = {
                             buf="fp8", n_groups=8, topk_groups=4, shared=True),
     "dbrx": Workload("dbrx", T=16384, d=6144, N=16, k=4, F=10752, bias="zipf2"),
 }
+
+
+def decode(B: int) -> Workload:
+    """A decode step at the DeepSeek-V3 shape: B tokens, the same weights and
+    router as ``deepseek_v3`` (the worked example "how many experts does one
+    decode step touch?" of "MoE: what it costs to train and serve").  The
+    token draws are the first B rows of the T = 4096 batch (each chunk's
+    draws do not depend on how many are taken)."""
+    return WORKLOADS["deepseek_v3"].replace(name=f"deepseek_v3_decode{B}", T=B)
 
 
 def switch_capacity(T: int, N: int, factor: float = 1.25) -> int:

@@ -3,6 +3,8 @@
 Small cases span several tiles of every kernel with ragged tails; full-size
 cases run the workloads at their real shapes (all of routing, the plan and the
 dispatch buffer compared; y on sampled tokens)."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -243,9 +245,34 @@ def test_forward_matches_oracle_and_phases(name):
 
 # -------------------------------------------------------------- full sizes --
 
+@functools.lru_cache(maxsize=1)
+def _deepseek_experts():
+    """The DeepSeek-V3-shaped expert weights (22.5 GB), drawn once per session."""
+    return si.generate_experts(si.WORKLOADS["deepseek_v3"])
+
+
 @pytest.mark.parametrize("name", ["mixtral", "switch", "deepseek_v3", "dbrx"])
 def test_full_size_parity(name):
     wl = si.WORKLOADS[name]
-    inp = si.generate(wl)
+    if name == "deepseek_v3":
+        inp = dict(si.generate(wl, experts=False), **_deepseek_experts())
+    else:
+        inp = si.generate(wl)
     toks = sample_tokens(wl.T, 40)
     _run_and_check(wl, inp, y_tokens=toks)
+
+
+@pytest.mark.parametrize("B", [1, 32, 128])
+def test_decode_step_deepseek_shape(B):
+    """A decode step: B tokens (the prefill batch's first B) through the full
+    DeepSeek-V3-shaped layer, so most segments hold one row or none.  Routing,
+    plan and fp8 dispatch buffer exact; y on every token at B = 1, on 8
+    sampled tokens otherwise; the experts touched are those with a nonzero
+    count."""
+    wl = si.decode(B)
+    inp = dict(si.generate(wl, experts=False), **_deepseek_experts())
+    toks = None if B == 1 else sample_tokens(B, 8)
+    gpu, _ = _run_and_check(wl, inp, y_tokens=toks)
+    touched = int((gpu["counts"] > 0).sum())
+    print(f"  experts touched: {touched} of {wl.N}", flush=True)
+    assert touched <= min(wl.N, B * wl.k)
