@@ -249,7 +249,7 @@ def _phases(wl, g, x, steps, warmup):
         M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
         ev[3].record()
         if wl.shared:
-            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
+            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared, ws=L.ws)
         ev[4].record()
         L.combine(x)
         ev[5].record()
@@ -392,7 +392,7 @@ def main():
         M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
         ev and ev[3].record()
         if wl.shared:
-            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared)
+            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared, ws=L.ws)
         ev and ev[4].record()
         L.combine(x)
 

@@ -171,10 +171,14 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* off
  * costs" / "Capacity factor and token dropping": a shared expert every token
  * passes through): h_shared = act(Ws1 x, Ws3 x), out_shared = Ws2 h_shared.
  *   x [T][d]; ws1, ws3 [F][d] (ws3 NULL unless SwiGLU); ws2 [d][F];
- *   h_shared [T][F] scratch; out_shared [T][d] out.  All dtype. */
+ *   h_shared [T][F] scratch; out_shared [T][d] out.  All dtype.
+ *   ws     NULL, or a workspace of moe_workspace_bytes(s) bytes: with it, a
+ *          GEMM of few output tiles (few tokens) is split along K over all CUs
+ *          and its float32 partials added in a fixed order (results differ from
+ *          the call without ws only in float32 rounding order). */
 moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1,
                              const void* ws3, const void* ws2, void* h_shared,
-                             void* out_shared, void* stream);
+                             void* out_shared, void* ws, size_t ws_bytes, void* stream);
 
 /* All experts: moe_expert_up + moe_expert_down, plus moe_shared_expert when
  * has_shared (x, ws1, ws3, ws2, out_shared required then, else ignored).  The

@@ -27,6 +27,8 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align_up(off + nb_route * N * 4);
   L.route_base = off;
   off = align_up(off + nb_route * N * 4);
+  L.route_lpart = off;
+  off = align_up(off + static_cast<size_t>(moe::route_split_ranges(s)) * T * N * 4);
   L.disp_hist = off;
   off = align_up(off + nb_disp * N * 4);
   L.gemm_split = off;
@@ -124,7 +126,8 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_g, const f
   char* base = static_cast<char*>(ws);
   float* psum = reinterpret_cast<float*>(base + L.route_psum);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, st);
+  float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, lpart, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux,
                                                nullptr, nullptr, st));
@@ -190,20 +193,23 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* off
 }
 
 moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1, const void* ws3,
-                             const void* ws2, void* h_shared, void* out_shared, void* stream) {
+                             const void* ws2, void* h_shared, void* out_shared, void* ws,
+                             size_t ws_bytes, void* stream) {
   moe_status c = check_shape(s);
   if (c != MOE_OK) return c;
   if (s->T == 0) return MOE_OK;
   if (!x || !ws1 || !ws2 || !h_shared || !out_shared) return MOE_ERR_ARG;
   if (s->act == MOE_ACT_SWIGLU && !ws3) return MOE_ERR_ARG;
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the shared expert sees the unquantised input: same dtype as x
   moe_shape sd = *s;
   sd.buf_dtype = sd.dtype;
   hipError_t e = moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared,
-                                       nullptr, st);
+                                       split, st);
   if (e == hipSuccess)
-    e = moe::launch_expert_down(sd, h_shared, nullptr, s->T, 1, ws2, out_shared, nullptr, st);
+    e = moe::launch_expert_down(sd, h_shared, nullptr, s->T, 1, ws2, out_shared, split, st);
   return hip_status(e);
 }
 
@@ -223,7 +229,7 @@ moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_
   if (r != MOE_OK) return r;
   r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
   if (r != MOE_OK || !s->has_shared) return r;
-  return moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, stream);
+  return moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shared, const void* x,
@@ -259,7 +265,8 @@ moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g
   float* psum = reinterpret_cast<float*>(base + L.route_psum);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
   int32_t* tbase = reinterpret_cast<int32_t*>(base + L.route_base);
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, st);
+  float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, st);
   if (e == hipSuccess)
     e = moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux, offsets,
                                    tbase, st);

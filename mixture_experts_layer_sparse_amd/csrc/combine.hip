@@ -39,9 +39,11 @@ __device__ __forceinline__ void add_bf16x8(float* acc, uint4 v) {
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ out_shared,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    uint16_t* __restrict__ y, int64_t T, int k, int d, int passthrough) {
+    uint16_t* __restrict__ y, int64_t T, int k, int d, int passthrough, int wpt) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t t = gw / wpt;                    // wpt waves share a token's row
+  const int part = static_cast<int>(gw - t * wpt);
   if (t >= T) return;
   int pj[kMaxTopK];
   float wj[kMaxTopK];
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
   }
   const int nch = d / 8;
 #pragma unroll MOE_COMBINE_UNROLL
-  for (int c = lane; c < nch; c += 64) {
+  for (int c = part * 64 + lane; c < nch; c += 64 * wpt) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
@@ -81,11 +83,13 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
 __global__ __launch_bounds__(256) void combine_f32_kernel(
     const float* __restrict__ out, const float* __restrict__ out_shared,
     const float* __restrict__ x, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    float* __restrict__ y, int64_t T, int k, int d, int passthrough) {
+    float* __restrict__ y, int64_t T, int k, int d, int passthrough, int wpt) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t t = gw / wpt;
+  const int part = static_cast<int>(gw - t * wpt);
   if (t >= T) return;
-  for (int c = lane; c < d; c += 64) {
+  for (int c = part * 64 + lane; c < d; c += 64 * wpt) {
     float acc = 0.f;
     for (int j = 0; j < k; ++j) {
       int p = pos[t * k + j];
@@ -103,18 +107,26 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
 hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_shared,
                           const void* x, const int32_t* pos, const float* w, void* y,
                           hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(ceil_div(s.T, 4)));
+  // One wave per token, or, with few tokens, several waves per token (each a
+  // strided share of the row's 64-lane chunks) so that ~2048 waves keep
+  // enough loads in flight: a single wave walking a 7168-wide row waits out
+  // the memory latency once per chunk.
+  const int64_t chunks = s.dtype == MOE_BF16 ? s.d / 8 / 64 : s.d / 64;
+  int64_t wpt = ceil_div(2048, s.T);
+  if (wpt > chunks) wpt = chunks;
+  if (wpt < 1) wpt = 1;
+  dim3 grid(static_cast<unsigned>(ceil_div(s.T * wpt, 4)));
   const int pt = s.drop == MOE_DROP_PASSTHROUGH ? 1 : 0;
   if (s.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(out_shared),
                        static_cast<const uint16_t*>(x), pos, w, static_cast<uint16_t*>(y), s.T,
-                       s.k, s.d, pt);
+                       s.k, s.d, pt, static_cast<int>(wpt));
   else
     hipLaunchKernelGGL(combine_f32_kernel, grid, dim3(256), 0, st,
                        static_cast<const float*>(out), static_cast<const float*>(out_shared),
                        static_cast<const float*>(x), pos, w, static_cast<float*>(y), s.T, s.k,
-                       s.d, pt);
+                       s.d, pt, static_cast<int>(wpt));
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ struct GemmArgs {
   int split_slots;         // > 0: tail split over this many workgroup slots (see below)
   float* part;             // split-K tail: [units][256][256] float32 partial tiles
   int32_t* part_meta;      // split-K tail: [0] = tail tiles, then (row0, row_end, ntile) per tile
-  int ksplit;              // split-K tail: K ranges per tail tile
+  int split_k_max;         // > 0: the tail is split along K (up to this many ranges per tile)
 };
 
 // silu(u) = u / (1 + e^-u) with the hardware reciprocal (about 1 ulp): the result is rounded to
@@ -174,14 +174,17 @@ __device__ __forceinline__ int swz(int row) {
 // the bytes per FLOP of a whole tile and runs at about half its rate, so the
 // split pays only while all quarters fit in one round (4 r <= S).  When the
 // caller provides scratch (part), the tail launch instead splits each of the r
-// tiles along K into ksplit ranges (SPLITK = true, whole 256x256 tiles, so at
-// the main kernel's rate); the float32 partial tiles are then added in range
-// order by gg_splitk_reduce, which applies the epilogue.  Both launches count the
-// same tile list from `offsets`; every output element is still computed by one
-// workgroup over the whole K.
+// tiles along K into ksplit = 4 ranges (SPLITK = true, whole 256x256 tiles, so
+// at the main kernel's rate), and when the whole list has at most S / 2 tiles
+// (a decode step, a small dense call) every tile goes to the tail, split into
+// min(split_k_max, S / tiles) ranges, so that all CUs stream its weights.  The
+// float32 partial tiles are then added in range order by gg_splitk_reduce,
+// which applies the epilogue.  The launches count the same tile list from
+// `offsets`; without split-K every output element is computed by one workgroup
+// over the whole K.
 template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
-  static_assert(!SPLITK || (TAIL && !REG), "split-K is a tail mode of the LDS-DMA pipeline");
+  static_assert(!SPLITK || TAIL, "split-K is a tail mode");
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
   constexpr int BK = 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
@@ -245,12 +248,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   const int NT = g.nt;
   const int total = MT * NT;
   int cut = total;                               // main tiles [0, cut), tail tiles [cut, total)
-  if (g.split_slots > 0) {
-    const int r = total % g.split_slots;
-    if (r > 0 && 4 * r <= g.split_slots) cut = total - r;
+  int ksplit = kSplitK;                          // K ranges per tail tile (split-K tail)
+  if (g.split_slots > 0 && total > 0) {
+    const int S_ = g.split_slots;
+    if (g.split_k_max > 0 && 2 * total <= S_) {
+      // few tiles (a decode step, a small dense call): all of them split
+      cut = 0;
+      ksplit = S_ / total < g.split_k_max ? S_ / total : g.split_k_max;
+    } else if (!REG) {
+      const int r = total % S_;
+      if (r > 0 && 4 * r <= S_) cut = total - r;
+    }
   }
-  const int items = TAIL ? (SPLITK ? g.ksplit : 4) * (total - cut) : cut;
-  if (SPLITK && blockIdx.x == 0 && tid == 0) g.part_meta[0] = total - cut;
+  const int items = TAIL ? (SPLITK ? ksplit : 4) * (total - cut) : cut;
+  if (SPLITK && blockIdx.x == 0 && tid == 0) {
+    g.part_meta[0] = total - cut;
+    g.part_meta[1] = ksplit;
+  }
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, S = gridDim.x >> 3;
 
   // segment of tile-list entry Lm: mt_start[e] * NT <= Lm < mt_start[e + 1] * NT
@@ -305,11 +319,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       if (QUARTERS && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
       if (SPLITK) {
         const int sp = L / (total - cut);
-        kbeg = sp * KT / g.ksplit;
-        kend = (sp + 1) * KT / g.ksplit;
+        kbeg = sp * KT / ksplit;
+        kend = (sp + 1) * KT / ksplit;
         unit = L;
         if (sp == 0 && tid == 0) {
-          int32_t* m = g.part_meta + 1 + 3 * (Lm - cut);
+          int32_t* m = g.part_meta + 2 + 3 * (Lm - cut);
           m[0] = row0;
           m[1] = row_end;
           m[2] = ntile;
@@ -439,8 +453,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
       for (int kk = 0; kk < BK / 32; ++kk) compute(cur, kk);
     }
-    if (kt + 1 < KT) store_regs(nxt, Q);
-    if (kt + 1 + RB < KT) load_regs(kt + 1 + RB, Q);
+    if (kt + 1 < kend) store_regs(nxt, Q);
+    if (kt + 1 + RB < kend) load_regs(kt + 1 + RB, Q);
     if (wave_rows) {
 #pragma unroll
       for (int kk = BK / 32; kk < BK / 16; ++kk) compute(cur, kk);
@@ -576,16 +590,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     if constexpr (REG) {
-      load_regs(0, I0{});
+      load_regs(kbeg, I0{});
       store_regs(sm0, I0{});
-      if (KT > 1) load_regs(1, I1{});
-      if (RB > 1 && KT > 2) load_regs(2, I0{});
+      if (kend - kbeg > 1) load_regs(kbeg + 1, I1{});
+      if (RB > 1 && kend - kbeg > 2) load_regs(kbeg + 2, I0{});
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      // step kt stores the registers of step kt + 1: buffer (kt + 1) % RB
-      for (int kt = 0; kt < KT; kt += 2) {
+      // step kt stores the registers of step kt + 1: buffer (kt + 1 - kbeg) % RB
+      for (int kt = kbeg; kt < kend; kt += 2) {
         step(kt, sm0, sm1, I1{});
-        if (kt + 1 < KT) step(kt + 1, sm1, sm0, I0{});
+        if (kt + 1 < kend) step(kt + 1, sm1, sm0, I0{});
       }
     } else {
       // the tile's first two steps were issued before the previous epilogue
@@ -681,36 +695,52 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 // epilogue.  Unit sp * tiles + t holds range sp of tail tile t.  Grid (tail tiles at most, 16): block y covers 16 of the tile's
 // 256 rows, thread c one tile column (SwiGLU: c < 128 pairs the W1 column
 // (c / 32) * 64 + c % 32 with the W3 column 32 further).
-template <int EPI, bool FP8A>
+template <int EPI, bool FP8A, int BM>
 __global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
-  constexpr int TB = 256;                        // tile rows and columns
+  constexpr int TB = 256;                        // tile columns (BM rows)
   constexpr bool GATED = EPI == EPI_SWIGLU;
-  const int t = blockIdx.x, ntail = g.part_meta[0];
+  const int t = blockIdx.x, ntail = g.part_meta[0], ksplit = g.part_meta[1];
   if (t >= ntail) return;
-  const int32_t* m = g.part_meta + 1 + 3 * t;
+  const int32_t* m = g.part_meta + 2 + 3 * t;
   const int row0 = m[0], row_end = m[1], ntile = m[2];
   const int c = threadIdx.x;
   if (GATED && c >= TB / 2) return;
-  const float* pt = g.part + static_cast<int64_t>(t) * (TB * TB);
-  const int64_t range_stride = static_cast<int64_t>(ntail) * (TB * TB);
+  const float* pt = g.part + static_cast<int64_t>(t) * (BM * TB);
+  const int64_t range_stride = static_cast<int64_t>(ntail) * (BM * TB);
+#pragma unroll 2
   for (int rr = 0; rr < 16; ++rr) {
     const int lr = blockIdx.y * 16 + rr;
     const int row = row0 + lr;
     if (row >= row_end) break;
     const float sc = FP8A ? g.a_scale[row] : 1.0f;
+    // (the ranges' loads issued together, then added in range order)
     if (GATED) {
       const int pu = (c >> 5) * 64 + (c & 31);
+      float pv[kSplitKMax], pg[kSplitKMax];
+#pragma unroll
+      for (int sp = 0; sp < kSplitKMax; ++sp) {
+        pv[sp] = sp < ksplit ? pt[sp * range_stride + lr * TB + pu] : 0.f;
+        pg[sp] = sp < ksplit ? pt[sp * range_stride + lr * TB + pu + 32] : 0.f;
+      }
       float u = 0.f, gt = 0.f;
-      for (int sp = 0; sp < g.ksplit; ++sp) {
-        u += pt[sp * range_stride + lr * TB + pu];
-        gt += pt[sp * range_stride + lr * TB + pu + 32];
+#pragma unroll
+      for (int sp = 0; sp < kSplitKMax; ++sp) {
+        if (sp < ksplit) {
+          u += pv[sp];
+          gt += pg[sp];
+        }
       }
       const int col = ntile * (TB / 2) + c;
       if (col < g.n_out)
         g.out[static_cast<int64_t>(row) * g.n_out + col] = to_bf16(silu_fast(u * sc) * (gt * sc));
     } else {
+      float pv[kSplitKMax];
+#pragma unroll
+      for (int sp = 0; sp < kSplitKMax; ++sp) pv[sp] = sp < ksplit ? pt[sp * range_stride + lr * TB + c] : 0.f;
       float v = 0.f;
-      for (int sp = 0; sp < g.ksplit; ++sp) v += pt[sp * range_stride + lr * TB + c];
+#pragma unroll
+      for (int sp = 0; sp < kSplitKMax; ++sp)
+        if (sp < ksplit) v += pv[sp];
       v *= sc;
       if (EPI == EPI_SILU) v = silu_fast(v);
       if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
@@ -797,7 +827,19 @@ hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
 // ms; with bf16 activations the same change loses 6%).
 int split_slots() { return (device_cu_count() / 8) * 8; }
 
-int pick_bm(int64_t rows, int n_seg, bool fp8_a) {
+// Few tiles (a decode step, a small dense call): at most S / 2 tiles of 128
+// rows, each of at most min(rows, segments) segments holding fewer than 128
+// rows.  With split-K scratch these run as 128-row register-staged tiles (the
+// pipeline with the most bytes in flight, which weight streaming needs), every
+// tile split along K so that all CUs stream its weights.
+bool skinny(int64_t rows, int n_seg, int64_t nt) {
+  const int64_t segs = rows < n_seg ? rows : n_seg;
+  const int64_t mt = ceil_div(rows, 128) > segs ? ceil_div(rows, 128) : segs;
+  return 2 * mt * nt <= split_slots();
+}
+
+int pick_bm(int64_t rows, int n_seg, bool fp8_a, int64_t nt, bool split) {
+  if (split && skinny(rows, n_seg, nt)) return 128;
   const int64_t avg = n_seg > 0 ? rows / n_seg : rows;
   return avg >= (fp8_a ? 96 : 384) ? 256 : 128;
 }
@@ -815,43 +857,65 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, 
   if (bm == 256) {
     const int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
     g.split_slots = split_slots();
+    // the scratch header holds the tail's tile count, range count and up to S / 2 tiles' rows
+    if (2 + 3 * (g.split_slots / 2) > static_cast<int>(kSplitMetaBytes / 4)) split = nullptr;
+    g.split_k_max = split != nullptr ? kSplitKMax : 0;
     hipError_t err = launch_gg_on<256, 256, 2, 4, EPI, FP8A, false, false>(g, mtu * nt, st);
     if (err != hipSuccess) return err;
     if (split == nullptr)
       return launch_gg_on<128, 128, 2, 2, EPI, FP8A, false, true>(g, 4 * mtu * nt, st);
-    // split-K tail (scratch from the caller): whole tiles, kSplitK ranges each
-    g.ksplit = kSplitK;
+    // split-K tail (scratch from the caller): whole tiles, K ranges each
     g.part_meta = static_cast<int32_t*>(split);
     g.part = reinterpret_cast<float*>(static_cast<char*>(split) + kSplitMetaBytes);
-    err = launch_gg_on<256, 256, 2, 4, EPI, FP8A, false, true, true>(g, kSplitK * mtu * nt, st);
+    err = launch_gg_on<256, 256, 2, 4, EPI, FP8A, false, true, true>(g, kSplitKMax * mtu * nt, st);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gg_splitk_reduce<EPI, FP8A>), dim3(g.split_slots / 4, 16), dim3(256), 0,
+    hipLaunchKernelGGL((gg_splitk_reduce<EPI, FP8A, 256>), dim3(g.split_slots / 2, 16), dim3(256), 0,
                        st, g);
     return hipGetLastError();
   }
-  (void)split;
+  // 128-row tiles; with scratch (given only when the list is expected to hold
+  // at most S / 2 tiles) every tile is split along K over all CUs
   const int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
-  g.split_slots = 0;
-  return launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
+  g.split_slots = split != nullptr ? split_slots() : 0;
+  if (2 + 3 * (g.split_slots / 2) > static_cast<int>(kSplitMetaBytes / 4)) split = nullptr, g.split_slots = 0;
+  g.split_k_max = split != nullptr ? kSplitKMax : 0;
+  hipError_t err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
+  if (err != hipSuccess || split == nullptr) return err;
+  g.part_meta = static_cast<int32_t*>(split);
+  g.part = reinterpret_cast<float*>(static_cast<char*>(split) + kSplitMetaBytes);
+  err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true>(g, kSplitKMax * mtu * nt, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((gg_splitk_reduce<EPI, FP8A, 128>), dim3(g.split_slots / 2, 8), dim3(256), 0, st, g);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-// Scratch of the split-K tail for this shape's grouped GEMMs: none when
-// neither uses 256-row tiles, else kSplitK partial tiles for each of at most
-// min(S / 4, tiles) tail tiles.
+// Scratch of the split-K tails of this shape's grouped GEMMs (routed, and the
+// shared expert's dense ones): none when none uses 256-row tiles or few tiles,
+// else one float32 partial tile (at most 256x256) per tail work unit, at most S
+// of them (a tail of r <= S / 4 tiles in 4 ranges, or t <= S / 2 tiles in at
+// most S / t ranges).
 size_t gemm_split_bytes(const moe_shape& s) {
   if (s.dtype != MOE_BF16) return 0;
   const int64_t rows = s.T * s.k;
-  const bool up256 = pick_bm(rows, s.N, s.buf_dtype == MOE_FP8_E4M3) == 256;
-  const bool down256 = pick_bm(rows, s.N, false) == 256;
-  if (!up256 && !down256) return 0;
-  const int64_t mtu = ceil_div(rows, 256) + s.N;
   const int64_t nt_up = s.act == MOE_ACT_SWIGLU ? ceil_div(s.F, 128) : ceil_div(s.F, 256);
   const int64_t nt_down = ceil_div(s.d, 256);
-  const int64_t tiles = mtu * ((up256 ? nt_up : 0) > (down256 ? nt_down : 0) ? nt_up : nt_down);
-  const int64_t tail = std::min<int64_t>(split_slots() / 4, tiles);
-  return kSplitMetaBytes + static_cast<size_t>(tail) * kSplitK * 256 * 256 * 4;
+  const bool fp8 = s.buf_dtype == MOE_FP8_E4M3;
+  int64_t tiles = 0;
+  auto add = [&](int64_t r, int n_seg, bool f8, int64_t nt) {
+    if (skinny(r, n_seg, nt) || pick_bm(r, n_seg, f8, nt, false) == 256)
+      tiles = std::max(tiles, (ceil_div(r, 128) + (n_seg > 1 ? n_seg : 0)) * nt);
+  };
+  add(rows, s.N, fp8, nt_up);
+  add(rows, s.N, false, nt_down);
+  if (s.has_shared) {
+    add(s.T, 1, false, nt_up);
+    add(s.T, 1, false, nt_down);
+  }
+  if (tiles == 0) return 0;
+  const int64_t units = std::min<int64_t>(split_slots(), kSplitKMax * tiles);
+  return kSplitMetaBytes + static_cast<size_t>(units) * 256 * 256 * 4;
 }
 
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
@@ -881,7 +945,9 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
   g.out = static_cast<uint16_t*>(h);
   const bool gated = s.act == MOE_ACT_SWIGLU;
   g.nt = static_cast<int>(gated ? ceil_div(s.F, 128) : ceil_div(s.F, 256));
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8);
+  const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8, g.nt, sk);
+  if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
   if (gated) return fp8 ? dispatch_up<EPI_SWIGLU, true>(bm, g, rows, n_seg, dense, split, st)
                         : dispatch_up<EPI_SWIGLU, false>(bm, g, rows, n_seg, dense, split, st);
   if (s.act == MOE_ACT_RELU) return fp8 ? dispatch_up<EPI_RELU, true>(bm, g, rows, n_seg, dense, split, st)
@@ -915,7 +981,9 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.b_stride = static_cast<int64_t>(s.d) * s.F;
   g.out = static_cast<uint16_t*>(out);
   g.nt = static_cast<int>(ceil_div(s.d, 256));
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, false);
+  const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, false, g.nt, sk);
+  if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
   return dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, split, st);
 }
 

@@ -14,6 +14,7 @@ constexpr int kMaxTopK = 8;
 constexpr int kRouteTile = 16;     // tokens per router workgroup
 constexpr int kDispatchBlock = 256;  // tokens per dispatch-plan block
 constexpr int kSplitK = 4;           // K ranges per tail tile of a split-K grouped GEMM tail
+constexpr int kSplitKMax = 8;        // K ranges per tile when a grouped GEMM has few tiles
 constexpr size_t kSplitMetaBytes = 4096;  // header of the split-K scratch (tile count, tile rows)
 
 // ---------------------------------------------------------------- helpers --
@@ -38,6 +39,7 @@ struct WsLayout {
   size_t route_psum;    // float   [nb_route][N]
   size_t route_hist;    // int32   [nb_route][N]
   size_t route_base;    // int32   [nb_route][N]
+  size_t route_lpart;   // float   [route_split_ranges(s)][T][N] partial logits (few tokens only)
   size_t disp_hist;     // int32   [nb_disp][N]
   size_t gemm_split;    // split-K tail scratch of the grouped GEMMs (gemm_split_bytes(s))
   size_t h;             // dtype   [T*k][F]
@@ -49,9 +51,14 @@ WsLayout ws_layout(const moe_shape& s);
 // ---------------------------------------------------------------- launchers --
 // Each returns hipSuccess or the launch error; shapes are already validated.
 
+// With few tokens (route_split_ranges(s) > 0) the logits are first computed as
+// partial sums over that many d-ranges into lpart by a separate kernel spread
+// over the experts, so that the router weights are read about once instead of
+// once per 16-token tile; the router then adds the partials in range order.
+int route_split_ranges(const moe_shape& s);
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        hipStream_t st);
+                        float* lpart, hipStream_t st);
 // offsets (may be null): exclusive scan of the kept counts, N + 1 entries.
 // base (may be null): [nb_route][N] assignments to each expert in earlier tiles.
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,

@@ -32,6 +32,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = kRouteTile;
+constexpr int kRouteSplitMax = 8;      // d-ranges of the split logits at most
 
 struct RouteArgs {
   const void* x;
@@ -44,6 +45,8 @@ struct RouteArgs {
   int32_t* hist;
   int64_t T;
   int d, N, k, n_groups, topk_groups, gsk;
+  const float* lpart;   // partial logits [lsplit][T][N] from logits_split_kernel, or null
+  int lsplit;
 };
 
 // Key ordering "larger logit first, then lower expert index"; 0 = no candidate.
@@ -282,6 +285,74 @@ __device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf,
   }
 }
 
+// Partial logits for few tokens: one wave per (16 tokens, 16 experts, d-range)
+// unit, one 16x16x32 MFMA per 32-wide k-step (A = token rows, B = router rows,
+// loaded straight from memory; rows past T or N read as zero).  Unit order is
+// range-fastest, so the waves of a workgroup share token and router rows.
+__global__ __launch_bounds__(256) void logits_split_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wg,
+                                                           float* __restrict__ lpart, int64_t T,
+                                                           int d, int N, int ks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t TB = (T + 15) / 16;
+  const int EB = (N + 15) / 16;
+  if (unit >= TB * EB * ks) return;
+  const int kr = static_cast<int>(unit % ks);
+  const int64_t rest = unit / ks;
+  const int eb = static_cast<int>(rest % EB);
+  const int64_t tb = rest / EB;
+  const int nst = d / 32;
+  const int s0 = kr * nst / ks, s1 = (kr + 1) * nst / ks;
+  const int r = lane & 15, kc = lane >> 4;
+  const int64_t t = tb * 16 + r;
+  const int e = eb * 16 + r;
+  const bool tok = t < T, ex = e < N;
+  const uint16_t* xr = x + (tok ? t : 0) * d + kc * 8;
+  const uint16_t* wr = wg + static_cast<int64_t>(ex ? e : 0) * d + kc * 8;
+  const bf16x8 zero = {};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;
+  for (int st = s0; st < s1; st += U) {
+    bf16x8 av[U], bv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = (st + u < s1 ? st + u : s0) * 32;
+      av[u] = tok ? *reinterpret_cast<const bf16x8*>(xr + k0) : zero;
+      bv[u] = ex ? *reinterpret_cast<const bf16x8*>(wr + k0) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (st + u < s1) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
+  }
+  // acc[j]: token row 4 * kc + j, expert column r
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t2 = tb * 16 + 4 * kc + j;
+    if (t2 < T && ex) lpart[(static_cast<int64_t>(kr) * T + t2) * N + e] = acc[j];
+  }
+}
+
+// Logits of a 16-token tile from the partials: the d-ranges added in order.
+__device__ void logits_from_partials(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
+  for (int q = threadIdx.x; q < TM * a.N; q += RW * 64) {
+    const int m = q / a.N, e = q % a.N;
+    const int64_t t = t0 + m;
+    float v = 0.f;
+    if (t < a.T) {
+      float pv[kRouteSplitMax];
+#pragma unroll
+      for (int kr = 0; kr < kRouteSplitMax; ++kr)      // (all loads in flight together)
+        pv[kr] = kr < a.lsplit ? a.lpart[(static_cast<int64_t>(kr) * a.T + t) * a.N + e] : 0.f;
+#pragma unroll
+      for (int kr = 0; kr < kRouteSplitMax; ++kr)
+        if (kr < a.lsplit) v += pv[kr];
+      if (a.bias) v += a.bias[e];
+    }
+    lt[m * ldl + e] = v;
+  }
+}
+
 // fp32 path: plain dot products, one (token, expert) pair per thread at a time.
 __device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
   const float* x = static_cast<const float*>(a.x);
@@ -403,7 +474,8 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
 
   for (int e = threadIdx.x; e < kMaxExperts; e += RW * 64) hl[e] = 0;
   if (BF16) {
-    if (a.d % SCH == 0) logits_bf16_staged(a, t0, sbuf, part, lt, ldl);
+    if (a.lpart) logits_from_partials(a, t0, lt, ldl);
+    else if (a.d % SCH == 0) logits_bf16_staged(a, t0, sbuf, part, lt, ldl);
     else logits_bf16(a, t0, part, lt, ldl);
   } else {
     logits_f32(a, t0, lt, ldl);
@@ -469,7 +541,29 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
     uint64_t gmask = ~0ull;
     if (G > 1) {
       float gs = 0.f;
-      if (lane < G) {
+      if (a.gsk <= 2 && gsz <= 64 && (gsz & (gsz - 1)) == 0) {
+        // a group is an aligned run of gsz lanes of one of the four 64-expert
+        // slices: a butterfly over it merges (largest, second largest) pairs
+        float gsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float t1 = v[i], t2 = -INFINITY;
+          for (int off = 1; off < gsz; off <<= 1) {
+            const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+            t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+            t1 = fmaxf(t1, o1);
+          }
+          gsv[i] = a.gsk == 1 ? t1 : t1 + t2;
+        }
+        // lane g < G fetches group g's score from the group's first lane
+        const int src_i = (lane * gsz) >> 6, src_lane = (lane * gsz) & 63;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float val = __shfl(gsv[i], src_lane & 63);
+          if (i == src_i) gs = val;
+        }
+        if (lane >= G) gs = 0.f;
+      } else if (lane < G) {
         float top[kMaxTopK];
 #pragma unroll
         for (int q = 0; q < kMaxTopK; ++q) top[q] = -INFINITY;
@@ -521,7 +615,7 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
         int e = key_index(best);
         e = e < N ? e : N - 1;                    // unreachable guard (k <= candidates)
         sel_e[j] = e;
-        sel_v[j] = row[e];
+        sel_v[j] = key_value(best);              // (the logit, with -0 read as +0)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (e == lane + 64 * i) cand[i] = false;
@@ -662,11 +756,32 @@ size_t route_lds_bytes(const moe_shape& s) {
 }
 }  // namespace
 
+// Split logits below 512 tokens (fewer than 32 router tiles, each of which
+// would read all of W_g): up to kRouteSplitMax d-ranges, so that about 512
+// waves share the work.
+int route_split_ranges(const moe_shape& s) {
+  if (s.dtype != MOE_BF16 || s.T <= 0 || s.T >= 512 || s.d % 32 != 0) return 0;
+  const int64_t units = ceil_div(s.T, 16) * ceil_div(s.N, 16);
+  int64_t ks = ceil_div(512, units);
+  if (ks > kRouteSplitMax) ks = kRouteSplitMax;
+  if (ks > s.d / 32) ks = s.d / 32;
+  return static_cast<int>(ks < 1 ? 1 : ks);
+}
+
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        hipStream_t st) {
+                        float* lpart, hipStream_t st) {
+  const int ks = route_split_ranges(s);
   RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
-              s.n_groups, s.topk_groups, s.group_score_k};
+              s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks};
+  if (ks > 0) {
+    const int64_t units = ceil_div(s.T, 16) * ceil_div(s.N, 16) * ks;
+    hipLaunchKernelGGL(logits_split_kernel, dim3(static_cast<unsigned>(ceil_div(units, 4))), dim3(256), 0,
+                       st, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), lpart, s.T,
+                       s.d, s.N, ks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid(static_cast<unsigned>(ceil_div(s.T, TM)));
   const size_t lds = route_lds_bytes(s);
   // allow dynamic LDS above the default limit (the largest staging buffer)

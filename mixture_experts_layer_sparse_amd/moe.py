@@ -86,7 +86,7 @@ _SIGS = {
     "moe_route_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P, c_size_t, _P]),
     "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
     "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
-    "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
+    "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
     "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
     "moe_forward": (c_int32, [POINTER(Shape)] + [_P] * 25 + [_P, c_size_t, _P]),
@@ -266,7 +266,7 @@ def expert_down(s: Shape, h, offsets, w2, out=None, ws=None):
     return out
 
 
-def shared_expert(s: Shape, x, ws1, ws3, ws2, h_shared=None, out_shared=None):
+def shared_expert(s: Shape, x, ws1, ws3, ws2, h_shared=None, out_shared=None, ws=None):
     T, d, F = s.T, s.d, s.F
     _check(ws1, "ws1", (F, d), s.torch_dtype)
     _check(ws3, "ws3", (F, d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
@@ -276,7 +276,7 @@ def shared_expert(s: Shape, x, ws1, ws3, ws2, h_shared=None, out_shared=None):
     if out_shared is None:
         out_shared = torch.empty((T, d), dtype=s.torch_dtype, device=x.device)
     _call("moe_shared_expert", ctypes.byref(s), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(ws2),
-          _ptr(h_shared), _ptr(out_shared), _stream())
+          _ptr(h_shared), _ptr(out_shared), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     return out_shared
 
 
