@@ -65,9 +65,18 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act;
 typedef enum { MOE_DROP_PASSTHROUGH = 0, MOE_DROP_ZERO = 1 } moe_drop;
+/* Weights of the selected experts.  SPARSE: a softmax over the k selected logits
+ * ("Part 5" / "The Math" and "1.1 The Router Kernel"); each token's weights sum
+ * to 1.  FULL: the probability each selected expert has under the softmax over
+ * all N logits, not renormalised ("moe communication costs" / "Router design":
+ * y = sum over the top-k of G(x)_i E_i(x) with G(x) = softmax(W_g x); Switch's
+ * single expert is weighted by its router probability); a token's weights sum
+ * to at most 1. */
+typedef enum { MOE_GATE_SPARSE = 0, MOE_GATE_FULL = 1 } moe_gate;
 
 /* Shape and options of one layer.  Enumerations are stored as int32_t so that
- * the struct layout is fixed: 8 + 14 * 4 = 64 bytes, alpha at offset 60. */
+ * the struct layout is fixed: 8 + 15 * 4 = 68 bytes padded to 72, alpha at
+ * offset 60, gate at offset 64. */
 typedef struct moe_shape {
   int64_t T;             /* tokens, >= 0 */
   int32_t d;             /* hidden size */
@@ -89,6 +98,7 @@ typedef struct moe_shape {
   int32_t act;           /* moe_act */
   int32_t drop;          /* moe_drop: what a dropped slot contributes */
   float alpha;           /* L_aux coefficient ("Load balancing": typically 0.01-0.1) */
+  int32_t gate;          /* moe_gate: how the selected experts are weighted */
 } moe_shape;
 
 /* Bytes of device scratch needed by moe_route, moe_dispatch and moe_experts for
@@ -107,7 +117,9 @@ moe_status moe_check_shape(const moe_shape* s);
  *   x       [T][d] dtype          W_g [N][d] dtype (stored like x)
  *   bias    [N] float32 or NULL   added to the logits before every use
  *   idx     [T][k] int32 out      expert ids, slot 0 = largest logit
- *   w       [T][k] float32 out    sparse-softmax weights (each row sums to 1)
+ *   w       [T][k] float32 out    gate weights: sparse softmax over the selection
+ *                                 (each row sums to 1), or with gate = MOE_GATE_FULL
+ *                                 each selected expert's full-softmax probability
  *   counts  [N] int32 out         assignments per expert before capacity drops
  *   kept_counts [N] int32 out     min(counts, capacity) (= counts if unlimited)
  *   p, f    [N] float32 out or NULL   mean full-softmax probability; counts/(T k)

@@ -82,6 +82,7 @@ moe_status check_shape(const moe_shape* s) {
     return MOE_ERR_ARG;
   }
   if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_ARG;
+  if (s->gate != MOE_GATE_SPARSE && s->gate != MOE_GATE_FULL) return MOE_ERR_ARG;
   // positions and row indices are int32
   if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (s->dtype == MOE_BF16 && (s->d % 64 != 0 || s->F % 64 != 0)) return MOE_ERR_UNSUPPORTED;

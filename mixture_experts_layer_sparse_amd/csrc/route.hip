@@ -47,6 +47,7 @@ struct RouteArgs {
   int d, N, k, n_groups, topk_groups, gsk;
   const float* lpart;   // partial logits [lsplit][T][N] from logits_split_kernel, or null
   int lsplit;
+  int gate;             // moe_gate
 };
 
 // Key ordering "larger logit first, then lower expert index"; 0 = no candidate.
@@ -447,7 +448,9 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j < k) {
       a.idx[t * k + j] = sel_e[j];
-      a.w[t * k + j] = __expf(sel_v[j] - sel_v[0]) / den;
+      // full gate: the expert's probability in the softmax written to prow
+      a.w[t * k + j] = a.gate == MOE_GATE_FULL ? __expf(sel_v[j] - mx) / zs
+                                               : __expf(sel_v[j] - sel_v[0]) / den;
       atomicAdd(&hl[sel_e[j]], 1);
     }
   }
@@ -630,7 +633,9 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k && lane == j) {
         a.idx[t * k + j] = sel_e[j];
-        a.w[t * k + j] = __expf(sel_v[j] - sel_v[0]) / den;
+        // full gate: the expert's probability in the softmax summed into p
+        a.w[t * k + j] = a.gate == MOE_GATE_FULL ? __expf(sel_v[j] - mx) / zs
+                                                 : __expf(sel_v[j] - sel_v[0]) / den;
         atomicAdd(&hl[sel_e[j]], 1);
       }
     }
@@ -773,7 +778,7 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
                         float* lpart, hipStream_t st) {
   const int ks = route_split_ranges(s);
   RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
-              s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks};
+              s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks, s.gate};
   if (ks > 0) {
     const int64_t units = ceil_div(s.T, 16) * ceil_div(s.N, 16) * ks;
     hipLaunchKernelGGL(logits_split_kernel, dim3(static_cast<unsigned>(ceil_div(units, 4))), dim3(256), 0,

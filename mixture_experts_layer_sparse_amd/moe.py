@@ -21,10 +21,12 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_ACT_SILU, MOE_ACT_RELU, MOE_ACT_SWIGLU = range(3)
 MOE_DROP_PASSTHROUGH, MOE_DROP_ZERO = range(2)
+MOE_GATE_SPARSE, MOE_GATE_FULL = range(2)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 _ACT = {"silu": MOE_ACT_SILU, "relu": MOE_ACT_RELU, "swiglu": MOE_ACT_SWIGLU}
 _DROP = {"passthrough": MOE_DROP_PASSTHROUGH, "zero": MOE_DROP_ZERO}
+_GATE = {"sparse": MOE_GATE_SPARSE, "full": MOE_GATE_FULL}
 
 
 class MoeError(RuntimeError):
@@ -38,7 +40,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("N", c_int32), ("k", c_int32), ("F", c_int32),
                 ("capacity", c_int32), ("n_groups", c_int32), ("topk_groups", c_int32),
                 ("group_score_k", c_int32), ("has_shared", c_int32), ("dtype", c_int32),
-                ("buf_dtype", c_int32), ("act", c_int32), ("drop", c_int32), ("alpha", c_float)]
+                ("buf_dtype", c_int32), ("act", c_int32), ("drop", c_int32), ("alpha", c_float),
+                ("gate", c_int32)]
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -60,19 +63,21 @@ class Shape(ctypes.Structure):
 
 def make_shape(T, d, N, k, F, act="swiglu", dtype="bf16", buf=None, capacity=0,
                drop="passthrough", n_groups=0, topk_groups=0, group_score_k=2, shared=False,
-               alpha=0.01) -> Shape:
+               alpha=0.01, gate="sparse") -> Shape:
     return Shape(T=T, d=d, N=N, k=k, F=F, capacity=capacity, n_groups=n_groups,
                  topk_groups=topk_groups, group_score_k=group_score_k,
                  has_shared=1 if shared else 0, dtype=_DT[dtype], buf_dtype=_DT[buf or dtype],
-                 act=_ACT[act], drop=_DROP[drop], alpha=alpha)
+                 act=_ACT[act], drop=_DROP[drop], alpha=alpha, gate=_GATE[gate])
 
 
 def shape_of(wl) -> Shape:
     """Shape from any object with the workload attributes (T, d, N, k, F, act,
-    dtype, buf, capacity, drop, n_groups, topk_groups, group_score_k, shared, alpha)."""
+    dtype, buf, capacity, drop, n_groups, topk_groups, group_score_k, shared, alpha, and
+    optionally gate)."""
     return make_shape(wl.T, wl.d, wl.N, wl.k, wl.F, act=wl.act, dtype=wl.dtype, buf=wl.buf,
                       capacity=wl.capacity, drop=wl.drop, n_groups=wl.n_groups,
                       topk_groups=wl.topk_groups, group_score_k=wl.group_score_k,
+                      gate=getattr(wl, "gate", "sparse"),
                       shared=wl.shared, alpha=wl.alpha)
 
 

@@ -81,7 +81,7 @@ def adopt(wl, logits: np.ndarray, oracle_idx: np.ndarray, gpu_idx: np.ndarray,
     """Merge the GPU's routing into the oracle's where it is admissible.
 
     Returns {"idx", "w", "adopted": [tokens], "bad": [tokens]}.  ``w`` is the
-    oracle's float64 sparse softmax for the (possibly adopted) selection."""
+    oracle's float64 gate weights for the (possibly adopted) selection."""
     gpu_idx = np.asarray(gpu_idx).astype(np.int64).reshape(oracle_idx.shape)
     idx = oracle_idx.astype(np.int64).copy()
     diff = np.flatnonzero(np.any(idx != gpu_idx, axis=1))
@@ -92,7 +92,7 @@ def adopt(wl, logits: np.ndarray, oracle_idx: np.ndarray, gpu_idx: np.ndarray,
             adopted.append(int(t))
         else:
             bad.append(int(t))
-    w = moe.sparse_softmax(logits, idx) if idx.size else np.zeros(idx.shape)
+    w = moe.gate_weights(wl, logits, idx) if idx.size else np.zeros(idx.shape)
     return {"idx": idx.astype(np.int32), "w": w, "adopted": adopted, "bad": bad}
 
 

@@ -99,6 +99,17 @@ def full_softmax(l: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
+def gate_weights(wl, l: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Weights of the selected experts.  "sparse": the softmax over the k
+    selected logits ([Part5] The Math, 1.1).  "full": each selected expert's
+    probability under the softmax over all N logits, not renormalised
+    ([Glossary] "Router design": y = sum over the top-k of G(x)_i E_i(x),
+    G(x) = softmax(W_g x))."""
+    if getattr(wl, "gate", "sparse") == "full":
+        return np.take_along_axis(full_softmax(l), idx.astype(np.int64), axis=1)
+    return sparse_softmax(l, idx)
+
+
 def load_stats(l: np.ndarray, idx: np.ndarray, N: int, capacity: int, alpha: float) -> dict:
     """counts, kept_counts, f, p and L_aux = alpha * N * sum_i f_i p_i.
     [Glossary] "Load balancing": f_i the fraction of routed assignments that go
@@ -119,12 +130,12 @@ def load_stats(l: np.ndarray, idx: np.ndarray, N: int, capacity: int, alpha: flo
 
 
 def route(wl, x: np.ndarray, wg: np.ndarray, bias: np.ndarray | None) -> dict:
-    """Router: logits, group limit, top-k, sparse softmax, load statistics.
+    """Router: logits, group limit, top-k, gate weights, load statistics.
     ``x`` and ``wg`` are float64 (already widened)."""
     l = router_logits(x, wg, bias)
     mask = group_mask(l, wl.n_groups, wl.topk_groups, wl.group_score_k)
     idx = top_k(l, mask, wl.k)
-    w = sparse_softmax(l, idx)
+    w = gate_weights(wl, l, idx)
     out = {"logits": l, "idx": idx, "w": w}
     out.update(load_stats(l, idx, wl.N, wl.capacity, wl.alpha))
     return out

@@ -65,6 +65,7 @@ class Workload:
     shared: bool = False
     bias: str | None = None      # None | "zipf2"
     alpha: float = 0.01
+    gate: str = "sparse"         # "sparse" (softmax over the k selected) | "full" (full-softmax probability)
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":

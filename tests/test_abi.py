@@ -43,15 +43,17 @@ def test_struct_layout_matches_c(M, tmp_path):
     import subprocess
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(moe_shape),'
-                   ' offsetof(moe_shape, d), offsetof(moe_shape, drop), offsetof(moe_shape, alpha));'
+                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(moe_shape),'
+                   ' offsetof(moe_shape, d), offsetof(moe_shape, drop), offsetof(moe_shape, alpha),'
+                   ' offsetof(moe_shape, gate));'
                    'return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
-    size, off_d, off_drop, off_alpha = map(int, subprocess.run([str(exe)], capture_output=True,
+    size, off_d, off_drop, off_alpha, off_gate = map(int, subprocess.run([str(exe)], capture_output=True,
                                                                text=True, check=True).stdout.split())
-    assert ctypes.sizeof(M.Shape) == size == 64
-    assert (M.Shape.d.offset, M.Shape.drop.offset, M.Shape.alpha.offset) == (off_d, off_drop, off_alpha)
+    assert ctypes.sizeof(M.Shape) == size == 72
+    assert (M.Shape.d.offset, M.Shape.drop.offset, M.Shape.alpha.offset, M.Shape.gate.offset) == \
+        (off_d, off_drop, off_alpha, off_gate)
 
 
 def _s(M, **kw):

@@ -154,6 +154,26 @@ def test_gemm_main_and_tail():
     _check_tail_paths(wl, gpu)
 
 
+FULL_GATE_CASES = {
+    "tiny_f32": lambda: si.WORKLOADS["tiny"],
+    "switch_k1_capacity": lambda: si.small("switch"),
+    "mixtral": lambda: si.small("mixtral"),
+    "mixtral_one_token": lambda: si.small("mixtral", T=1),
+    "deepseek_groups_fp8_shared": lambda: si.small("deepseek_v3"),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_GATE_CASES))
+def test_full_softmax_gate(name):
+    """gate = full: each selected expert weighted by its probability under the
+    softmax over all N logits.  Lane and wave selection paths, split logits
+    (one token), groups, capacity drops and the fp8 buffer; every output
+    against the oracle, y on all tokens."""
+    wl = FULL_GATE_CASES[name]().replace(gate="full")
+    gpu, _ = _run_and_check(wl, max_adopted=2)
+    assert np.all(gpu["w"].sum(axis=1) <= 1.0 + 1e-6)
+
+
 def test_groups_k_le_group_span():
     wl = si.small("deepseek_v3", T=333, N=32, k=3, n_groups=4, topk_groups=1, F=128)
     _run_and_check(wl)

@@ -214,6 +214,39 @@ def test_weights_sum_to_one_and_k1_is_one():
             assert np.all(w == 1.0)
 
 
+def test_full_gate_closed_forms():
+    """Full-softmax gate weights ([Glossary] "Router design": the selected
+    experts' G(x)_i, not renormalised): with two experts and k = 1 the weight
+    is the logistic function of the logit gap; with k = N each row is the whole
+    softmax (a permutation of it) and sums to 1; for any k a row is the sparse
+    softmax scaled by the selected experts' total probability (written out with
+    math.exp, independently of the oracle's NumPy softmax)."""
+    full = si.WORKLOADS["tiny"].replace(gate="full")
+    rng = np.random.default_rng(11)
+    l = rng.standard_normal((100, 2)) * 3
+    w = moe.gate_weights(full, l, moe.top_k(l, np.ones_like(l, bool), 1))
+    for t in range(100):
+        gap = abs(l[t, 0] - l[t, 1])
+        assert w[t, 0] == pytest.approx(1.0 / (1.0 + math.exp(-gap)), rel=1e-14)
+    l = rng.standard_normal((50, 8)) * 4
+    for k in (1, 3, 8):
+        idx = moe.top_k(l, np.ones_like(l, bool), k)
+        wf = moe.gate_weights(full, l, idx)
+        ws = moe.gate_weights(si.WORKLOADS["tiny"], l, idx)
+        assert np.array_equal(ws, moe.sparse_softmax(l, idx))
+        for t in range(50):
+            z = [math.exp(v) for v in l[t]]
+            tot = sum(z)
+            sel = sum(z[e] for e in idx[t])
+            for j, e in enumerate(idx[t]):
+                assert wf[t, j] == pytest.approx(z[e] / tot, rel=1e-13)
+                assert wf[t, j] == pytest.approx(ws[t, j] * sel / tot, rel=1e-13)
+        if k == 8:
+            assert np.allclose(wf.sum(1), 1.0, rtol=0, atol=1e-14)
+        else:
+            assert np.all(wf.sum(1) < 1.0)
+
+
 def test_ties_go_to_lower_index():
     l = np.zeros((1, 8))
     assert moe.top_k(l, np.ones_like(l, bool), 3).tolist() == [[0, 1, 2]]
