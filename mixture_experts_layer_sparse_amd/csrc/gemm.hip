@@ -654,34 +654,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       continue;
     }
 
-    // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32
+    // epilogue: acc[i][j][r] is row i*32 + 8*(r/4) + 4*(lane/32) + r%4, column j*32 + lane%32.
+    // Rows r, r + 1 (r even) and the columns of lanes L, L + 1 (L even) form 2x2
+    // blocks: lane L gives its row-(r + 1) value to lane L + 1 and takes that lane's
+    // row-r value (one DPP swap), so that lane L writes both outputs of row r and
+    // lane L + 1 both of row r + 1, each as one 32-bit store.
+    const bool odd = lane & 1;
+    auto store_pair = [&](int i, int r, int col_lane, float v0, float v1) {
+      const uint32_t b0 = to_bf16(v0), b1 = to_bf16(v1);
+      const uint32_t got = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(
+          static_cast<int>(odd ? b0 : b1), 0xB1 /* quad_perm [1,0,3,2] */, 0xF, 0xF, false));
+      const uint32_t word = odd ? (got | (b1 << 16)) : (b0 | (got << 16));
+      const int row = erow0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
+      const int col = col_lane - (odd ? 1 : 0);
+      if (row < erow_end && col < g.n_out)
+        *reinterpret_cast<uint32_t*>(g.out + static_cast<int64_t>(row) * g.n_out + col) = word;
+    };
 #pragma unroll
     for (int i = 0; i < TMI; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = erow0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= erow_end) continue;
-        const float sc = FP8A ? g.a_scale[row] : 1.0f;
-        uint16_t* orow = g.out + static_cast<int64_t>(row) * g.n_out;
+      for (int r = 0; r < 16; r += 2) {
+        float sc0 = 1.0f, sc1 = 1.0f;
+        if (FP8A) {
+          const int row0 = erow0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          sc0 = row0 < erow_end ? g.a_scale[row0] : 0.f;
+          sc1 = row0 + 1 < erow_end ? g.a_scale[row0 + 1] : 0.f;
+        }
         if (GATED) {
 #pragma unroll
           for (int j = 0; j < TNI / 2; ++j) {
             const int col = entile * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
-            if (col < g.n_out) {
-              const float u = acc[i][j][r] * sc, gt = acc[i][j + TNI / 2][r] * sc;
-              orow[col] = to_bf16(silu_fast(u) * gt);
-            }
+            const float v0 = silu_fast(acc[i][j][r] * sc0) * (acc[i][j + TNI / 2][r] * sc0);
+            const float v1 = silu_fast(acc[i][j][r + 1] * sc1) * (acc[i][j + TNI / 2][r + 1] * sc1);
+            store_pair(i, r, col, v0, v1);
           }
         } else {
 #pragma unroll
           for (int j = 0; j < TNI; ++j) {
             const int col = entile * BN + wn * WN + j * 32 + (lane & 31);
-            if (col < g.n_out) {
-              float v = acc[i][j][r] * sc;
-              if (EPI == EPI_SILU) v = silu_fast(v);
-              if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-              orow[col] = to_bf16(v);
-            }
+            float v0 = acc[i][j][r] * sc0, v1 = acc[i][j][r + 1] * sc1;
+            if (EPI == EPI_SILU) v0 = silu_fast(v0), v1 = silu_fast(v1);
+            if (EPI == EPI_RELU) v0 = fmaxf(v0, 0.f), v1 = fmaxf(v1, 0.f);
+            store_pair(i, r, col, v0, v1);
           }
         }
       }
