@@ -217,6 +217,29 @@ def expert_weight_bytes(wl):
     return (wl.N + (1 if wl.shared else 0)) * m * wl.F * wl.d * s
 
 
+def graph_step_time(step, steps, warmup):
+    """Seconds per step when one step (a function that launches the layer's
+    kernels on the current stream, allocating nothing) is captured once in a
+    HIP graph and replayed: the kernels without host launch gaps."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def _to_dev(arr):
     import numpy as np
     import torch
@@ -314,19 +337,21 @@ def decode(steps, warmup):
     del inp
     m = 3 if base.swiglu else 2
     per_expert = m * base.F * base.d * 2
-    print("| B | experts touched (uniform estimate) | us/step | tokens/s | route+dispatch us | GEMM up us | "
-          "GEMM down us | shared us | combine us | weight bytes streamed | weight GB/s (% HBM) |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    print("| B | experts touched (uniform estimate) | us/step | us/step, graph replay | tokens/s (graph) | "
+          "route+dispatch us | GEMM up us | GEMM down us | shared us | combine us | weight bytes streamed | "
+          "weight GB/s (% HBM) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for B in (1, 32, 128):
         wl = si.decode(B)
         x = g["x"][:B].contiguous()
         L, ph, wall = _phases(wl, g, x, steps, warmup)
+        gwall = graph_step_time(lambda: L.forward(x), steps, warmup)
         touched = int((L.counts > 0).sum().item())
         est = base.N * (1.0 - (1.0 - base.k / base.N) ** B)
         wbytes = (touched + (1 if base.shared else 0)) * per_expert
         gemm_us = ph[1] + ph[2] + ph[3]
         wgb = wbytes / (gemm_us * 1e-6) / 1e9
-        print(f"| {B} | {touched} ({est:.1f}) | {wall * 1e6:.1f} | {B / wall:,.0f} | {ph[0]:.1f} | {ph[1]:.1f} | "
+        print(f"| {B} | {touched} ({est:.1f}) | {wall * 1e6:.1f} | {gwall * 1e6:.1f} | {B / gwall:,.0f} | {ph[0]:.1f} | {ph[1]:.1f} | "
               f"{ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | {wbytes / 2**30:.2f} GiB | "
               f"{wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
         del L, x
@@ -424,6 +449,9 @@ def main():
     L.forward(x)
     torch.cuda.synchronize()
     assert torch.equal(y_split, L.y), "phase-by-phase and moe_forward results differ"
+    # the same layer captured once in a HIP graph and replayed (the kernels
+    # without host launch gaps); reported beside the eager steps
+    gwall = graph_step_time(lambda: L.forward(x), a.steps, a.warmup)
 
     up, down, shared = gemm_flops(wl, R)
     rb, db, cb = alg_bytes(wl, R)
@@ -462,6 +490,7 @@ def main():
                           "GBps": (rb + db + cb) / mem_t / 1e9,
                           "frac_hbm": (rb + db + cb) / mem_t / 1e9 / PEAK_HBM_GBPS},
         "phases_us": {k: v * 1e3 for k, v in ph_ms.items()},
+        "graph_replay": {"ms_per_step": gwall * 1e3, "tokens_per_s": wl.T / gwall},
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_sample_tokens or wl.T)
