@@ -64,7 +64,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act;
-typedef enum { MOE_DROP_PASSTHROUGH = 0, MOE_DROP_ZERO = 1 } moe_drop;
+/* What a slot dropped by the capacity contributes ("moe communication costs" /
+ * "Capacity factor and token dropping": overflow tokens either skip the layer
+ * through the residual or go to a shared fallback expert).  PASSTHROUGH: w * x[t];
+ * ZERO: nothing; FALLBACK: w * S(x[t]), S the shared expert (has_shared must be 1;
+ * its always-on term is still added once). */
+typedef enum { MOE_DROP_PASSTHROUGH = 0, MOE_DROP_ZERO = 1, MOE_DROP_FALLBACK = 2 } moe_drop;
 /* Weights of the selected experts.  SPARSE: a softmax over the k selected logits
  * ("Part 5" / "The Math" and "1.1 The Router Kernel"); each token's weights sum
  * to 1.  FULL: the probability each selected expert has under the softmax over

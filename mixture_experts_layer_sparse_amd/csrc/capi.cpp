@@ -70,7 +70,9 @@ moe_status check_shape(const moe_shape* s) {
   if (s->buf_dtype != s->dtype && !(s->buf_dtype == MOE_FP8_E4M3 && s->dtype == MOE_BF16))
     return s->buf_dtype == MOE_FP8_E4M3 ? MOE_ERR_UNSUPPORTED : MOE_ERR_ARG;
   if (s->act < MOE_ACT_SILU || s->act > MOE_ACT_SWIGLU) return MOE_ERR_ARG;
-  if (s->drop != MOE_DROP_PASSTHROUGH && s->drop != MOE_DROP_ZERO) return MOE_ERR_ARG;
+  if (s->drop != MOE_DROP_PASSTHROUGH && s->drop != MOE_DROP_ZERO && s->drop != MOE_DROP_FALLBACK)
+    return MOE_ERR_ARG;
+  if (s->drop == MOE_DROP_FALLBACK && s->has_shared != 1) return MOE_ERR_ARG;
   if (s->n_groups > 1) {
     const int G = s->n_groups;
     if (G > 64 || s->N % G != 0) return MOE_ERR_ARG;

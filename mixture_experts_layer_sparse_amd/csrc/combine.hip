@@ -39,7 +39,7 @@ __device__ __forceinline__ void add_bf16x8(float* acc, uint4 v) {
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ out_shared,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    uint16_t* __restrict__ y, int64_t T, int k, int d, int passthrough, int wpt) {
+    uint16_t* __restrict__ y, int64_t T, int k, int d, int drop_mode, int wpt) {
   const int lane = threadIdx.x & 63;
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t t = gw / wpt;                    // wpt waves share a token's row
@@ -64,8 +64,11 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
               reinterpret_cast<const u32x4*>(out + static_cast<int64_t>(pj[j]) * d) + c);
           const uint4 v = make_uint4(q[0], q[1], q[2], q[3]);
           acc_bf16x8(acc, v, wj[j]);
-        } else if (passthrough) {
+        } else if (drop_mode == MOE_DROP_PASSTHROUGH) {
           uint4 v = reinterpret_cast<const uint4*>(x + t * d)[c];
+          acc_bf16x8(acc, v, wj[j]);
+        } else if (drop_mode == MOE_DROP_FALLBACK) {
+          uint4 v = reinterpret_cast<const uint4*>(out_shared + t * d)[c];
           acc_bf16x8(acc, v, wj[j]);
         }
       }
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
 __global__ __launch_bounds__(256) void combine_f32_kernel(
     const float* __restrict__ out, const float* __restrict__ out_shared,
     const float* __restrict__ x, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    float* __restrict__ y, int64_t T, int k, int d, int passthrough, int wpt) {
+    float* __restrict__ y, int64_t T, int k, int d, int drop_mode, int wpt) {
   const int lane = threadIdx.x & 63;
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t t = gw / wpt;
@@ -95,7 +98,8 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
       int p = pos[t * k + j];
       float wj = w[t * k + j];
       if (p >= 0) acc = fmaf(wj, out[static_cast<int64_t>(p) * d + c], acc);
-      else if (passthrough) acc = fmaf(wj, x[t * d + c], acc);
+      else if (drop_mode == MOE_DROP_PASSTHROUGH) acc = fmaf(wj, x[t * d + c], acc);
+      else if (drop_mode == MOE_DROP_FALLBACK) acc = fmaf(wj, out_shared[t * d + c], acc);
     }
     if (out_shared) acc += out_shared[t * d + c];
     y[t * d + c] = acc;
@@ -116,7 +120,7 @@ hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_s
   if (wpt > chunks) wpt = chunks;
   if (wpt < 1) wpt = 1;
   dim3 grid(static_cast<unsigned>(ceil_div(s.T * wpt, 4)));
-  const int pt = s.drop == MOE_DROP_PASSTHROUGH ? 1 : 0;
+  const int pt = s.drop;
   if (s.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(out_shared),

@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_ACT_SILU, MOE_ACT_RELU, MOE_ACT_SWIGLU = range(3)
-MOE_DROP_PASSTHROUGH, MOE_DROP_ZERO = range(2)
+MOE_DROP_PASSTHROUGH, MOE_DROP_ZERO, MOE_DROP_FALLBACK = range(3)
 MOE_GATE_SPARSE, MOE_GATE_FULL = range(2)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 _ACT = {"silu": MOE_ACT_SILU, "relu": MOE_ACT_RELU, "swiglu": MOE_ACT_SWIGLU}
-_DROP = {"passthrough": MOE_DROP_PASSTHROUGH, "zero": MOE_DROP_ZERO}
+_DROP = {"passthrough": MOE_DROP_PASSTHROUGH, "zero": MOE_DROP_ZERO, "fallback": MOE_DROP_FALLBACK}
 _GATE = {"sparse": MOE_GATE_SPARSE, "full": MOE_GATE_FULL}
 
 

@@ -55,7 +55,7 @@ def _ordered(scores, sub):
     return ranked
 
 
-def route_token(lt, N, k, n_groups=0, topk_groups=0, score_k=2):
+def route_token(lt, N, k, n_groups=0, topk_groups=0, score_k=2, gate="sparse"):
     items = list(range(N))
     if n_groups > 1:
         gsz = N // n_groups
@@ -71,6 +71,10 @@ def route_token(lt, N, k, n_groups=0, topk_groups=0, score_k=2):
         groups = _best_subset(gs, list(range(n_groups)), topk_groups)
         items = [e for g in sorted(groups) for e in range(g * gsz, (g + 1) * gsz)]
     sel = _ordered(lt, _best_subset(lt, items, k))
+    if gate == "full":                    # the selected experts' probabilities over all N
+        m = max(lt)
+        s = sum(math.exp(v - m) for v in lt)
+        return sel, [math.exp(lt[e] - m) / s for e in sel]
     m = lt[sel[0]]
     z = [math.exp(lt[e] - m) for e in sel]
     s = sum(z)
@@ -142,7 +146,8 @@ def forward(wl, x, wg, bias, w1, w3, w2, ws=None, xq=None):
     lg = logits(x, wg, bias)
     idx, w = [], []
     for lt in lg:
-        s, ww = route_token(lt, wl.N, wl.k, wl.n_groups, wl.topk_groups, wl.group_score_k)
+        s, ww = route_token(lt, wl.N, wl.k, wl.n_groups, wl.topk_groups, wl.group_score_k,
+                            getattr(wl, "gate", "sparse"))
         idx.append(s)
         w.append(ww)
     counts, kept, f, p, laux = stats(lg, idx, wl.N, wl.k, wl.capacity, wl.alpha)
@@ -157,6 +162,8 @@ def forward(wl, x, wg, bias, w1, w3, w2, ws=None, xq=None):
                 o = ffn(wl.act, xin[t], w1[e], w3[e] if w3 is not None else None, w2[e])
             elif wl.drop == "passthrough":
                 o = x[t]
+            elif wl.drop == "fallback":
+                o = ffn(wl.act, x[t], ws[0], ws[1], ws[2])
             else:
                 o = [0.0] * wl.d
             for i in range(wl.d):

@@ -235,9 +235,10 @@ def expert_ffn(act: str, a: np.ndarray, w1: np.ndarray, w3: np.ndarray | None,
 
 def combine(wl, x: np.ndarray, w: np.ndarray, pos: np.ndarray, o_rows: np.ndarray,
             shared: np.ndarray | None) -> np.ndarray:
-    """y[t] = sum_j w[t][j] * (O[pos[t][j]] if kept, else x[t] (pass-through)
-    or 0) + S[t].  [Glossary] y = sum over TopK of weight times E_i(x);
-    "Capacity factor and token dropping" for dropped slots."""
+    """y[t] = sum_j w[t][j] * (O[pos[t][j]] if kept, else x[t] (pass-through),
+    0, or S[t] (fallback to the shared expert)) + S[t].  [Glossary] y = sum over
+    TopK of weight times E_i(x); "Capacity factor and token dropping" for
+    dropped slots (skip through the residual, or a shared fallback expert)."""
     T, d = x.shape
     y = np.zeros((T, d))
     for j in range(w.shape[1] if w.ndim == 2 else 0):
@@ -247,6 +248,8 @@ def combine(wl, x: np.ndarray, w: np.ndarray, pos: np.ndarray, o_rows: np.ndarra
         term[kept] = o_rows[pj[kept]]
         if wl.drop == "passthrough":
             term[~kept] = x[~kept]
+        elif wl.drop == "fallback":
+            term[~kept] = shared[~kept]
         y += w[:, j:j + 1] * term
     if shared is not None:
         y += shared

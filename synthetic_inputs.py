@@ -58,7 +58,7 @@ class Workload:
     dtype: str = "bf16"          # storage of x, W_g, expert weights and y: "f32" | "bf16"
     buf: str = "bf16"            # dispatch buffer: "f32" | "bf16" | "fp8"
     capacity: int = 0            # <= 0: no limit
-    drop: str = "passthrough"    # "passthrough" | "zero"
+    drop: str = "passthrough"    # "passthrough" | "zero" | "fallback" (the shared expert)
     n_groups: int = 0            # 0: no group limit
     topk_groups: int = 0
     group_score_k: int = 2

@@ -76,6 +76,12 @@ def test_shape_checks(M):
     assert M.check_shape(_s(M, dtype="f32", buf="fp8")) == M.MOE_ERR_UNSUPPORTED
     assert M.check_shape(_s(M, dtype="bf16", d=72)) == M.MOE_ERR_UNSUPPORTED
     assert M.check_shape(_s(M, N=16, k=9)) == M.MOE_ERR_UNSUPPORTED
+    # the fallback drop mode needs the shared expert; the gate is one of two values
+    assert M.check_shape(_s(M, drop="fallback")) == M.MOE_ERR_ARG
+    assert M.check_shape(_s(M, drop="fallback", shared=True)) == M.MOE_OK
+    assert M.check_shape(_s(M, gate="full")) == M.MOE_OK
+    assert M.check_shape(_s(M).replace(gate=2)) == M.MOE_ERR_ARG
+    assert M.check_shape(_s(M).replace(drop=3)) == M.MOE_ERR_ARG
 
 
 def test_null_pointers_and_workspace_rejected_on_host(M):

@@ -174,6 +174,26 @@ def test_full_softmax_gate(name):
     assert np.all(gpu["w"].sum(axis=1) <= 1.0 + 1e-6)
 
 
+FALLBACK_CASES = {
+    "switch_k1": lambda: si.small("switch", shared=True, drop="fallback"),
+    "deepseek_fp8_groups": lambda: si.small("deepseek_v3", capacity=70, drop="fallback"),
+    "f32": lambda: si.Workload("fb32", T=333, d=64, N=8, k=2, F=96, act="silu", dtype="f32",
+                               buf="f32", capacity=70, shared=True, drop="fallback"),
+}
+
+
+@pytest.mark.parametrize("name", list(FALLBACK_CASES))
+def test_drop_to_shared_fallback(name):
+    """drop = fallback: a slot over the capacity is served by the shared expert
+    (its output row weighted by the slot's weight) on top of the always-on
+    term.  Every output against the oracle, y on all tokens, with drops."""
+    wl = FALLBACK_CASES[name]()
+    gpu, errs = _run_and_check(wl, max_adopted=2)
+    assert gpu["drop"].sum() > 0
+    if wl.dtype == "f32":
+        assert errs["y"] <= 1e-5
+
+
 def test_groups_k_le_group_span():
     wl = si.small("deepseek_v3", T=333, N=32, k=3, n_groups=4, topk_groups=1, F=128)
     _run_and_check(wl)

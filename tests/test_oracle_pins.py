@@ -356,6 +356,33 @@ def test_shared_identity_doubles():
     assert np.allclose(out["y"], 2 * x, atol=1e-12)
 
 
+def test_fallback_to_shared_expert_closed_forms():
+    """drop = fallback: a slot over the capacity is served by the shared expert
+    S.  With identity routed experts and an identity S every slot gives x, so
+    y = x + x whatever drops; with zero routed experts only the dropped slots
+    and the always-on term remain: y = (1 + sum of the dropped weights) x."""
+    d, N, k, T = 8, 4, 2, 30
+    wl = si.Workload("fb", T=T, d=d, N=N, k=k, F=2 * d, act="relu", dtype="f32", buf="f32",
+                     shared=True, capacity=6, drop="fallback")
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    eye = np.eye(d, dtype=np.float32)
+    W1 = np.concatenate([eye, -eye]); W2 = np.concatenate([eye, -eye], axis=1)
+    inp = {"x": x, "wg": rng.standard_normal((N, d)).astype(np.float32), "bias": None,
+           "w1": np.stack([W1] * N), "w3": None, "w2": np.stack([W2] * N),
+           "ws1": W1, "ws3": None, "ws2": W2}
+    out = moe.forward(wl, inp)
+    assert out["drop"].sum() > 0
+    assert np.allclose(out["y"], 2 * x, rtol=0, atol=1e-12)
+    inp0 = dict(inp, w1=np.zeros_like(inp["w1"]), w2=np.zeros_like(inp["w2"]))
+    out = moe.forward(wl, inp0)
+    dropped = np.where(out["drop"], out["w"], 0.0).sum(1)
+    assert np.allclose(out["y"], x * (1.0 + dropped)[:, None], rtol=0, atol=1e-12)
+    # the other drop modes on the same routing: pass-through gives 2x, zero x (1 + 1 - dropped)
+    out = moe.forward(wl.replace(drop="zero"), inp)
+    assert np.allclose(out["y"], x * (2.0 - dropped)[:, None], rtol=0, atol=1e-12)
+
+
 def _tiny_cases():
     yield si.WORKLOADS["tiny"].replace(T=24, d=12, F=10)
     yield si.Workload("sw", T=30, d=10, N=6, k=1, F=14, act="relu", dtype="f32", buf="f32", capacity=4)
@@ -366,6 +393,10 @@ def _tiny_cases():
     yield si.Workload("db", T=25, d=10, N=8, k=3, F=9, act="swiglu", dtype="bf16", buf="bf16",
                       bias="zipf2")
     yield si.Workload("kN", T=9, d=6, N=5, k=5, F=7, act="silu", dtype="f32", buf="f32")
+    yield si.Workload("fullgate", T=16, d=10, N=6, k=2, F=9, act="swiglu", dtype="bf16",
+                      buf="bf16", n_groups=2, topk_groups=1, gate="full")
+    yield si.Workload("fallback", T=30, d=10, N=6, k=2, F=8, act="relu", dtype="f32", buf="f32",
+                      capacity=5, drop="fallback", shared=True)
 
 
 @pytest.mark.parametrize("wl", list(_tiny_cases()), ids=lambda w: w.name)
