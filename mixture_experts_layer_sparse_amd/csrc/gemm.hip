@@ -194,6 +194,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   constexpr int A_PW = A_BYTES / 1024 / NW;        // 1 KB wave-loads per wave per stage
   constexpr int B_PW = B_BYTES / 1024 / NW;
   constexpr int LPW = A_PW + B_PW;                 // loads per wave per stage
+  // LDS-DMA loads of one step in two bursts: B (weights) right after the step
+  // barrier, A in the first K slice of the next step (see fstep).  Only for
+  // the gate/up GEMMs, whose A (the dispatch buffer) every n-tile re-reads, so
+  // it comes from the caches and needs less time in flight; the down GEMM's A
+  // (h) streams, and there the later A loads measured slower.
+  constexpr bool SPLIT_AB = !REG && EPI != EPI_STORE;
   constexpr int A_CPR = ROWA / 16, B_CPR = ROWB / 16;   // 16-byte chunks per row
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TMI = WM / 32, TNI = WN / 32;
@@ -471,10 +477,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // loads of step kt + 2 (into the stage just freed) issued one after each
   // MFMA: a wave that issues them all at once stalls on the full load
   // queue with its MFMAs unissued.
-  auto dma = [&](int kt, uint8_t* stg) {
+  auto dma = [&](int kt, uint8_t* stg, bool with_a) {
     const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
+    if (with_a) {
 #pragma unroll
-    for (int j = 0; j < A_PW; ++j) lds_dma16(rs_a(j), stg + (wave * A_PW + j) * 1024, a_off[j], ka);
+      for (int j = 0; j < A_PW; ++j) lds_dma16(rs_a(j), stg + (wave * A_PW + j) * 1024, a_off[j], ka);
+    }
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
       const int gi = wave * B_PW + j;
@@ -515,14 +523,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
   };
   // MFMAs of fragment buffer P (the NI live row blocks) with the loads of
-  // step kt2 into stg spread between them.  Past the last step the loads go
-  // through an empty descriptor (every lane out of range: no memory access)
-  // rather than a branch: a branch would duplicate the loads, and the
-  // compiler then no longer tells the two stages apart and waits for all
-  // loads before every fragment read.
-  auto mm_dma = [&](auto P, auto NI, int kt2, uint8_t* stg) __attribute__((always_inline)) {
+  // step kt2 into stg spread between them: A and B pieces, only A (WHAT = 1)
+  // or only B (WHAT = 2).  Past the last step the loads go through an empty
+  // descriptor (every lane out of range: no memory access) rather than a
+  // branch: a branch would duplicate the loads, and the compiler then no
+  // longer tells the two stages apart and waits for all loads before every
+  // fragment read.
+  auto mm_dma = [&](auto P, auto NI, int kt2, uint8_t* stg, auto WHAT) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     constexpr int NMM = decltype(NI)::value * TNI;
+    constexpr int what = decltype(WHAT)::value;
+    constexpr int U0 = what == 2 ? A_PW : 0;                  // first piece (A pieces first)
+    constexpr int NL = what == 1 ? A_PW : (what == 2 ? B_PW : LPW);
     const bool live = kt2 < kend;
 
     const __amdgpu_buffer_rsrc_t rb0 = live ? rsB0 : rs_null;
@@ -540,17 +552,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     };
     if constexpr (NMM == 0) {
 #pragma unroll
-      for (int u = 0; u < LPW; ++u) issue(u);
+      for (int u = 0; u < NL; ++u) issue(U0 + u);
     } else {
 #pragma unroll
       for (int q = 0; q < NMM; ++q) {
         acc[q / TNI][q % TNI] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             fa[p][q / TNI], fb[p][q % TNI], acc[q / TNI][q % TNI], 0, 0, 0);
 #pragma unroll
-        for (int u = q * LPW / NMM; u < (q + 1) * LPW / NMM; ++u) issue(u);
+        for (int u = q * NL / NMM; u < (q + 1) * NL / NMM; ++u) issue(U0 + u);
       }
       // keep that order through scheduling: one MFMA, then its loads
-      sched_mfma_loads<NMM, LPW>(std::make_integer_sequence<int, NMM>{});
+      sched_mfma_loads<NMM, NL>(std::make_integer_sequence<int, NMM>{});
     }
   };
   using P0 = std::integral_constant<int, 0>;
@@ -561,9 +573,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // wholly past the segment end are left out, so that a segment's partial
   // last m-tile costs about its share of rows; every NI runs the same loads
   // and barriers.
+  // With SPLIT_AB the first slice's MFMAs carry the A loads of step kt + 1
+  // into nxt (its B came with the previous step; nxt's last readers passed
+  // that step's barrier), and the last slice's only the B loads of step kt + 2.
+  using W_AB = std::integral_constant<int, 0>;
+  using W_A = std::integral_constant<int, 1>;
+  using W_B = std::integral_constant<int, 2>;
   auto fstep = [&](int kt, uint8_t* cur, uint8_t* nxt, auto NI) __attribute__((always_inline)) {
     ldfr(cur, 1, P1{}, NI);
-    mm(P0{}, NI);
+    if constexpr (SPLIT_AB) mm_dma(P0{}, NI, kt + 1, nxt, W_A{});
+    else mm(P0{}, NI);
     ldfr(cur, 2, P0{}, NI);
     mm(P1{}, NI);
     ldfr(cur, 3, P1{}, NI);
@@ -572,14 +591,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     wait_lgkm0();                             // own reads of cur done
     __builtin_amdgcn_s_barrier();
     ldfr(nxt, 0, P0{}, NI);
-    mm_dma(P1{}, NI, kt + 2, cur);
+    if constexpr (SPLIT_AB) mm_dma(P1{}, NI, kt + 2, cur, W_B{});
+    else mm_dma(P1{}, NI, kt + 2, cur, W_AB{});
   };
 
   if (!next_tile()) return;
   bind_tile();
   if constexpr (!REG) {
-    dma(kbeg, sm0);
-    dma(kbeg + 1, sm1);                          // (past the range: unused bytes, in range or zero)
+    dma(kbeg, sm0, true);
+    dma(kbeg + 1, sm1, !SPLIT_AB);               // (past the range: unused bytes, in range or zero)
   }
   for (;;) {
 #pragma unroll
@@ -628,8 +648,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     if (more) {
       bind_tile();
       if constexpr (!REG) {
-        dma(kbeg, sm0);
-        dma(kbeg + 1, sm1);
+        dma(kbeg, sm0, true);
+        dma(kbeg + 1, sm1, !SPLIT_AB);
       }
     }
 
