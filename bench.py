@@ -1,7 +1,7 @@
 """Benchmark of the sparse MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--no-cpu-baseline] [--mode bench|copy|sweep|decode|summarize]
+                    [--no-cpu-baseline] [--mode bench|copy|sweep|decode|memory|summarize]
 
 One step = one whole layer forward (route, dispatch, grouped GEMM up, grouped
 GEMM down, shared expert if any, combine) over one batch of seeded synthetic
@@ -20,6 +20,8 @@ for the hardware byte counters) and exits.  --mode sweep times every workload
 family at full size, phase by phase, and prints a markdown table.  --mode
 decode times decode steps (B = 1, 32, 128 tokens) at the DeepSeek-V3 shape:
 experts touched and the expert-weight bytes streamed against the HBM peak.
+--mode memory times the memory-bound phases alone, warm and with the caches
+flushed before every launch (median and p10/p90).
 """
 from __future__ import annotations
 
@@ -48,7 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens whose expert FFNs the CPU oracle runs (0: all T)")
-    ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep", "decode"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep", "decode", "memory"],
+                    default="bench")
     ap.add_argument("--prof", default=None,
                     help="summarize: directory holding trace/ fetch/ write/ cfetch/ cwrite/ "
                          "rocprofv3 csv output")
@@ -358,6 +361,74 @@ def decode(steps, warmup):
         torch.cuda.empty_cache()
 
 
+def memory(steps, warmup):
+    """The memory-bound phases alone (route + dispatch, combine; also route
+    and dispatch as separate calls) at every bf16 workload's full size, each
+    launch timed with its own HIP events: warm (launches back to back) and
+    cold (a 1 GiB buffer, four times the Infinity Cache, written untimed
+    before every launch, so the inputs come from HBM).  Reports the median
+    and p10/p90 duration and the algorithmic bytes at the median against the
+    HBM peak, with a plain device copy of the same order of size as the
+    ceiling.  Prints a markdown table."""
+    import numpy as np
+    import torch
+    import synthetic_inputs as si
+    from mixture_experts_layer_sparse_amd import moe as M
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def timed(fn, cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps + warmup)]
+        for i, (e0, e1) in enumerate(ev):
+            if cold:
+                flush.fill_(i & 0xFF)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = np.array([e0.elapsed_time(e1) for e0, e1 in ev[warmup:]]) * 1e3
+        return np.percentile(us, [50, 10, 90])
+
+    print("| workload | phase | algorithmic MiB | warm us (p10-p90) | warm GB/s (% HBM) | "
+          "cold us (p10-p90) | cold GB/s (% HBM) |")
+    print("|---|---|---|---|---|---|---|")
+
+    def row(name, phase, nbytes, fn):
+        cells = []
+        for cold in (False, True):
+            med, p10, p90 = timed(fn, cold)
+            gbs = nbytes / (med * 1e-6) / 1e9
+            cells += [f"{med:.1f} ({p10:.1f}-{p90:.1f})", f"{gbs:.0f} ({100 * gbs / PEAK_HBM_GBPS:.1f}%)"]
+        print(f"| {name} | {phase} | {nbytes / 2**20:.1f} | " + " | ".join(cells) + " |", flush=True)
+
+    for n in (1 << 26, 1 << 28):        # 64 MiB (fits the Infinity Cache) and 256 MiB copies
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        row("device copy", f"{n >> 20} MiB", 2 * n, lambda: dst.copy_(src))
+        del src, dst
+    for name in ("mixtral", "switch", "deepseek_v3", "dbrx"):
+        wl = si.WORKLOADS[name]
+        inp = si.generate(wl)
+        g = {k: _to_dev(v) for k, v in inp.items()}
+        del inp
+        x = g["x"]
+        s = M.shape_of(wl)
+        L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
+                    ws3=g["ws3"], ws2=g["ws2"])
+        L.forward(x)                     # fills the expert outputs the combine reads
+        torch.cuda.synchronize()
+        R = int(L.offsets[-1].item())
+        rb, db, cb = alg_bytes(wl, R)
+        label = f"{name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k})"
+        row(label, "route + dispatch", rb + db, lambda: L.route_dispatch(x))
+        row(label, "route", rb, lambda: L.route(x))
+        row(label, "dispatch", db, lambda: L.dispatch(x))
+        row(label, "combine", cb, lambda: L.combine(x))
+        del L, g, x
+        torch.cuda.empty_cache()
+
+
 def main():
     a = parse()
     if a.mode == "summarize":
@@ -368,6 +439,9 @@ def main():
         return
     if a.mode == "decode":
         decode(a.steps, a.warmup)
+        return
+    if a.mode == "memory":
+        memory(a.steps, a.warmup)
         return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))

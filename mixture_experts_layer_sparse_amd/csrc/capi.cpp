@@ -3,6 +3,7 @@
 // conventions of include/moe.h hold without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 
 #include "moe_internal.h"
@@ -27,8 +28,11 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align_up(off + nb_route * N * 4);
   L.route_base = off;
   off = align_up(off + nb_route * N * 4);
+  L.route_prod = off;
+  off = align_up(off + N * 8 + 4);
   L.route_lpart = off;
-  off = align_up(off + static_cast<size_t>(moe::route_split_ranges(s)) * T * N * 4);
+  off = align_up(off + std::max(static_cast<size_t>(moe::route_split_ranges(s)) * T * N * 4,
+                                moe::router_gemm_bytes(s)));
   L.disp_hist = off;
   off = align_up(off + nb_disp * N * 4);
   L.gemm_split = off;
@@ -130,10 +134,12 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_g, const f
   float* psum = reinterpret_cast<float*>(base + L.route_psum);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
   float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, lpart, st);
+  double* prod = reinterpret_cast<double*>(base + L.route_prod);
+  int32_t* done = reinterpret_cast<int32_t*>(prod + s->N);
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, lpart, done, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux,
-                                               nullptr, nullptr, st));
+                                               nullptr, nullptr, prod, done, st));
 }
 
 moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* offsets,
@@ -269,10 +275,12 @@ moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
   int32_t* tbase = reinterpret_cast<int32_t*>(base + L.route_base);
   float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, st);
+  double* prod = reinterpret_cast<double*>(base + L.route_prod);
+  int32_t* done = reinterpret_cast<int32_t*>(prod + s->N);
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, done, st);
   if (e == hipSuccess)
     e = moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux, offsets,
-                                   tbase, st);
+                                   tbase, prod, done, st);
   if (e == hipSuccess)
     e = moe::launch_dispatch_copy_planned(*s, x, idx, tbase, offsets, pos, src, drop, x_perm,
                                           row_scale, st);

@@ -952,6 +952,48 @@ size_t gemm_split_bytes(const moe_shape& s) {
   return kSplitMetaBytes + static_cast<size_t>(units) * 256 * 256 * 4;
 }
 
+// The router kernel's own logits re-read W_g (N d bf16) per 16 tokens; the GEMM
+// instead writes and re-reads float32 partials of 1 KB per token and K range.
+// Measured: the GEMM pays at N = 256, d = 7168 (router 142 -> 76 us at 4096
+// tokens) and not at N = 128, d = 1024 (43 -> 60 us at 8192 tokens).
+bool router_gemm(const moe_shape& s) {
+  return s.dtype == MOE_BF16 && s.N >= 64 && s.N <= kRouterTileCols &&
+         static_cast<int64_t>(s.N) * s.d >= (1 << 19) && s.T >= 512 && s.d % 64 == 0 &&
+         skinny(s.T, 1, 1);
+}
+
+size_t router_gemm_bytes(const moe_shape& s) {
+  if (!router_gemm(s)) return 0;
+  return kSplitMetaBytes + static_cast<size_t>(split_slots()) * kRouterTileRows * kRouterTileCols * 4;
+}
+
+// The split-K tail alone (few tiles: every tile in min(8, S / tiles) K
+// ranges), register-staged 128 x 256 tiles; no reduction, the router reads
+// the partials.
+hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* wg, void* scratch,
+                                hipStream_t st) {
+  GemmArgs g{};
+  g.a = x;
+  g.a_scale = nullptr;
+  g.offsets = nullptr;
+  g.rows = s.T;
+  g.n_seg = 1;
+  g.K = s.d;
+  g.n_out = s.N;
+  g.b0 = static_cast<const uint16_t*>(wg);
+  g.b1 = nullptr;
+  g.b_stride = static_cast<int64_t>(s.N) * s.d;
+  g.out = nullptr;
+  g.nt = 1;
+  g.split_slots = split_slots();
+  g.split_k_max = kSplitKMax;
+  g.part_meta = static_cast<int32_t*>(scratch);
+  g.part = reinterpret_cast<float*>(static_cast<char*>(scratch) + kSplitMetaBytes);
+  const int mtu = static_cast<int>(ceil_div(s.T, kRouterTileRows));
+  return launch_gg_on<kRouterTileRows, kRouterTileCols, 2, 4, EPI_STORE, false, true, true, true>(
+      g, kSplitKMax * mtu, st);
+}
+
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg, const void* w1,
                             const void* w3, void* h, void* split, hipStream_t st) {

@@ -16,6 +16,10 @@ constexpr int kDispatchBlock = 256;  // tokens per dispatch-plan block
 constexpr int kSplitK = 4;           // K ranges per tail tile of a split-K grouped GEMM tail
 constexpr int kSplitKMax = 8;        // K ranges per tile when a grouped GEMM has few tiles
 constexpr size_t kSplitMetaBytes = 4096;  // header of the split-K scratch (tile count, tile rows)
+// Router logits through the grouped GEMM: split-K partial tiles of this many
+// token rows and expert columns, stored tile after tile in range-major order.
+constexpr int kRouterTileRows = 128;
+constexpr int kRouterTileCols = 256;
 
 // ---------------------------------------------------------------- helpers --
 
@@ -39,7 +43,9 @@ struct WsLayout {
   size_t route_psum;    // float   [nb_route][N]
   size_t route_hist;    // int32   [nb_route][N]
   size_t route_base;    // int32   [nb_route][N]
-  size_t route_lpart;   // float   [route_split_ranges(s)][T][N] partial logits (few tokens only)
+  size_t route_prod;    // double  [N], then the statistics kernel's arrival counter
+  size_t route_lpart;   // partial logits: float [route_split_ranges(s)][T][N] (few tokens), or
+                        // router_gemm_bytes(s) of split-K scratch (wide routers)
   size_t disp_hist;     // int32   [nb_disp][N]
   size_t gemm_split;    // split-K tail scratch of the grouped GEMMs (gemm_split_bytes(s))
   size_t h;             // dtype   [T*k][F]
@@ -58,12 +64,15 @@ WsLayout ws_layout(const moe_shape& s);
 int route_split_ranges(const moe_shape& s);
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        float* lpart, hipStream_t st);
+                        float* lpart, int32_t* done, hipStream_t st);
 // offsets (may be null): exclusive scan of the kept counts, N + 1 entries.
 // base (may be null): [nb_route][N] assignments to each expert in earlier tiles.
+// prod: [N] doubles of scratch (each expert's f p, for L_aux); done: the
+// counter that launch_route zeroed (the same workspace, launched before this).
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
                                  int32_t* counts, int32_t* kept, float* p, float* f,
-                                 float* l_aux, int32_t* offsets, int32_t* base, hipStream_t st);
+                                 float* l_aux, int32_t* offsets, int32_t* base, double* prod,
+                                 int32_t* done, hipStream_t st);
 
 hipError_t launch_dispatch_hist(const moe_shape& s, const int32_t* idx, int32_t* hist,
                                 hipStream_t st);
@@ -89,6 +98,18 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
                               hipStream_t st);
 size_t gemm_split_bytes(const moe_shape& s);
+
+// Wide routers (bf16, at least 64 experts, N d >= 2^19, 512 to 16384 tokens): the logits as
+// one dense split-K GEMM of x [T][d] with W_g [N][d], so that each 128-token
+// tile reads W_g once (instead of every 16-token router tile reading all of
+// it).  The float32 partials stay in `scratch` (router_gemm_bytes(s)): a
+// header whose words 0 and 1 hold the tile count and the K-range count,
+// followed at kSplitMetaBytes by the partial tiles; the router adds the ranges
+// in order.
+bool router_gemm(const moe_shape& s);
+size_t router_gemm_bytes(const moe_shape& s);
+hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* wg, void* scratch,
+                                hipStream_t st);
 
 hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_shared,
                           const void* x, const int32_t* pos, const float* w, void* y,

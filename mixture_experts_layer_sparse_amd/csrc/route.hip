@@ -1,6 +1,7 @@
 // Router: logits (skinny GEMM), group limit, top-k, sparse softmax and the
-// per-block load statistics, fused in one kernel; plus a one-workgroup
-// finalisation of counts, f, p and L_aux.
+// per-block load statistics, fused in one kernel; then the statistics over
+// all blocks (counts, f, p, the per-tile prefix) spread over the experts, and
+// one small workgroup for the scan over experts and L_aux.
 //
 // What it computes follows "moe communication costs" / "Router design" (logits
 // W_g x; the top-k entries pick the experts), "Part 5" / "1.1 The Router Kernel"
@@ -33,6 +34,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = kRouteTile;
 constexpr int kRouteSplitMax = 8;      // d-ranges of the split logits at most
+static_assert(kSplitKMax <= kRouteSplitMax, "the router adds every K range of the logits GEMM");
 
 struct RouteArgs {
   const void* x;
@@ -45,9 +47,13 @@ struct RouteArgs {
   int32_t* hist;
   int64_t T;
   int d, N, k, n_groups, topk_groups, gsk;
-  const float* lpart;   // partial logits [lsplit][T][N] from logits_split_kernel, or null
+  const float* lpart;   // partial logits (range kr, token t, expert e at kr * lrange + t * lld + e), or null
   int lsplit;
+  int64_t lrange;
+  int lld;
+  const int32_t* lmeta; // non-null: the range count and the tile count come from this split-K header
   int gate;             // moe_gate
+  int32_t* done;        // arrival counter of the statistics workgroups, zeroed here
 };
 
 // Key ordering "larger logit first, then lower expert index"; 0 = no candidate.
@@ -335,7 +341,8 @@ __global__ __launch_bounds__(256) void logits_split_kernel(const uint16_t* __res
 }
 
 // Logits of a 16-token tile from the partials: the d-ranges added in order.
-__device__ void logits_from_partials(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
+__device__ void logits_from_partials(const RouteArgs& a, int ks, int64_t lrange, int64_t t0, float* lt,
+                                     int ldl) {
   for (int q = threadIdx.x; q < TM * a.N; q += RW * 64) {
     const int m = q / a.N, e = q % a.N;
     const int64_t t = t0 + m;
@@ -344,10 +351,10 @@ __device__ void logits_from_partials(const RouteArgs& a, int64_t t0, float* lt, 
       float pv[kRouteSplitMax];
 #pragma unroll
       for (int kr = 0; kr < kRouteSplitMax; ++kr)      // (all loads in flight together)
-        pv[kr] = kr < a.lsplit ? a.lpart[(static_cast<int64_t>(kr) * a.T + t) * a.N + e] : 0.f;
+        pv[kr] = kr < ks ? a.lpart[kr * lrange + t * a.lld + e] : 0.f;
 #pragma unroll
       for (int kr = 0; kr < kRouteSplitMax; ++kr)
-        if (kr < a.lsplit) v += pv[kr];
+        if (kr < ks) v += pv[kr];
       if (a.bias) v += a.bias[e];
     }
     lt[m * ldl + e] = v;
@@ -456,6 +463,76 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
   }
 }
 
+// Butterflies over aligned runs of `width` lanes (a power of two, at most
+// 32): every lane of the run ends with the run's maximum / sum (a + b == b + a
+// exactly, so all lanes agree).
+__device__ __forceinline__ float run_max_f(float v, int width) {
+  for (int off = 1; off < width; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float run_sum_f(float v, int width) {
+  for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ uint64_t run_max_u64(uint64_t v, int width) {
+  for (int off = 1; off < width; off <<= 1) {
+    const uint64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Selection for N <= 32 experts without a group limit, all tokens of the tile
+// at once: token m owns the NP lanes m * NP .. m * NP + NP - 1 (NP = N rounded
+// up to a power of two, so a token's lanes never straddle a wave), lane e of
+// them expert e.  The full softmax comes from butterflies over the token's
+// lanes; top-k takes k rounds of a maximum over keys (logit, ~index), so equal
+// logits go to the lower index as in an in-order scan with strict >.  Writes
+// each token's p row to prow (for p) and its k picks; counts go to the block
+// histogram.
+__device__ void select_lanes(const RouteArgs& a, const float* lt, int ldl, int64_t t0,
+                             float (*prow)[SMALL_N + 1], int* hl) {
+  const int N = a.N, k = a.k;
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  const int m = threadIdx.x / NP, e = threadIdx.x % NP;   // (TM * NP <= 512 threads)
+  const bool tok = m < TM && t0 + m < a.T;
+  const bool live = tok && e < N;
+  const float v = live ? lt[m * ldl + e] : -INFINITY;
+  const float mx = run_max_f(v, NP);
+  const float z = live ? __expf(v - mx) : 0.f;
+  const float zs = run_sum_f(z, NP);
+  if (m < TM && e < N) prow[m][e] = live ? z / zs : 0.f;
+  uint64_t key = live ? sel_key(v, e) : 0ull;
+  int sel_e[kMaxTopK];
+  float sel_v[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      const uint64_t best = run_max_u64(key, NP);
+      sel_e[j] = key_index(best);
+      sel_v[j] = key_value(best);                // (the logit, with -0 read as +0)
+      if (e == sel_e[j]) key = 0ull;
+    }
+  }
+  if (!tok) return;
+  float den = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) den += __expf(sel_v[j] - sel_v[0]);
+  const int64_t t = t0 + m;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k && e == j) {
+      a.idx[t * k + j] = sel_e[j];
+      // full gate: the expert's probability in the softmax written to prow
+      a.w[t * k + j] = a.gate == MOE_GATE_FULL ? __expf(sel_v[j] - mx) / zs
+                                               : __expf(sel_v[j] - sel_v[0]) / den;
+      atomicAdd(&hl[sel_e[j]], 1);
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
@@ -476,8 +553,16 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TM;
 
   for (int e = threadIdx.x; e < kMaxExperts; e += RW * 64) hl[e] = 0;
+  // (the statistics kernel runs after this one on the same stream)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.done = 0;
   if (BF16) {
-    if (a.lpart) logits_from_partials(a, t0, lt, ldl);
+    if (a.lpart) {
+      // range count and range stride: from the split-K header when the GEMM wrote the partials
+      const int ks = a.lmeta ? a.lmeta[1] : a.lsplit;
+      const int64_t lrange = a.lmeta ? static_cast<int64_t>(a.lmeta[0]) * (kRouterTileRows * kRouterTileCols)
+                                     : a.lrange;
+      logits_from_partials(a, ks, lrange, t0, lt, ldl);
+    }
     else if (a.d % SCH == 0) logits_bf16_staged(a, t0, sbuf, part, lt, ldl);
     else logits_bf16(a, t0, part, lt, ldl);
   } else {
@@ -492,8 +577,20 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
     }
   }
 
+  if (N <= SMALL_N && a.n_groups <= 1) {
+    select_lanes(a, lt, ldl, t0, pl, hl);
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += RW * 64) {
+      float sum = 0.f;
+#pragma unroll
+      for (int m2 = 0; m2 < TM; ++m2) sum += pl[m2][e];
+      a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
+      a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
+    }
+    return;
+  }
   if (N <= SMALL_N) {
-    // one lane per token
+    // group limit: one lane per token
     const int m = threadIdx.x;
     if (m < TM) {
       if (t0 + m < a.T) {
@@ -655,93 +752,175 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
   }
 }
 
-// One workgroup of 1024 threads.  Thread (part, e) covers a contiguous range of
-// tiles for expert e and sums its p partials and counts in increasing tile
-// order; the P parts are combined in a fixed tree order, so the result does not
-// depend on timing.  With `offsets`, the exclusive scan of the kept counts over
-// experts is written; with `base`, a second pass writes for every tile and
-// expert the number of assignments to the expert in earlier tiles, from which
-// the dispatch copy places each token without a separate plan step.
-__global__ __launch_bounds__(1024) void route_finalize_kernel(const float* psum, const int32_t* hist,
-                                                              int nb, int64_t T, int N, int k,
-                                                              int cap, float alpha, int32_t* counts,
-                                                              int32_t* kept, float* p, float* f,
-                                                              float* l_aux, int32_t* offsets,
-                                                              int32_t* base) {
-  __shared__ double sp[1024];
-  __shared__ int sc[1024];
-  __shared__ int pc[1024];               // per-part counts, kept for the tile prefix
-  __shared__ double prod[kMaxExperts];
-  __shared__ int kc[kMaxExperts];
-  int NP = 1;
-  while (NP < N) NP <<= 1;
-  const int P = 1024 / NP;
-  const int e = threadIdx.x % NP, part = threadIdx.x / NP;
-  const int b0 = static_cast<int>(static_cast<int64_t>(part) * nb / P);
-  const int b1 = static_cast<int>(static_cast<int64_t>(part + 1) * nb / P);
+// Statistics over all router tiles, spread over the experts so that the
+// per-tile partials (tiles x N values, 512 KB at 8192 tokens and 128 experts)
+// are read by many CUs instead of one.  Workgroup b owns experts se*b ..
+// se*b + se - 1 (se = 8 up to 8 experts, so that one workgroup does all, else
+// 4); thread (part, e) sums the p partials and counts of a contiguous range
+// of tiles for its expert in increasing tile order, the parts are combined in
+// a fixed tree order (so the result does not depend on timing), and the
+// expert's counts, kept count, p, f and f*p are written.  With `base`, an
+// exclusive prefix over the parts gives every tile the number of assignments
+// to the expert in earlier tiles, from which the dispatch copy places each
+// token without a separate plan step.  The last workgroup to arrive then
+// scans the kept counts over the experts into offsets and sums L_aux.
+constexpr int ST = 256;                // threads per statistics workgroup (= kMaxExperts)
+constexpr int SKEEP = 16;              // tiles per batch of loads issued together
+
+int stats_experts_per_block(int N) { return N <= 8 ? 8 : 4; }
+
+__global__ __launch_bounds__(ST) void route_stats_kernel(const float* psum, const int32_t* hist,
+                                                         int nb, int64_t T, int N, int k, int cap,
+                                                         int32_t* counts, int32_t* kept, float* p,
+                                                         float* f, double* prod, int32_t* base,
+                                                         float alpha, int32_t* offsets, float* l_aux,
+                                                         int32_t* done, int se) {
+  static_assert(ST == kMaxExperts, "the last workgroup scans all experts, one per thread");
+  __shared__ double sp[ST];
+  __shared__ int sc[ST];
+  __shared__ int pc[ST];
+  __shared__ int is_last;
+  const int tid = threadIdx.x;
+  const int nparts = ST / se;
+  const int el = tid % se, part = tid / se;
+  const int e = blockIdx.x * se + el;
+  const bool ex = e < N;
+  const int b0 = static_cast<int>(static_cast<int64_t>(part) * nb / nparts);
+  const int b1 = static_cast<int>(static_cast<int64_t>(part + 1) * nb / nparts);
+  // batches of SKEEP tiles whose loads are issued together; the first
+  // batch's counts stay in registers for the tile prefix
+  int hv[SKEEP];
   double s = 0.0;
   int c = 0;
-  if (e < N) {
-#pragma unroll 4
-    for (int b = b0; b < b1; ++b) {
-      s += static_cast<double>(psum[static_cast<int64_t>(b) * N + e]);
-      c += hist[static_cast<int64_t>(b) * N + e];
+  for (int bb = b0; bb < b1; bb += SKEEP) {
+    int hb[SKEEP];
+    float pb[SKEEP];
+#pragma unroll
+    for (int i = 0; i < SKEEP; ++i) {
+      const bool in = ex && bb + i < b1;
+      hb[i] = in ? hist[static_cast<int64_t>(bb + i) * N + e] : 0;
+      pb[i] = in ? psum[static_cast<int64_t>(bb + i) * N + e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < SKEEP; ++i) {
+      s += static_cast<double>(pb[i]);
+      c += hb[i];
+      if (bb == b0) hv[i] = hb[i];
     }
   }
-  sp[threadIdx.x] = s;
-  sc[threadIdx.x] = c;
-  pc[threadIdx.x] = c;
+  if (b0 >= b1) {
+#pragma unroll
+    for (int i = 0; i < SKEEP; ++i) hv[i] = 0;
+  }
+  sp[tid] = s;
+  sc[tid] = c;
+  pc[tid] = c;
   __syncthreads();
-  for (int half = P / 2; half >= 1; half >>= 1) {
+  for (int half = nparts / 2; half >= 1; half >>= 1) {
     if (part < half) {
-      sp[threadIdx.x] += sp[threadIdx.x + half * NP];
-      sc[threadIdx.x] += sc[threadIdx.x + half * NP];
+      sp[tid] += sp[tid + half * se];
+      sc[tid] += sc[tid + half * se];
     }
     __syncthreads();
   }
-  if (part == 0 && e < N) {
-    const int64_t cnt = sc[e];
-    const double pe = sp[e] / static_cast<double>(T);
+  int kv = 0;
+  double pr = 0.0;
+  if (part == 0 && ex) {
+    const int64_t cnt = sc[el];
+    const double pe = sp[el] / static_cast<double>(T);
     const double fe = static_cast<double>(cnt) / (static_cast<double>(T) * k);
-    const int32_t kp = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
     counts[e] = static_cast<int32_t>(cnt);
-    kept[e] = kp;
-    kc[e] = kp;
+    kv = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
+    pr = fe * pe;
+    kept[e] = kv;
     if (p) p[e] = static_cast<float>(pe);
     if (f) f[e] = static_cast<float>(fe);
-    prod[e] = fe * pe;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (l_aux) {
-      double acc = 0.0;
-      for (int q = 0; q < N; ++q) acc += prod[q];
-      l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
-    }
-    if (offsets) {
-      int run = 0;
-      for (int q = 0; q < N; ++q) {
-        offsets[q] = run;
-        run += kc[q];
-      }
-      offsets[N] = run;
-    }
+    prod[e] = pr;
   }
   if (base) {
     // exclusive prefix of the part counts over parts (Hillis-Steele, then shift)
-    for (int off = 1; off < P; off <<= 1) {
-      const int v = part >= off ? pc[threadIdx.x - off * NP] : 0;
+    for (int off = 1; off < nparts; off <<= 1) {
+      const int v = part >= off ? pc[tid - off * se] : 0;
       __syncthreads();
-      pc[threadIdx.x] += v;
+      pc[tid] += v;
       __syncthreads();
+    }
+    if (ex) {
+      int run = part > 0 ? pc[tid - se] : 0;
+#pragma unroll
+      for (int i = 0; i < SKEEP; ++i) {
+        if (b0 + i < b1) {
+          base[static_cast<int64_t>(b0 + i) * N + e] = run;
+          run += hv[i];
+        }
+      }
+      for (int bb = b0 + SKEEP; bb < b1; bb += SKEEP) {
+        int hb[SKEEP];
+#pragma unroll
+        for (int i = 0; i < SKEEP; ++i) hb[i] = bb + i < b1 ? hist[static_cast<int64_t>(bb + i) * N + e] : 0;
+#pragma unroll
+        for (int i = 0; i < SKEEP; ++i) {
+          if (bb + i < b1) {
+            base[static_cast<int64_t>(bb + i) * N + e] = run;
+            run += hb[i];
+          }
+        }
+      }
     }
   }
-  if (base && e < N) {
-    int run = part > 0 ? pc[threadIdx.x - NP] : 0;
-    for (int b = b0; b < b1; ++b) {
-      base[static_cast<int64_t>(b) * N + e] = run;
-      run += hist[static_cast<int64_t>(b) * N + e];
+  // The scan over the experts, by the last workgroup to arrive: each writer's
+  // stores are made visible at device scope before its workgroup counts
+  // itself, and the last one acquires them (a single workgroup has them in
+  // its own registers).  Which workgroup is last does not change the result
+  // (fixed orders over the experts).
+  if (gridDim.x > 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+      is_last = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                static_cast<int>(gridDim.x) - 1;
+    __syncthreads();
+  } else {
+    is_last = 1;
+  }
+  if (is_last) {
+    int NP = 1;
+    while (NP < N) NP <<= 1;
+    if (gridDim.x > 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      kv = tid < N ? __hip_atomic_load(kept + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      pr = tid < N ? __hip_atomic_load(prod + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+    } else {
+      // thread el of part 0 holds expert el; move it to thread e
+      __syncthreads();
+      if (part == 0) {
+        sc[el] = kv;
+        sp[el] = pr;
+      }
+      __syncthreads();
+      kv = tid < N ? sc[tid] : 0;
+      pr = tid < N ? sp[tid] : 0.0;
     }
+    __syncthreads();                             // (sp and sc: the part sums are no longer needed)
+    sc[tid] = kv;
+    sp[tid] = pr;
+    __syncthreads();
+    // the exclusive scan of the kept counts (Hillis-Steele) and L_aux = alpha N sum f p (a tree)
+    for (int off = 1; off < NP; off <<= 1) {
+      const int v = tid >= off ? sc[tid - off] : 0;
+      __syncthreads();
+      sc[tid] += v;
+      __syncthreads();
+    }
+    for (int half = NP / 2; half >= 1; half >>= 1) {
+      if (tid < half) sp[tid] += sp[tid + half];
+      __syncthreads();
+    }
+    if (offsets && tid < N) {
+      offsets[tid] = sc[tid] - kv;
+      if (tid == N - 1) offsets[N] = sc[tid];
+    }
+    if (l_aux && tid == 0) l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * sp[0]);
   }
 }
 
@@ -775,11 +954,18 @@ int route_split_ranges(const moe_shape& s) {
 
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        float* lpart, hipStream_t st) {
+                        float* lpart, int32_t* done, hipStream_t st) {
   const int ks = route_split_ranges(s);
   RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
-              s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks, s.gate};
-  if (ks > 0) {
+              s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks,
+              s.T * s.N, s.N, nullptr, s.gate, done};
+  if (router_gemm(s)) {
+    const hipError_t e = launch_router_logits(s, x, wg, lpart, st);
+    if (e != hipSuccess) return e;
+    a.lmeta = reinterpret_cast<const int32_t*>(lpart);
+    a.lpart = reinterpret_cast<const float*>(reinterpret_cast<const char*>(lpart) + kSplitMetaBytes);
+    a.lld = kRouterTileCols;
+  } else if (ks > 0) {
     const int64_t units = ceil_div(s.T, 16) * ceil_div(s.N, 16) * ks;
     hipLaunchKernelGGL(logits_split_kernel, dim3(static_cast<unsigned>(ceil_div(units, 4))), dim3(256), 0,
                        st, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), lpart, s.T,
@@ -807,10 +993,13 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
 
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
                                  int32_t* counts, int32_t* kept, float* p, float* f,
-                                 float* l_aux, int32_t* offsets, int32_t* base, hipStream_t st) {
-  int nb = static_cast<int>(ceil_div(s.T, TM));
-  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(1024), 0, st, psum, hist, nb, s.T, s.N,
-                     s.k, s.capacity, s.alpha, counts, kept, p, f, l_aux, offsets, base);
+                                 float* l_aux, int32_t* offsets, int32_t* base, double* prod,
+                                 int32_t* done, hipStream_t st) {
+  const int nb = static_cast<int>(ceil_div(s.T, TM));
+  const int se = stats_experts_per_block(s.N);
+  hipLaunchKernelGGL(route_stats_kernel, dim3(static_cast<unsigned>(ceil_div(s.N, se))), dim3(ST), 0, st,
+                     psum, hist, nb, s.T, s.N, s.k, s.capacity, counts, kept, p, f, prod, base, s.alpha,
+                     offsets, l_aux, done, se);
   return hipGetLastError();
 }
 
