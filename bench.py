@@ -121,9 +121,9 @@ def _src_hash(path):
 
 
 def _short(name):
-    for key in ("gg_kernel", "route_kernel", "route_finalize_kernel", "disp_hist_kernel",
-                "disp_plan_kernel", "disp_copy_kernel", "disp_fp8_kernel", "combine_bf16_kernel",
-                "combine_f32_kernel", "__amd_rocclr_copyBuffer"):
+    for key in ("gg_splitk_reduce", "gg_kernel", "logits_split_kernel", "route_kernel", "route_stats_kernel",
+                "disp_hist_kernel", "disp_plan_kernel", "disp_copy_kernel", "disp_fp8_kernel",
+                "combine_bf16_kernel", "combine_f32_kernel", "__amd_rocclr_copyBuffer"):
         if key in name:
             i = name.find(key)
             j = name.find("(", i)

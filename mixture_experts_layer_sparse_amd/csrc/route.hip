@@ -755,34 +755,42 @@ __global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
 // Statistics over all router tiles, spread over the experts so that the
 // per-tile partials (tiles x N values, 512 KB at 8192 tokens and 128 experts)
 // are read by many CUs instead of one.  Workgroup b owns experts se*b ..
-// se*b + se - 1 (se = 8 up to 8 experts, so that one workgroup does all, else
-// 4); thread (part, e) sums the p partials and counts of a contiguous range
-// of tiles for its expert in increasing tile order, the parts are combined in
-// a fixed tree order (so the result does not depend on timing), and the
-// expert's counts, kept count, p, f and f*p are written.  With `base`, an
-// exclusive prefix over the parts gives every tile the number of assignments
-// to the expert in earlier tiles, from which the dispatch copy places each
-// token without a separate plan step.  The last workgroup to arrive then
-// scans the kept counts over the experts into offsets and sums L_aux.
-constexpr int ST = 256;                // threads per statistics workgroup (= kMaxExperts)
+// se*b + se - 1 (se = 8 up to 8 experts, so that one workgroup of 1024 threads
+// does all, else 4 per workgroup of 256).  Lane l of wave w handles expert
+// l % se over tile range (part) w * 64 / se + l / se, summing its p partials
+// and counts in increasing tile order; the parts are combined by shuffles
+// inside each wave and then wave by wave in order (fixed orders, so the
+// result does not depend on timing), and the expert's counts, kept count, p,
+// f and f*p are written.  With `base`, the prefix over the parts (a shuffle
+// scan inside the wave plus the earlier waves' totals) gives every tile the
+// number of assignments to the expert in earlier tiles, from which the
+// dispatch copy places each token without a separate plan step.  The last
+// workgroup to arrive then scans the kept counts over the experts into
+// offsets and sums L_aux.  (Reductions through LDS with a barrier per level
+// cost 300-400 cycles a level at 16 waves.)
+constexpr int ST = 256;                // threads per statistics workgroup, several workgroups (= kMaxExperts)
+constexpr int ST1 = 1024;              // threads of a lone statistics workgroup
 constexpr int SKEEP = 16;              // tiles per batch of loads issued together
 
 int stats_experts_per_block(int N) { return N <= 8 ? 8 : 4; }
 
-__global__ __launch_bounds__(ST) void route_stats_kernel(const float* psum, const int32_t* hist,
+__global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, const int32_t* hist,
                                                          int nb, int64_t T, int N, int k, int cap,
                                                          int32_t* counts, int32_t* kept, float* p,
                                                          float* f, double* prod, int32_t* base,
                                                          float alpha, int32_t* offsets, float* l_aux,
                                                          int32_t* done, int se) {
-  static_assert(ST == kMaxExperts, "the last workgroup scans all experts, one per thread");
-  __shared__ double sp[ST];
-  __shared__ int sc[ST];
-  __shared__ int pc[ST];
+  static_assert(ST == kMaxExperts && ST1 >= ST, "the last workgroup scans all experts, one per thread");
+  __shared__ double wsum[ST1 / 64][8];   // per-wave totals of p and counts, per expert (se <= 8)
+  __shared__ int wcnt[ST1 / 64][8];
+  __shared__ int xk[ST / 64];            // last workgroup: per-wave totals over the experts
+  __shared__ double xp[ST / 64];
   __shared__ int is_last;
-  const int tid = threadIdx.x;
-  const int nparts = ST / se;
-  const int el = tid % se, part = tid / se;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = static_cast<int>(blockDim.x) >> 6;
+  const int pw = 64 / se;                // parts per wave
+  const int nparts = nw * pw;
+  const int el = lane % se, part = wave * pw + lane / se;
   const int e = blockIdx.x * se + el;
   const bool ex = e < N;
   const int b0 = static_cast<int>(static_cast<int64_t>(part) * nb / nparts);
@@ -812,22 +820,31 @@ __global__ __launch_bounds__(ST) void route_stats_kernel(const float* psum, cons
 #pragma unroll
     for (int i = 0; i < SKEEP; ++i) hv[i] = 0;
   }
-  sp[tid] = s;
-  sc[tid] = c;
-  pc[tid] = c;
-  __syncthreads();
-  for (int half = nparts / 2; half >= 1; half >>= 1) {
-    if (part < half) {
-      sp[tid] += sp[tid + half * se];
-      sc[tid] += sc[tid + half * se];
-    }
-    __syncthreads();
+  // the wave's totals over its parts (lanes of one expert are se apart) and
+  // the inclusive prefix of the counts over them
+  double ts = s;
+  int tc = c, inc = c;
+  for (int off = se; off < 64; off <<= 1) {
+    ts += __shfl_xor(ts, off);
+    tc += __shfl_xor(tc, off);
+    const int v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
   }
+  if (lane < se) {
+    wsum[wave][el] = ts;
+    wcnt[wave][el] = tc;
+  }
+  __syncthreads();
   int kv = 0;
   double pr = 0.0;
-  if (part == 0 && ex) {
-    const int64_t cnt = sc[el];
-    const double pe = sp[el] / static_cast<double>(T);
+  if (wave == 0 && lane < se && ex) {            // (part 0)
+    double st = 0.0;
+    int64_t cnt = 0;
+    for (int w = 0; w < nw; ++w) {
+      st += wsum[w][el];
+      cnt += wcnt[w][el];
+    }
+    const double pe = st / static_cast<double>(T);
     const double fe = static_cast<double>(cnt) / (static_cast<double>(T) * k);
     counts[e] = static_cast<int32_t>(cnt);
     kv = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
@@ -837,90 +854,81 @@ __global__ __launch_bounds__(ST) void route_stats_kernel(const float* psum, cons
     if (f) f[e] = static_cast<float>(fe);
     prod[e] = pr;
   }
-  if (base) {
-    // exclusive prefix of the part counts over parts (Hillis-Steele, then shift)
-    for (int off = 1; off < nparts; off <<= 1) {
-      const int v = part >= off ? pc[tid - off * se] : 0;
-      __syncthreads();
-      pc[tid] += v;
-      __syncthreads();
+  if (base && ex) {
+    int run = inc - c;                           // earlier parts of this wave, then earlier waves
+    for (int w = 0; w < wave; ++w) run += wcnt[w][el];
+#pragma unroll
+    for (int i = 0; i < SKEEP; ++i) {
+      if (b0 + i < b1) {
+        base[static_cast<int64_t>(b0 + i) * N + e] = run;
+        run += hv[i];
+      }
     }
-    if (ex) {
-      int run = part > 0 ? pc[tid - se] : 0;
+    for (int bb = b0 + SKEEP; bb < b1; bb += SKEEP) {
+      int hb[SKEEP];
+#pragma unroll
+      for (int i = 0; i < SKEEP; ++i) hb[i] = bb + i < b1 ? hist[static_cast<int64_t>(bb + i) * N + e] : 0;
 #pragma unroll
       for (int i = 0; i < SKEEP; ++i) {
-        if (b0 + i < b1) {
-          base[static_cast<int64_t>(b0 + i) * N + e] = run;
-          run += hv[i];
-        }
-      }
-      for (int bb = b0 + SKEEP; bb < b1; bb += SKEEP) {
-        int hb[SKEEP];
-#pragma unroll
-        for (int i = 0; i < SKEEP; ++i) hb[i] = bb + i < b1 ? hist[static_cast<int64_t>(bb + i) * N + e] : 0;
-#pragma unroll
-        for (int i = 0; i < SKEEP; ++i) {
-          if (bb + i < b1) {
-            base[static_cast<int64_t>(bb + i) * N + e] = run;
-            run += hb[i];
-          }
+        if (bb + i < b1) {
+          base[static_cast<int64_t>(bb + i) * N + e] = run;
+          run += hb[i];
         }
       }
     }
   }
-  // The scan over the experts, by the last workgroup to arrive: each writer's
-  // stores are made visible at device scope before its workgroup counts
-  // itself, and the last one acquires them (a single workgroup has them in
-  // its own registers).  Which workgroup is last does not change the result
-  // (fixed orders over the experts).
-  if (gridDim.x > 1) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid == 0)
-      is_last = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-                static_cast<int>(gridDim.x) - 1;
-    __syncthreads();
-  } else {
-    is_last = 1;
-  }
-  if (is_last) {
-    int NP = 1;
-    while (NP < N) NP <<= 1;
-    if (gridDim.x > 1) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      kv = tid < N ? __hip_atomic_load(kept + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-      pr = tid < N ? __hip_atomic_load(prod + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
-    } else {
-      // thread el of part 0 holds expert el; move it to thread e
-      __syncthreads();
-      if (part == 0) {
-        sc[el] = kv;
-        sp[el] = pr;
+  // The scan over the experts (fixed orders): the exclusive scan of the kept
+  // counts into offsets and L_aux = alpha N sum f p.
+  if (gridDim.x == 1) {
+    // one workgroup, N <= se <= 8: wave 0's lanes e < N hold expert e
+    if (wave == 0) {
+      int ki = kv;
+      double tp = pr;
+      for (int off = 1; off < 8; off <<= 1) {
+        const int v = __shfl_up(ki, off);
+        if (lane >= off) ki += v;
+        tp += __shfl_xor(tp, off);
       }
-      __syncthreads();
-      kv = tid < N ? sc[tid] : 0;
-      pr = tid < N ? sp[tid] : 0.0;
+      if (offsets && lane < N) {
+        offsets[lane] = ki - kv;
+        if (lane == N - 1) offsets[N] = ki;
+      }
+      if (l_aux && lane == 0) l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * tp);
     }
-    __syncthreads();                             // (sp and sc: the part sums are no longer needed)
-    sc[tid] = kv;
-    sp[tid] = pr;
-    __syncthreads();
-    // the exclusive scan of the kept counts (Hillis-Steele) and L_aux = alpha N sum f p (a tree)
-    for (int off = 1; off < NP; off <<= 1) {
-      const int v = tid >= off ? sc[tid - off] : 0;
-      __syncthreads();
-      sc[tid] += v;
-      __syncthreads();
-    }
-    for (int half = NP / 2; half >= 1; half >>= 1) {
-      if (tid < half) sp[tid] += sp[tid + half];
-      __syncthreads();
-    }
-    if (offsets && tid < N) {
-      offsets[tid] = sc[tid] - kv;
-      if (tid == N - 1) offsets[N] = sc[tid];
-    }
-    if (l_aux && tid == 0) l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * sp[0]);
+    return;
+  }
+  // Several workgroups: the last to arrive does it.  Each writer's stores are
+  // made visible at device scope before its workgroup counts itself, and the
+  // last one acquires them; which workgroup is last does not change the result.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  kv = tid < N ? __hip_atomic_load(kept + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  pr = tid < N ? __hip_atomic_load(prod + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+  int ki = kv;
+  double tp = pr;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(ki, off);
+    if (lane >= off) ki += v;
+    tp += __shfl_xor(tp, off);
+  }
+  if (lane == 63) xk[wave] = ki;
+  if (lane == 0) xp[wave] = tp;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) ki += xk[w];
+  if (offsets && tid < N) {
+    offsets[tid] = ki - kv;
+    if (tid == N - 1) offsets[N] = ki;
+  }
+  if (l_aux && tid == 0) {
+    double acc = 0.0;
+    for (int w = 0; w < nw; ++w) acc += xp[w];
+    l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
   }
 }
 
@@ -997,7 +1005,8 @@ hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const in
                                  int32_t* done, hipStream_t st) {
   const int nb = static_cast<int>(ceil_div(s.T, TM));
   const int se = stats_experts_per_block(s.N);
-  hipLaunchKernelGGL(route_stats_kernel, dim3(static_cast<unsigned>(ceil_div(s.N, se))), dim3(ST), 0, st,
+  const int blocks = static_cast<int>(ceil_div(s.N, se));
+  hipLaunchKernelGGL(route_stats_kernel, dim3(blocks), dim3(blocks == 1 ? ST1 : ST), 0, st,
                      psum, hist, nb, s.T, s.N, s.k, s.capacity, counts, kept, p, f, prod, base, s.alpha,
                      offsets, l_aux, done, se);
   return hipGetLastError();
