@@ -855,10 +855,12 @@ hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
 }
 
 // Tile height: 256 rows read each weight n-tile once per 256 rows of an
-// expert, 128 rows waste less on short segments.  With fp8 activations the A
-// rows cost half as much, so the taller tile pays from shorter segments
-// (measured: DeepSeek-V3-shaped gate/up, ~128 rows per expert, 4.18 -> 3.96
-// ms; with bf16 activations the same change loses 6%).
+// expert, 128 rows waste less on short segments.  The taller tile pays from
+// this many rows per expert on average: 96 with fp8 activations (A rows cost
+// half as much; measured at the DeepSeek-V3-shaped gate/up, ~128 rows per
+// expert, 4.18 -> 3.96 ms) and for the down GEMM (1.84 -> 1.80 ms there), 384
+// for the gate/up GEMM with bf16 activations (the change to 96 lost 6%).
+constexpr int kBm256RowsFp8 = 96, kBm256RowsUp = 384, kBm256RowsDown = 96;
 int split_slots() { return (device_cu_count() / 8) * 8; }
 
 // Few tiles (a decode step, a small dense call): at most S / 2 tiles of 128
@@ -872,10 +874,10 @@ bool skinny(int64_t rows, int n_seg, int64_t nt) {
   return 2 * mt * nt <= split_slots();
 }
 
-int pick_bm(int64_t rows, int n_seg, bool fp8_a, int64_t nt, bool split) {
+int pick_bm(int64_t rows, int n_seg, int min_avg_256, int64_t nt, bool split) {
   if (split && skinny(rows, n_seg, nt)) return 128;
   const int64_t avg = n_seg > 0 ? rows / n_seg : rows;
-  return avg >= (fp8_a ? 96 : 384) ? 256 : 128;
+  return avg >= min_avg_256 ? 256 : 128;
 }
 
 
@@ -937,15 +939,15 @@ size_t gemm_split_bytes(const moe_shape& s) {
   const int64_t nt_down = ceil_div(s.d, 256);
   const bool fp8 = s.buf_dtype == MOE_FP8_E4M3;
   int64_t tiles = 0;
-  auto add = [&](int64_t r, int n_seg, bool f8, int64_t nt) {
-    if (skinny(r, n_seg, nt) || pick_bm(r, n_seg, f8, nt, false) == 256)
+  auto add = [&](int64_t r, int n_seg, int min_avg_256, int64_t nt) {
+    if (skinny(r, n_seg, nt) || pick_bm(r, n_seg, min_avg_256, nt, false) == 256)
       tiles = std::max(tiles, (ceil_div(r, 128) + (n_seg > 1 ? n_seg : 0)) * nt);
   };
-  add(rows, s.N, fp8, nt_up);
-  add(rows, s.N, false, nt_down);
+  add(rows, s.N, fp8 ? kBm256RowsFp8 : kBm256RowsUp, nt_up);
+  add(rows, s.N, kBm256RowsDown, nt_down);
   if (s.has_shared) {
-    add(s.T, 1, false, nt_up);
-    add(s.T, 1, false, nt_down);
+    add(s.T, 1, kBm256RowsUp, nt_up);
+    add(s.T, 1, kBm256RowsDown, nt_down);
   }
   if (tiles == 0) return 0;
   const int64_t units = std::min<int64_t>(split_slots(), kSplitKMax * tiles);
@@ -1022,7 +1024,7 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
   const bool gated = s.act == MOE_ACT_SWIGLU;
   g.nt = static_cast<int>(gated ? ceil_div(s.F, 128) : ceil_div(s.F, 256));
   const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8, g.nt, sk);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8 ? kBm256RowsFp8 : kBm256RowsUp, g.nt, sk);
   if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
   if (gated) return fp8 ? dispatch_up<EPI_SWIGLU, true>(bm, g, rows, n_seg, dense, split, st)
                         : dispatch_up<EPI_SWIGLU, false>(bm, g, rows, n_seg, dense, split, st);
@@ -1058,7 +1060,7 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.out = static_cast<uint16_t*>(out);
   g.nt = static_cast<int>(ceil_div(s.d, 256));
   const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, false, g.nt, sk);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, kBm256RowsDown, g.nt, sk);
   if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
   return dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, split, st);
 }

@@ -534,7 +534,7 @@ __device__ void select_lanes(const RouteArgs& a, const float* lt, int ldl, int64
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(RW * 64) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
   // on the other paths, it holds the d-split partials [KS][TM][NP] (16 KB) and
   // the logit tile [TM][kMaxExperts + 1].  Sized at launch (route_lds_bytes):
