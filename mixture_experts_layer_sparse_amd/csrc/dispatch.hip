@@ -168,7 +168,7 @@ struct PlanArgs {
 };
 
 __device__ __forceinline__ void plan_token(const PlanArgs& pa, int64_t T, int k, int64_t t, int lane,
-                                           int pj[kMaxTopK]) {
+                                           int pj[kMaxTopK], bool writer = true) {
   constexpr int TM = kRouteTile;
   const int64_t tile = t / TM, t0 = tile * TM;
   const int before = static_cast<int>(t - t0) * k;        // idx entries of earlier tokens in the tile
@@ -186,7 +186,7 @@ __device__ __forceinline__ void plan_token(const PlanArgs& pa, int64_t T, int k,
         if (pa.cap <= 0 || r < pa.cap) p = pa.offsets[e] + r;
       }
       pj[j] = p;
-      if (lane == 0) {
+      if (writer && lane == 0) {
         pa.pos[t * k + j] = p;
         pa.drop[t * k + j] = p < 0 ? 1 : 0;
         if (p >= 0) pa.src[p] = static_cast<int32_t>(t);
@@ -252,46 +252,59 @@ __device__ __forceinline__ float absmax8(uint4 v) {
   return m;
 }
 
-// fp8 dispatch: one wave per token.  Rows up to 64*MAXC chunks of 8 bf16 stay in
-// registers; longer rows are read twice.
-template <int MAXC, bool PLANNED>
+// fp8 dispatch: WPT waves per token (4 when the call has few tokens, so that a
+// token's row is read and written by 256 lanes instead of 64: one wave took
+// 13.5 us for a 7168-wide row).  Rows up to 64*WPT*MAXC chunks of 8 bf16 stay
+// in registers; longer rows are read twice.
+template <int MAXC, bool PLANNED, int WPT>
 __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restrict__ x, int64_t T,
                                                        int k, int d,
                                                        const int32_t* __restrict__ pos,
                                                        uint8_t* __restrict__ xp,
                                                        float* __restrict__ row_scale, PlanArgs pa) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  static_assert(4 % WPT == 0, "a token's waves share one workgroup");
+  __shared__ float wmax[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = wave % WPT;                     // this wave's part of the token's row
+  const int tl = sub * 64 + lane;                 // lane within the token
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (4 / WPT) + wave / WPT;
+  if (t >= T) return;                             // (whole tokens: the waves of one token agree)
   int pj[kMaxTopK];
   if (PLANNED) {
-    plan_token(pa, T, k, t, lane, pj);
+    plan_token(pa, T, k, t, lane, pj, sub == 0);
   } else {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
   }
   const int nch = d / 8;
   const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
-  const bool in_regs = nch <= 64 * MAXC;
+  const bool in_regs = nch <= 64 * WPT * MAXC;
   uint4 buf[MAXC];
   float amax = 0.f;
   if (in_regs) {
 #pragma unroll
     for (int q = 0; q < MAXC; ++q) {
-      int c = lane + 64 * q;
+      int c = tl + 64 * WPT * q;
       buf[q] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
       amax = fmaxf(amax, absmax8(buf[q]));
     }
   } else {
-    for (int c = lane; c < nch; c += 64) amax = fmaxf(amax, absmax8(xr[c]));
+    for (int c = tl; c < nch; c += 64 * WPT) amax = fmaxf(amax, absmax8(xr[c]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (WPT > 1) {
+    // (a max is exact in any order)
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) amax = fmaxf(amax, wmax[wave - sub + w]);
+  }
   // rows below 2^-100 (zero included) count as zero rows: 448/amax would overflow
   const bool tiny = amax < 0x1p-100f;
   const float inv = tiny ? 1.f : __fdiv_rn(448.0f, amax);
   const float scale = tiny ? 1.f : __fdiv_rn(amax, 448.0f);
-  if (lane == 0) {
+  if (tl == 0) {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
       if (pj[j] >= 0) row_scale[pj[j]] = scale;
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
   if (in_regs) {
 #pragma unroll
     for (int q = 0; q < MAXC; ++q) {
-      int c = lane + 64 * q;
+      int c = tl + 64 * WPT * q;
       if (c < nch) {
         uint2 code = quant8(buf[q], inv);
 #pragma unroll
@@ -308,7 +321,7 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
       }
     }
   } else {
-    for (int c = lane; c < nch; c += 64) {
+    for (int c = tl; c < nch; c += 64 * WPT) {
       uint2 code = quant8(xr[c], inv);
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j)
@@ -341,14 +354,23 @@ hipError_t launch_copy(const moe_shape& s, const void* x, const int32_t* pos, vo
   dim3 grid(static_cast<unsigned>(ceil_div(s.T, 4)));
   const PlanArgs none{};
   if (s.buf_dtype == MOE_FP8_E4M3) {
-    if (pa)
-      hipLaunchKernelGGL((disp_fp8_kernel<16, true>), grid, dim3(256), 0, st,
-                         static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
-                         static_cast<uint8_t*>(x_perm), row_scale, *pa);
-    else
-      hipLaunchKernelGGL((disp_fp8_kernel<16, false>), grid, dim3(256), 0, st,
-                         static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
-                         static_cast<uint8_t*>(x_perm), row_scale, none);
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint8_t* xp = static_cast<uint8_t*>(x_perm);
+    if (s.T < 512) {                              // few tokens: four waves per token
+      const dim3 g1(static_cast<unsigned>(s.T));
+      if (pa)
+        hipLaunchKernelGGL((disp_fp8_kernel<4, true, 4>), g1, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
+                           row_scale, *pa);
+      else
+        hipLaunchKernelGGL((disp_fp8_kernel<4, false, 4>), g1, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
+                           row_scale, none);
+    } else if (pa) {
+      hipLaunchKernelGGL((disp_fp8_kernel<16, true, 1>), grid, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
+                         row_scale, *pa);
+    } else {
+      hipLaunchKernelGGL((disp_fp8_kernel<16, false, 1>), grid, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
+                         row_scale, none);
+    }
   } else {
     int es = s.dtype == MOE_BF16 ? 2 : 4;
     if (pa)

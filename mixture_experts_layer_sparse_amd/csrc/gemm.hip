@@ -654,22 +654,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     }
 
     if constexpr (SPLITK) {
-      // the raw float32 partial tile, rows and columns in tile order.  The lane
-      // index is made opaque here so that the compiler computes the store
-      // offsets now instead of keeping all of them live across the tile loop
-      // (which spills).
+      // the raw float32 partial tile, rows and columns in tile order; rows past
+      // the segment end are left out (the reduction never reads them; a
+      // decode step's one-row tiles would otherwise write 128x the bytes).
+      // The lane index is made opaque here so that the compiler computes the
+      // store offsets now instead of keeping all of them live across the tile
+      // loop (which spills).
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      float* pt = g.part + static_cast<int64_t>(eunit) * (BM * BN) +
-                  (wm * WM + 4 * (ln >> 5)) * BN + wn * WN + (ln & 31);
+      const int live = erow_end - erow0 - wm * WM;          // rows of this wave's part in the segment
+      const int lrow = 4 * (ln >> 5);
+      float* pt = g.part + static_cast<int64_t>(eunit) * (BM * BN) + (wm * WM + lrow) * BN + wn * WN + (ln & 31);
 #pragma unroll
-      for (int i = 0; i < TMI; ++i)
+      for (int i = 0; i < TMI; ++i) {
+        if (i * 32 < live) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = i * 32 + 8 * (r >> 2) + (r & 3);
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + 8 * (r >> 2) + (r & 3);
+            if (lr + lrow < live) {
 #pragma unroll
-          for (int j = 0; j < TNI; ++j) pt[lr * BN + j * 32] = acc[i][j][r];
+              for (int j = 0; j < TNI; ++j) pt[lr * BN + j * 32] = acc[i][j][r];
+            }
+          }
         }
+      }
       if (!more) break;
       continue;
     }
@@ -910,13 +918,24 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, 
     return hipGetLastError();
   }
   // 128-row tiles; with scratch (given only when the list is expected to hold
-  // at most S / 2 tiles) every tile is split along K over all CUs
+  // at most S / 2 tiles) every tile is split along K over all CUs.  The
+  // whole-tile launch takes the list when it turns out longer (the kernel
+  // counts it); it is left out when the list is short for certain: every
+  // m-tile holds a row and every nonempty segment adds at most one partial
+  // m-tile, so there are at most min(rows, (rows + 127 s) / 128) of them, s =
+  // min(rows, segments) (an empty launch still costs ~4.5 us).
   const int mtu = static_cast<int>(ceil_div(rows, 128)) + (dense ? 0 : n_seg);
   g.split_slots = split != nullptr ? split_slots() : 0;
   if (2 + 3 * (g.split_slots / 2) > static_cast<int>(kSplitMetaBytes / 4)) split = nullptr, g.split_slots = 0;
   g.split_k_max = split != nullptr ? kSplitKMax : 0;
-  hipError_t err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
-  if (err != hipSuccess || split == nullptr) return err;
+  const int64_t segs = dense ? 1 : (rows < n_seg ? rows : n_seg);
+  const int64_t mt_most = dense ? ceil_div(rows, 128) : std::min<int64_t>(rows, (rows + 127 * segs) / 128);
+  const bool all_split = split != nullptr && 2 * mt_most * nt <= g.split_slots;
+  hipError_t err = hipSuccess;
+  if (!all_split) {
+    err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
+    if (err != hipSuccess || split == nullptr) return err;
+  }
   g.part_meta = static_cast<int32_t*>(split);
   g.part = reinterpret_cast<float*>(static_cast<char*>(split) + kSplitMetaBytes);
   err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true>(g, kSplitKMax * mtu * nt, st);

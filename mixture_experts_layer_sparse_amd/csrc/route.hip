@@ -33,7 +33,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = kRouteTile;
-constexpr int kRouteSplitMax = 8;      // d-ranges of the split logits at most
+constexpr int kRouteSplitMax = 16;     // K ranges of partial logits the router adds at most
+constexpr int kLogitsSplitMax = 8;     // d-ranges of the few-token split logits at most
 static_assert(kSplitKMax <= kRouteSplitMax, "the router adds every K range of the logits GEMM");
 
 struct RouteArgs {
@@ -955,7 +956,7 @@ int route_split_ranges(const moe_shape& s) {
   if (s.dtype != MOE_BF16 || s.T <= 0 || s.T >= 512 || s.d % 32 != 0) return 0;
   const int64_t units = ceil_div(s.T, 16) * ceil_div(s.N, 16);
   int64_t ks = ceil_div(512, units);
-  if (ks > kRouteSplitMax) ks = kRouteSplitMax;
+  if (ks > kLogitsSplitMax) ks = kLogitsSplitMax;
   if (ks > s.d / 32) ks = s.d / 32;
   return static_cast<int>(ks < 1 ? 1 : ks);
 }

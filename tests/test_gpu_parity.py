@@ -247,18 +247,20 @@ def test_fp8_quantiser_exhaustive_bf16_patterns():
         a_bits = si.f32_to_bf16_bits(anchor[ok].astype(np.float32))
         assert np.array_equal(bf16_to_f64(a_bits), anchor[ok])       # exact anchors
         rows.append(np.concatenate([vals[ok], a_bits[:, None]], axis=1))
-    x = np.concatenate(rows)
-    T, d = x.shape
-    wl = si.Workload("q", T=T, d=d, N=4, k=1, F=64, act="swiglu", dtype="bf16", buf="fp8")
-    s = M.shape_of(wl)
-    idx = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
-    dsp = M.dispatch(s, dev(x), idx)
-    torch.cuda.synchronize()
-    codes, scale = om.quantize_fp8_rows(x, "bf16")
-    got_c, got_s = host(dsp["x_perm"]), host(dsp["row_scale"])
-    bad = np.flatnonzero(np.any(got_c != codes, axis=1))
-    assert bad.size == 0, (bad[:5], x[bad[0]][:8], got_c[bad[0]][:8], codes[bad[0]][:8])
-    assert np.array_equal(got_s, scale)
+    x_all = np.concatenate(rows)
+    # all rows (one wave per token), then the first 300 (below 512 tokens: four waves per token)
+    for x in (x_all, x_all[:300]):
+        T, d = x.shape
+        wl = si.Workload("q", T=T, d=d, N=4, k=1, F=64, act="swiglu", dtype="bf16", buf="fp8")
+        s = M.shape_of(wl)
+        idx = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+        dsp = M.dispatch(s, dev(x), idx)
+        torch.cuda.synchronize()
+        codes, scale = om.quantize_fp8_rows(x, "bf16")
+        got_c, got_s = host(dsp["x_perm"]), host(dsp["row_scale"])
+        bad = np.flatnonzero(np.any(got_c != codes, axis=1))
+        assert bad.size == 0, (T, bad[:5], x[bad[0]][:8], got_c[bad[0]][:8], codes[bad[0]][:8])
+        assert np.array_equal(got_s, scale)
 
 
 def test_determinism_bitwise():
