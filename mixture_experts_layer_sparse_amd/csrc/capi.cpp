@@ -135,11 +135,11 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_g, const f
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
   float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
   double* prod = reinterpret_cast<double*>(base + L.route_prod);
-  int32_t* done = reinterpret_cast<int32_t*>(prod + s->N);
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, lpart, done, st);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux,
-                                               nullptr, nullptr, prod, done, st));
+  const moe::RouteStats rs{counts, kept_counts, p, f, l_aux, nullptr, nullptr, prod,
+                           reinterpret_cast<int32_t*>(prod + s->N)};
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, logits, psum, hist, lpart, rs, st);
+  if (e == hipSuccess && !moe::route_folds_stats(*s)) e = moe::launch_route_finalize(*s, psum, hist, rs, st);
+  return hip_status(e);
 }
 
 moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* offsets,
@@ -276,11 +276,10 @@ moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g
   int32_t* tbase = reinterpret_cast<int32_t*>(base + L.route_base);
   float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
   double* prod = reinterpret_cast<double*>(base + L.route_prod);
-  int32_t* done = reinterpret_cast<int32_t*>(prod + s->N);
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, done, st);
-  if (e == hipSuccess)
-    e = moe::launch_route_finalize(*s, psum, hist, counts, kept_counts, p, f, l_aux, offsets,
-                                   tbase, prod, done, st);
+  const moe::RouteStats rs{counts, kept_counts, p, f, l_aux, offsets, tbase, prod,
+                           reinterpret_cast<int32_t*>(prod + s->N)};
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, rs, st);
+  if (e == hipSuccess && !moe::route_folds_stats(*s)) e = moe::launch_route_finalize(*s, psum, hist, rs, st);
   if (e == hipSuccess)
     e = moe::launch_dispatch_copy_planned(*s, x, idx, tbase, offsets, pos, src, drop, x_perm,
                                           row_scale, st);

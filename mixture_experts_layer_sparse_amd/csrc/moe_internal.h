@@ -62,17 +62,30 @@ WsLayout ws_layout(const moe_shape& s);
 // over the experts, so that the router weights are read about once instead of
 // once per 16-token tile; the router then adds the partials in range order.
 int route_split_ranges(const moe_shape& s);
+// The load statistics over all router tiles.  p, f, l_aux may be null;
+// offsets (may be null): exclusive scan of the kept counts, N + 1 entries;
+// base (may be null): [nb_route][N] assignments to each expert in earlier
+// tiles; prod: [N] doubles of scratch (each expert's f p, for L_aux); done: a
+// counter in the workspace that the router kernel zeroes.
+struct RouteStats {
+  int32_t* counts;
+  int32_t* kept;
+  float* p;
+  float* f;
+  float* l_aux;
+  int32_t* offsets;
+  int32_t* base;
+  double* prod;
+  int32_t* done;
+};
+// With one router tile (T <= kRouteTile) the router kernel writes the
+// statistics itself; otherwise launch_route_finalize must follow launch_route.
+bool route_folds_stats(const moe_shape& s);
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        float* lpart, int32_t* done, hipStream_t st);
-// offsets (may be null): exclusive scan of the kept counts, N + 1 entries.
-// base (may be null): [nb_route][N] assignments to each expert in earlier tiles.
-// prod: [N] doubles of scratch (each expert's f p, for L_aux); done: the
-// counter that launch_route zeroed (the same workspace, launched before this).
+                        float* lpart, const RouteStats& rs, hipStream_t st);
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
-                                 int32_t* counts, int32_t* kept, float* p, float* f,
-                                 float* l_aux, int32_t* offsets, int32_t* base, double* prod,
-                                 int32_t* done, hipStream_t st);
+                                 const RouteStats& rs, hipStream_t st);
 
 hipError_t launch_dispatch_hist(const moe_shape& s, const int32_t* idx, int32_t* hist,
                                 hipStream_t st);

@@ -54,7 +54,10 @@ struct RouteArgs {
   int lld;
   const int32_t* lmeta; // non-null: the range count and the tile count come from this split-K header
   int gate;             // moe_gate
-  int32_t* done;        // arrival counter of the statistics workgroups, zeroed here
+  RouteStats rs;        // rs.done: arrival counter of the statistics workgroups, zeroed here
+  int fold;             // one tile: this kernel writes the final statistics (rs) itself
+  int cap;
+  float alpha;
 };
 
 // Key ordering "larger logit first, then lower expert index"; 0 = no candidate.
@@ -534,6 +537,69 @@ __device__ void select_lanes(const RouteArgs& a, const float* lt, int ldl, int64
   }
 }
 
+// The scan over the experts, by a whole workgroup (fixed orders): thread e <
+// N holds expert e's kept count and f p; writes the exclusive scan of the kept
+// counts into offsets and L_aux = alpha N sum f p.  A shuffle scan and a
+// butterfly inside each wave, then the waves in order through LDS (xk, xp:
+// one entry per wave).
+__device__ void scan_experts(int kv, double pr, int N, float alpha, int32_t* offsets, float* l_aux,
+                             int* xk, double* xp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (N + 63) / 64;
+  int ki = kv;
+  double tp = pr;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(ki, off);
+    if (lane >= off) ki += v;
+    tp += __shfl_xor(tp, off);
+  }
+  if (wave < nw && lane == 63) xk[wave] = ki;
+  if (wave < nw && lane == 0) xp[wave] = tp;
+  __syncthreads();
+  if (tid < N) {
+    for (int w = 0; w < wave; ++w) ki += xk[w];
+    if (offsets) {
+      offsets[tid] = ki - kv;
+      if (tid == N - 1) offsets[N] = ki;
+    }
+  }
+  if (l_aux && tid == 0) {
+    double acc = 0.0;
+    for (int w = 0; w < nw; ++w) acc += xp[w];
+    l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
+  }
+}
+
+// End of a router workgroup, every thread with e = threadIdx.x (sum: the
+// tile's p summed over its tokens, cnt: the tile's count, for e < N): the
+// tile's partials for the statistics kernel, or, when the call has only this
+// tile, the final statistics (the statistics kernel's formulas; no earlier
+// tiles, so every base is 0).
+__device__ void tile_stats(const RouteArgs& a, int e, float sum, int cnt, int* xk, double* xp) {
+  const int N = a.N;
+  if (!a.fold) {
+    if (e < N) {
+      a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
+      a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = cnt;
+    }
+    return;
+  }
+  int kv = 0;
+  double pr = 0.0;
+  if (e < N) {
+    const double pe = static_cast<double>(sum) / static_cast<double>(a.T);
+    const double fe = static_cast<double>(cnt) / (static_cast<double>(a.T) * a.k);
+    a.rs.counts[e] = cnt;
+    kv = a.cap > 0 ? (cnt < a.cap ? cnt : a.cap) : cnt;
+    a.rs.kept[e] = kv;
+    if (a.rs.p) a.rs.p[e] = static_cast<float>(pe);
+    if (a.rs.f) a.rs.f[e] = static_cast<float>(fe);
+    if (a.rs.base) a.rs.base[e] = 0;
+    pr = fe * pe;
+  }
+  scan_experts(kv, pr, N, a.alpha, a.rs.offsets, a.rs.l_aux, xk, xp);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
@@ -548,6 +614,9 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ float ps[RW][kMaxExperts];  // wave partial sums of p (large N)
   __shared__ float pl[TM][SMALL_N + 1];  // per-token p (small N)
   __shared__ int hl[kMaxExperts];
+  __shared__ int xk[RW];
+  __shared__ double xp[RW];
+  static_assert(RW * 64 >= kMaxExperts, "thread e ends expert e's statistics");
   const int ldl = kMaxExperts + 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = a.N, k = a.k;
@@ -555,7 +624,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 
   for (int e = threadIdx.x; e < kMaxExperts; e += RW * 64) hl[e] = 0;
   // (the statistics kernel runs after this one on the same stream)
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.done = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && !a.fold) *a.rs.done = 0;
   if (BF16) {
     if (a.lpart) {
       // range count and range stride: from the split-K header when the GEMM wrote the partials
@@ -581,13 +650,13 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (N <= SMALL_N && a.n_groups <= 1) {
     select_lanes(a, lt, ldl, t0, pl, hl);
     __syncthreads();
-    for (int e = threadIdx.x; e < N; e += RW * 64) {
-      float sum = 0.f;
+    const int e = threadIdx.x;
+    float sum = 0.f;
+    if (e < N) {
 #pragma unroll
       for (int m2 = 0; m2 < TM; ++m2) sum += pl[m2][e];
-      a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
-      a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
     }
+    tile_stats(a, e, sum, e < N ? hl[e] : 0, xk, xp);
     return;
   }
   if (N <= SMALL_N) {
@@ -601,12 +670,11 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < N; e += RW * 64) {
-      float sum = 0.f;
+    const int e = threadIdx.x;
+    float sum = 0.f;
+    if (e < N)
       for (int m2 = 0; m2 < TM; ++m2) sum += pl[m2][e];
-      a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
-      a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
-    }
+    tile_stats(a, e, sum, e < N ? hl[e] : 0, xk, xp);
     return;
   }
 
@@ -745,11 +813,12 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     if (e < N) ps[wave][e] = psr[i];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += RW * 64) {
+  {
+    const int e = threadIdx.x;
     float sum = 0.f;
-    for (int w = 0; w < RW; ++w) sum += ps[w][e];
-    a.psum[static_cast<int64_t>(blockIdx.x) * N + e] = sum;
-    a.hist[static_cast<int64_t>(blockIdx.x) * N + e] = hl[e];
+    if (e < N)
+      for (int w = 0; w < RW; ++w) sum += ps[w][e];
+    tile_stats(a, e, sum, e < N ? hl[e] : 0, xk, xp);
   }
 }
 
@@ -777,15 +846,18 @@ int stats_experts_per_block(int N) { return N <= 8 ? 8 : 4; }
 
 __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, const int32_t* hist,
                                                          int nb, int64_t T, int N, int k, int cap,
-                                                         int32_t* counts, int32_t* kept, float* p,
-                                                         float* f, double* prod, int32_t* base,
-                                                         float alpha, int32_t* offsets, float* l_aux,
-                                                         int32_t* done, int se) {
+                                                         float alpha, RouteStats rs, int se) {
+  int32_t* const counts = rs.counts;
+  int32_t* const kept = rs.kept;
+  float* const p = rs.p;
+  float* const f = rs.f;
+  double* const prod = rs.prod;
+  int32_t* const base = rs.base;
   static_assert(ST == kMaxExperts && ST1 >= ST, "the last workgroup scans all experts, one per thread");
   __shared__ double wsum[ST1 / 64][8];   // per-wave totals of p and counts, per expert (se <= 8)
   __shared__ int wcnt[ST1 / 64][8];
-  __shared__ int xk[ST / 64];            // last workgroup: per-wave totals over the experts
-  __shared__ double xp[ST / 64];
+  __shared__ int xk[ST1 / 64];           // the scan over the experts: per-wave totals
+  __shared__ double xp[ST1 / 64];
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = static_cast<int>(blockDim.x) >> 6;
@@ -881,21 +953,8 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
   // The scan over the experts (fixed orders): the exclusive scan of the kept
   // counts into offsets and L_aux = alpha N sum f p.
   if (gridDim.x == 1) {
-    // one workgroup, N <= se <= 8: wave 0's lanes e < N hold expert e
-    if (wave == 0) {
-      int ki = kv;
-      double tp = pr;
-      for (int off = 1; off < 8; off <<= 1) {
-        const int v = __shfl_up(ki, off);
-        if (lane >= off) ki += v;
-        tp += __shfl_xor(tp, off);
-      }
-      if (offsets && lane < N) {
-        offsets[lane] = ki - kv;
-        if (lane == N - 1) offsets[N] = ki;
-      }
-      if (l_aux && lane == 0) l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * tp);
-    }
+    // one workgroup, N <= se <= 8: wave 0's lanes e < N already hold expert e
+    scan_experts(kv, pr, N, alpha, rs.offsets, rs.l_aux, xk, xp);
     return;
   }
   // Several workgroups: the last to arrive does it.  Each writer's stores are
@@ -904,33 +963,14 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0)
-    is_last = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+    is_last = __hip_atomic_fetch_add(rs.done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
               static_cast<int>(gridDim.x) - 1;
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   kv = tid < N ? __hip_atomic_load(kept + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
   pr = tid < N ? __hip_atomic_load(prod + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
-  int ki = kv;
-  double tp = pr;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(ki, off);
-    if (lane >= off) ki += v;
-    tp += __shfl_xor(tp, off);
-  }
-  if (lane == 63) xk[wave] = ki;
-  if (lane == 0) xp[wave] = tp;
-  __syncthreads();
-  for (int w = 0; w < wave; ++w) ki += xk[w];
-  if (offsets && tid < N) {
-    offsets[tid] = ki - kv;
-    if (tid == N - 1) offsets[N] = ki;
-  }
-  if (l_aux && tid == 0) {
-    double acc = 0.0;
-    for (int w = 0; w < nw; ++w) acc += xp[w];
-    l_aux[0] = static_cast<float>(static_cast<double>(alpha) * N * acc);
-  }
+  scan_experts(kv, pr, N, alpha, rs.offsets, rs.l_aux, xk, xp);
 }
 
 }  // namespace
@@ -961,13 +1001,15 @@ int route_split_ranges(const moe_shape& s) {
   return static_cast<int>(ks < 1 ? 1 : ks);
 }
 
+bool route_folds_stats(const moe_shape& s) { return s.T <= TM; }
+
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        float* lpart, int32_t* done, hipStream_t st) {
+                        float* lpart, const RouteStats& rs, hipStream_t st) {
   const int ks = route_split_ranges(s);
   RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
               s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks,
-              s.T * s.N, s.N, nullptr, s.gate, done};
+              s.T * s.N, s.N, nullptr, s.gate, rs, route_folds_stats(s) ? 1 : 0, s.capacity, s.alpha};
   if (router_gemm(s)) {
     const hipError_t e = launch_router_logits(s, x, wg, lpart, st);
     if (e != hipSuccess) return e;
@@ -1001,15 +1043,12 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
 }
 
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
-                                 int32_t* counts, int32_t* kept, float* p, float* f,
-                                 float* l_aux, int32_t* offsets, int32_t* base, double* prod,
-                                 int32_t* done, hipStream_t st) {
+                                 const RouteStats& rs, hipStream_t st) {
   const int nb = static_cast<int>(ceil_div(s.T, TM));
   const int se = stats_experts_per_block(s.N);
   const int blocks = static_cast<int>(ceil_div(s.N, se));
   hipLaunchKernelGGL(route_stats_kernel, dim3(blocks), dim3(blocks == 1 ? ST1 : ST), 0, st,
-                     psum, hist, nb, s.T, s.N, s.k, s.capacity, counts, kept, p, f, prod, base, s.alpha,
-                     offsets, l_aux, done, se);
+                     psum, hist, nb, s.T, s.N, s.k, s.capacity, s.alpha, rs, se);
   return hipGetLastError();
 }
 

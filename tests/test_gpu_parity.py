@@ -220,6 +220,23 @@ def test_router_logits_gemm(name):
     _run_and_check(wl, y_tokens=sample_tokens(wl.T, 256) if wl.T > 4096 else None)
 
 
+# At most 16 tokens (one router tile) the router kernel writes the load
+# statistics itself; 17 tokens take the statistics kernel again.
+ONE_TILE_CASES = {
+    "t10_groups_capacity": dict(T=10, d=256, N=32, k=3, F=128, n_groups=4, topk_groups=2, capacity=1),
+    "t16_wave_bias": dict(T=16, d=512, N=64, k=4, F=128, bias="zipf2"),
+    "t17_two_tiles": dict(T=17, d=512, N=64, k=4, F=128, capacity=2),
+}
+
+
+@pytest.mark.parametrize("name", list(ONE_TILE_CASES))
+def test_one_router_tile(name):
+    wl = si.Workload("ot_" + name, **ONE_TILE_CASES[name])
+    gpu, _ = _run_and_check(wl)
+    if wl.capacity:
+        assert gpu["drop"].sum() > 0
+
+
 def test_groups_k_le_group_span():
     wl = si.small("deepseek_v3", T=333, N=32, k=3, n_groups=4, topk_groups=1, F=128)
     _run_and_check(wl)
@@ -282,6 +299,7 @@ FORWARD_CASES = {
     "deepseek_fp8_groups_shared": lambda: si.small("deepseek_v3"),
     "dbrx_skew": lambda: si.small("dbrx"),
     "single_token": lambda: si.small("mixtral", T=1),
+    "one_tile_groups_capacity": lambda: si.Workload("otc", **ONE_TILE_CASES["t10_groups_capacity"]),
     "many_tiles_capacity": lambda: si.Workload("mbf", T=20011, d=64, N=16, k=2, F=128,
                                                act="swiglu", dtype="bf16", buf="bf16",
                                                capacity=2300),
