@@ -34,7 +34,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = kRouteTile;
 constexpr int kRouteSplitMax = 16;     // K ranges of partial logits the router adds at most
-constexpr int kLogitsSplitMax = 8;     // d-ranges of the few-token split logits at most
+constexpr int kLogitsSplitMax = 16;    // d-ranges of the few-token split logits at most
 static_assert(kSplitKMax <= kRouteSplitMax, "the router adds every K range of the logits GEMM");
 
 struct RouteArgs {
@@ -76,24 +76,80 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
+// Cross-lane steps on the DPP network (VALU, a few cycles each) instead of
+// LDS permutes (a hundred or more cycles each, and the selection is a long
+// chain of them): within each row of 16 lanes, swaps of lanes 1 and 2 apart
+// (quad_perm) and the half-row and row mirrors, which pair every lane with one
+// in the other half (8 or 16 lanes); the four rows then meet through lanes 0,
+// 16, 32 and 48 (readlane).  Max, sum and the top-2 merge are symmetric in the
+// pair, so every lane of a run ends with the same value.  Every lane must be
+// active.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ float lanef(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ uint64_t lane64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// All-reduces over aligned runs of `width` lanes (a power of two up to 64).
+__device__ __forceinline__ float run_max_f(float v, int width) {
+  if (width > 1) v = fmaxf(v, dppf<kDppXor1>(v));
+  if (width > 2) v = fmaxf(v, dppf<kDppXor2>(v));
+  if (width > 4) v = fmaxf(v, dppf<kDppHalfMirror>(v));
+  if (width > 8) v = fmaxf(v, dppf<kDppMirror>(v));
+  if (width > 16) v = fmaxf(v, __shfl_xor(v, 16));
+  if (width > 32) v = fmaxf(v, __shfl_xor(v, 32));
   return v;
+}
+__device__ __forceinline__ float run_sum_f(float v, int width) {
+  if (width > 1) v += dppf<kDppXor1>(v);
+  if (width > 2) v += dppf<kDppXor2>(v);
+  if (width > 4) v += dppf<kDppHalfMirror>(v);
+  if (width > 8) v += dppf<kDppMirror>(v);
+  if (width > 16) v += __shfl_xor(v, 16);
+  if (width > 32) v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ uint64_t run_max_u64(uint64_t v, int width) {
+  if (width > 1) v = umax64(v, dpp64<kDppXor1>(v));
+  if (width > 2) v = umax64(v, dpp64<kDppXor2>(v));
+  if (width > 4) v = umax64(v, dpp64<kDppHalfMirror>(v));
+  if (width > 8) v = umax64(v, dpp64<kDppMirror>(v));
+  if (width > 16) v = umax64(v, __shfl_xor(v, 16));
+  if (width > 32) v = umax64(v, __shfl_xor(v, 32));
+  return v;
+}
+// Whole wave: rows by DPP, then the four row results through readlane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = run_max_u64(v, 16);
+  return umax64(umax64(lane64(v, 0), lane64(v, 16)), umax64(lane64(v, 32), lane64(v, 48)));
 }
 __device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = run_max_f(v, 16);
+  return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
 }
-// Butterfly sum: every lane ends with the same value (a + b == b + a exactly).
 __device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v = run_sum_f(v, 16);
+  return (lanef(v, 0) + lanef(v, 16)) + (lanef(v, 32) + lanef(v, 48));
 }
 
 constexpr int RW = 8;                  // waves per router workgroup
@@ -467,25 +523,6 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
   }
 }
 
-// Butterflies over aligned runs of `width` lanes (a power of two, at most
-// 32): every lane of the run ends with the run's maximum / sum (a + b == b + a
-// exactly, so all lanes agree).
-__device__ __forceinline__ float run_max_f(float v, int width) {
-  for (int off = 1; off < width; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ float run_sum_f(float v, int width) {
-  for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
-__device__ __forceinline__ uint64_t run_max_u64(uint64_t v, int width) {
-  for (int off = 1; off < width; off <<= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // Selection for N <= 32 experts without a group limit, all tokens of the tile
 // at once: token m owns the NP lanes m * NP .. m * NP + NP - 1 (NP = N rounded
 // up to a power of two, so a token's lanes never straddle a wave), lane e of
@@ -703,8 +740,9 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       zs += z[i];
     }
     zs = wave_sum_f(zs);
+    const float rzs = 1.0f / zs;                  // (one division per token; p is a float32 mean)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) psr[i] += z[i] / zs;
+    for (int i = 0; i < 4; ++i) psr[i] += z[i] * rzs;
 
     // group limit: lane g scores group g by the sum of its gsk largest logits
     uint64_t gmask = ~0ull;
@@ -717,11 +755,16 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float t1 = v[i], t2 = -INFINITY;
-          for (int off = 1; off < gsz; off <<= 1) {
-            const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+          auto merge = [&](float o1, float o2) {
             t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
             t1 = fmaxf(t1, o1);
-          }
+          };
+          if (gsz > 1) merge(dppf<kDppXor1>(t1), dppf<kDppXor1>(t2));
+          if (gsz > 2) merge(dppf<kDppXor2>(t1), dppf<kDppXor2>(t2));
+          if (gsz > 4) merge(dppf<kDppHalfMirror>(t1), dppf<kDppHalfMirror>(t2));
+          if (gsz > 8) merge(dppf<kDppMirror>(t1), dppf<kDppMirror>(t2));
+          if (gsz > 16) merge(__shfl_xor(t1, 16), __shfl_xor(t2, 16));
+          if (gsz > 32) merge(__shfl_xor(t1, 32), __shfl_xor(t2, 32));
           gsv[i] = a.gsk == 1 ? t1 : t1 + t2;
         }
         // lane g < G fetches group g's score from the group's first lane
@@ -755,39 +798,35 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       uint64_t gkey = lane < G ? sel_key(gs, lane) : 0ull;
       gmask = 0ull;
       for (int q = 0; q < a.topk_groups; ++q) {
-        const uint64_t best = wave_max_u64(gkey);
+        // (up to 16 groups all sit in lanes 0-15: one row's reduction)
+        const uint64_t best = G <= 16 ? lane64(run_max_u64(gkey, 16), 0) : wave_max_u64(gkey);
         int g = key_index(best);
         g = g < G ? g : G - 1;
         gmask |= 1ull << g;
         if (lane == g) gkey = 0ull;
       }
     }
-    // top-k by repeated wave max over (logit, ~index)
-    bool cand[4];
+    // top-k by repeated wave max over keys (logit, ~index), built once; the
+    // winner's key (unique: it holds the index) is cleared after each round
+    uint64_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      cand[i] = ok[i] && ((gmask >> (e / gsz)) & 1ull);
+      key[i] = ok[i] && ((gmask >> (e / gsz)) & 1ull) ? sel_key(v[i], e) : 0ull;
     }
     int sel_e[kMaxTopK];
     float sel_v[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k) {
-        uint64_t kb = 0ull;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint64_t kk = cand[i] ? sel_key(v[i], lane + 64 * i) : 0ull;
-          kb = kk > kb ? kk : kb;
-        }
-        const uint64_t best = wave_max_u64(kb);
+        const uint64_t best = wave_max_u64(umax64(umax64(key[0], key[1]), umax64(key[2], key[3])));
         int e = key_index(best);
         e = e < N ? e : N - 1;                    // unreachable guard (k <= candidates)
         sel_e[j] = e;
         sel_v[j] = key_value(best);              // (the logit, with -0 read as +0)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (e == lane + 64 * i) cand[i] = false;
+          if (key[i] == best) key[i] = 0ull;
       }
     }
     // softmax over the k selected logits, summed in slot order
