@@ -26,7 +26,10 @@
  *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by
  *     the caller.  The library never allocates, frees, or keeps state between
  *     calls.  Scratch memory comes from the caller through `ws`/`ws_bytes`
- *     (size from moe_workspace_bytes).
+ *     (size from moe_workspace_bytes); its contents need no initialisation and
+ *     carry nothing from one call to the next.  Calls that may run at the same
+ *     time (on different streams) must use different workspaces: a call's
+ *     kernels communicate through it (partial sums, counters, split-K tiles).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues kernels on it: no host synchronisation, no device-to-host read.
  *     Outputs are valid once the stream has reached that point.
