@@ -13,7 +13,6 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
 constexpr int kRouteTile = 16;     // tokens per router workgroup
 constexpr int kDispatchBlock = 256;  // tokens per dispatch-plan block
-constexpr int kSplitK = 4;           // K ranges per tail tile of a split-K grouped GEMM tail
 constexpr int kSplitKMax = 16;       // K ranges per tile when a grouped GEMM has few tiles
 constexpr size_t kSplitMetaBytes = 4096;  // header of the split-K scratch (tile count, tile rows)
 // Router logits through the grouped GEMM: split-K partial tiles of this many
