@@ -1,7 +1,7 @@
 // Router: logits (skinny GEMM), group limit, top-k, sparse softmax and the
-// per-block load statistics, fused in one kernel; then the statistics over
-// all blocks (counts, f, p, the per-tile prefix) spread over the experts, and
-// one small workgroup for the scan over experts and L_aux.
+// per-tile load statistics, fused in one kernel; then the statistics over all
+// tiles (counts, f, p, the per-tile prefix, the offsets and L_aux) in a kernel
+// spread over the experts, or, with a single tile, in the router kernel itself.
 //
 // What it computes follows "moe communication costs" / "Router design" (logits
 // W_g x; the top-k entries pick the experts), "Part 5" / "1.1 The Router Kernel"
@@ -11,14 +11,16 @@
 // costs to train and serve" / "Limit how many machines a token touches".
 //
 // Design (differs from the page's one-thread-per-token kernel): a workgroup of
-// 8 waves owns 16 tokens.  For bf16 the logits come from 16x16x32 bf16 MFMAs
-// reading x and W_g straight from global memory (each x element is read once;
-// W_g is small and stays in L2); the waves split the experts and the d-loop and
-// their partial sums are added in a fixed order.  Selection: with at most 32
-// experts one lane handles one token, scanning experts in index order in
-// registers; with more, one wave handles one token with 64-bit wave
-// max-reductions on keys (logit, ~index).  Either way the result does not
-// depend on thread timing.
+// 8 waves owns 16 tokens.  For bf16 the logits come from 16x16x32 bf16 MFMAs:
+// x staged through LDS (each element read once), W_g fragments from L2; the
+// waves split the experts and the d-loop and their partial sums are added in a
+// fixed order.  With few tokens the logits are first computed as partials
+// spread over more waves, and for wide routers (many experts times a wide d)
+// as one dense split-K GEMM; the router then adds the partials in order.
+// Selection: with at most 32 experts a token's lanes hold one expert each (one
+// lane per token under a group limit); with more, one wave handles one token.
+// Both use maximum reductions on keys (logit, ~index), so equal logits go to
+// the lower index, and nothing depends on thread timing.
 #include "moe_internal.h"
 
 // k-steps of loads each wave issues before their MFMAs
