@@ -897,6 +897,7 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
   static_assert(ST == kMaxExperts && ST1 >= ST, "the last workgroup scans all experts, one per thread");
   __shared__ double wsum[ST1 / 64][8];   // per-wave totals of p and counts, per expert (se <= 8)
   __shared__ int wcnt[ST1 / 64][8];
+  __shared__ int wpre[ST1 / 64][8];      // counts of the expert in earlier waves
   __shared__ int xk[ST1 / 64];           // the scan over the experts: per-wave totals
   __shared__ double xp[ST1 / 64];
   __shared__ int is_last;
@@ -949,28 +950,46 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
     wcnt[wave][el] = tc;
   }
   __syncthreads();
+  // wave 0 combines the waves: lane (w, e) holds wave w's totals of expert e,
+  // 64 / se waves per pass; a shuffle scan gives each wave's prefix and a
+  // butterfly the pass total, the passes added in order (fixed orders)
   int kv = 0;
   double pr = 0.0;
-  if (wave == 0 && lane < se && ex) {            // (part 0)
+  if (wave == 0) {
+    const int per = 64 / se, wl = lane / se;
     double st = 0.0;
-    int64_t cnt = 0;
-    for (int w = 0; w < nw; ++w) {
-      st += wsum[w][el];
-      cnt += wcnt[w][el];
+    int cnt = 0;
+    for (int w0 = 0; w0 < nw; w0 += per) {
+      const int w = w0 + wl;
+      const double vs = w < nw ? wsum[w][el] : 0.0;
+      const int vc = w < nw ? wcnt[w][el] : 0;
+      int ic = vc, pc = vc;
+      double ps = vs;
+      for (int off = se; off < 64; off <<= 1) {
+        const int v = __shfl_up(ic, off);
+        if (lane >= off) ic += v;
+        ps += __shfl_xor(ps, off);
+        pc += __shfl_xor(pc, off);
+      }
+      if (w < nw) wpre[w][el] = cnt + ic - vc;
+      st += ps;
+      cnt += pc;
     }
-    const double pe = st / static_cast<double>(T);
-    const double fe = static_cast<double>(cnt) / (static_cast<double>(T) * k);
-    counts[e] = static_cast<int32_t>(cnt);
-    kv = cap > 0 ? static_cast<int32_t>(cnt < cap ? cnt : cap) : static_cast<int32_t>(cnt);
-    pr = fe * pe;
-    kept[e] = kv;
-    if (p) p[e] = static_cast<float>(pe);
-    if (f) f[e] = static_cast<float>(fe);
-    prod[e] = pr;
+    if (lane < se && ex) {                       // (part 0)
+      const double pe = st / static_cast<double>(T);
+      const double fe = static_cast<double>(cnt) / (static_cast<double>(T) * k);
+      counts[e] = cnt;
+      kv = cap > 0 ? (cnt < cap ? cnt : cap) : cnt;
+      pr = fe * pe;
+      kept[e] = kv;
+      if (p) p[e] = static_cast<float>(pe);
+      if (f) f[e] = static_cast<float>(fe);
+      prod[e] = pr;
+    }
   }
+  __syncthreads();
   if (base && ex) {
-    int run = inc - c;                           // earlier parts of this wave, then earlier waves
-    for (int w = 0; w < wave; ++w) run += wcnt[w][el];
+    int run = inc - c + wpre[wave][el];          // earlier parts of this wave, then earlier waves
 #pragma unroll
     for (int i = 0; i < SKEEP; ++i) {
       if (b0 + i < b1) {
