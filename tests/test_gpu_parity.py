@@ -226,6 +226,7 @@ ONE_TILE_CASES = {
     "t10_groups_capacity": dict(T=10, d=256, N=32, k=3, F=128, n_groups=4, topk_groups=2, capacity=1),
     "t16_wave_bias": dict(T=16, d=512, N=64, k=4, F=128, bias="zipf2"),
     "t17_two_tiles": dict(T=17, d=512, N=64, k=4, F=128, capacity=2),
+    "t5_f32": dict(T=5, d=64, N=8, k=2, F=128, act="silu", dtype="f32", buf="f32"),
 }
 
 
