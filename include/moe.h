@@ -115,7 +115,11 @@ typedef struct moe_shape {
  * shared expert).  Returns 0 for an invalid shape. */
 size_t moe_workspace_bytes(const moe_shape* s);
 
-/* Checks a shape; MOE_OK when every call supports it. */
+/* Checks a shape; MOE_OK when every call supports it.  MOE_ERR_ARG for sizes
+ * or fields out of their ranges (see moe_shape); MOE_ERR_UNSUPPORTED for valid
+ * combinations this build does not run: k or group_score_k above 8, an fp8
+ * dispatch buffer with float32 storage, T*k above INT32_MAX, and for bfloat16
+ * d or F not a multiple of 64 or one expert matrix (F*d*2 bytes) above 4 GiB. */
 moe_status moe_check_shape(const moe_shape* s);
 
 /* Router.  "moe communication costs" / "Router design" (logits W_g x, no noise at

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstdint>
 
 #include "moe_internal.h"
 
@@ -92,6 +93,10 @@ moe_status check_shape(const moe_shape* s) {
   // positions and row indices are int32
   if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (s->dtype == MOE_BF16 && (s->d % 64 != 0 || s->F % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  // the grouped GEMMs read each expert matrix through a buffer resource with a
+  // 32-bit byte range
+  if (s->dtype == MOE_BF16 && static_cast<int64_t>(s->F) * s->d * 2 > static_cast<int64_t>(UINT32_MAX))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -76,6 +76,9 @@ def test_shape_checks(M):
     assert M.check_shape(_s(M, dtype="f32", buf="fp8")) == M.MOE_ERR_UNSUPPORTED
     assert M.check_shape(_s(M, dtype="bf16", d=72)) == M.MOE_ERR_UNSUPPORTED
     assert M.check_shape(_s(M, N=16, k=9)) == M.MOE_ERR_UNSUPPORTED
+    # one bf16 expert matrix beyond the 32-bit byte range of a buffer resource
+    assert M.check_shape(_s(M, dtype="bf16", d=32768, F=65536)) == M.MOE_ERR_UNSUPPORTED
+    assert M.check_shape(_s(M, dtype="bf16", d=16384, F=65536)) == M.MOE_OK
     # the fallback drop mode needs the shared expert; the gate is one of two values
     assert M.check_shape(_s(M, drop="fallback")) == M.MOE_ERR_ARG
     assert M.check_shape(_s(M, drop="fallback", shared=True)) == M.MOE_OK
