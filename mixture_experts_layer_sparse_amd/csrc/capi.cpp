@@ -20,7 +20,7 @@ size_t elem_size(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); 
 WsLayout ws_layout(const moe_shape& s) {
   WsLayout L{};
   const size_t T = static_cast<size_t>(s.T), N = static_cast<size_t>(s.N);
-  const size_t nb_route = static_cast<size_t>(ceil_div(s.T, kRouteTile));
+  const size_t nb_route = static_cast<size_t>(ceil_div(s.T, kRouteTileMin));
   const size_t nb_disp = static_cast<size_t>(ceil_div(s.T, kDispatchBlock));
   size_t off = 0;
   L.route_psum = off;

@@ -165,11 +165,12 @@ struct PlanArgs {
   int32_t* src;
   uint8_t* drop;
   int N, cap;
+  int tile;                // tokens per router tile
 };
 
 __device__ __forceinline__ void plan_token(const PlanArgs& pa, int64_t T, int k, int64_t t, int lane,
                                            int pj[kMaxTopK], bool writer = true) {
-  constexpr int TM = kRouteTile;
+  const int TM = pa.tile;
   const int64_t tile = t / TM, t0 = tile * TM;
   const int before = static_cast<int>(t - t0) * k;        // idx entries of earlier tokens in the tile
   // lane l holds entries l and l + 64 of the tile (TM * k <= 128)
@@ -395,7 +396,7 @@ hipError_t launch_dispatch_copy_planned(const moe_shape& s, const void* x, const
                                         const int32_t* base, const int32_t* offsets,
                                         int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm,
                                         float* row_scale, hipStream_t st) {
-  const PlanArgs pa{idx, base, offsets, pos, src, drop, s.N, s.capacity};
+  const PlanArgs pa{idx, base, offsets, pos, src, drop, s.N, s.capacity, route_tile(s)};
   return launch_copy(s, x, pos, x_perm, row_scale, &pa, st);
 }
 

@@ -11,7 +11,8 @@ namespace moe {
 
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
-constexpr int kRouteTile = 16;     // tokens per router workgroup
+constexpr int kRouteTile = 16;     // tokens per router workgroup (at most; route_tile)
+constexpr int kRouteTileMin = 8;   // the smaller router tile
 constexpr int kDispatchBlock = 256;  // tokens per dispatch-plan block
 constexpr int kSplitKMax = 16;       // K ranges per tile when a grouped GEMM has few tiles
 constexpr size_t kSplitMetaBytes = 4096;  // header of the split-K scratch (tile count, tile rows)
@@ -77,6 +78,9 @@ struct RouteStats {
   double* prod;
   int32_t* done;
 };
+// Tokens per router tile (workgroup) for this shape: 8 or 16 (every
+// per-tile count and base, and the dispatch copy's ranks, use it).
+int route_tile(const moe_shape& s);
 // With one router tile (T <= kRouteTile) the router kernel writes the
 // statistics itself; otherwise launch_route_finalize must follow launch_route.
 bool route_folds_stats(const moe_shape& s);

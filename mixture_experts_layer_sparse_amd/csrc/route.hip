@@ -34,7 +34,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = kRouteTile;
 constexpr int kRouteSplitMax = 16;     // K ranges of partial logits the router adds at most
 constexpr int kLogitsSplitMax = 16;    // d-ranges of the few-token split logits at most
 static_assert(kSplitKMax <= kRouteSplitMax, "the router adds every K range of the logits GEMM");
@@ -161,6 +160,7 @@ constexpr int SMALL_N = 32;            // up to this many experts one lane selec
 // split the experts into CG column groups of 16-expert blocks and d into KS
 // slices (CG * KS = 8); each wave issues the loads of 8 k-steps before their
 // MFMAs, so that about 32 KB per wave are in flight.
+template <int TM>
 __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* lt, int ldl) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -226,7 +226,8 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
     if (i < nblk) {
       const int col = (cg + i * CG) * 16 + lr;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part[(ks * TM + (lane >> 4) * 4 + r) * NP + col] = acc[i][r];
+      for (int r = 0; r < 4; ++r)
+        if ((lane >> 4) * 4 + r < TM) part[(ks * TM + (lane >> 4) * 4 + r) * NP + col] = acc[i][r];
     }
   }
   __syncthreads();
@@ -257,6 +258,7 @@ constexpr int SPH = 8;                 // chunks per staging phase (8 x 16 rows 
 // 16-byte pieces q stored at (q & ~15) | ((q & 15) ^ r): a fragment read (16
 // rows, one piece each) then touches 16 different bank groups.  Rows past T
 // read as zeros (buffer range).  part / lt live in buf once the loads are done.
+template <int TM>
 __device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf, float* part,
                                    float* lt, int ldl) {
   const int lane = threadIdx.x & 63;
@@ -319,8 +321,10 @@ __device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf,
       for (int u = 0; u < U; ++u) {
         const int st = s + u < s1 ? s + u : s1 - 1;
         const int ch = st / (SCH / 32), q = (st % (SCH / 32)) * 4 + kc;
-        av[u] = *reinterpret_cast<const bf16x8*>(buf + (ch * TM + lr) * 1024 +
-                                                 (((q & ~15) | ((q & 15) ^ lr)) << 4));
+        // (with 8-token tiles the MFMA's rows 8-15 repeat rows 0-7; their results are dropped)
+        const int lrow = lr % TM;
+        av[u] = *reinterpret_cast<const bf16x8*>(buf + (ch * TM + lrow) * 1024 +
+                                                 (((q & ~15) | ((q & 15) ^ lrow)) << 4));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -339,7 +343,8 @@ __device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf,
     if (i < nblk) {
       const int col = (cg + i * CG) * 16 + lr;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part[(ks * TM + kc * 4 + r) * NP + col] = acc[i][r];
+      for (int r = 0; r < 4; ++r)
+        if (kc * 4 + r < TM) part[(ks * TM + kc * 4 + r) * NP + col] = acc[i][r];
     }
   }
   __syncthreads();
@@ -403,6 +408,7 @@ __global__ __launch_bounds__(256) void logits_split_kernel(const uint16_t* __res
 }
 
 // Logits of a 16-token tile from the partials: the d-ranges added in order.
+template <int TM>
 __device__ void logits_from_partials(const RouteArgs& a, int ks, int64_t lrange, int64_t t0, float* lt,
                                      int ldl) {
   for (int q = threadIdx.x; q < TM * a.N; q += RW * 64) {
@@ -424,6 +430,7 @@ __device__ void logits_from_partials(const RouteArgs& a, int ks, int64_t lrange,
 }
 
 // fp32 path: plain dot products, one (token, expert) pair per thread at a time.
+template <int TM>
 __device__ void logits_f32(const RouteArgs& a, int64_t t0, float* lt, int ldl) {
   const float* x = static_cast<const float*>(a.x);
   const float* wg = static_cast<const float*>(a.wg);
@@ -533,6 +540,7 @@ __device__ void select_lane(const RouteArgs& a, const float* row, float* prow, i
 // logits go to the lower index as in an in-order scan with strict >.  Writes
 // each token's p row to prow (for p) and its k picks; counts go to the block
 // histogram.
+template <int TM>
 __device__ void select_lanes(const RouteArgs& a, const float* lt, int ldl, int64_t t0,
                              float (*prow)[SMALL_N + 1], int* hl) {
   const int N = a.N, k = a.k;
@@ -639,7 +647,7 @@ __device__ void tile_stats(const RouteArgs& a, int e, float sum, int cnt, int* x
   scan_experts(kv, pr, N, a.alpha, a.rs.offsets, a.rs.l_aux, xk, xp);
 }
 
-template <bool BF16>
+template <bool BF16, int TM>
 __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
   // on the other paths, it holds the d-split partials [KS][TM][NP] (16 KB) and
@@ -670,12 +678,12 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       const int ks = a.lmeta ? a.lmeta[1] : a.lsplit;
       const int64_t lrange = a.lmeta ? static_cast<int64_t>(a.lmeta[0]) * (kRouterTileRows * kRouterTileCols)
                                      : a.lrange;
-      logits_from_partials(a, ks, lrange, t0, lt, ldl);
+      logits_from_partials<TM>(a, ks, lrange, t0, lt, ldl);
     }
-    else if (a.d % SCH == 0) logits_bf16_staged(a, t0, sbuf, part, lt, ldl);
-    else logits_bf16(a, t0, part, lt, ldl);
+    else if (a.d % SCH == 0) logits_bf16_staged<TM>(a, t0, sbuf, part, lt, ldl);
+    else logits_bf16<TM>(a, t0, part, lt, ldl);
   } else {
-    logits_f32(a, t0, lt, ldl);
+    logits_f32<TM>(a, t0, lt, ldl);
   }
   __syncthreads();
 
@@ -687,7 +695,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 
   if (N <= SMALL_N && a.n_groups <= 1) {
-    select_lanes(a, lt, ldl, t0, pl, hl);
+    select_lanes<TM>(a, lt, ldl, t0, pl, hl);
     __syncthreads();
     const int e = threadIdx.x;
     float sum = 0.f;
@@ -1038,7 +1046,7 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
 namespace {
 // dynamic LDS of route_kernel: the staged x chunks of one phase, at least the
 // partials and the logit tile
-size_t route_lds_bytes(const moe_shape& s) {
+size_t route_lds_bytes(const moe_shape& s, int TM) {
   const size_t minimum = 16384 + static_cast<size_t>(TM) * (kMaxExperts + 1) * 4;
   size_t staged = 0;
   if (s.dtype == MOE_BF16 && s.d % SCH == 0) {
@@ -1061,7 +1069,20 @@ int route_split_ranges(const moe_shape& s) {
   return static_cast<int>(ks < 1 ? 1 : ks);
 }
 
-bool route_folds_stats(const moe_shape& s) { return s.T <= TM; }
+// 8-token tiles where the logits come from partials (no x staging, no W_g
+// re-reads): twice the workgroups, one token per wave, for the selection
+// (DeepSeek-V3 shape: route + dispatch 122 -> 119 us).  Where the router
+// kernel computes the logits, 16: 8-token tiles there re-read W_g twice as
+// often and measured slower (Mixtral shape: router 17.4 -> 19.8 us, although
+// two half-size staging buffers then share a CU).  A call with at most 16
+// tokens keeps one tile.
+int route_tile(const moe_shape& s) {
+  if (s.dtype != MOE_BF16 || s.T <= kRouteTile) return kRouteTile;
+  const bool partials = router_gemm(s) || route_split_ranges(s) > 0;
+  return partials ? kRouteTileMin : kRouteTile;
+}
+
+bool route_folds_stats(const moe_shape& s) { return s.T <= kRouteTile; }
 
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
@@ -1084,27 +1105,32 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid(static_cast<unsigned>(ceil_div(s.T, TM)));
-  const size_t lds = route_lds_bytes(s);
+  const int tm = route_tile(s);
+  dim3 grid(static_cast<unsigned>(ceil_div(s.T, tm)));
+  const size_t lds = route_lds_bytes(s, tm);
   // allow dynamic LDS above the default limit (the largest staging buffer)
   static const bool attr_set = [] {
-    const int most = SPH * TM * 1024;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<true>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
-           hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<false>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
+    const int most = SPH * kRouteTile * 1024;
+    auto set = [&](const void* f) {
+      return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
+    };
+    return set(reinterpret_cast<const void*>(route_kernel<true, kRouteTile>)) &&
+           set(reinterpret_cast<const void*>(route_kernel<true, kRouteTileMin>)) &&
+           set(reinterpret_cast<const void*>(route_kernel<false, kRouteTile>));
   }();
   if (!attr_set) return hipErrorInvalidValue;
-  if (s.dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(RW * 64), lds, st, a);
+  if (s.dtype != MOE_BF16)
+    hipLaunchKernelGGL((route_kernel<false, kRouteTile>), grid, dim3(RW * 64), lds, st, a);
+  else if (tm == kRouteTileMin)
+    hipLaunchKernelGGL((route_kernel<true, kRouteTileMin>), grid, dim3(RW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(RW * 64), lds, st, a);
+    hipLaunchKernelGGL((route_kernel<true, kRouteTile>), grid, dim3(RW * 64), lds, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
                                  const RouteStats& rs, hipStream_t st) {
-  const int nb = static_cast<int>(ceil_div(s.T, TM));
+  const int nb = static_cast<int>(ceil_div(s.T, route_tile(s)));
   const int se = stats_experts_per_block(s.N);
   const int blocks = static_cast<int>(ceil_div(s.N, se));
   hipLaunchKernelGGL(route_stats_kernel, dim3(blocks), dim3(blocks == 1 ? ST1 : ST), 0, st,
