@@ -8,6 +8,8 @@
 // Written as a gather (one wave per output token reads its k expert rows)
 // rather than a scatter-add, so no atomics are needed and the float32 sum runs
 // in slot order 0..k-1, then the shared expert, with one rounding at the end.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 #ifndef MOE_COMBINE_UNROLL
@@ -111,12 +113,14 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
 hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_shared,
                           const void* x, const int32_t* pos, const float* w, void* y,
                           hipStream_t st) {
-  // One wave per token, or, with few tokens, several waves per token (each a
-  // strided share of the row's 64-lane chunks) so that ~2048 waves keep
-  // enough loads in flight: a single wave walking a 7168-wide row waits out
-  // the memory latency once per chunk.
+  // Several waves per token, each a strided share of the row's 64-lane
+  // chunks: enough that a wave's chunk loop is one unrolled pass (all its loads
+  // in flight together; a wave walking a long row waits out the memory latency
+  // once per pass), and with few tokens enough for ~2048 waves in all.
+  // Measured against one wave per token: DBRX shape 195 -> 168 us, DeepSeek-V3
+  // 122 -> 102 us, Mixtral 27.2 -> 26.1 us; one chunk per wave was no better.
   const int64_t chunks = s.dtype == MOE_BF16 ? s.d / 8 / 64 : s.d / 64;
-  int64_t wpt = ceil_div(2048, s.T);
+  int64_t wpt = std::max<int64_t>(ceil_div(2048, s.T), ceil_div(chunks, MOE_COMBINE_UNROLL));
   if (wpt > chunks) wpt = chunks;
   if (wpt < 1) wpt = 1;
   dim3 grid(static_cast<unsigned>(ceil_div(s.T * wpt, 4)));
