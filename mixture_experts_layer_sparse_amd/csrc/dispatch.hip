@@ -24,6 +24,8 @@
 // the earlier tokens of the same tile that chose the expert), so the layer
 // needs neither disp_hist nor disp_plan.  The order is the same token order, so
 // the permutation is the same.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -202,13 +204,15 @@ template <bool PLANNED>
 __global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restrict__ x, int64_t T,
                                                         int k, int row_bytes,
                                                         const int32_t* __restrict__ pos,
-                                                        uint8_t* __restrict__ xp, PlanArgs pa) {
+                                                        uint8_t* __restrict__ xp, PlanArgs pa, int wpt) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t t = gw / wpt;                    // wpt waves share a token's row
+  const int part = static_cast<int>(gw - t * wpt);
   if (t >= T) return;
   int pj[kMaxTopK];
   if (PLANNED) {
-    plan_token(pa, T, k, t, lane, pj);
+    plan_token(pa, T, k, t, lane, pj, part == 0);
   } else {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restric
   const int nch = row_bytes / 16;
   const uint4* xr = reinterpret_cast<const uint4*>(x + t * row_bytes);
 #pragma unroll 4
-  for (int c = lane; c < nch; c += 64) {
+  for (int c = part * 64 + lane; c < nch; c += 64 * wpt) {
     const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr) + c);
     const uint4 v = make_uint4(q[0], q[1], q[2], q[3]);
 #pragma unroll
@@ -253,10 +257,10 @@ __device__ __forceinline__ float absmax8(uint4 v) {
   return m;
 }
 
-// fp8 dispatch: WPT waves per token (4 when the call has few tokens, so that a
-// token's row is read and written by 256 lanes instead of 64: one wave took
-// 13.5 us for a 7168-wide row).  Rows up to 64*WPT*MAXC chunks of 8 bf16 stay
-// in registers; longer rows are read twice.
+// fp8 dispatch: WPT waves per token in one workgroup (the row's max |x| meets
+// in LDS), so that a token's row is read and written by 64 * WPT lanes.  Rows
+// up to 64*WPT*MAXC chunks of 8 bf16 stay in registers; longer rows are read
+// twice.
 template <int MAXC, bool PLANNED, int WPT>
 __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restrict__ x, int64_t T,
                                                        int k, int d,
@@ -352,36 +356,37 @@ hipError_t launch_dispatch_plan(const moe_shape& s, const int32_t* idx, const in
 namespace {
 hipError_t launch_copy(const moe_shape& s, const void* x, const int32_t* pos, void* x_perm,
                        float* row_scale, const PlanArgs* pa, hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(ceil_div(s.T, 4)));
   const PlanArgs none{};
   if (s.buf_dtype == MOE_FP8_E4M3) {
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint8_t* xp = static_cast<uint8_t*>(x_perm);
-    if (s.T < 512) {                              // few tokens: four waves per token
-      const dim3 g1(static_cast<unsigned>(s.T));
-      if (pa)
-        hipLaunchKernelGGL((disp_fp8_kernel<4, true, 4>), g1, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
-                           row_scale, *pa);
-      else
-        hipLaunchKernelGGL((disp_fp8_kernel<4, false, 4>), g1, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
-                           row_scale, none);
-    } else if (pa) {
-      hipLaunchKernelGGL((disp_fp8_kernel<16, true, 1>), grid, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
-                         row_scale, *pa);
-    } else {
-      hipLaunchKernelGGL((disp_fp8_kernel<16, false, 1>), grid, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
-                         row_scale, none);
-    }
-  } else {
-    int es = s.dtype == MOE_BF16 ? 2 : 4;
+    // four waves per token, one workgroup (a 7168-wide row: DeepSeek-V3 decode
+    // 13.5 -> 8 us, prefill route + dispatch 114 -> 112 us, against one wave);
+    // rows past 64 * 4 * 4 chunks of 8 are read twice
+    const dim3 g1(static_cast<unsigned>(s.T));
     if (pa)
-      hipLaunchKernelGGL(disp_copy_kernel<true>, grid, dim3(256), 0, st,
-                         static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
-                         static_cast<uint8_t*>(x_perm), *pa);
+      hipLaunchKernelGGL((disp_fp8_kernel<4, true, 4>), g1, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
+                         row_scale, *pa);
     else
-      hipLaunchKernelGGL(disp_copy_kernel<false>, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((disp_fp8_kernel<4, false, 4>), g1, dim3(256), 0, st, xs, s.T, s.k, s.d, pos, xp,
+                         row_scale, none);
+  } else {
+    const int es = s.dtype == MOE_BF16 ? 2 : 4;
+    // waves per token: enough that a wave's chunk loop is one unrolled pass
+    // (its loads in flight together), and with few tokens ~2048 waves in all
+    // (DBRX shape: route + dispatch 304 -> 292 us)
+    const int64_t iters = ceil_div(s.d * es / 16, 64);          // 16-byte chunks per lane, one wave a row
+    int64_t wpt = std::max<int64_t>(ceil_div(2048, s.T), ceil_div(iters, 4));
+    if (wpt > iters) wpt = iters;
+    const dim3 gw(static_cast<unsigned>(ceil_div(s.T * wpt, 4)));
+    if (pa)
+      hipLaunchKernelGGL(disp_copy_kernel<true>, gw, dim3(256), 0, st,
                          static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
-                         static_cast<uint8_t*>(x_perm), none);
+                         static_cast<uint8_t*>(x_perm), *pa, static_cast<int>(wpt));
+    else
+      hipLaunchKernelGGL(disp_copy_kernel<false>, gw, dim3(256), 0, st,
+                         static_cast<const uint8_t*>(x), s.T, s.k, s.d * es, pos,
+                         static_cast<uint8_t*>(x_perm), none, static_cast<int>(wpt));
   }
   return hipGetLastError();
 }

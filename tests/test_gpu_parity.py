@@ -266,7 +266,7 @@ def test_fp8_quantiser_exhaustive_bf16_patterns():
         assert np.array_equal(bf16_to_f64(a_bits), anchor[ok])       # exact anchors
         rows.append(np.concatenate([vals[ok], a_bits[:, None]], axis=1))
     x_all = np.concatenate(rows)
-    # all rows (one wave per token), then the first 300 (below 512 tokens: four waves per token)
+    # all rows, then the first 300 (a ragged grid)
     for x in (x_all, x_all[:300]):
         T, d = x.shape
         wl = si.Workload("q", T=T, d=d, N=4, k=1, F=64, act="swiglu", dtype="bf16", buf="fp8")
