@@ -411,6 +411,8 @@ __global__ __launch_bounds__(256) void logits_split_kernel(const uint16_t* __res
 template <int TM>
 __device__ void logits_from_partials(const RouteArgs& a, int ks, int64_t lrange, int64_t t0, float* lt,
                                      int ldl) {
+  // (four entries' range loads in flight together: DeepSeek-V3 router 57.4 -> 55.4 us)
+#pragma unroll 4
   for (int q = threadIdx.x; q < TM * a.N; q += RW * 64) {
     const int m = q / a.N, e = q % a.N;
     const int64_t t = t0 + m;
