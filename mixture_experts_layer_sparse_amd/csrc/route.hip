@@ -234,9 +234,13 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* 
   for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
     const int m = q / N, e = q % N;
     float v = 0.f;
+    float pk[RW];
 #pragma unroll
     for (int kk = 0; kk < RW; ++kk)             // (KS <= RW: the reads issued together, added in order)
-      if (kk < KS) v += part[(kk * TM + m) * NP + e];
+      pk[kk] = part[((kk < KS ? kk : KS - 1) * TM + m) * NP + e];
+#pragma unroll
+    for (int kk = 0; kk < RW; ++kk)
+      if (kk < KS) v += pk[kk];
     if (a.bias) v += a.bias[e];
     lt[m * ldl + e] = v;
   }
@@ -351,9 +355,13 @@ __device__ void logits_bf16_staged(const RouteArgs& a, int64_t t0, uint8_t* buf,
   for (int q = threadIdx.x; q < TM * N; q += RW * 64) {
     const int m = q / N, e = q % N;
     float v = 0.f;
+    float pk[RW];
 #pragma unroll
     for (int kk = 0; kk < RW; ++kk)             // (KS <= RW: the reads issued together, added in order)
-      if (kk < KS) v += part[(kk * TM + m) * NP + e];
+      pk[kk] = part[((kk < KS ? kk : KS - 1) * TM + m) * NP + e];
+#pragma unroll
+    for (int kk = 0; kk < RW; ++kk)
+      if (kk < KS) v += pk[kk];
     if (a.bias) v += a.bias[e];
     lt[m * ldl + e] = v;
   }
