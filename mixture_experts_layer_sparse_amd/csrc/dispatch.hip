@@ -171,35 +171,66 @@ struct PlanArgs {
 };
 
 __device__ __forceinline__ void plan_token(const PlanArgs& pa, int64_t T, int k, int64_t t, int lane,
-                                           int pj[kMaxTopK], bool writer = true) {
+                                           int pj[kMaxTopK]) {
   const int TM = pa.tile;
   const int64_t tile = t / TM, t0 = tile * TM;
   const int before = static_cast<int>(t - t0) * k;        // idx entries of earlier tokens in the tile
-  // lane l holds entries l and l + 64 of the tile (TM * k <= 128)
+  // The loads go out in two batches: the tile's earlier entries and this
+  // token's choices, then the choices' tile bases and offsets (two latencies,
+  // not three per choice).  Lane l holds entries l and l + 64 of the tile
+  // (TM * k <= 128).
   const int v0 = (lane < before) ? pa.idx[t0 * k + lane] : -1;
   const int v1 = (lane + 64 < before) ? pa.idx[t0 * k + lane + 64] : -1;
+  int e[kMaxTopK], b[kMaxTopK], o[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) e[j] = j < k ? pa.idx[t * k + j] : -1;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
-    pj[j] = -1;
-    if (j < k) {
-      const int e = pa.idx[t * k + j];
-      int p = -1;
-      if (static_cast<unsigned>(e) < static_cast<unsigned>(pa.N)) {
-        const int r = pa.base[tile * pa.N + e] + __popcll(__ballot(v0 == e)) + __popcll(__ballot(v1 == e));
-        if (pa.cap <= 0 || r < pa.cap) p = pa.offsets[e] + r;
-      }
-      pj[j] = p;
-      if (writer && lane == 0) {
-        pa.pos[t * k + j] = p;
-        pa.drop[t * k + j] = p < 0 ? 1 : 0;
-        if (p >= 0) pa.src[p] = static_cast<int32_t>(t);
-      }
+    const bool ok = static_cast<unsigned>(e[j]) < static_cast<unsigned>(pa.N);
+    b[j] = ok ? pa.base[tile * pa.N + e[j]] : 0;
+    o[j] = ok ? pa.offsets[e[j]] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    int p = -1;
+    if (static_cast<unsigned>(e[j]) < static_cast<unsigned>(pa.N)) {
+      const int r = b[j] + __popcll(__ballot(v0 == e[j])) + __popcll(__ballot(v1 == e[j]));
+      if (pa.cap <= 0 || r < pa.cap) p = o[j] + r;
     }
+    // the same in every lane: as a scalar, a slot's row base is an SGPR pair
+    pj[j] = __builtin_amdgcn_readfirstlane(p);
   }
 }
 
-// One wave per token; 16-byte chunks.  Row bytes must be a multiple of 16.
-// PLANNED: positions from plan_token, else read from pos.
+// pos, drop and src of one token, from lane 0 of one of its waves.  They are
+// written after the rows: the row stores then follow each other with no wait
+// for a store issued before them.
+__device__ __forceinline__ void plan_write(const PlanArgs& pa, int k, int64_t t, const int pj[kMaxTopK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) {
+      pa.pos[t * k + j] = pj[j];
+      pa.drop[t * k + j] = pj[j] < 0 ? 1 : 0;
+      if (pj[j] >= 0) pa.src[pj[j]] = static_cast<int32_t>(t);
+    }
+}
+
+// Positions handed in by the caller, one token's k entries (the same address in
+// every lane, hence uniform).
+__device__ __forceinline__ void given_positions(const int32_t* pos, int k, int64_t t, int pj[kMaxTopK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? __builtin_amdgcn_readfirstlane(pos[t * k + j]) : -1;
+}
+
+// wpt waves per token; 16-byte chunks.  Row bytes must be a multiple of 16.
+// PLANNED: positions from plan_token, else read from pos.  A lane's first
+// kCopyAhead chunks are loaded before the positions, so that the row's latency
+// overlaps theirs (the host picks wpt so that these are all of them).  The
+// loads are unconditional, their index clamped into the row: under a
+// condition, even a uniform one, the compiler waited for each before the next.
+// Rows are then stored slot by slot, to a scalar row base plus a fixed
+// per-chunk offset, so that no store waits for an earlier one to leave.
+constexpr int kCopyAhead = 4;
 template <bool PLANNED>
 __global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restrict__ x, int64_t T,
                                                         int k, int row_bytes,
@@ -210,24 +241,33 @@ __global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restric
   const int64_t t = gw / wpt;                    // wpt waves share a token's row
   const int part = static_cast<int>(gw - t * wpt);
   if (t >= T) return;
-  int pj[kMaxTopK];
-  if (PLANNED) {
-    plan_token(pa, T, k, t, lane, pj, part == 0);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
-  }
   const int nch = row_bytes / 16;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + t * row_bytes);
-#pragma unroll 4
-  for (int c = part * 64 + lane; c < nch; c += 64 * wpt) {
-    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr) + c);
-    const uint4 v = make_uint4(q[0], q[1], q[2], q[3]);
+  const int c0 = part * 64 + lane, cs = 64 * wpt;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * row_bytes);
+  u32x4 q[kCopyAhead];
+#pragma unroll
+  for (int i = 0; i < kCopyAhead; ++i)       // (index clamped into the row; such lanes store nothing)
+    q[i] = __builtin_nontemporal_load(xr + min(c0 + i * cs, nch - 1));
+  int pj[kMaxTopK];
+  if (PLANNED)
+    plan_token(pa, T, k, t, lane, pj);
+  else
+    given_positions(pos, k, t, pj);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (pj[j] < 0) continue;
+    u32x4* dst = reinterpret_cast<u32x4*>(xp + static_cast<int64_t>(pj[j]) * row_bytes);
+#pragma unroll
+    for (int i = 0; i < kCopyAhead; ++i)
+      if (c0 + i * cs < nch) dst[c0 + i * cs] = q[i];
+  }
+  for (int c = c0 + kCopyAhead * cs; c < nch; c += cs) {
+    const u32x4 r = __builtin_nontemporal_load(xr + c);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
-      if (pj[j] >= 0)
-        reinterpret_cast<uint4*>(xp + static_cast<int64_t>(pj[j]) * row_bytes)[c] = v;
+      if (pj[j] >= 0) reinterpret_cast<u32x4*>(xp + static_cast<int64_t>(pj[j]) * row_bytes)[c] = r;
   }
+  if (PLANNED && part == 0 && lane == 0) plan_write(pa, k, t, pj);
 }
 
 __device__ __forceinline__ uint2 quant8(uint4 v, float inv) {
@@ -274,25 +314,27 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
   const int tl = sub * 64 + lane;                 // lane within the token
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (4 / WPT) + wave / WPT;
   if (t >= T) return;                             // (whole tokens: the waves of one token agree)
-  int pj[kMaxTopK];
-  if (PLANNED) {
-    plan_token(pa, T, k, t, lane, pj, sub == 0);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? pos[t * k + j] : -1;
-  }
   const int nch = d / 8;
   const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
   const bool in_regs = nch <= 64 * WPT * MAXC;
   uint4 buf[MAXC];
   float amax = 0.f;
   if (in_regs) {
+    // the row's loads go out before the positions' (their latencies overlap)
 #pragma unroll
     for (int q = 0; q < MAXC; ++q) {
       int c = tl + 64 * WPT * q;
       buf[q] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
-      amax = fmaxf(amax, absmax8(buf[q]));
     }
+  }
+  int pj[kMaxTopK];
+  if (PLANNED)
+    plan_token(pa, T, k, t, lane, pj);
+  else
+    given_positions(pos, k, t, pj);
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) amax = fmaxf(amax, absmax8(buf[q]));
   } else {
     for (int c = tl; c < nch; c += 64 * WPT) amax = fmaxf(amax, absmax8(xr[c]));
   }
@@ -309,21 +351,18 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
   const bool tiny = amax < 0x1p-100f;
   const float inv = tiny ? 1.f : __fdiv_rn(448.0f, amax);
   const float scale = tiny ? 1.f : __fdiv_rn(amax, 448.0f);
-  if (tl == 0) {
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (pj[j] >= 0) row_scale[pj[j]] = scale;
-  }
   if (in_regs) {
+    // codes first, then slot by slot (scalar row base, fixed per-chunk offsets)
+    uint2 code[MAXC];
 #pragma unroll
-    for (int q = 0; q < MAXC; ++q) {
-      int c = tl + 64 * WPT * q;
-      if (c < nch) {
-        uint2 code = quant8(buf[q], inv);
+    for (int q = 0; q < MAXC; ++q) code[q] = quant8(buf[q], inv);
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
-          if (pj[j] >= 0) reinterpret_cast<uint2*>(xp + static_cast<int64_t>(pj[j]) * d)[c] = code;
-      }
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (pj[j] < 0) continue;
+      uint2* dst = reinterpret_cast<uint2*>(xp + static_cast<int64_t>(pj[j]) * d);
+#pragma unroll
+      for (int q = 0; q < MAXC; ++q)
+        if (tl + 64 * WPT * q < nch) dst[tl + 64 * WPT * q] = code[q];
     }
   } else {
     for (int c = tl; c < nch; c += 64 * WPT) {
@@ -332,6 +371,12 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
       for (int j = 0; j < kMaxTopK; ++j)
         if (pj[j] >= 0) reinterpret_cast<uint2*>(xp + static_cast<int64_t>(pj[j]) * d)[c] = code;
     }
+  }
+  if (tl == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (pj[j] >= 0) row_scale[pj[j]] = scale;
+    if (PLANNED) plan_write(pa, k, t, pj);
   }
 }
 
@@ -376,7 +421,7 @@ hipError_t launch_copy(const moe_shape& s, const void* x, const int32_t* pos, vo
     // (its loads in flight together), and with few tokens ~2048 waves in all
     // (DBRX shape: route + dispatch 304 -> 292 us)
     const int64_t iters = ceil_div(s.d * es / 16, 64);          // 16-byte chunks per lane, one wave a row
-    int64_t wpt = std::max<int64_t>(ceil_div(2048, s.T), ceil_div(iters, 4));
+    int64_t wpt = std::max<int64_t>(ceil_div(2048, s.T), ceil_div(iters, kCopyAhead));
     if (wpt > iters) wpt = iters;
     const dim3 gw(static_cast<unsigned>(ceil_div(s.T * wpt, 4)));
     if (pa)
