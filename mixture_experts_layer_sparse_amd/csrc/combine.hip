@@ -5,7 +5,7 @@
 // serve" keeps combine in BF16; a dropped slot ("Capacity factor and token
 // dropping") passes the token through or contributes nothing.
 //
-// Written as a gather (one wave per output token reads its k expert rows)
+// Written as a gather (the waves of an output token read its k expert rows)
 // rather than a scatter-add, so no atomics are needed and the float32 sum runs
 // in slot order 0..k-1, then the shared expert, with one rounding at the end.
 #include <algorithm>
@@ -13,7 +13,7 @@
 #include "moe_internal.h"
 
 #ifndef MOE_COMBINE_UNROLL
-#define MOE_COMBINE_UNROLL 2
+#define MOE_COMBINE_UNROLL 1
 #endif
 
 namespace moe {
@@ -37,51 +37,87 @@ __device__ __forceinline__ void add_bf16x8(float* acc, uint4 v) {
     acc[2 * i + 1] += __uint_as_float(q[i] & 0xFFFF0000u);
   }
 }
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* acc) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+  return r;
+}
 
+// K slots per token; SHARED: add the shared expert's row.  Each slot's source
+// row is wave-uniform: the expert output, or for a dropped slot x (pass-through;
+// also read, and not added, where a drop contributes zero) or the shared
+// expert's output (fallback).  All of a wave's loads go out unconditionally,
+// their chunk index clamped into the row, before the first is used: loads under
+// a condition made the compiler wait for each before issuing the next.
+template <int K, bool SHARED>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ out_shared,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    uint16_t* __restrict__ y, int64_t T, int k, int d, int drop_mode, int wpt) {
+    uint16_t* __restrict__ y, int64_t T, int d, int drop_mode, int wpt) {
+  constexpr int U = MOE_COMBINE_UNROLL;
   const int lane = threadIdx.x & 63;
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t t = gw / wpt;                    // wpt waves share a token's row
   const int part = static_cast<int>(gw - t * wpt);
   if (t >= T) return;
-  int pj[kMaxTopK];
-  float wj[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    pj[j] = j < k ? pos[t * k + j] : -1;
-    wj[j] = j < k ? w[t * k + j] : 0.f;
-  }
   const int nch = d / 8;
-#pragma unroll MOE_COMBINE_UNROLL
-  for (int c = part * 64 + lane; c < nch; c += 64 * wpt) {
+  const int c0 = part * 64 + lane, cs = 64 * wpt;
+  const bool fallback = drop_mode == MOE_DROP_FALLBACK && out_shared != nullptr;
+  const u32x4* src[K];
+  float wj[K];
+  bool use[K];
+  int pv[K], wv[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {              // (all loaded before the first is used)
+    pv[j] = pos[t * K + j];
+    wv[j] = __float_as_int(w[t * K + j]);
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int p = __builtin_amdgcn_readfirstlane(pv[j]);
+    wj[j] = __int_as_float(__builtin_amdgcn_readfirstlane(wv[j]));
+    const uint16_t* row = p >= 0 ? out + static_cast<int64_t>(p) * d : fallback ? out_shared + t * d : x + t * d;
+    src[j] = reinterpret_cast<const u32x4*>(row);
+    use[j] = p >= 0 || drop_mode == MOE_DROP_PASSTHROUGH || fallback;
+  }
+  const u32x4* shr = reinterpret_cast<const u32x4*>(SHARED ? out_shared + t * d : x);
+  u32x4* yr = reinterpret_cast<u32x4*>(y + t * d);
+  u32x4 v[U][K], sh[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int cc = min(c0 + i * cs, nch - 1);
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[i][j] = __builtin_nontemporal_load(src[j] + cc);
+    if (SHARED) sh[i] = __builtin_nontemporal_load(shr + cc);
+  }
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int c = c0 + i * cs;
+    if (c < nch) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        if (use[j]) acc_bf16x8(acc, make_uint4(v[i][j][0], v[i][j][1], v[i][j][2], v[i][j][3]), wj[j]);
+      if (SHARED) add_bf16x8(acc, make_uint4(sh[i][0], sh[i][1], sh[i][2], sh[i][3]));
+      yr[c] = pack_bf16x8(acc);
+    }
+  }
+  // rows longer than the host's split assumes: the rest chunk by chunk
+  for (int c = c0 + U * cs; c < nch; c += cs) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        if (pj[j] >= 0) {
-          const u32x4 q = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(out + static_cast<int64_t>(pj[j]) * d) + c);
-          const uint4 v = make_uint4(q[0], q[1], q[2], q[3]);
-          acc_bf16x8(acc, v, wj[j]);
-        } else if (drop_mode == MOE_DROP_PASSTHROUGH) {
-          uint4 v = reinterpret_cast<const uint4*>(x + t * d)[c];
-          acc_bf16x8(acc, v, wj[j]);
-        } else if (drop_mode == MOE_DROP_FALLBACK) {
-          uint4 v = reinterpret_cast<const uint4*>(out_shared + t * d)[c];
-          acc_bf16x8(acc, v, wj[j]);
-        }
+    for (int j = 0; j < K; ++j)
+      if (use[j]) {
+        const u32x4 q = src[j][c];
+        acc_bf16x8(acc, make_uint4(q[0], q[1], q[2], q[3]), wj[j]);
       }
+    if (SHARED) {
+      const u32x4 q = shr[c];
+      add_bf16x8(acc, make_uint4(q[0], q[1], q[2], q[3]));
     }
-    if (out_shared) add_bf16x8(acc, reinterpret_cast<const uint4*>(out_shared + t * d)[c]);
-    uint4 r;
-    r.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-    r.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    r.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-    r.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-    reinterpret_cast<uint4*>(y + t * d)[c] = r;
+    yr[c] = pack_bf16x8(acc);
   }
 }
 
@@ -114,23 +150,41 @@ hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_s
                           const void* x, const int32_t* pos, const float* w, void* y,
                           hipStream_t st) {
   // Several waves per token, each a strided share of the row's 64-lane
-  // chunks: enough that a wave's chunk loop is one unrolled pass (all its loads
-  // in flight together; a wave walking a long row waits out the memory latency
-  // once per pass), and with few tokens enough for ~2048 waves in all.
-  // Measured against one wave per token: DBRX shape 195 -> 168 us, DeepSeek-V3
-  // 122 -> 102 us, Mixtral 27.2 -> 26.1 us; one chunk per wave was no better.
+  // chunks: as many as give each lane MOE_COMBINE_UNROLL chunks (its loads, all
+  // k slots of all its chunks, in flight together), and with few tokens enough
+  // for ~2048 waves in all.  One chunk per lane measured best (Mixtral shape
+  // 21.0 us against 21.4 with two and 21.2 with four; DBRX shape 160 / 161 /
+  // 161 us; DeepSeek-V3 103 / 104 / 110 us).
   const int64_t chunks = s.dtype == MOE_BF16 ? s.d / 8 / 64 : s.d / 64;
   int64_t wpt = std::max<int64_t>(ceil_div(2048, s.T), ceil_div(chunks, MOE_COMBINE_UNROLL));
   if (wpt > chunks) wpt = chunks;
   if (wpt < 1) wpt = 1;
   dim3 grid(static_cast<unsigned>(ceil_div(s.T * wpt, 4)));
   const int pt = s.drop;
-  if (s.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16_kernel, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(out_shared),
-                       static_cast<const uint16_t*>(x), pos, w, static_cast<uint16_t*>(y), s.T,
-                       s.k, s.d, pt, static_cast<int>(wpt));
-  else
+  if (s.dtype == MOE_BF16) {
+    const uint16_t* o = static_cast<const uint16_t*>(out);
+    const uint16_t* os = static_cast<const uint16_t*>(out_shared);
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint16_t* ys = static_cast<uint16_t*>(y);
+    const int wp = static_cast<int>(wpt);
+    const bool sh = out_shared != nullptr;
+    switch (s.k) {
+#define MOE_COMBINE_K(K)                                                                          \
+  case K:                                                                                         \
+    if (sh)                                                                                       \
+      hipLaunchKernelGGL((combine_bf16_kernel<K, true>), grid, dim3(256), 0, st, o, os, xs, pos, w, \
+                         ys, s.T, s.d, pt, wp);                                                   \
+    else                                                                                          \
+      hipLaunchKernelGGL((combine_bf16_kernel<K, false>), grid, dim3(256), 0, st, o, os, xs, pos, \
+                         w, ys, s.T, s.d, pt, wp);                                                \
+    break;
+      MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
+      MOE_COMBINE_K(5) MOE_COMBINE_K(6) MOE_COMBINE_K(7) MOE_COMBINE_K(8)
+#undef MOE_COMBINE_K
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else
     hipLaunchKernelGGL(combine_f32_kernel, grid, dim3(256), 0, st,
                        static_cast<const float*>(out), static_cast<const float*>(out_shared),
                        static_cast<const float*>(x), pos, w, static_cast<float*>(y), s.T, s.k,

@@ -929,7 +929,10 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
   const int b0 = static_cast<int>(static_cast<int64_t>(part) * nb / nparts);
   const int b1 = static_cast<int>(static_cast<int64_t>(part + 1) * nb / nparts);
   // batches of SKEEP tiles whose loads are issued together; the first
-  // batch's counts stay in registers for the tile prefix
+  // batch's counts stay in registers for the tile prefix.  The loads are
+  // unconditional (tile and expert clamped into the arrays; such values are
+  // then dropped): under a condition the compiler waited for each in turn.
+  const int ec = ex ? e : N - 1;
   int hv[SKEEP];
   double s = 0.0;
   int c = 0;
@@ -938,9 +941,15 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
     float pb[SKEEP];
 #pragma unroll
     for (int i = 0; i < SKEEP; ++i) {
+      const int64_t at = static_cast<int64_t>(min(bb + i, nb - 1)) * N + ec;
+      hb[i] = hist[at];
+      pb[i] = psum[at];
+    }
+#pragma unroll
+    for (int i = 0; i < SKEEP; ++i) {
       const bool in = ex && bb + i < b1;
-      hb[i] = in ? hist[static_cast<int64_t>(bb + i) * N + e] : 0;
-      pb[i] = in ? psum[static_cast<int64_t>(bb + i) * N + e] : 0.f;
+      hb[i] = in ? hb[i] : 0;
+      pb[i] = in ? pb[i] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < SKEEP; ++i) {
@@ -1018,7 +1027,7 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
     for (int bb = b0 + SKEEP; bb < b1; bb += SKEEP) {
       int hb[SKEEP];
 #pragma unroll
-      for (int i = 0; i < SKEEP; ++i) hb[i] = bb + i < b1 ? hist[static_cast<int64_t>(bb + i) * N + e] : 0;
+      for (int i = 0; i < SKEEP; ++i) hb[i] = hist[static_cast<int64_t>(min(bb + i, nb - 1)) * N + e];
 #pragma unroll
       for (int i = 0; i < SKEEP; ++i) {
         if (bb + i < b1) {
