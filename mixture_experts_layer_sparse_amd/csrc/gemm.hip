@@ -102,6 +102,7 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from a buffer into registers (reads past the end return zero).
 // Kept in a device function: the host compilation pass only needs the kernel stub.
@@ -739,9 +740,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 
 // Split-K tail: adds the ksplit float32 partials of each tail tile in range
 // order (fixed, so the result does not depend on timing) and applies the
-// epilogue.  Unit sp * tiles + t holds range sp of tail tile t.  Grid (tail tiles at most, 16): block y covers 16 of the tile's
-// 256 rows, thread c one tile column (SwiGLU: c < 128 pairs the W1 column
-// (c / 32) * 64 + c % 32 with the W3 column 32 further).
+// epilogue.  Unit sp * tiles + t holds range sp of tail tile t.  Grid (tail
+// tiles at most, BM / 16): block y covers 16 of the tile's rows.  SwiGLU pairs
+// output column c < 128 with the W1 column (c / 32) * 64 + c % 32 and the W3
+// column 32 further.
 template <int EPI, bool FP8A, int BM>
 __global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
   constexpr int TB = 256;                        // tile columns (BM rows)
@@ -750,49 +752,60 @@ __global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
   if (t >= ntail) return;
   const int32_t* m = g.part_meta + 2 + 3 * t;
   const int row0 = m[0], row_end = m[1], ntile = m[2];
-  const int c = threadIdx.x;
-  if (GATED && c >= TB / 2) return;
-  const float* pt = g.part + static_cast<int64_t>(t) * (BM * TB);
+  // A thread owns 4 adjacent output columns (16-byte partial loads, one 8-byte
+  // store): 64 threads cover a tile row (gated: 32, each reading 4 up and the
+  // 4 gate columns 32 further on), and the 4 waves take every 4th of the
+  // workgroup's 16 rows.
+  const int q = threadIdx.x & 63, sub = threadIdx.x >> 6;
+  if (GATED && q >= TB / 8) return;
+  const int pc = GATED ? (q >> 3) * 64 + (q & 7) * 4 : 4 * q;      // first partial column
+  const int col = ntile * (GATED ? TB / 2 : TB) + 4 * q;           // first output column
+  const bool vec = (g.n_out & 3) == 0 && col + 3 < g.n_out;
+  const float* pt = g.part + static_cast<int64_t>(t) * (BM * TB) + pc;
   const int64_t range_stride = static_cast<int64_t>(ntail) * (BM * TB);
 #pragma unroll 2
-  for (int rr = 0; rr < 16; ++rr) {
+  for (int rr = sub; rr < 16; rr += 4) {
     const int lr = blockIdx.y * 16 + rr;
     const int row = row0 + lr;
     if (row >= row_end) break;
     const float sc = FP8A ? g.a_scale[row] : 1.0f;
+    const float* pr = pt + lr * TB;
     // (the ranges' loads issued together, then added in range order)
-    if (GATED) {
-      const int pu = (c >> 5) * 64 + (c & 31);
-      float pv[kSplitKMax], pg[kSplitKMax];
+    f32x4 pv[kSplitKMax], pg[kSplitKMax];
 #pragma unroll
-      for (int sp = 0; sp < kSplitKMax; ++sp) {
-        pv[sp] = sp < ksplit ? pt[sp * range_stride + lr * TB + pu] : 0.f;
-        pg[sp] = sp < ksplit ? pt[sp * range_stride + lr * TB + pu + 32] : 0.f;
-      }
-      float u = 0.f, gt = 0.f;
+    for (int sp = 0; sp < kSplitKMax; ++sp) {
+      pv[sp] = sp < ksplit ? *reinterpret_cast<const f32x4*>(pr + sp * range_stride) : f32x4{};
+      if (GATED) pg[sp] = sp < ksplit ? *reinterpret_cast<const f32x4*>(pr + sp * range_stride + 32) : f32x4{};
+    }
+    f32x4 u{}, gt{};
 #pragma unroll
-      for (int sp = 0; sp < kSplitKMax; ++sp) {
-        if (sp < ksplit) {
-          u += pv[sp];
-          gt += pg[sp];
-        }
+    for (int sp = 0; sp < kSplitKMax; ++sp) {
+      if (sp < ksplit) {
+        u += pv[sp];
+        if (GATED) gt += pg[sp];
       }
-      const int col = ntile * (TB / 2) + c;
-      if (col < g.n_out)
-        g.out[static_cast<int64_t>(row) * g.n_out + col] = to_bf16(silu_fast(u * sc) * (gt * sc));
+    }
+    uint16_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v;
+      if (GATED) {
+        v = silu_fast(u[i] * sc) * (gt[i] * sc);
+      } else {
+        v = u[i] * sc;
+        if (EPI == EPI_SILU) v = silu_fast(v);
+        if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+      }
+      o[i] = to_bf16(v);
+    }
+    uint16_t* dst = g.out + static_cast<int64_t>(row) * g.n_out + col;
+    if (vec) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                                                  o[2] | (static_cast<uint32_t>(o[3]) << 16));
     } else {
-      float pv[kSplitKMax];
 #pragma unroll
-      for (int sp = 0; sp < kSplitKMax; ++sp) pv[sp] = sp < ksplit ? pt[sp * range_stride + lr * TB + c] : 0.f;
-      float v = 0.f;
-#pragma unroll
-      for (int sp = 0; sp < kSplitKMax; ++sp)
-        if (sp < ksplit) v += pv[sp];
-      v *= sc;
-      if (EPI == EPI_SILU) v = silu_fast(v);
-      if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-      const int col = ntile * TB + c;
-      if (col < g.n_out) g.out[static_cast<int64_t>(row) * g.n_out + col] = to_bf16(v);
+      for (int i = 0; i < 4; ++i)
+        if (col + i < g.n_out) dst[i] = o[i];
     }
   }
 }
