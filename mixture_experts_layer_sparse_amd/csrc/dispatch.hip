@@ -16,10 +16,10 @@
 //              the stable in-block rank of every assignment from wave ballots
 //              (match on the expert-id bits) plus a wave-ordered LDS prefix.
 //              No atomics decide a position, so the permutation is unique.
-//   disp_copy  one wave per token: read the row once, write it to each kept
+//   disp_copy  a few waves per token: read the row once, write it to each kept
 //              slot's position (bf16/f32 copy, or fp8 e4m3 with a per-token scale).
 // Within a whole layer the router has already counted each expert's
-// assignments per tile of 16 tokens, and its finalisation turns them into
+// assignments per router tile (8 or 16 tokens), and its finalisation turns them into
 // per-tile bases; the copy then places its token itself (the tile's base plus
 // the earlier tokens of the same tile that chose the expert), so the layer
 // needs neither disp_hist nor disp_plan.  The order is the same token order, so
