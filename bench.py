@@ -95,8 +95,14 @@ def cpu_baseline(wl, inp, n_tok):
     t_all = time.perf_counter() - t0
     t_ffn = max(t_all - t_route, 1e-9)
     per_tok = t_route / wl.T + t_ffn / n_tok
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    # what np.show_runtime() prints, in one line: the BLAS library, its
+    # threading layer and thread count
+    blas = "; ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer')}, "
+                     f"{p.get('num_threads')} threads)" for p in pools)
     return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "numpy": np.__version__, "blas": blas,
             "sample": f"routing + plan for all {wl.T} tokens ({t_route:.2f} s); expert FFNs + "
                       f"combine for {n_tok} evenly spaced tokens ({t_ffn:.2f} s); float64 NumPy"}
 
@@ -293,11 +299,36 @@ def _phases(wl, g, x, steps, warmup):
     return L, ph, wall
 
 
+def load_report(wl, L):
+    """The layer's load statistics as the library returned them (no oracle):
+    per-expert counts before drops, drops, f, p and L_aux.  Returns a dict."""
+    import numpy as np
+    counts = L.counts.cpu().numpy()
+    kept = L.kept_counts.cpu().numpy()
+    f = L.f.cpu().numpy()
+    p = L.p.cpu().numpy()
+    mean = wl.T * wl.k / wl.N
+    rep = {"workload": wl.name, "l_aux": float(L.l_aux.item()), "alpha": wl.alpha,
+           "counts_min": int(counts.min()), "counts_max": int(counts.max()),
+           "hot_over_mean": float(counts.max() / mean), "dropped": int(counts.sum() - kept.sum()),
+           "experts_over_capacity": int((counts > wl.capacity).sum()) if wl.capacity > 0 else 0,
+           "f_sum": float(f.sum()), "f_max": float(f.max()), "p_sum": float(p.sum()),
+           "p_min": float(p.min()), "p_max": float(p.max())}
+    if wl.N <= 16:
+        rep["counts"] = counts.tolist()
+        rep["f"] = [round(float(v), 5) for v in f]
+        rep["p"] = [round(float(v), 5) for v in p]
+    return rep
+
+
 def sweep(steps, warmup):
     """Every workload family at its full size, phase by phase (the kernels of
-    moe_forward); prints a markdown table."""
+    moe_forward); prints a markdown table, then each workload's load
+    statistics (counts histogram, drops, f, p, L_aux) as the library returned
+    them."""
     import torch
     import synthetic_inputs as si
+    reports = []
 
     print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | GEMM down us | shared us | "
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
@@ -321,8 +352,21 @@ def sweep(steps, warmup):
               f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | "
               f"{tf:.0f} ({100 * tf / PEAK_BF16_TFLOPS:.1f}%) | {wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) | "
               f"{mgb:.0f} ({100 * mgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
+        reports.append(load_report(wl, L))
         del L, g, x
         torch.cuda.empty_cache()
+    print()
+    print("| workload | L_aux (alpha) | counts min / max (hot / mean) | dropped (experts over C) | "
+          "sum f, max f | sum p, min p, max p |")
+    print("|---|---|---|---|---|---|")
+    for r in reports:
+        print(f"| {r['workload']} | {r['l_aux']:.5f} ({r['alpha']}) | {r['counts_min']} / {r['counts_max']} "
+              f"({r['hot_over_mean']:.2f}) | {r['dropped']} ({r['experts_over_capacity']}) | "
+              f"{r['f_sum']:.6f}, {r['f_max']:.5f} | {r['p_sum']:.6f}, {r['p_min']:.5f}, {r['p_max']:.5f} |")
+    print()
+    for r in reports:
+        if "counts" in r:
+            print(f"{r['workload']}: per-expert counts {r['counts']}; f {r['f']}; p {r['p']}")
 
 
 def decode(steps, warmup):
@@ -554,7 +598,9 @@ def main():
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": profiled_traffic(UP_KERNEL.get(wl.name)),
-                     "traffic_unit": "bytes per launch (HBM read + write)"},
+                     "traffic_unit": "bytes per launch: L2-miss bytes (FETCH_SIZE + WRITE_SIZE, each "
+                                     "scaled by a plain copy of known size); Infinity Cache hits "
+                                     "count as misses"},
         "grouped_gemm_pct_mfma_peak": 100.0 * (up + down + shared) / gemm_t / 1e12 / PEAK_BF16_TFLOPS,
         # route and dispatch run as one call, so their bytes are timed together
         "dispatch_GBps": (rb + db) / (ph_ms["route_dispatch"] * 1e-3) / 1e9,

@@ -19,26 +19,34 @@ from its own float64 logits.  Anything else is a mismatch.
 from __future__ import annotations
 
 import itertools
+import math
 
 import numpy as np
 
 from . import moe
 
 
-def _admissible_sets(scores: np.ndarray, allowed: np.ndarray, m: int, delta: float):
-    """All m-subsets of ``allowed`` indices admissible under the tie band."""
+def _band(scores: np.ndarray, allowed: np.ndarray, m: int, delta: float):
+    """The tie band of an m-selection among the ``allowed`` indices: ``must``
+    (scores clearly above the m-th largest, thr + delta) and ``band`` (scores
+    within delta of it).  An m-subset S is admissible exactly when
+    must <= S <= must | band."""
     cand = np.flatnonzero(allowed)
     vals = scores[cand]
     order = cand[np.argsort(-vals, kind="stable")]
     thr = scores[order[m - 1]]
-    must = [int(i) for i in cand if scores[i] > thr + delta]
-    band = [int(i) for i in cand if abs(scores[i] - thr) <= delta]
-    need = m - len(must)
-    if need < 0 or need > len(band):
-        return []
-    if len(band) > 16:                      # pathological: all equal; bound the enumeration
-        return None
-    return [set(must) | set(c) for c in itertools.combinations(band, need)]
+    must = {int(i) for i in cand if scores[i] > thr + delta}
+    band = {int(i) for i in cand if abs(scores[i] - thr) <= delta}
+    return must, band
+
+
+def _set_admissible(sel: set, must: set, band: set, m: int) -> bool:
+    return len(sel) == m and must <= sel and sel <= (must | band)
+
+
+# group sets enumerated at most (a tie among more groups is checked by the
+# necessary conditions only)
+_MAX_GROUP_SETS = 1 << 16
 
 
 def admissible(wl, l_t: np.ndarray, sel: np.ndarray, tol: float = 1e-5) -> bool:
@@ -53,25 +61,37 @@ def admissible(wl, l_t: np.ndarray, sel: np.ndarray, tol: float = 1e-5) -> bool:
     for a, b in zip(sel[:-1], sel[1:]):
         if l_t[a] < l_t[b] - delta:
             return False
-    if wl.n_groups > 1:
-        gsz = N // wl.n_groups
-        gs = moe.group_scores(l_t[None, :], wl.n_groups, wl.group_score_k)[0]
-        gsets = _admissible_sets(gs, np.ones(wl.n_groups, bool), wl.topk_groups, delta)
-        if gsets is None:
-            return True
-        masks = []
-        for gset in gsets:
-            mk = np.zeros(N, bool)
-            for g in gset:
-                mk[g * gsz:(g + 1) * gsz] = True
-            masks.append(mk)
-    else:
-        masks = [np.ones(N, bool)]
-    for mk in masks:
-        if not all(mk[e] for e in sel):
-            continue
-        sets = _admissible_sets(l_t, mk, k, delta)
-        if sets is None or set(sel) in sets:
+    S = set(sel)
+    if wl.n_groups <= 1:
+        must, band = _band(l_t, np.ones(N, bool), k, delta)
+        return _set_admissible(S, must, band, k)
+    G, gsz, kg = wl.n_groups, N // wl.n_groups, wl.topk_groups
+    gs = moe.group_scores(l_t[None, :], G, wl.group_score_k)[0]
+    gmust, gband = _band(gs, np.ones(G, bool), kg, delta)
+    used = {e // gsz for e in sel}
+    # the groups a selection may use: an admissible group set holds gmust, lies
+    # inside gmust | gband and has kg groups, so the used groups must fit too
+    if not used <= (gmust | gband):
+        return False
+    free = sorted(gband - gmust - used)
+    need = kg - len(gmust | used)
+    if need < 0 or need > len(free):
+        return False
+    if math.comb(len(free), need) > _MAX_GROUP_SETS:
+        # a tie among very many groups: every expert of the used and the
+        # clearly better groups is a candidate; the selection must hold every
+        # expert clearly above the band of that candidate set
+        mk = np.zeros(N, bool)
+        for g in gmust | used:
+            mk[g * gsz:(g + 1) * gsz] = True
+        must, band = _band(l_t, mk, k, delta)
+        return must <= S
+    for fill in itertools.combinations(free, need):
+        mk = np.zeros(N, bool)
+        for g in gmust | used | set(fill):
+            mk[g * gsz:(g + 1) * gsz] = True
+        must, band = _band(l_t, mk, k, delta)
+        if _set_admissible(S, must, band, k):
             return True
     return False
 

@@ -86,8 +86,9 @@ def top_k(l: np.ndarray, mask: np.ndarray, k: int) -> np.ndarray:
 
 def sparse_softmax(l: np.ndarray, idx: np.ndarray) -> np.ndarray:
     """w[t][j] = exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k selected
-    logits only ([Part5] "Apply Softmax only to the top-2 scores", generalised
-    to k; max-subtracted for stability as the kernel does)."""
+    logits only ([Part5] "1.1 The Router Kernel": the softmax runs over the two
+    kept scores alone; generalised here to k; max-subtracted for stability as
+    the kernel does)."""
     sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
     z = np.exp(sel - sel.max(axis=1, keepdims=True))
     return z / z.sum(axis=1, keepdims=True)

@@ -60,3 +60,39 @@ def test_rel_l2():
     a = np.array([1.0, 2.0, 2.0])
     assert compare.rel_l2(a, a) == 0.0
     assert abs(compare.rel_l2(a * 1.01, a) - 0.01) < 1e-12
+
+
+def test_twenty_way_tie_keeps_the_clear_winners():
+    """A token whose logits tie 20 ways below two clear leaders: any selection
+    of the leaders plus band members is admissible, one that leaves a leader
+    out is not (checked without enumerating the band's subsets)."""
+    w = wl(N=24, k=4)
+    l = np.zeros((1, 24))
+    l[0, 5], l[0, 17] = 3.0, 2.0
+    l[0, 20:] = -1.0                              # below the band
+    o = moe.top_k(l, np.ones_like(l, bool), 4)
+    assert o.tolist() == [[5, 17, 0, 1]]
+    r = compare.adopt(w, l, o, np.array([[5, 17, 19, 3]]))
+    assert r["adopted"] == [0] and r["bad"] == []
+    r = compare.adopt(w, l, o, np.array([[5, 19, 3, 2]]))       # leader 17 left out
+    assert r["bad"] == [0]
+    r = compare.adopt(w, l, o, np.array([[5, 17, 3, 21]]))      # 21 is below the band
+    assert r["bad"] == [0]
+
+
+def test_many_group_tie_keeps_the_clear_group():
+    """64 groups of one expert with 40 of them tied: a selection must keep the
+    clearly best group's expert, whichever tied groups fill the rest."""
+    w = wl(N=64, k=2, n_groups=64, topk_groups=20, group_score_k=1)
+    l = np.full((1, 64), -2.0)
+    l[0, :40] = 0.0
+    l[0, 50] = 5.0
+    mask = moe.group_mask(l, 64, 20, 1)
+    o = moe.top_k(l, mask, 2)
+    assert o.tolist() == [[50, 0]]
+    r = compare.adopt(w, l, o, np.array([[50, 33]]))
+    assert r["adopted"] == [0]
+    r = compare.adopt(w, l, o, np.array([[33, 12]]))             # the clear winner left out
+    assert r["bad"] == [0]
+    r = compare.adopt(w, l, o, np.array([[50, 45]]))             # expert 45 is below the band
+    assert r["bad"] == [0]

@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle.
 
 Small cases span several tiles of every kernel with ragged tails; full-size
-cases run the workloads at their real shapes (all of routing, the plan and the
-dispatch buffer compared; y on sampled tokens)."""
+cases run the workloads at their real shapes through moe_forward (all of
+routing, the plan, the dispatch buffer and y on every token compared), with
+the single-phase calls bit for bit equal to it."""
 import functools
 
 import numpy as np
@@ -304,6 +305,18 @@ FORWARD_CASES = {
     "many_tiles_capacity": lambda: si.Workload("mbf", T=20011, d=64, N=16, k=2, F=128,
                                                act="swiglu", dtype="bf16", buf="bf16",
                                                capacity=2300),
+    # 8-token router tiles: bf16 below 512 tokens (logits from split partials)
+    "split_logits_t300": lambda: si.small("mixtral", T=300),
+    "split_logits_t511_capacity_fp8": lambda: si.small("mixtral", T=511, N=16, k=4, buf="fp8",
+                                                       capacity=100),
+    # 8-token router tiles: wide routers (logits from the split-K GEMM), with
+    # capacity drops, the fp8 buffer, groups and the shared expert
+    "wide_router_fp8_capacity": lambda: si.Workload("wr", T=600, d=8192, N=64, k=4, F=128,
+                                                    act="swiglu", dtype="bf16", buf="fp8",
+                                                    capacity=40),
+    "wide_router_groups_shared": lambda: si.Workload("wrg", T=1003, d=8192, N=64, k=8, F=128,
+                                                     act="swiglu", dtype="bf16", buf="fp8",
+                                                     n_groups=8, topk_groups=4, shared=True),
 }
 
 
@@ -313,21 +326,23 @@ def test_forward_matches_oracle_and_phases(name):
     per-tile counts); its outputs must pass the oracle checks and equal, bit
     for bit, those of moe_route, moe_dispatch, moe_experts and moe_combine
     called one after the other."""
-    from moe_gpu_util import run_gpu_forward
     wl = FORWARD_CASES[name]()
     print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} cap={wl.capacity}", flush=True)
-    inp = si.generate(wl)
-    fwd = run_gpu_forward(wl, inp)
-    errs = check_layer(wl, inp, fwd, max_adopted=2)
+    _forward_and_phases(wl, si.generate(wl), max_adopted=2)
+
+
+def _forward_and_phases(wl, inp, y_tokens=None, max_adopted=None):
+    """moe_forward (the measured path: router tiles, per-tile bases and the
+    planned copy) against the oracle, then the single-phase calls (standalone
+    histogram and plan kernels) bit for bit against it; inputs uploaded once."""
+    from moe_gpu_util import assert_same_results, run_gpu_forward, upload
+    g = upload(wl, inp)
+    fwd = run_gpu_forward(wl, inp, g=g)
+    errs = check_layer(wl, inp, fwd, y_tokens=y_tokens, max_adopted=max_adopted)
     print(f"  {errs}", flush=True)
-    ph = run_gpu(wl, inp)
-    R = int(fwd["offsets"][-1])
-    for key in ("idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "drop", "y"):
-        assert np.array_equal(fwd[key], ph[key]), key
-    for key in ("src", "x_perm", "out"):
-        assert np.array_equal(fwd[key][:R], ph[key][:R]), key
-    if wl.buf == "fp8":
-        assert np.array_equal(fwd["row_scale"][:R], ph["row_scale"][:R])
+    ph = run_gpu(wl, inp, logits=False, g=g)
+    assert_same_results(fwd, ph, wl.buf == "fp8")
+    return fwd, errs
 
 
 # ------------------------------------------------------------ graph replay --
@@ -336,6 +351,7 @@ GRAPH_CASES = {
     "mixtral_ragged": lambda: si.small("mixtral", T=1001),
     "deepseek_fp8_groups_shared": lambda: si.small("deepseek_v3"),
     "one_token_split_paths": lambda: si.small("mixtral", T=1),
+    "deepseek_v3_full": lambda: si.WORKLOADS["deepseek_v3"],
 }
 
 
@@ -348,7 +364,7 @@ def test_graph_replay_matches_eager(name):
     from moe_gpu_util import upload
     wl = GRAPH_CASES[name]()
     print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k}", flush=True)
-    g = upload(wl, si.generate(wl))
+    g = upload(wl, _inputs(wl))
     s = M.shape_of(wl)
     L = M.Layer(s, g["wg"], g["w1"], g.get("w3"), g["w2"], bias=g.get("bias"), ws1=g.get("ws1"),
                 ws3=g.get("ws3"), ws2=g.get("ws2"))
@@ -384,28 +400,45 @@ def _deepseek_experts():
     return si.generate_experts(si.WORKLOADS["deepseek_v3"])
 
 
+def _inputs(wl):
+    """Seeded inputs; the DeepSeek-V3-shaped expert weights come from the
+    session's one draw."""
+    if wl.N == 256 and wl.d == 7168 and wl.F == 2048:
+        return dict(si.generate(wl, experts=False), **_deepseek_experts())
+    return si.generate(wl)
+
+
 @pytest.mark.parametrize("name", ["mixtral", "switch", "deepseek_v3", "dbrx"])
 def test_full_size_parity(name):
+    """Every workload at its full size through moe_forward, the path that is
+    benchmarked: routing, statistics, plan and dispatch buffer exact, the
+    expert outputs and y of every token against the float64 oracle (each row
+    on its own and the whole tensor), and the single-phase calls bit for bit
+    equal to it.  The DeepSeek-V3 shape also reports y against the same layer
+    without the fp8 dispatch step."""
     wl = si.WORKLOADS[name]
-    if name == "deepseek_v3":
-        inp = dict(si.generate(wl, experts=False), **_deepseek_experts())
-    else:
-        inp = si.generate(wl)
-    toks = sample_tokens(wl.T, 40)
-    _run_and_check(wl, inp, y_tokens=toks)
+    print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} F={wl.F}", flush=True)
+    gpu, errs = _forward_and_phases(wl, _inputs(wl))
+    if name == "switch":
+        print(f"  drops: {int(gpu['drop'].sum())}, experts over capacity: "
+              f"{int((gpu['counts'] > wl.capacity).sum())}", flush=True)
+        assert gpu["drop"].sum() > 0
+    if wl.buf == "fp8":
+        print(f"  y vs fp8-defined oracle {errs['y']:.4e}, vs oracle without fp8 step "
+              f"{errs['y_vs_no_fp8']:.4e}", flush=True)
+        assert errs["y_vs_no_fp8"] <= 2e-2
 
 
 @pytest.mark.parametrize("B", [1, 32, 128])
 def test_decode_step_deepseek_shape(B):
     """A decode step: B tokens (the prefill batch's first B) through the full
-    DeepSeek-V3-shaped layer, so most segments hold one row or none.  Routing,
-    plan and fp8 dispatch buffer exact; y on every token at B = 1, on 8
-    sampled tokens otherwise; the experts touched are those with a nonzero
-    count."""
+    DeepSeek-V3-shaped layer, so most segments hold one row or none.  Through
+    moe_forward (few-token router split, split-K GEMMs) against the oracle on
+    every token, and the single-phase calls bit for bit equal to it; the
+    experts touched are those with a nonzero count."""
     wl = si.decode(B)
-    inp = dict(si.generate(wl, experts=False), **_deepseek_experts())
-    toks = None if B == 1 else sample_tokens(B, 8)
-    gpu, _ = _run_and_check(wl, inp, y_tokens=toks)
+    print(f"case decode B={B}", flush=True)
+    gpu, _ = _forward_and_phases(wl, _inputs(wl))
     touched = int((gpu["counts"] > 0).sum())
     print(f"  experts touched: {touched} of {wl.N}", flush=True)
     assert touched <= min(wl.N, B * wl.k)

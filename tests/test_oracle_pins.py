@@ -52,19 +52,26 @@ def test_dispatch_buffer_bytes_from_a_real_plan():
     assert R * d * 1 == g["mib_fp8"] * 2 ** 20
 
 
-def experts_touched(experts, top_k, batch):
-    # the page's worked-example function (share of experts a decode step reads)
-    if not 0 < top_k <= experts or batch < 0:
-        raise ValueError("need 0 < top_k <= experts and batch >= 0")
-    return 1 - (1 - top_k / experts) ** batch
+def touched_share(n_experts, k, batch):
+    """Expected share of n_experts that a batch of tokens reads when each token
+    picks k of them uniformly: an expert is missed by one token with
+    probability 1 - k/n_experts, so by all of them with that to the power of
+    the batch size.  Arguments outside 0 < k <= n_experts, batch >= 0 are
+    rejected (the page's worked example states the same domain)."""
+    if batch < 0 or k <= 0 or k > n_experts:
+        raise ValueError(f"touched_share: bad arguments n={n_experts} k={k} batch={batch}")
+    miss_one = 1.0 - k / n_experts
+    return 1.0 - math.pow(miss_one, batch)
 
 
 def test_experts_touched_page_asserts():
     g = golden()["experts_touched"]
     for B, want in g["cases"]:
-        assert round(experts_touched(g["N"], g["k"], B), 3) == want
+        assert round(touched_share(g["N"], g["k"], B), 3) == want
     with pytest.raises(ValueError):
-        experts_touched(8, 9, 1)
+        touched_share(8, 9, 1)
+    with pytest.raises(ValueError):
+        touched_share(8, 2, -1)
 
 
 def test_experts_touched_empirical_deepseek_routing():
@@ -297,7 +304,8 @@ def test_dispatch_plan_invariants_and_drops():
     for e in range(N):
         seg = plan["src"][plan["offsets"][e]:plan["offsets"][e + 1]]
         assert np.all(np.diff(seg) > 0)
-        assert np.all(idx[seg] == e, axis=1).sum() == 0 or True
+        # every row of the segment is a token that chose e
+        assert all(e in idx[t] for t in seg)
         # drops: exactly max(0, counts - C), the highest-t tokens of the expert
         toks = np.flatnonzero(np.any(idx == e, axis=1))
         dropped = [t for t in toks if plan["drop"][t][list(idx[t]).index(e)]]
@@ -339,6 +347,36 @@ def test_relu_identity_experts_give_x():
     out = moe.forward(wl.replace(capacity=7, drop="zero"), inp)
     lost = np.where(out["drop"], out["w"], 0.0).sum(1)
     assert np.allclose(out["y"], x * (1 - lost)[:, None], atol=1e-12)
+
+
+def test_silu_and_swiglu_closed_forms():
+    """The SiLU and SwiGLU experts against closed forms that follow from
+    silu(v) = v * sigmoid(v) and sigmoid(v) + sigmoid(-v) = 1:
+      * silu(0) = 0, silu(1) = 1 / (1 + e^-1) = 0.7310585786300049...;
+      * SiLU with W1 = [I; -I], W2 = [I, I]: silu(v) + silu(-v) = v tanh(v/2)
+        (NumPy's tanh; a sign slip inside silu flips the result's sign);
+      * SwiGLU with W1 = [I; -I], W3 = [I; I], W2 = [I, -I]: the gate is v in
+        both halves, so the output is v (silu(v) - silu(-v)) = v * v (a swap of
+        the gate and W1 halves gives v^2 tanh(v/2) instead);
+    so the layer returns x tanh(x/2) and x * x (sum_j w_j = 1)."""
+    assert moe.activation("silu", np.array([0.0]))[0] == 0.0
+    assert moe.activation("silu", np.array([1.0]))[0] == pytest.approx(0.7310585786300049, rel=1e-15)
+    d, N, k, T = 12, 4, 2, 30
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((T, d)) * 3).astype(np.float32)
+    eye = np.eye(d, dtype=np.float32)
+    W1 = np.concatenate([eye, -eye])
+    common = {"x": x, "wg": rng.standard_normal((N, d)).astype(np.float32), "bias": None}
+    xs = x.astype(np.float64)
+    wl = si.Workload("silu_cf", T=T, d=d, N=N, k=k, F=2 * d, act="silu", dtype="f32", buf="f32")
+    out = moe.forward(wl, dict(common, w1=np.stack([W1] * N), w3=None,
+                               w2=np.stack([np.concatenate([eye, eye], axis=1)] * N)))
+    assert np.allclose(out["y"], xs * np.tanh(xs / 2.0), rtol=1e-12, atol=1e-12)
+    wl = wl.replace(name="swiglu_cf", act="swiglu")
+    out = moe.forward(wl, dict(common, w1=np.stack([W1] * N),
+                               w3=np.stack([np.concatenate([eye, eye])] * N),
+                               w2=np.stack([np.concatenate([eye, -eye], axis=1)] * N)))
+    assert np.allclose(out["y"], xs * xs, rtol=1e-12, atol=1e-12)
 
 
 def test_shared_identity_doubles():
