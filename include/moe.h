@@ -62,8 +62,14 @@ typedef enum {
   MOE_ERR_ARG = 1,
   MOE_ERR_UNSUPPORTED = 2,
   MOE_ERR_WORKSPACE = 3,
-  MOE_ERR_HIP = 4
+  MOE_ERR_HIP = 4,
+  MOE_ERR_TOO_LARGE = 5   /* moe_route_dispatch_noalloc: the shape's scratch exceeds
+                             MOE_STATIC_SCRATCH_BYTES */
 } moe_status;
+
+/* Size of the library's static device scratch (one per GPU, held until the
+ * process ends), used only by moe_route_dispatch_noalloc. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act;
@@ -236,6 +242,26 @@ moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g
                               int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
                               void* x_perm, float* row_scale, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* moe_route_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its kernels' scratch (router partials,
+ * per-tile counts and bases, split logits) lives in a static device array of
+ * MOE_STATIC_SCRATCH_BYTES (48 MiB) per GPU; the call allocates nothing.  The
+ * caller still passes every input and output; arguments, layouts, results and
+ * the other errors are those of moe_route_dispatch.  A shape whose scratch
+ * (the router regions of moe_workspace_bytes' layout: about 12 bytes per
+ * 8 tokens per expert, plus up to 32 MiB of partial logits for wide routers
+ * or fewer than 512 tokens) exceeds the array returns MOE_ERR_TOO_LARGE
+ * before any launch.  Every call on one GPU shares that GPU's array: calls
+ * that may overlap in time on one GPU (different streams, or threads) race
+ * and give undefined results; serialise them, or use moe_route_dispatch with
+ * separate workspaces. */
+moe_status moe_route_dispatch_noalloc(const moe_shape* s, const void* x, const void* w_g,
+                                      const float* bias, int32_t* idx, float* w, int32_t* counts,
+                                      int32_t* kept_counts, float* p, float* f, float* l_aux,
+                                      int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                                      void* x_perm, float* row_scale, void* stream);
 
 /* The whole layer: moe_route_dispatch, moe_experts, moe_combine, enqueued on
  * one stream; results equal those of the four single-phase calls.  Every

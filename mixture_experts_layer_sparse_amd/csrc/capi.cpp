@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -120,6 +121,7 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or type combination";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_TOO_LARGE: return "shape needs more scratch than the static buffer holds";
   }
   return "unknown status";
 }
@@ -257,21 +259,31 @@ moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shar
                                         static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g,
-                              const float* bias, int32_t* idx, float* w, int32_t* counts,
-                              int32_t* kept_counts, float* p, float* f, float* l_aux,
-                              int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
-                              void* x_perm, float* row_scale, void* ws, size_t ws_bytes,
-                              void* stream) {
-  moe_status r = check_shape(s);
-  if (r != MOE_OK) return r;
-  if (s->T == 0) return MOE_OK;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_route_dispatch (before the workspace), shared with
+// its no-allocation variant.
+moe_status route_dispatch_args(const moe_shape* s, const void* x, const void* w_g, int32_t* idx,
+                               float* w, int32_t* counts, int32_t* kept_counts, int32_t* offsets,
+                               int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm,
+                               float* row_scale) {
   if (!x || !w_g || !idx || !w || !counts || !kept_counts || !offsets || !pos || !src || !drop ||
-      !x_perm || !ws)
+      !x_perm)
     return MOE_ERR_ARG;
   if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+// Launches of moe_route_dispatch on a checked shape, with ws holding at least
+// ws_layout(*s).disp_hist bytes.
+moe_status route_dispatch_launch(const moe_shape* s, const void* x, const void* w_g,
+                                 const float* bias, int32_t* idx, float* w, int32_t* counts,
+                                 int32_t* kept_counts, float* p, float* f, float* l_aux,
+                                 int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                                 void* x_perm, float* row_scale, void* ws, void* stream) {
   const WsLayout L = moe::ws_layout(*s);
-  if (ws_bytes < L.disp_hist) return MOE_ERR_WORKSPACE;
   // the router's per-tile counts give every tile's base, so the row copy
   // places its token itself; the results equal moe_route then moe_dispatch
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -289,6 +301,74 @@ moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g
     e = moe::launch_dispatch_copy_planned(*s, x, idx, tbase, offsets, pos, src, drop, x_perm,
                                           row_scale, st);
   return hip_status(e);
+}
+
+// Scratch of moe_route_dispatch_noalloc: one array per GPU, held until the
+// process ends.  Host code must not pass the array's name to a kernel (on the
+// host it only stands in for the symbol); the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int kMaxDevices = 64;
+static_assert(MOE_STATIC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route_dispatch(const moe_shape* s, const void* x, const void* w_g,
+                              const float* bias, int32_t* idx, float* w, int32_t* counts,
+                              int32_t* kept_counts, float* p, float* f, float* l_aux,
+                              int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                              void* x_perm, float* row_scale, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status r = check_shape(s);
+  if (r != MOE_OK) return r;
+  if (s->T == 0) return MOE_OK;
+  r = route_dispatch_args(s, x, w_g, idx, w, counts, kept_counts, offsets, pos, src, drop, x_perm,
+                          row_scale);
+  if (r != MOE_OK) return r;
+  if (!ws) return MOE_ERR_ARG;
+  if (ws_bytes < moe::ws_layout(*s).disp_hist) return MOE_ERR_WORKSPACE;
+  return route_dispatch_launch(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets,
+                               pos, src, drop, x_perm, row_scale, ws, stream);
+}
+
+moe_status moe_route_dispatch_noalloc(const moe_shape* s, const void* x, const void* w_g,
+                                      const float* bias, int32_t* idx, float* w, int32_t* counts,
+                                      int32_t* kept_counts, float* p, float* f, float* l_aux,
+                                      int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                                      void* x_perm, float* row_scale, void* stream) {
+  moe_status r = check_shape(s);
+  if (r != MOE_OK) return r;
+  if (s->T == 0) return MOE_OK;
+  r = route_dispatch_args(s, x, w_g, idx, w, counts, kept_counts, offsets, pos, src, drop, x_perm,
+                          row_scale);
+  if (r != MOE_OK) return r;
+  if (moe::ws_layout(*s).disp_hist > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  r = static_scratch(&ws);
+  if (r != MOE_OK) return r;
+  // every scratch word the kernels read is written earlier in the same call
+  // (per-tile partials, the split logits, the arrival counter zeroed by the
+  // router kernel), so nothing is cleared here
+  return route_dispatch_launch(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets,
+                               pos, src, drop, x_perm, row_scale, ws, stream);
 }
 
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,

@@ -17,7 +17,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
-MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_TOO_LARGE = range(6)
+STATIC_SCRATCH_BYTES = 48 << 20      # MOE_STATIC_SCRATCH_BYTES
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_ACT_SILU, MOE_ACT_RELU, MOE_ACT_SWIGLU = range(3)
 MOE_DROP_PASSTHROUGH, MOE_DROP_ZERO, MOE_DROP_FALLBACK = range(3)
@@ -89,6 +90,7 @@ _SIGS = {
     "moe_route": (c_int32, [POINTER(Shape)] + [_P] * 11 + [_P, c_size_t, _P]),
     "moe_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 8 + [_P, c_size_t, _P]),
     "moe_route_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P, c_size_t, _P]),
+    "moe_route_dispatch_noalloc": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P]),
     "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
     "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
     "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
@@ -212,16 +214,19 @@ def dispatch(s: Shape, x, idx, ws=None, out=None) -> dict:
     return o
 
 
-def route_dispatch(s: Shape, x, wg, bias=None, ws=None) -> dict:
+def route_dispatch(s: Shape, x, wg, bias=None, ws=None, noalloc=False, out=None) -> dict:
     """moe_route_dispatch: the outputs of route() and dispatch() (no logits)
-    from one call, with the dispatch plan folded into the row copy."""
+    from one call, with the dispatch plan folded into the row copy.  With
+    ``noalloc`` the call is moe_route_dispatch_noalloc (the library's static
+    scratch, no workspace; ``ws`` is ignored).  ``out``: output tensors to
+    fill (as returned by an earlier call), else allocated here."""
     T, N, k, d = s.T, s.N, s.k, s.d
     dev = x.device
     _check(x, "x", (T, d), s.torch_dtype)
     _check(wg, "wg", (N, d), s.torch_dtype)
     _check(bias, "bias", (N,), torch.float32, required=False)
     fp8 = s.buf_dtype == MOE_FP8_E4M3
-    o = {
+    o = out if out is not None else {
         "idx": torch.empty((T, k), dtype=torch.int32, device=dev),
         "w": torch.empty((T, k), dtype=torch.float32, device=dev),
         "counts": torch.empty(N, dtype=torch.int32, device=dev),
@@ -236,11 +241,15 @@ def route_dispatch(s: Shape, x, wg, bias=None, ws=None) -> dict:
         "x_perm": torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=dev),
         "row_scale": torch.empty(T * k, dtype=torch.float32, device=dev) if fp8 else None,
     }
+    args = [ctypes.byref(s), _ptr(x), _ptr(wg), _ptr(bias), _ptr(o["idx"]), _ptr(o["w"]),
+            _ptr(o["counts"]), _ptr(o["kept_counts"]), _ptr(o["p"]), _ptr(o["f"]), _ptr(o["l_aux"]),
+            _ptr(o["offsets"]), _ptr(o["pos"]), _ptr(o["src"]), _ptr(o["drop"]), _ptr(o["x_perm"]),
+            _ptr(o.get("row_scale"))]
+    if noalloc:
+        _call("moe_route_dispatch_noalloc", *args, _stream())
+        return o
     ws = ws if ws is not None else alloc_workspace(s, dev)
-    _call("moe_route_dispatch", ctypes.byref(s), _ptr(x), _ptr(wg), _ptr(bias), _ptr(o["idx"]),
-          _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["kept_counts"]), _ptr(o["p"]), _ptr(o["f"]),
-          _ptr(o["l_aux"]), _ptr(o["offsets"]), _ptr(o["pos"]), _ptr(o["src"]), _ptr(o["drop"]),
-          _ptr(o["x_perm"]), _ptr(o.get("row_scale")), _ptr(ws), ws.numel(), _stream())
+    _call("moe_route_dispatch", *args, _ptr(ws), ws.numel(), _stream())
     return o
 
 
