@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the layer with the dispatch buffer (row copy, then the up GEMM on it) "
+                         "instead of the fused gather")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens whose expert FFNs the CPU oracle runs (0: all T)")
     ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep", "decode", "memory"],
@@ -59,15 +62,51 @@ def parse():
     return ap.parse_args()
 
 
-def alg_bytes(wl, R):
-    """Algorithmic (minimum) HBM bytes of the memory phases; R kept rows."""
+def alg_bytes(wl, R, fused=False):
+    """Algorithmic (minimum) HBM bytes of the memory phases; R kept rows.
+    Fused (no dispatch buffer): the dispatch phase is the plan alone (idx read,
+    pos, drop and src written), plus for an fp8 buffer the one quantising pass
+    over x (codes in token order, one scale per kept row)."""
     sx = 2 if wl.dtype == "bf16" else 4
     sb = 1 if wl.buf == "fp8" else sx
     T, d, N, k = wl.T, wl.d, wl.N, wl.k
     route = T * d * sx + N * d * sx + 8 * T * k + 4 * N
-    dispatch = T * d * sx + R * d * sb + (4 * R if wl.buf == "fp8" else 0) + 8 * T * k + 4 * R
+    if fused:
+        dispatch = 9 * T * k + 4 * R + ((T * d * sx + T * d + 4 * R) if wl.buf == "fp8" else 0)
+    else:
+        dispatch = T * d * sx + R * d * sb + (4 * R if wl.buf == "fp8" else 0) + 8 * T * k + 4 * R
     combine = R * d * sx + T * d * sx + (T * d * sx if wl.shared else 0) + 8 * T * k
     return route, dispatch, combine
+
+
+def layer_step(wl, L, x, h, hs):
+    """One layer forward phase by phase, the kernels of moe_forward (fused or
+    not, as the layer was made), with HIP events recorded between the phases
+    when given: ev[0] before, ev[1] after route + dispatch (or route + plan),
+    ev[2] after the up GEMM, ev[3] after the down GEMM, ev[4] after the shared
+    expert, ev[5] after the combine."""
+    from mixture_experts_layer_sparse_amd import moe as M
+    s = L.s
+
+    def step(ev=None):
+        ev and ev[0].record()
+        if L.fused:
+            L.route_plan(x)
+            ev and ev[1].record()
+            L.expert_up_gather(x, h)
+        else:
+            L.route_dispatch(x)
+            ev and ev[1].record()
+            M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
+        ev and ev[2].record()
+        M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
+        ev and ev[3].record()
+        if wl.shared:
+            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared, ws=L.ws)
+        ev and ev[4].record()
+        L.combine(x)
+        ev and ev[5].record()
+    return step
 
 
 def gemm_flops(wl, R):
@@ -109,12 +148,19 @@ def cpu_baseline(wl, inp, n_tok):
 
 COUNTER_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_mixtral_counters.md")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sparse_amd", "csrc", "gemm.hip")
+# counter passes of the summary (each pass its own rocprofv3 run): name, counters
+COUNTER_PASSES = [
+    ("fetch", "FETCH_SIZE"),
+    ("write", "WRITE_SIZE"),
+    ("mfma", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE"),
+    ("lds", "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE"),
+    ("occ", "OccupancyPercent"),
+]
 PROFILE_CMDS = [
-    "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- python3 bench.py",
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
-    "python3 bench.py --no-cpu-baseline --steps 3 --warmup 1",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
-    "python3 bench.py --no-cpu-baseline --steps 3 --warmup 1",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
+    "python3 bench.py --no-cpu-baseline",
+    *[f"rocprofv3 --pmc {c} --output-format csv -d <dir>/{n} -o run -- "
+      "python3 bench.py --no-cpu-baseline --steps 3 --warmup 1" for n, c in COUNTER_PASSES],
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/cfetch -o run -- python3 bench.py --mode copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/cwrite -o run -- python3 bench.py --mode copy",
 ]
@@ -128,8 +174,8 @@ def _src_hash(path):
 
 def _short(name):
     for key in ("gg_splitk_reduce", "gg_kernel", "logits_split_kernel", "route_kernel", "route_stats_kernel",
-                "disp_hist_kernel", "disp_plan_kernel", "disp_copy_kernel", "disp_fp8_kernel",
-                "combine_bf16_kernel", "combine_f32_kernel", "__amd_rocclr_copyBuffer"):
+                "disp_hist_kernel", "disp_plan_tiles_kernel", "disp_plan_kernel", "disp_copy_kernel",
+                "disp_fp8_kernel", "combine_bf16_kernel", "combine_f32_kernel", "__amd_rocclr_copyBuffer"):
         if key in name:
             i = name.find(key)
             j = name.find("(", i)
@@ -137,59 +183,109 @@ def _short(name):
     return None
 
 
-def summarize(prof, out):
-    """Markdown summary of a rocprofv3 session of this benchmark: average
-    kernel durations, HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE scaled
-    by what the same counters read for a plain copy of known size."""
+def summarize(prof, out, steps, warmup):
+    """Markdown summary of a rocprofv3 session of this benchmark: per kernel,
+    the average duration over the timed steps only (dispatches warmup ..
+    warmup + steps - 1 of that kernel, in start order: the bench launches each
+    kernel once per step, and its warm-up, check and graph-replay calls come
+    before or after), its registers and LDS from the trace, the L2-miss bytes
+    per dispatch from FETCH_SIZE / WRITE_SIZE scaled by what the same counters
+    read for a plain copy of known size, MFMA busy share, LDS bank-conflict
+    cycles and occupancy."""
     import csv
     from collections import defaultdict
 
+    def rows_of(sub, fname):
+        path = os.path.join(prof, sub, fname)
+        if not os.path.exists(path):
+            return []
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
     def counters(sub, name):
         agg = defaultdict(list)
-        with open(os.path.join(prof, sub, "run_counter_collection.csv")) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] == name:
-                    k = _short(r["Kernel_Name"])
-                    if k:
-                        agg[k].append(float(r["Counter_Value"]))
+        for r in rows_of(sub, "run_counter_collection.csv"):
+            if r["Counter_Name"] == name:
+                k = _short(r["Kernel_Name"])
+                if k:
+                    agg[k].append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in agg.items()}
 
-    stats = {}
-    with open(os.path.join(prof, "trace", "run_kernel_stats.csv")) as f:
-        for r in csv.DictReader(f):
-            k = _short(r["Name"])
-            if k:
-                stats[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    calls = defaultdict(list)
+    for r in rows_of("trace", "run_kernel_trace.csv"):
+        k = _short(r["Kernel_Name"])
+        if k:
+            calls[k].append(r)
+    kern = {}
+    for k, rs in calls.items():
+        rs.sort(key=lambda r: int(r["Start_Timestamp"]))
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        timed = dur[warmup:warmup + steps] if len(dur) >= warmup + steps else dur
+        r0 = rs[0]
+        regs = (f"{r0.get('Arch_VGPR_Count', '?')}+{r0.get('Accum_VGPR_Count', '?')} / "
+                f"{r0.get('SGPR_Count', '?')} / {int(r0.get('LDS_Block_Size', 0) or 0) // 1024} / "
+                f"{r0.get('Scratch_Size', '?')}")
+        kern[k] = {"calls": len(dur), "timed_us": sum(timed) / len(timed), "all_us": sum(dur) / len(dur),
+                   "regs": regs, "wg": r0.get("Workgroup_Size_X", "?"), "grid": r0.get("Grid_Size_X", "?")}
     fetch, write = counters("fetch", "FETCH_SIZE"), counters("write", "WRITE_SIZE")
     cf = counters("cfetch", "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
     cw = counters("cwrite", "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    mfma, mops = counters("mfma", "MfmaUtil"), counters("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    gui = counters("mfma", "GRBM_GUI_ACTIVE")
+    bankc, ldsact = counters("lds", "SQ_LDS_BANK_CONFLICT"), counters("lds", "SQ_LDS_IDX_ACTIVE")
+    occ = counters("occ", "OccupancyPercent")
     copy_kib = (1 << 28) / 1024
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
-    rows, table = {}, []
-    for k, (calls, us) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+    rows, table, table2 = {}, [], []
+    for k, v in sorted(kern.items(), key=lambda kv: -kv[1]["timed_us"]):
         if k.startswith("__amd"):
             continue
         fb = fetch.get(k, 0.0) * 1024 * f_scale
         wb = write.get(k, 0.0) * 1024 * w_scale
-        rows[k] = {"avg_us": us, "fetch_bytes": fb, "write_bytes": wb}
-        table.append(f"| `{k}` | {calls} | {us:.1f} | {fb / 2**20:.1f} | {wb / 2**20:.1f} |")
+        rows[k] = {"avg_us": v["timed_us"], "avg_us_all_calls": v["all_us"], "fetch_bytes": fb,
+                   "write_bytes": wb}
+        table.append(f"| `{k}` | {v['calls']} | {v['timed_us']:.1f} | {v['all_us']:.1f} | {fb / 2**20:.1f} | "
+                     f"{wb / 2**20:.1f} |")
+        # the shader clock under the profiler: active GPU cycles over the dispatch's duration
+        clk = gui.get(k, 0.0) / (v["all_us"] * 1e3) if k in gui else 0.0
+        bf16_tflop = mops.get(k, 0.0) * 512 / 1e12
+        table2.append(f"| `{k}` | {v['regs']} | {v['wg']} x {int(v['grid']) // max(int(v['wg']), 1) if str(v['grid']).isdigit() else '?'} | "
+                      f"{mfma.get(k, 0.0):.1f} | {bf16_tflop:.3f} | {bankc.get(k, 0.0):.3g} | "
+                      f"{ldsact.get(k, 0.0):.3g} | {occ.get(k, 0.0):.1f} | {clk:.2f} |")
     data = {"gemm_src_sha256_16": _src_hash(GEMM_SRC), "fetch_scale": f_scale,
-            "write_scale": w_scale, "kernels": rows}
+            "write_scale": w_scale, "timed_steps": [warmup, steps], "kernels": rows}
     text = "\n".join([
-        "# Grouped GEMM and memory kernels, Mixtral-shaped layer (T=4096, d=4096, N=8, k=2, F=14336, bf16)",
+        "# Kernels of one layer forward, Mixtral-shaped layer (T=4096, d=4096, N=8, k=2, F=14336, bf16)",
         "",
         "rocprofv3 on one MI355X; commands (run from the repository root, `<dir>` a scratch directory):",
         "",
         *[f"    {c}" for c in PROFILE_CMDS],
         "",
-        "Summarised with `python3 bench.py --mode summarize --prof <dir> --out <this file>`.",
+        f"Summarised with `python3 bench.py --mode summarize --prof <dir> --out <this file>`. Durations are "
+        f"averaged over the timed steps only (each kernel's dispatches {warmup} to {warmup + steps - 1} in start "
+        f"order); the average over all dispatches (warm-up, the check call and the graph replays included) "
+        f"is beside it.",
         "",
-        f"Counter scale factors from the 256 MiB copy: FETCH_SIZE x {f_scale:.3f}, "
-        f"WRITE_SIZE x {w_scale:.3f} (the copy reads and writes 256 MiB each).",
+        f"L2-miss bytes: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} (the factors that make a plain "
+        f"256 MiB copy read and write 256 MiB). These count every L2 miss, whether the Infinity Cache or HBM "
+        f"serves it.",
         "",
-        "| kernel | calls | avg us | HBM read MiB/dispatch | HBM write MiB/dispatch |",
-        "|---|---|---|---|---|",
+        "| kernel | dispatches | avg us (timed) | avg us (all) | L2-miss read MiB/dispatch | "
+        "L2-miss write MiB/dispatch |",
+        "|---|---|---|---|---|---|",
         *table,
+        "",
+        "Registers (arch VGPR + accumulation VGPR / SGPR), LDS KiB and scratch bytes per lane from the kernel "
+        "trace; workgroup size x workgroups; MfmaUtil = MFMA-busy cycles / (active cycles x SIMDs), %; bf16 "
+        "MFMA TFLOP per dispatch from SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS bank-conflict and LDS-active "
+        "cycles (summed over the SEs); OccupancyPercent; clock = GRBM_GUI_ACTIVE cycles per dispatch over the "
+        "dispatch's average duration, GHz (the counter runs are short, so their first dispatches run at a "
+        "higher clock than a long run).",
+        "",
+        "| kernel | VGPR / SGPR / LDS / scratch | launch | MfmaUtil % | bf16 MFMA TFLOP | LDS bank-conflict "
+        "cycles | LDS active cycles | occupancy % | clock GHz |",
+        "|---|---|---|---|---|---|---|---|---|",
+        *table2,
         "",
         "Machine-readable (bench.py reads this to fill `roofline.traffic` while `gemm.hip` is unchanged):",
         "",
@@ -259,7 +355,7 @@ def _to_dev(arr):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
-def _phases(wl, g, x, steps, warmup):
+def _phases(wl, g, x, steps, warmup, fused=True):
     """Runs the kernels of moe_forward phase by phase; returns (layer, mean
     phase times in us [route+dispatch, up, down, shared, combine], wall time
     per step in s)."""
@@ -268,23 +364,10 @@ def _phases(wl, g, x, steps, warmup):
     from mixture_experts_layer_sparse_amd import moe as M
     s = M.shape_of(wl)
     L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
-                ws3=g["ws3"], ws2=g["ws2"])
+                ws3=g["ws3"], ws2=g["ws2"], fused=fused)
     h = torch.empty((wl.T * wl.k, wl.F), dtype=s.torch_dtype, device="cuda")
     hs = torch.empty((wl.T, wl.F), dtype=s.torch_dtype, device="cuda") if wl.shared else None
-
-    def step(ev):
-        ev[0].record()
-        L.route_dispatch(x)
-        ev[1].record()
-        M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
-        ev[2].record()
-        M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
-        ev[3].record()
-        if wl.shared:
-            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared, ws=L.ws)
-        ev[4].record()
-        L.combine(x)
-        ev[5].record()
+    step = layer_step(wl, L, x, h, hs)
 
     E = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps + warmup)]
     for i in range(warmup):
@@ -342,7 +425,7 @@ def sweep(steps, warmup):
         L, ph, wall = _phases(wl, g, x, steps, warmup)
         R = int(L.offsets[-1].item())
         up, down, shared = gemm_flops(wl, R)
-        rb, db, cb = alg_bytes(wl, R)
+        rb, db, cb = alg_bytes(wl, R, fused=True)
         gemm_us = ph[1] + ph[2] + ph[3]
         tf = (up + down + shared) / (gemm_us * 1e-6) / 1e12
         wgb = expert_weight_bytes(wl) / (gemm_us * 1e-6) / 1e9
@@ -466,6 +549,11 @@ def memory(steps, warmup):
         rb, db, cb = alg_bytes(wl, R)
         label = f"{name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k})"
         row(label, "route + dispatch", rb + db, lambda: L.route_dispatch(x))
+        Lf = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
+                     ws3=g["ws3"], ws2=g["ws2"], fused=True)
+        rf, df, _ = alg_bytes(wl, R, fused=True)
+        row(label, "route + plan (fused layer)", rf + df, lambda: Lf.route_plan(x))
+        del Lf
         row(label, "route", rb, lambda: L.route(x))
         row(label, "dispatch", db, lambda: L.dispatch(x))
         row(label, "combine", cb, lambda: L.combine(x))
@@ -476,7 +564,7 @@ def memory(steps, warmup):
 def main():
     a = parse()
     if a.mode == "summarize":
-        summarize(a.prof, a.out or COUNTER_FILE)
+        summarize(a.prof, a.out or COUNTER_FILE, a.steps, a.warmup)
         return
     if a.mode == "sweep":
         sweep(a.steps, a.warmup)
@@ -518,46 +606,30 @@ def main():
 
     g = {k: dev(v) for k, v in inp.items()}
     s = M.shape_of(wl)
+    fused = not a.unfused
     L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
-                ws3=g["ws3"], ws2=g["ws2"])
+                ws3=g["ws3"], ws2=g["ws2"], fused=fused)
     x = g["x"]
     dt = s.torch_dtype
     h = torch.empty((wl.T * wl.k, wl.F), dtype=dt, device="cuda")
     hs = torch.empty((wl.T, wl.F), dtype=dt, device="cuda") if wl.shared else None
-
-    def step(ev=None):
-        # the same kernels as moe_forward, phase by phase (route + dispatch is
-        # one call: the dispatch plan is folded into the row copy)
-        L.route_dispatch(x)
-        ev and ev[1].record()
-        M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
-        ev and ev[2].record()
-        M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
-        ev and ev[3].record()
-        if wl.shared:
-            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared, ws=L.ws)
-        ev and ev[4].record()
-        L.combine(x)
+    # the same kernels as moe_forward, phase by phase
+    step = layer_step(wl, L, x, h, hs)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    E = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(a.steps)]
+    E = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        E[i][5].record()
         step(E[i])
-        E[i][6].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ph = {"route_dispatch": [], "gemm_up": [], "gemm_down": [], "shared": [], "combine": []}
     for e in E:
-        ph["route_dispatch"].append(e[5].elapsed_time(e[1]))
-        ph["gemm_up"].append(e[1].elapsed_time(e[2]))
-        ph["gemm_down"].append(e[2].elapsed_time(e[3]))
-        ph["shared"].append(e[3].elapsed_time(e[4]))
-        ph["combine"].append(e[4].elapsed_time(e[6]))
+        for j, key in enumerate(ph):
+            ph[key].append(e[j].elapsed_time(e[j + 1]))
     ph_ms = {k: float(np.mean(v)) for k, v in ph.items()}
     ms = wall * 1e3 / a.steps
     R = int(L.offsets[-1].item())
@@ -572,7 +644,7 @@ def main():
     gwall = graph_step_time(lambda: L.forward(x), a.steps, a.warmup)
 
     up, down, shared = gemm_flops(wl, R)
-    rb, db, cb = alg_bytes(wl, R)
+    rb, db, cb = alg_bytes(wl, R, fused)
     t_up = ph_ms["gemm_up"] * 1e-3
     achieved = up / t_up / 1e12
     gemm_t = (ph_ms["gemm_up"] + ph_ms["gemm_down"] + ph_ms["shared"]) * 1e-3
@@ -591,7 +663,8 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "N": wl.N, "k": wl.k, "F": wl.F,
-                   "act": wl.act, "dispatch_buffer": wl.buf, "capacity": wl.capacity,
+                   "act": wl.act, "dispatch_buffer": "none (fused gather)" if fused else wl.buf,
+                   "activations": wl.buf, "capacity": wl.capacity,
                    "groups": [wl.n_groups, wl.topk_groups], "shared_expert": wl.shared,
                    "kept_rows": R},
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM up (gate/up + activation)",
@@ -604,7 +677,8 @@ def main():
         "grouped_gemm_pct_mfma_peak": 100.0 * (up + down + shared) / gemm_t / 1e12 / PEAK_BF16_TFLOPS,
         # route and dispatch run as one call, so their bytes are timed together
         "dispatch_GBps": (rb + db) / (ph_ms["route_dispatch"] * 1e-3) / 1e9,
-        "dispatch_GBps_covers": "route + dispatch (moe_route_dispatch)",
+        "dispatch_GBps_covers": ("route + plan (moe_route_plan; no dispatch copy: the up GEMM gathers x "
+                                 "through src)") if fused else "route + dispatch (moe_route_dispatch)",
         "combine_GBps": cb / (ph_ms["combine"] * 1e-3) / 1e9,
         "memory_phases": {"bytes": rb + db + cb, "us": mem_t * 1e6,
                           "GBps": (rb + db + cb) / mem_t / 1e9,

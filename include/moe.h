@@ -263,10 +263,41 @@ moe_status moe_route_dispatch_noalloc(const moe_shape* s, const void* x, const v
                                       int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
                                       void* x_perm, float* row_scale, void* stream);
 
+/* Route then plan, without the expert-ordered copy of x: the first phase of the
+ * fused layer, whose up GEMM reads each row of x through src
+ * (moe_expert_up_gather).  "MoE: what it costs to train and serve" / "In
+ * short" and "Expert parallelism and two all-to-alls": the dispatch overlaps
+ * with the expert computation instead of running as its own pass.  Outputs and
+ * errors as moe_route_dispatch (idx, w, counts, kept_counts, p, f, l_aux,
+ * offsets, pos, src, drop are identical), except:
+ *   x_codes   [T][d] uint8 out (FP8 buffer only, else ignored): token t's e4m3
+ *             codes in row t (moe_dispatch's quantiser, stored once per token)
+ *   row_scale [T*k] float32 out (FP8 buffer only): the token's scale at each
+ *             kept slot's position, as moe_dispatch writes it. */
+moe_status moe_route_plan(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                          int32_t* idx, float* w, int32_t* counts, int32_t* kept_counts, float* p,
+                          float* f, float* l_aux, int32_t* offsets, int32_t* pos, int32_t* src,
+                          uint8_t* drop, void* x_codes, float* row_scale, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* moe_expert_up with a gathered operand: row r of expert e's segment reads row
+ * src[r] of a ([T][d]: x for a bf16/f32 buffer, the token-order codes of
+ * moe_route_plan for an FP8 buffer, with row_scale [T*k] by position).  h and
+ * the arithmetic are those of moe_expert_up on the dispatch buffer (bit for
+ * bit the same).  MOE_ERR_UNSUPPORTED when T*d*element size exceeds 4 GiB - 1
+ * (32-bit row offsets).  ws as for moe_expert_up. */
+moe_status moe_expert_up_gather(const moe_shape* s, const void* a, const float* row_scale,
+                                const int32_t* offsets, const int32_t* src, const void* w1,
+                                const void* w3, void* h, void* ws, size_t ws_bytes, void* stream);
+
 /* The whole layer: moe_route_dispatch, moe_experts, moe_combine, enqueued on
  * one stream; results equal those of the four single-phase calls.  Every
  * output buffer is required except p, f, l_aux (may be NULL) and the
- * shared-expert buffers (ignored unless has_shared). */
+ * shared-expert buffers (ignored unless has_shared).  With x_perm == NULL the
+ * layer runs fused: moe_route_plan, moe_expert_up_gather, moe_expert_down,
+ * the shared expert and moe_combine, with no dispatch buffer (row_scale may
+ * then be NULL too; the fp8 codes and scales live in the workspace); every
+ * other output is bit for bit that of the unfused call. */
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
                        const void* w1, const void* w3, const void* w2,
                        const void* ws1, const void* ws3, const void* ws2,

@@ -37,6 +37,11 @@ WsLayout ws_layout(const moe_shape& s) {
                                 moe::router_gemm_bytes(s)));
   L.disp_hist = off;
   off = align_up(off + nb_disp * N * 4);
+  const bool fp8 = s.buf_dtype == MOE_FP8_E4M3;
+  L.x_codes = off;
+  if (fp8) off = align_up(off + T * static_cast<size_t>(s.d));
+  L.rscale = off;
+  if (fp8) off = align_up(off + T * static_cast<size_t>(s.k) * 4);
   L.gemm_split = off;
   off = align_up(off + moe::gemm_split_bytes(s));
   L.h = off;
@@ -371,6 +376,60 @@ moe_status moe_route_dispatch_noalloc(const moe_shape* s, const void* x, const v
                                pos, src, drop, x_perm, row_scale, ws, stream);
 }
 
+moe_status moe_route_plan(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                          int32_t* idx, float* w, int32_t* counts, int32_t* kept_counts, float* p,
+                          float* f, float* l_aux, int32_t* offsets, int32_t* pos, int32_t* src,
+                          uint8_t* drop, void* x_codes, float* row_scale, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status r = check_shape(s);
+  if (r != MOE_OK) return r;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !w_g || !idx || !w || !counts || !kept_counts || !offsets || !pos || !src || !drop || !ws)
+    return MOE_ERR_ARG;
+  const bool fp8 = s->buf_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!x_codes || !row_scale)) return MOE_ERR_ARG;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.disp_hist) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* psum = reinterpret_cast<float*>(base + L.route_psum);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.route_hist);
+  int32_t* tbase = reinterpret_cast<int32_t*>(base + L.route_base);
+  float* lpart = reinterpret_cast<float*>(base + L.route_lpart);
+  double* prod = reinterpret_cast<double*>(base + L.route_prod);
+  const moe::RouteStats rs{counts, kept_counts, p, f, l_aux, offsets, tbase, prod,
+                           reinterpret_cast<int32_t*>(prod + s->N)};
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, rs, st);
+  if (e == hipSuccess && !moe::route_folds_stats(*s)) e = moe::launch_route_finalize(*s, psum, hist, rs, st);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch_plan_fused(*s, x, idx, tbase, offsets, pos, src, drop, x_codes, row_scale, st);
+  return hip_status(e);
+}
+
+namespace {
+// The gathered up GEMM reads rows of a [T][d] operand through 32-bit offsets.
+bool gather_fits(const moe_shape& s) {
+  const int64_t es = s.buf_dtype == MOE_FP8_E4M3 ? 1 : (s.dtype == MOE_BF16 ? 2 : 4);
+  return s.T * static_cast<int64_t>(s.d) * es <= static_cast<int64_t>(UINT32_MAX);
+}
+}  // namespace
+
+moe_status moe_expert_up_gather(const moe_shape* s, const void* a, const float* row_scale,
+                                const int32_t* offsets, const int32_t* src, const void* w1,
+                                const void* w3, void* h, void* ws, size_t ws_bytes, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!a || !offsets || !src || !w1 || !h) return MOE_ERR_ARG;
+  if (s->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
+  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  if (!gather_fits(*s)) return MOE_ERR_UNSUPPORTED;
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
+  return hip_status(moe::launch_expert_up(*s, a, row_scale, offsets, s->T * s->k, s->N, w1, w3, h,
+                                          split, static_cast<hipStream_t>(stream), src, s->T));
+}
+
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
                        const void* w1, const void* w3, const void* w2, const void* ws1,
                        const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
@@ -383,19 +442,43 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
   if (s->T == 0) return MOE_OK;
   // every check of the three calls up front, so that nothing is launched on error
   if (!x || !w_g || !w1 || !w2 || !idx || !w || !counts || !kept_counts || !offsets || !pos ||
-      !src || !drop || !x_perm || !out || !y || !ws)
+      !src || !drop || !out || !y || !ws)
     return MOE_ERR_ARG;
+  const bool fused = x_perm == nullptr;
   if (s->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
-  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  if (!fused && s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
   if (s->has_shared && (!ws1 || !ws2 || !out_shared || (s->act == MOE_ACT_SWIGLU && !ws3)))
     return MOE_ERR_ARG;
-  if (ws_bytes < moe::ws_layout(*s).total) return MOE_ERR_WORKSPACE;
-  r = moe_route_dispatch(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets, pos,
-                         src, drop, x_perm, row_scale, ws, ws_bytes, stream);
+  if (fused && !gather_fits(*s)) return MOE_ERR_UNSUPPORTED;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!fused) {
+    r = moe_route_dispatch(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets, pos,
+                           src, drop, x_perm, row_scale, ws, ws_bytes, stream);
+    if (r != MOE_OK) return r;
+    r = moe_experts(s, x_perm, row_scale, offsets, w1, w3, w2, x, ws1, ws3, ws2, out, out_shared, ws,
+                    ws_bytes, stream);
+    if (r != MOE_OK) return r;
+    return moe_combine(s, out, out_shared, x, pos, w, y, stream);
+  }
+  // fused dispatch: no expert-ordered copy of x; the up GEMM gathers its rows
+  // through src from x (or from x's fp8 codes in token order)
+  char* base = static_cast<char*>(ws);
+  const bool fp8 = s->buf_dtype == MOE_FP8_E4M3;
+  void* codes = fp8 ? base + L.x_codes : nullptr;
+  float* rsc = fp8 ? (row_scale ? row_scale : reinterpret_cast<float*>(base + L.rscale)) : nullptr;
+  r = moe_route_plan(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets, pos, src, drop,
+                     codes, rsc, ws, ws_bytes, stream);
   if (r != MOE_OK) return r;
-  r = moe_experts(s, x_perm, row_scale, offsets, w1, w3, w2, x, ws1, ws3, ws2, out, out_shared, ws,
-                  ws_bytes, stream);
+  r = moe_expert_up_gather(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, ws, ws_bytes,
+                           stream);
   if (r != MOE_OK) return r;
+  r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
+  if (r != MOE_OK) return r;
+  if (s->has_shared) {
+    r = moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, ws, ws_bytes, stream);
+    if (r != MOE_OK) return r;
+  }
   return moe_combine(s, out, out_shared, x, pos, w, y, stream);
 }
 

@@ -222,6 +222,17 @@ __device__ __forceinline__ void given_positions(const int32_t* pos, int k, int64
   for (int j = 0; j < kMaxTopK; ++j) pj[j] = j < k ? __builtin_amdgcn_readfirstlane(pos[t * k + j]) : -1;
 }
 
+// The plan alone (the fused layer: the up GEMM reads x through src, so no
+// rows are copied): one wave per token writes its pos, drop and src.
+__global__ __launch_bounds__(256) void disp_plan_tiles_kernel(int64_t T, int k, PlanArgs pa) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int pj[kMaxTopK];
+  plan_token(pa, T, k, t, lane, pj);
+  if (lane == 0) plan_write(pa, k, t, pj);
+}
+
 // wpt waves per token; 16-byte chunks.  Row bytes must be a multiple of 16.
 // PLANNED: positions from plan_token, else read from pos.  A lane's first
 // kCopyAhead chunks are loaded before the positions, so that the row's latency
@@ -301,7 +312,11 @@ __device__ __forceinline__ float absmax8(uint4 v) {
 // in LDS), so that a token's row is read and written by 64 * WPT lanes.  Rows
 // up to 64*WPT*MAXC chunks of 8 bf16 stay in registers; longer rows are read
 // twice.
-template <int MAXC, bool PLANNED, int WPT>
+//
+// TOKEN_ORDER (the fused layer, whose up GEMM gathers its rows through src):
+// the codes are written once, to row t of xp ([T][d]), and only the kept
+// slots' scales go to their positions.
+template <int MAXC, bool PLANNED, int WPT, bool TOKEN_ORDER = false>
 __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restrict__ x, int64_t T,
                                                        int k, int d,
                                                        const int32_t* __restrict__ pos,
@@ -351,7 +366,16 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
   const bool tiny = amax < 0x1p-100f;
   const float inv = tiny ? 1.f : __fdiv_rn(448.0f, amax);
   const float scale = tiny ? 1.f : __fdiv_rn(amax, 448.0f);
-  if (in_regs) {
+  if (TOKEN_ORDER) {
+    uint2* dst = reinterpret_cast<uint2*>(xp + t * d);
+    if (in_regs) {
+#pragma unroll
+      for (int q = 0; q < MAXC; ++q)
+        if (tl + 64 * WPT * q < nch) dst[tl + 64 * WPT * q] = quant8(buf[q], inv);
+    } else {
+      for (int c = tl; c < nch; c += 64 * WPT) dst[c] = quant8(xr[c], inv);
+    }
+  } else if (in_regs) {
     // codes first, then slot by slot (scalar row base, fixed per-chunk offsets)
     uint2 code[MAXC];
 #pragma unroll
@@ -448,6 +472,22 @@ hipError_t launch_dispatch_copy_planned(const moe_shape& s, const void* x, const
                                         float* row_scale, hipStream_t st) {
   const PlanArgs pa{idx, base, offsets, pos, src, drop, s.N, s.capacity, route_tile(s)};
   return launch_copy(s, x, pos, x_perm, row_scale, &pa, st);
+}
+
+hipError_t launch_dispatch_plan_fused(const moe_shape& s, const void* x, const int32_t* idx,
+                                      const int32_t* base, const int32_t* offsets, int32_t* pos,
+                                      int32_t* src, uint8_t* drop, void* x_tok, float* row_scale,
+                                      hipStream_t st) {
+  const PlanArgs pa{idx, base, offsets, pos, src, drop, s.N, s.capacity, route_tile(s)};
+  if (s.buf_dtype == MOE_FP8_E4M3) {
+    hipLaunchKernelGGL((disp_fp8_kernel<4, true, 4, true>), dim3(static_cast<unsigned>(s.T)), dim3(256),
+                       0, st, static_cast<const uint16_t*>(x), s.T, s.k, s.d, pos,
+                       static_cast<uint8_t*>(x_tok), row_scale, pa);
+  } else {
+    hipLaunchKernelGGL(disp_plan_tiles_kernel, dim3(static_cast<unsigned>(ceil_div(s.T, 4))), dim3(256),
+                       0, st, s.T, s.k, pa);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

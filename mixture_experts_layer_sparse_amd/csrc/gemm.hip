@@ -58,8 +58,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 enum Epi { EPI_STORE = 0, EPI_SILU = 1, EPI_RELU = 2, EPI_SWIGLU = 3 };
 
 struct GemmArgs {
-  const void* a;           // [rows][K] bf16 bits, or e4m3 codes
+  const void* a;           // [rows][K] bf16 bits, or e4m3 codes; with `gather`, [a_total][K]
   const float* a_scale;    // [rows] per-row scale (fp8 A) or null
+  const int32_t* gather;   // null, or [rows]: row r of the product reads A row gather[r]
+  int64_t a_total;         // rows of A when gathering
   const int32_t* offsets;  // [n_seg + 1], or null: one dense segment of `rows`
   int64_t rows;
   int n_seg;
@@ -292,7 +294,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   const int fr = lane & 31, fk = lane >> 5;
 
   // per-lane source offsets of this wave's A loads (the K step is added as
-  // soffset); relative to the tile's first row, so the same for every tile
+  // soffset): relative to the tile's first row, so the same for every tile,
+  // or, when gathering, from the base of A through the tile's row indices
+  // (set by bind_tile)
   uint32_t a_off[A_PW];
 #pragma unroll
   for (int j = 0; j < A_PW; ++j) {
@@ -300,6 +304,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     const int c = (lane % A_CPR) ^ swz<ROWA>(r);
     a_off[j] = static_cast<uint32_t>(r * K * SA + c * 16);
   }
+  const bool gather = g.gather != nullptr;
 
   // The current tile (wave-uniform values).  Tile order: expert-major, then
   // n-tile, then the expert's m-tiles, so the m-tiles of an expert consume
@@ -369,8 +374,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // the segment end measured about 12% slower at 128-row segments.
   __amdgpu_buffer_rsrc_t rs_a_whole = rs_null;
   auto bind_tile = [&]() {
-    a_tile = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(row0) * K * SA;
-    const uint64_t a_bytes = static_cast<uint64_t>(g.rows - row0) * K * SA;
+    uint64_t a_bytes;
+    if (gather) {
+      // A rows of the tile through the row indices (rows past the segment end
+      // read row 0: loaded, never stored); the host keeps a_total * K * SA
+      // within the 32-bit range of the offsets
+      a_tile = static_cast<const uint8_t*>(g.a);
+      a_bytes = static_cast<uint64_t>(g.a_total) * K * SA;
+      int tok[A_PW];
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j) {
+        const int r = (wave * A_PW + j) * (1024 / ROWA) + lane / A_CPR;
+        tok[j] = g.gather[min(row0 + r, row_end - 1)];      // (loads issued together)
+      }
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j) {
+        const int r = (wave * A_PW + j) * (1024 / ROWA) + lane / A_CPR;
+        const int c = (lane % A_CPR) ^ swz<ROWA>(r);
+        const int t = row0 + r < row_end ? tok[j] : 0;
+        a_off[j] = static_cast<uint32_t>(t) * static_cast<uint32_t>(K * SA) + static_cast<uint32_t>(c * 16);
+      }
+    } else {
+      a_tile = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(row0) * K * SA;
+      a_bytes = static_cast<uint64_t>(g.rows - row0) * K * SA;
+    }
     a_nrec = a_bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(a_bytes);
     const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
     rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
@@ -823,6 +850,7 @@ __device__ __forceinline__ int seg_of(const int32_t* offsets, int n_seg, int r) 
 
 __global__ __launch_bounds__(256) void f32_up_kernel(const float* __restrict__ a,
                                                      const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ gather,
                                                      int64_t rows, int n_seg, int K, int F,
                                                      const float* __restrict__ w1,
                                                      const float* __restrict__ w3,
@@ -833,7 +861,7 @@ __global__ __launch_bounds__(256) void f32_up_kernel(const float* __restrict__ a
   const int64_t R = offsets ? offsets[n_seg] : rows;
   if (r >= R) return;
   const int e = offsets ? seg_of(offsets, n_seg, static_cast<int>(r)) : 0;
-  const float* ar = a + r * K;
+  const float* ar = a + (gather ? static_cast<int64_t>(gather[r]) : r) * K;
   const float* u1 = w1 + (static_cast<int64_t>(e) * F + f) * K;
   float u = 0.f, gt = 0.f;
   for (int j = 0; j < K; ++j) u = fmaf(ar[j], u1[j], u);
@@ -1035,12 +1063,13 @@ hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w
 
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg, const void* w1,
-                            const void* w3, void* h, void* split, hipStream_t st) {
+                            const void* w3, void* h, void* split, hipStream_t st,
+                            const int32_t* gather, int64_t a_rows) {
   if (s.dtype == MOE_F32) {
     int64_t n = rows * s.F;
     dim3 grid(static_cast<unsigned>(ceil_div(n, 256)));
     hipLaunchKernelGGL(f32_up_kernel, grid, dim3(256), 0, st, static_cast<const float*>(a),
-                       offsets, rows, n_seg, s.d, s.F, static_cast<const float*>(w1),
+                       offsets, gather, rows, n_seg, s.d, s.F, static_cast<const float*>(w1),
                        static_cast<const float*>(w3), static_cast<float*>(h), s.act);
     return hipGetLastError();
   }
@@ -1049,6 +1078,8 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
   GemmArgs g{};
   g.a = a;
   g.a_scale = fp8 ? row_scale : nullptr;
+  g.gather = gather;
+  g.a_total = a_rows;
   g.offsets = offsets;
   g.rows = rows;
   g.n_seg = n_seg;

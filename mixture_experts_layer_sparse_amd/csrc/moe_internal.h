@@ -47,6 +47,8 @@ struct WsLayout {
   size_t route_lpart;   // partial logits: float [route_split_ranges(s)][T][N] (few tokens), or
                         // router_gemm_bytes(s) of split-K scratch (wide routers)
   size_t disp_hist;     // int32   [nb_disp][N]
+  size_t x_codes;       // fp8 codes of x in token order [T][d] (fused layer with an fp8 buffer)
+  size_t rscale;        // float   [T*k] row scales (fused layer with an fp8 buffer)
   size_t gemm_split;    // split-K tail scratch of the grouped GEMMs (gemm_split_bytes(s))
   size_t h;             // dtype   [T*k][F]
   size_t h_shared;      // dtype   [T][F]
@@ -104,12 +106,24 @@ hipError_t launch_dispatch_copy_planned(const moe_shape& s, const void* x, const
                                         int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm,
                                         float* row_scale, hipStream_t st);
 
+// The fused layer's plan: pos, src and drop as launch_dispatch_copy_planned
+// writes them, without copying rows (the up GEMM gathers x through src).  For
+// an fp8 buffer, each token's codes go once to row t of x_tok ([T][d]) and
+// its scale to row_scale at each kept slot's position.
+hipError_t launch_dispatch_plan_fused(const moe_shape& s, const void* x, const int32_t* idx,
+                                      const int32_t* base, const int32_t* offsets, int32_t* pos,
+                                      int32_t* src, uint8_t* drop, void* x_tok, float* row_scale,
+                                      hipStream_t st);
+
 // Grouped GEMMs.  `offsets` == nullptr means one dense segment of `rows` rows.
+// `gather` (may be null): row r of the product reads row gather[r] of `a`,
+// which then has `a_rows` rows (a_rows * d * element size < 4 GiB).
 // `split` (may be null): gemm_split_bytes(s) of scratch for a split-K tail;
 // without it a mostly idle last round runs as quarter tiles.
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg,
-                            const void* w1, const void* w3, void* h, void* split, hipStream_t st);
+                            const void* w1, const void* w3, void* h, void* split, hipStream_t st,
+                            const int32_t* gather = nullptr, int64_t a_rows = 0);
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
                               hipStream_t st);

@@ -91,7 +91,9 @@ _SIGS = {
     "moe_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 8 + [_P, c_size_t, _P]),
     "moe_route_dispatch": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P, c_size_t, _P]),
     "moe_route_dispatch_noalloc": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P]),
+    "moe_route_plan": (c_int32, [POINTER(Shape)] + [_P] * 16 + [_P, c_size_t, _P]),
     "moe_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
+    "moe_expert_up_gather": (c_int32, [POINTER(Shape)] + [_P] * 7 + [_P, c_size_t, _P]),
     "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
     "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
     "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
@@ -253,6 +255,52 @@ def route_dispatch(s: Shape, x, wg, bias=None, ws=None, noalloc=False, out=None)
     return o
 
 
+def route_plan(s: Shape, x, wg, bias=None, ws=None, out=None) -> dict:
+    """moe_route_plan: route and plan without the expert-ordered copy (the
+    fused layer's first phase); for an fp8 buffer also the token-order codes
+    (``x_codes`` [T][d]) and the per-position row scales."""
+    T, N, k, d = s.T, s.N, s.k, s.d
+    dev = x.device
+    _check(x, "x", (T, d), s.torch_dtype)
+    _check(wg, "wg", (N, d), s.torch_dtype)
+    _check(bias, "bias", (N,), torch.float32, required=False)
+    fp8 = s.buf_dtype == MOE_FP8_E4M3
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = out if out is not None else {
+        "idx": torch.empty((T, k), **i32), "w": torch.empty((T, k), **f32),
+        "counts": torch.empty(N, **i32), "kept_counts": torch.empty(N, **i32),
+        "p": torch.empty(N, **f32), "f": torch.empty(N, **f32), "l_aux": torch.empty(1, **f32),
+        "offsets": torch.empty(N + 1, **i32), "pos": torch.empty((T, k), **i32),
+        "src": torch.empty(T * k, **i32), "drop": torch.empty((T, k), dtype=torch.uint8, device=dev),
+        "x_codes": torch.empty((T, d), dtype=torch.uint8, device=dev) if fp8 else None,
+        "row_scale": torch.empty(T * k, **f32) if fp8 else None,
+    }
+    ws = ws if ws is not None else alloc_workspace(s, dev)
+    _call("moe_route_plan", ctypes.byref(s), _ptr(x), _ptr(wg), _ptr(bias), _ptr(o["idx"]),
+          _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["kept_counts"]), _ptr(o["p"]), _ptr(o["f"]),
+          _ptr(o["l_aux"]), _ptr(o["offsets"]), _ptr(o["pos"]), _ptr(o["src"]), _ptr(o["drop"]),
+          _ptr(o.get("x_codes")), _ptr(o.get("row_scale")), _ptr(ws), ws.numel(), _stream())
+    return o
+
+
+def expert_up_gather(s: Shape, a, row_scale, offsets, src, w1, w3, h=None, ws=None):
+    """moe_expert_up_gather: the up GEMM reading row src[r] of ``a`` ([T][d]:
+    x, or the token-order fp8 codes from route_plan) for dispatch row r."""
+    R, F = s.T * s.k, s.F
+    fp8 = s.buf_dtype == MOE_FP8_E4M3
+    _check(a, "a", (s.T, s.d), torch.uint8 if fp8 else s.torch_dtype)
+    _check(offsets, "offsets", (s.N + 1,), torch.int32)
+    _check(src, "src", (R,), torch.int32)
+    _check(w1, "w1", (s.N, F, s.d), s.torch_dtype)
+    _check(w3, "w3", (s.N, F, s.d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
+    if h is None:
+        h = torch.empty((R, F), dtype=s.torch_dtype, device=a.device)
+    _call("moe_expert_up_gather", ctypes.byref(s), _ptr(a), _ptr(row_scale), _ptr(offsets), _ptr(src),
+          _ptr(w1), _ptr(w3), _ptr(h), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    return h
+
+
 def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None, ws=None):
     """ws: None (a mostly idle last tile round runs as quarter tiles) or a
     workspace from alloc_workspace (that round is split along K instead)."""
@@ -328,7 +376,7 @@ class Layer:
     a captured graph needs).  Buffers are exposed as attributes."""
 
     def __init__(self, s: Shape, wg, w1, w3, w2, bias=None, ws1=None, ws3=None, ws2=None,
-                 device="cuda"):
+                 device="cuda", fused=False):
         st = check_shape(s)
         if st != MOE_OK:
             raise MoeError("moe_check_shape", st)
@@ -359,8 +407,12 @@ class Layer:
         self.pos = torch.empty((T, k), **e)
         self.src = torch.empty(T * k, **e)
         self.drop = torch.empty((T, k), dtype=torch.uint8, device=device)
-        self.x_perm = torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=device)
+        # fused: no dispatch buffer (the up GEMM gathers rows of x through src)
+        self.fused = fused
+        self.x_perm = None if fused else torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=device)
         self.row_scale = torch.empty(T * k, **f) if s.buf_dtype == MOE_FP8_E4M3 else None
+        self.x_codes = (torch.empty((T, d), dtype=torch.uint8, device=device)
+                        if fused and s.buf_dtype == MOE_FP8_E4M3 else None)
         self.out = torch.empty((T * k, d), dtype=dt, device=device)
         self.out_shared = torch.empty((T, d), dtype=dt, device=device) if s.has_shared else None
         self.y = torch.empty((T, d), dtype=dt, device=device)
@@ -377,6 +429,22 @@ class Layer:
               _ptr(self.x_perm), _ptr(self.row_scale), _ptr(self.out), _ptr(self.out_shared),
               _ptr(self.y), _ptr(self.ws), self.ws.numel(), _stream())
         return self.y
+
+    # the fused layer's phases (the same kernels as forward() with fused=True)
+    def route_plan(self, x):
+        s = self.s
+        _call("moe_route_plan", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias),
+              _ptr(self.idx), _ptr(self.w), _ptr(self.counts), _ptr(self.kept_counts),
+              _ptr(self.p), _ptr(self.f), _ptr(self.l_aux), _ptr(self.offsets), _ptr(self.pos),
+              _ptr(self.src), _ptr(self.drop), _ptr(self.x_codes), _ptr(self.row_scale),
+              _ptr(self.ws), self.ws.numel(), _stream())
+
+    def expert_up_gather(self, x, h):
+        s = self.s
+        a = self.x_codes if self.x_codes is not None else x
+        _call("moe_expert_up_gather", ctypes.byref(s), _ptr(a), _ptr(self.row_scale),
+              _ptr(self.offsets), _ptr(self.src), _ptr(self.w1), _ptr(self.w3), _ptr(h),
+              _ptr(self.ws), self.ws.numel(), _stream())
 
     # forward in three calls (the same kernels): route + dispatch, experts, combine
     def route_dispatch(self, x):

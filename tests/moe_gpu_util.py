@@ -100,13 +100,14 @@ def rows_rel_err(a, b):
     return float(np.max(num / den)) if a.size else 0.0
 
 
-def run_gpu_forward(wl, inp, g=None):
+def run_gpu_forward(wl, inp, g=None, fused=False):
     """The whole layer in one call (moe_forward); host copies of its outputs
-    under the same names as run_gpu.  ``g`` as for run_gpu."""
+    under the same names as run_gpu.  ``g`` as for run_gpu.  ``fused``: no
+    dispatch buffer (x_perm is None), the up GEMM gathers x through src."""
     s = M.shape_of(wl)
     g = g if g is not None else upload(wl, inp)
     L = M.Layer(s, g["wg"], g["w1"], g.get("w3"), g["w2"], bias=g.get("bias"), ws1=g.get("ws1"),
-                ws3=g.get("ws3"), ws2=g.get("ws2"))
+                ws3=g.get("ws3"), ws2=g.get("ws2"), fused=fused)
     L.forward(g["x"])
     torch.cuda.synchronize()
     names = ["idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "src",
@@ -143,11 +144,12 @@ def check_layer(wl, inp, gpu, y_tokens=None, max_adopted=None):
     assert np.array_equal(gpu["pos"], full["pos"]), "pos"
     assert np.array_equal(gpu["src"][:R], full["src"]), "src"
     assert np.array_equal(gpu["drop"].astype(bool), full["drop"]), "drop"
-    # dispatch buffer: bit-exact
+    # dispatch buffer (absent in the fused layer): bit-exact
     if wl.buf == "fp8":
-        assert np.array_equal(gpu["x_perm"][:R], full["xperm"]), "fp8 codes"
+        if gpu["x_perm"] is not None:
+            assert np.array_equal(gpu["x_perm"][:R], full["xperm"]), "fp8 codes"
         assert np.array_equal(gpu["row_scale"][:R], full["row_scale"]), "fp8 scales"
-    else:
+    elif gpu["x_perm"] is not None:
         assert np.array_equal(gpu["x_perm"][:R], full["xperm"]), "x_perm"
     # expert outputs and y
     tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16
@@ -217,6 +219,8 @@ def assert_same_results(a, b, fp8):
     for key in PLAN_KEYS:
         assert np.array_equal(a[key], b[key]), key
     for key in ROW_KEYS:
+        if a[key] is None or b[key] is None:        # (the fused layer has no x_perm)
+            continue
         assert np.array_equal(a[key][:R], b[key][:R]), key
     if fp8:
         assert np.array_equal(a["row_scale"][:R], b["row_scale"][:R]), "row_scale"

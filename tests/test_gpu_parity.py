@@ -342,6 +342,11 @@ def _forward_and_phases(wl, inp, y_tokens=None, max_adopted=None):
     print(f"  {errs}", flush=True)
     ph = run_gpu(wl, inp, logits=False, g=g)
     assert_same_results(fwd, ph, wl.buf == "fp8")
+    # the fused layer (no dispatch buffer; the up GEMM gathers x through src)
+    # gives the same outputs bit for bit
+    fu = run_gpu_forward(wl, inp, g=g, fused=True)
+    assert fu["x_perm"] is None
+    assert_same_results(fu, fwd, wl.buf == "fp8")
     return fwd, errs
 
 
@@ -352,6 +357,9 @@ GRAPH_CASES = {
     "deepseek_fp8_groups_shared": lambda: si.small("deepseek_v3"),
     "one_token_split_paths": lambda: si.small("mixtral", T=1),
     "deepseek_v3_full": lambda: si.WORKLOADS["deepseek_v3"],
+    # the fused layer (no dispatch buffer)
+    "mixtral_ragged_fused": lambda: si.small("mixtral", T=1001),
+    "deepseek_v3_full_fused": lambda: si.WORKLOADS["deepseek_v3"],
 }
 
 
@@ -367,7 +375,7 @@ def test_graph_replay_matches_eager(name):
     g = upload(wl, _inputs(wl))
     s = M.shape_of(wl)
     L = M.Layer(s, g["wg"], g["w1"], g.get("w3"), g["w2"], bias=g.get("bias"), ws1=g.get("ws1"),
-                ws3=g.get("ws3"), ws2=g.get("ws2"))
+                ws3=g.get("ws3"), ws2=g.get("ws2"), fused=name.endswith("_fused"))
     x = g["x"]
     L.forward(x)
     torch.cuda.synchronize()
@@ -442,3 +450,43 @@ def test_decode_step_deepseek_shape(B):
     touched = int((gpu["counts"] > 0).sum())
     print(f"  experts touched: {touched} of {wl.N}", flush=True)
     assert touched <= min(wl.N, B * wl.k)
+
+
+# ------------------------------------------------------- fused dispatch phases --
+
+FUSED_PHASE_CASES = {
+    "mixtral_small": lambda: si.small("mixtral"),
+    "switch_capacity_128_row_tiles": lambda: si.small("switch"),
+    "deepseek_fp8_groups": lambda: si.small("deepseek_v3"),
+    "f32_tiny": lambda: si.WORKLOADS["tiny"],
+    "one_token": lambda: si.small("mixtral", T=1),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_PHASE_CASES))
+def test_fused_phases_equal_dispatch_buffer_phases(name):
+    """moe_route_plan + moe_expert_up_gather against moe_route_dispatch +
+    moe_expert_up: the same plan, the token-order fp8 codes equal the
+    dispatch buffer's rows, and h is bit for bit the same."""
+    from moe_gpu_util import upload
+    wl = FUSED_PHASE_CASES[name]()
+    print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k}", flush=True)
+    s = M.shape_of(wl)
+    g = upload(wl, si.generate(wl))
+    ws = M.alloc_workspace(s)
+    ref = M.route_dispatch(s, g["x"], g["wg"], g.get("bias"), ws=ws)
+    h_ref = M.expert_up(s, ref["x_perm"], ref["row_scale"], ref["offsets"], g["w1"], g.get("w3"), ws=ws)
+    torch.cuda.synchronize()
+    ws2 = M.alloc_workspace(s)
+    got = M.route_plan(s, g["x"], g["wg"], g.get("bias"), ws=ws2)
+    a = got["x_codes"] if wl.buf == "fp8" else g["x"]
+    h = M.expert_up_gather(s, a, got["row_scale"], got["offsets"], got["src"], g["w1"], g.get("w3"), ws=ws2)
+    torch.cuda.synchronize()
+    R = int(ref["offsets"][-1].item())
+    for key in ("idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "drop"):
+        assert torch.equal(got[key], ref[key]), key
+    assert torch.equal(got["src"][:R], ref["src"][:R])
+    if wl.buf == "fp8":
+        assert torch.equal(got["row_scale"][:R], ref["row_scale"][:R])
+        assert torch.equal(got["x_codes"][got["src"][:R].long()], ref["x_perm"][:R])
+    assert torch.equal(h[:R], h_ref[:R])
