@@ -31,6 +31,8 @@ the design notes):
     dropped slot passes the token through (weight times x) or contributes zero;
   * a router bias, when present, is added to the logits before every use;
   * the shared expert runs on the unquantised input with weight 1;
+  * MXFP4 expert weights (an option): each weight is its FP4 E2M1 code's
+    value times its 32-element block's E8M0 scale, decoded exactly;
   * fp8 dispatch: per token, amax = max|x|, inv = fl32(448 / amax),
     code = e4m3(fl32(x * inv)), scale = fl32(amax / 448); amax < 2^-100
     (zero included) gives inv = scale = 1, so every code is +-0.
@@ -39,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import E4M3_MAX, as_f64, e4m3_decode, e4m3_encode, f32
+from .numerics import E4M3_MAX, as_f64, as_weights, e4m3_decode, e4m3_encode, f32
 
 
 # ----------------------------------------------------------------- routing --
@@ -286,19 +288,28 @@ def forward(wl, inp: dict, ffn_tokens: np.ndarray | None = None,
     need = np.unique(pos[pos >= 0])
     o_rows = np.zeros((plan["src"].size, wl.d))
     offs = plan["offsets"]
+    # expert weights: the layer's storage type, or MXFP4 blocks decoded exactly
+    wf = getattr(wl, "wfmt", "bf16")
+    F, d = wl.F, wl.d
+
+    def w_up(a):
+        return as_weights(a, wf, wl.dtype, F, d)
+
+    def w_down(a):
+        return as_weights(a, wf, wl.dtype, d, F)
+
     for e in range(wl.N):
         sel = need[(need >= offs[e]) & (need < offs[e + 1])]
         if sel.size == 0:
             continue
-        w1 = as_f64(inp["w1"][e], wl.dtype)
-        w3 = as_f64(inp["w3"][e], wl.dtype) if inp.get("w3") is not None else None
-        w2 = as_f64(inp["w2"][e], wl.dtype)
+        w1 = w_up(inp["w1"][e])
+        w3 = w_up(inp["w3"][e]) if inp.get("w3") is not None else None
+        w2 = w_down(inp["w2"][e])
         o_rows[sel] = expert_ffn(wl.act, vals["rows"][sel], w1, w3, w2)
     shared = None
     if wl.shared:
-        ws3 = as_f64(inp["ws3"], wl.dtype) if inp.get("ws3") is not None else None
-        shared = expert_ffn(wl.act, x[toks], as_f64(inp["ws1"], wl.dtype), ws3,
-                            as_f64(inp["ws2"], wl.dtype))
+        ws3 = w_up(inp["ws3"]) if inp.get("ws3") is not None else None
+        shared = expert_ffn(wl.act, x[toks], w_up(inp["ws1"]), ws3, w_down(inp["ws2"]))
     y = combine(wl, x[toks], r["w"][toks], pos, o_rows, shared)
     out.update({"o_rows": o_rows, "shared": shared, "y": y, "y_tokens": toks})
     return out

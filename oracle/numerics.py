@@ -3,6 +3,11 @@
 bf16: a bfloat16 value is the float32 whose upper 16 bits are the stored bits
 and whose lower 16 bits are zero, so widening is exact.
 
+MXFP4 (the OCP microscaling format: blocks of 32 FP4 E2M1 elements sharing one
+E8M0 power-of-two scale, about 4.25 bits per weight): the expert weights of
+the gpt-oss models ("MoE: what it costs to train and serve", "Memory: sparsity
+only helps once it fits").  Decoding is exact in float64.
+
 fp8 e4m3fn (the OCP 8-bit float with 4 exponent bits, bias 7, 3 mantissa bits,
 no infinities, a single NaN mantissa pattern per sign, largest finite 448): the
 pages quantise activations to FP8 before dispatch ("MoE: what it costs to train
@@ -82,3 +87,57 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 def f32(a) -> np.ndarray:
     """Round to float32 (IEEE, nearest even)."""
     return np.asarray(a, dtype=np.float32)
+
+
+# ------------------------------------------------------------------- MXFP4 --
+
+MX_BLOCK = 32
+
+
+def fp4_e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of FP4 E2M1 codes (0..15) as float64: bit 3 the sign, bits 2-1 the
+    exponent (bias 1), bit 0 the mantissa; exponent field 0 is subnormal
+    (0 or 0.5).  The magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6; code 8 is -0."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    ex = (c >> 1) & 0x3
+    man = (c & 0x1).astype(np.float64)
+    mag = np.where(ex == 0, 0.5 * man, (1.0 + 0.5 * man) * np.exp2(ex - 1.0))
+    return sign * mag
+
+
+def e8m0_decode(e: np.ndarray) -> np.ndarray:
+    """Value of E8M0 scales (unsigned 8-bit exponents, bias 127, no mantissa):
+    2^(e - 127); 255 is NaN."""
+    e = np.asarray(e).astype(np.int64)
+    return np.where(e == 255, np.nan, np.exp2(e - 127.0))
+
+
+def mxfp4_split(buf: np.ndarray, rows: int, K: int) -> tuple:
+    """The two planes of an MXFP4 matrix [rows][K] stored as the library takes
+    it: rows * K / 2 bytes of codes (row-major; element 2i in the low nibble of
+    byte i, element 2i + 1 in the high nibble), then rows * K / 32 E8M0 scales
+    (row-major; scale b of a row covers its elements 32b .. 32b + 31)."""
+    buf = np.asarray(buf, np.uint8).ravel()
+    nc, ns = rows * K // 2, rows * K // MX_BLOCK
+    if buf.size != nc + ns:
+        raise ValueError(f"mxfp4 buffer of {buf.size} bytes for a [{rows}][{K}] matrix")
+    return buf[:nc].reshape(rows, K // 2), buf[nc:].reshape(rows, K // MX_BLOCK)
+
+
+def mxfp4_decode(buf: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Exact float64 values of an MXFP4 matrix [rows][K]: code value times its
+    block's scale."""
+    codes, scales = mxfp4_split(buf, rows, K)
+    el = np.empty((rows, K), np.int64)
+    el[:, 0::2] = codes & 0xF
+    el[:, 1::2] = codes >> 4
+    return fp4_e2m1_decode(el) * np.repeat(e8m0_decode(scales), MX_BLOCK, axis=1)
+
+
+def as_weights(a: np.ndarray, wfmt: str, dtype: str, rows: int, K: int) -> np.ndarray:
+    """One stored weight matrix [rows][K] widened to float64: MXFP4 buffers
+    decoded, else the layer's storage type widened."""
+    if wfmt == "mxfp4":
+        return mxfp4_decode(a, rows, K)
+    return as_f64(a, dtype)

@@ -27,7 +27,14 @@ Recipe (identical bytes go to the GPU and to the oracle):
   * x ~ N(0, 1); W_g, W1, W3 ~ N(0, 1/d); W2 ~ N(0, 1/F) (scale applied in fp32);
   * bf16 workloads round each fp32 draw to bf16 with round-to-nearest-even;
     bf16 tensors are returned as ``uint16`` bit patterns;
-  * the router bias (dbrx) is computed in float64 and stored as float32.
+  * the router bias (dbrx) is computed in float64 and stored as float32;
+  * MXFP4 expert weights (wfmt = "mxfp4"; the router stays in the layer's
+    type) are drawn directly in the format, no rounding involved: each weight
+    matrix [rows][K] is rows * K / 2 bytes of uniformly drawn code bytes (two
+    FP4 E2M1 codes each, every code equally likely), then rows * K / 32 E8M0
+    block scales drawn uniformly from e0 - 1, e0, e0 + 1, where e0 puts the
+    weights' root mean square near 1 / sqrt(K) (the 16 codes' values have mean
+    square 8.5625).
 """
 from __future__ import annotations
 
@@ -44,6 +51,8 @@ CHUNK = 1 << 22
 TAG_X, TAG_WG = 1, 2
 TAG_W1, TAG_W3, TAG_W2 = 10, 11, 12          # + 16 * expert
 TAG_WS1, TAG_WS3, TAG_WS2 = 5, 6, 7          # shared expert
+TAG_SCALE = 1 << 20                          # + the weight tag: MXFP4 block scales
+MX_BLOCK = 32                                # elements per MXFP4 scale block
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,6 +75,7 @@ class Workload:
     bias: str | None = None      # None | "zipf2"
     alpha: float = 0.01
     gate: str = "sparse"         # "sparse" (softmax over the k selected) | "full" (full-softmax probability)
+    wfmt: str = "bf16"           # expert weights: the layer's dtype ("bf16"/"f32") | "mxfp4"
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -135,6 +145,26 @@ def _fill(tag: int, count: int, scale: float, seed: int, bf16: bool) -> np.ndarr
     return out
 
 
+def _fill_ints(tag: int, count: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """``count`` uint8 values drawn uniformly from lo..hi, chunk by chunk as _fill."""
+    out = np.empty(count, dtype=np.uint8)
+    for c in range((count + CHUNK - 1) // CHUNK):
+        a, b = c * CHUNK, min(count, (c + 1) * CHUNK)
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tag, c)))
+        out[a:b] = rng.integers(lo, hi + 1, size=b - a, dtype=np.uint8)
+    return out
+
+
+def gen_mxfp4(wl: Workload, tag: int, rows: int, K: int) -> np.ndarray:
+    """One MXFP4 weight matrix [rows][K] as the library stores it: the code
+    bytes (row-major, element 2i in the low nibble of byte i), then the E8M0
+    block scales (row-major, K / 32 per row)."""
+    e0 = 127 + int(round(math.log2(1.0 / (math.sqrt(8.5625) * math.sqrt(K)))))
+    codes = _fill_ints(tag, rows * K // 2, 0, 255, wl.seed)
+    scales = _fill_ints(TAG_SCALE + tag, rows * K // MX_BLOCK, e0 - 1, e0 + 1, wl.seed)
+    return np.concatenate([codes, scales])
+
+
 def gen_tensor(wl: Workload, tag: int, shape: tuple, scale: float) -> np.ndarray:
     n = int(np.prod(shape)) if shape else 1
     return _fill(tag, n, scale, wl.seed, wl.dtype == "bf16").reshape(shape)
@@ -169,18 +199,32 @@ def generate(wl: Workload, experts: bool = True) -> dict:
 def generate_expert(wl: Workload, e: int) -> tuple:
     """(W1[e], W3[e] or None, W2[e]) for one routed expert."""
     d, F = wl.d, wl.F
+    if wl.wfmt == "mxfp4":
+        return (gen_mxfp4(wl, TAG_W1 + 16 * e, F, d),
+                gen_mxfp4(wl, TAG_W3 + 16 * e, F, d) if wl.swiglu else None,
+                gen_mxfp4(wl, TAG_W2 + 16 * e, d, F))
     w1 = gen_tensor(wl, TAG_W1 + 16 * e, (F, d), 1.0 / math.sqrt(d))
     w3 = gen_tensor(wl, TAG_W3 + 16 * e, (F, d), 1.0 / math.sqrt(d)) if wl.swiglu else None
     w2 = gen_tensor(wl, TAG_W2 + 16 * e, (d, F), 1.0 / math.sqrt(F))
     return w1, w3, w2
 
 
+def mxfp4_bytes(rows: int, K: int) -> int:
+    """Bytes of one MXFP4 matrix [rows][K]: codes and block scales."""
+    return rows * K // 2 + rows * K // MX_BLOCK
+
+
 def generate_experts(wl: Workload) -> dict:
     d, N, F = wl.d, wl.N, wl.F
-    dt = np.uint16 if wl.dtype == "bf16" else np.float32
-    w1 = np.empty((N, F, d), dtype=dt)
-    w3 = np.empty((N, F, d), dtype=dt) if wl.swiglu else None
-    w2 = np.empty((N, d, F), dtype=dt)
+    if wl.wfmt == "mxfp4":
+        w1 = np.empty((N, mxfp4_bytes(F, d)), dtype=np.uint8)
+        w3 = np.empty((N, mxfp4_bytes(F, d)), dtype=np.uint8) if wl.swiglu else None
+        w2 = np.empty((N, mxfp4_bytes(d, F)), dtype=np.uint8)
+    else:
+        dt = np.uint16 if wl.dtype == "bf16" else np.float32
+        w1 = np.empty((N, F, d), dtype=dt)
+        w3 = np.empty((N, F, d), dtype=dt) if wl.swiglu else None
+        w2 = np.empty((N, d, F), dtype=dt)
     for e in range(N):
         a, b, c = generate_expert(wl, e)
         w1[e] = a
@@ -188,7 +232,11 @@ def generate_experts(wl: Workload) -> dict:
             w3[e] = b
         w2[e] = c
     out = {"w1": w1, "w3": w3, "w2": w2, "ws1": None, "ws3": None, "ws2": None}
-    if wl.shared:
+    if wl.shared and wl.wfmt == "mxfp4":
+        out["ws1"] = gen_mxfp4(wl, TAG_WS1, F, d)
+        out["ws3"] = gen_mxfp4(wl, TAG_WS3, F, d) if wl.swiglu else None
+        out["ws2"] = gen_mxfp4(wl, TAG_WS2, d, F)
+    elif wl.shared:
         out["ws1"] = gen_tensor(wl, TAG_WS1, (F, d), 1.0 / math.sqrt(d))
         out["ws3"] = gen_tensor(wl, TAG_WS3, (F, d), 1.0 / math.sqrt(d)) if wl.swiglu else None
         out["ws2"] = gen_tensor(wl, TAG_WS2, (d, F), 1.0 / math.sqrt(F))

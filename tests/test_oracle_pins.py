@@ -475,3 +475,79 @@ def test_oracle_sampled_ffn_equals_full():
     toks = np.array([0, 7, 55, 119])
     part = moe.forward(wl, inp, ffn_tokens=toks)
     assert np.allclose(part["y"], full["y"][toks], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------- MXFP4 --
+
+def test_fp4_e2m1_code_table():
+    """The 16 FP4 E2M1 codes: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes
+    0-7 (the format's whole value set: 2 exponent bits with bias 1, 1 mantissa
+    bit, exponent 0 subnormal), the same negated for codes 8-15, code 8 being
+    -0."""
+    from oracle.numerics import fp4_e2m1_decode
+    v = fp4_e2m1_decode(np.arange(16))
+    assert v[:8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert v[8:].tolist() == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert math.copysign(1.0, v[8]) == -1.0 and math.copysign(1.0, v[0]) == 1.0
+
+
+def test_e8m0_and_mxfp4_decode_exhaustive():
+    """Every code at every finite E8M0 scale decodes to the code's value times
+    2^(e - 127) (math.ldexp, exact); scale 255 is NaN; element 2i sits in the
+    low nibble of byte i, and each 32-element block takes its own scale."""
+    from oracle.numerics import e8m0_decode, mxfp4_decode
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    e = np.arange(255)
+    assert np.all(e8m0_decode(e) == [math.ldexp(1.0, int(x) - 127) for x in e])
+    assert np.isnan(e8m0_decode(np.array([255]))[0])
+    # one row per scale: 32 elements cycling through the 16 codes twice
+    K = 32
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    buf = np.concatenate([np.tile(packed, 255), e.astype(np.uint8)])
+    got = mxfp4_decode(buf, 255, K)
+    for r in range(255):
+        for i, c in enumerate(codes):
+            want = math.ldexp(table[c & 7], r - 127) * (-1.0 if c & 8 else 1.0)
+            assert got[r, i] == want, (r, i)
+    # nibble order and per-block scales on a hand-made 1 x 64 row: byte 0 = 0x1F
+    # holds element 0 = code 0xF (-6) and element 1 = code 0x1 (0.5); the second
+    # block's scale is 2^1
+    row = np.zeros(32, np.uint8)
+    row[0] = 0x1F
+    row[16] = 0x2A                 # elements 32, 33: codes 0xA (-1), 0x2 (1)
+    got = mxfp4_decode(np.concatenate([row, np.array([127, 128], np.uint8)]), 1, 64)[0]
+    assert got[0] == -6.0 and got[1] == 0.5 and got[32] == -2.0 and got[33] == 2.0
+    assert np.count_nonzero(got) == 4
+
+
+def test_mxfp4_storage_is_the_pages_bits_per_weight():
+    g = golden()["mxfp4_bits_per_weight"]
+    for rows, K in ((2048, 7168), (7168, 2048), (4096, 1024)):
+        assert si.mxfp4_bytes(rows, K) * 8 / (rows * K) == g["bits"]
+
+
+def test_mxfp4_identity_experts_give_x():
+    """I and -I are exact in MXFP4 (codes 0x2 and 0xA at scale 2^0), so the
+    ReLU identity experts (W1 = [I; -I], W2 = [I, -I]) stored as MXFP4 return x
+    exactly, with capacity drops passing x through."""
+    d, N, k, T = 32, 4, 2, 40
+    wl = si.Workload("mxid", T=T, d=d, N=N, k=k, F=2 * d, act="relu", dtype="bf16", buf="bf16",
+                     capacity=15, wfmt="mxfp4")
+    rng = np.random.default_rng(13)
+
+    def mx(m):
+        # an exact MXFP4 encoding of a matrix of 0, +1, -1 (scale 2^0 everywhere)
+        c = np.where(m > 0, 0x2, np.where(m < 0, 0xA, 0x0)).astype(np.uint8)
+        packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        return np.concatenate([packed.ravel(), np.full(m.size // 32, 127, np.uint8)])
+
+    eye = np.eye(d)
+    w1 = mx(np.concatenate([eye, -eye]))
+    w2 = mx(np.concatenate([eye, -eye], axis=1))
+    x = si.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    inp = {"x": x, "wg": si.f32_to_bf16_bits(rng.standard_normal((N, d)).astype(np.float32)),
+           "bias": None, "w1": np.stack([w1] * N), "w3": None, "w2": np.stack([w2] * N)}
+    out = moe.forward(wl, inp)
+    assert out["drop"].sum() > 0
+    assert np.allclose(out["y"], as_f64(x, "bf16"), rtol=1e-14, atol=1e-14)
