@@ -400,8 +400,14 @@ moe_status moe_route_plan(const moe_shape* s, const void* x, const void* w_g, co
   const moe::RouteStats rs{counts, kept_counts, p, f, l_aux, offsets, tbase, prod,
                            reinterpret_cast<int32_t*>(prod + s->N)};
   hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, rs, st);
-  if (e == hipSuccess && !moe::route_folds_stats(*s)) e = moe::launch_route_finalize(*s, psum, hist, rs, st);
-  if (e == hipSuccess)
+  // with few tiles x experts the statistics launch also writes the plan (not
+  // for an fp8 buffer, whose quantising pass plans its token itself)
+  bool planned = false;
+  if (e == hipSuccess && !moe::route_folds_stats(*s)) {
+    if (fp8) e = moe::launch_route_finalize(*s, psum, hist, rs, st);
+    else e = moe::launch_route_finalize(*s, psum, hist, rs, st, idx, pos, src, drop, &planned);
+  }
+  if (e == hipSuccess && !planned)
     e = moe::launch_dispatch_plan_fused(*s, x, idx, tbase, offsets, pos, src, drop, x_codes, row_scale, st);
   return hip_status(e);
 }

@@ -233,8 +233,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   {
     int ntile = 0;
     if (tid < n_seg) {
-      const int so = g.offsets ? g.offsets[tid] : 0;
-      const int eo = g.offsets ? g.offsets[tid + 1] : static_cast<int>(g.rows);
+      // (segment bounds clamped into [0, rows]: valid offsets pass unchanged,
+      // and no other value can index past the row buffers)
+      const int rows_i = static_cast<int>(g.rows);
+      const int so = g.offsets ? min(max(g.offsets[tid], 0), rows_i) : 0;
+      const int eo = g.offsets ? min(max(g.offsets[tid + 1], so), rows_i) : rows_i;
       ntile = (eo - so + MBM - 1) / MBM;
       seg_off[tid] = so;
       if (tid == n_seg - 1) seg_off[n_seg] = eo;
@@ -858,7 +861,7 @@ __global__ __launch_bounds__(256) void f32_up_kernel(const float* __restrict__ a
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t r = q / F;
   const int f = static_cast<int>(q % F);
-  const int64_t R = offsets ? offsets[n_seg] : rows;
+  const int64_t R = offsets ? min(static_cast<int64_t>(offsets[n_seg]), rows) : rows;
   if (r >= R) return;
   const int e = offsets ? seg_of(offsets, n_seg, static_cast<int>(r)) : 0;
   const float* ar = a + (gather ? static_cast<int64_t>(gather[r]) : r) * K;
@@ -884,7 +887,7 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t r = q / d;
   const int n = static_cast<int>(q % d);
-  const int64_t R = offsets ? offsets[n_seg] : rows;
+  const int64_t R = offsets ? min(static_cast<int64_t>(offsets[n_seg]), rows) : rows;
   if (r >= R) return;
   const int e = offsets ? seg_of(offsets, n_seg, static_cast<int>(r)) : 0;
   const float* hr = h + r * F;

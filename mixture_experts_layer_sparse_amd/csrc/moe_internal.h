@@ -89,8 +89,13 @@ bool route_folds_stats(const moe_shape& s);
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
                         float* lpart, const RouteStats& rs, hipStream_t st);
+// With idx, pos, src and drop given, the statistics launch may also write
+// the plan of the fused layer (launch_dispatch_plan_fused's pos, src and
+// drop); *planned (may be null) says whether it did.
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
-                                 const RouteStats& rs, hipStream_t st);
+                                 const RouteStats& rs, hipStream_t st, const int32_t* idx = nullptr,
+                                 int32_t* pos = nullptr, int32_t* src = nullptr,
+                                 uint8_t* drop = nullptr, bool* planned = nullptr);
 
 hipError_t launch_dispatch_hist(const moe_shape& s, const int32_t* idx, int32_t* hist,
                                 hipStream_t st);

@@ -1060,6 +1060,124 @@ __global__ __launch_bounds__(ST1) void route_stats_kernel(const float* psum, con
   scan_experts(kv, pr, N, alpha, rs.offsets, rs.l_aux, xk, xp);
 }
 
+// Statistics over few (tiles x experts), in one launch spread over the router
+// tiles: every workgroup re-adds the per-tile counts (at most kTileStats
+// values, from L2) to get every expert's total and its own tile's base, scans
+// the kept counts into the offsets, and, when asked, places its tile's
+// assignments (the plan of the fused layer: rank = the tile's base + earlier
+// tokens of the tile that chose the expert).  Workgroup 0 also writes the
+// totals, kept counts, offsets, f, p and L_aux.  Thread i takes expert
+// i % NP and tiles i / NP, i / NP + 256 / NP, ... (NP = N rounded up to a
+// power of two), so each step of the loads reads whole rows of the per-tile
+// arrays; integer sums are exact in any order, and p's float partials are
+// added in double in a fixed order (tile order per thread, then thread order).
+constexpr int kTileStats = 16384;      // tiles x experts up to which this kernel replaces the one above
+constexpr int STS = 256;               // its threads
+
+struct PlanOut {
+  const int32_t* idx;    // null: statistics (and bases) only
+  int32_t* pos;
+  int32_t* src;
+  uint8_t* drop;
+};
+
+__global__ __launch_bounds__(STS) void route_stats_tiles_kernel(const float* __restrict__ psum,
+                                                               const int32_t* __restrict__ hist, int nb,
+                                                               int TM, int64_t T, int N, int k, int cap,
+                                                               float alpha, RouteStats rs, PlanOut po) {
+  __shared__ int rb[STS], rt[STS];       // per-thread partial base and total
+  __shared__ double rp[STS];             // per-thread partial sums of p (workgroup 0)
+  __shared__ int ebase[kMaxExperts];     // this tile's base per expert
+  __shared__ int eoff[kMaxExperts + 1];  // offsets
+  __shared__ int tidx[kRouteTile * kMaxTopK];
+  __shared__ int xk[RW];
+  __shared__ double xp[RW];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  const int e = tid % NP, q = tid / NP, nq = STS / NP;
+  const bool ex = e < N;
+  const bool first = b == 0;
+  // this tile's entries, loaded early (used by the plan at the end)
+  const int64_t t0 = static_cast<int64_t>(b) * TM;
+  const int n_tok = static_cast<int>(T - t0 < TM ? T - t0 : TM);
+  if (po.idx && tid < n_tok * k) tidx[tid] = po.idx[t0 * k + tid];
+  int cb = 0, ct = 0;
+  double ps = 0.0;
+  if (ex) {
+    // (8 rows' loads issued together; rows past nb are clamped and dropped)
+    for (int t = q; t < nb; t += 8 * nq) {
+      int hv[8];
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int tt = min(t + u * nq, nb - 1);
+        hv[u] = hist[static_cast<int64_t>(tt) * N + e];
+        pv[u] = first ? psum[static_cast<int64_t>(tt) * N + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int tt = t + u * nq;
+        if (tt < nb) {
+          ct += hv[u];
+          if (tt < b) cb += hv[u];
+          ps += static_cast<double>(pv[u]);
+        }
+      }
+    }
+  }
+  rb[tid] = cb;
+  rt[tid] = ct;
+  rp[tid] = ps;
+  __syncthreads();
+  int kv = 0;
+  double pr = 0.0;
+  if (tid < N) {
+    int sb = 0, st = 0;
+    double sp = 0.0;
+    for (int j = 0; j < nq; ++j) {
+      sb += rb[j * NP + tid];
+      st += rt[j * NP + tid];
+      sp += rp[j * NP + tid];
+    }
+    ebase[tid] = sb;
+    if (rs.base) rs.base[static_cast<int64_t>(b) * N + tid] = sb;
+    kv = cap > 0 ? (st < cap ? st : cap) : st;
+    if (first) {
+      const double pe = sp / static_cast<double>(T);
+      const double fe = static_cast<double>(st) / (static_cast<double>(T) * k);
+      rs.counts[tid] = st;
+      rs.kept[tid] = kv;
+      if (rs.p) rs.p[tid] = static_cast<float>(pe);
+      if (rs.f) rs.f[tid] = static_cast<float>(fe);
+      pr = fe * pe;
+    }
+  }
+  // the scan over the experts into this workgroup's offsets (and L_aux in workgroup 0)
+  scan_experts(kv, pr, N, alpha, eoff, first ? rs.l_aux : nullptr, xk, xp);
+  __syncthreads();
+  // (N + 1 entries: with N = 256 the last one is past the workgroup's threads)
+  if (first && rs.offsets)
+    for (int i = tid; i <= N; i += STS) rs.offsets[i] = eoff[i];
+  if (!po.idx) return;
+  // the plan of this tile: entry a = (token m, slot j), ranked after the
+  // earlier tokens' entries for the same expert (a token picks an expert once)
+  if (tid < n_tok * k) {
+    const int m = tid / k, j = tid - m * k;
+    const int ee = tidx[tid];
+    int p = -1;
+    if (static_cast<unsigned>(ee) < static_cast<unsigned>(N)) {
+      int r = ebase[ee];
+      for (int a = 0; a < m * k; ++a) r += tidx[a] == ee ? 1 : 0;
+      if (cap <= 0 || r < cap) p = eoff[ee] + r;
+    }
+    const int64_t t = t0 + m;
+    po.pos[t * k + j] = p;
+    po.drop[t * k + j] = p < 0 ? 1 : 0;
+    if (p >= 0) po.src[p] = static_cast<int32_t>(t);
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -1148,8 +1266,18 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const
 }
 
 hipError_t launch_route_finalize(const moe_shape& s, const float* psum, const int32_t* hist,
-                                 const RouteStats& rs, hipStream_t st) {
+                                 const RouteStats& rs, hipStream_t st, const int32_t* idx,
+                                 int32_t* pos, int32_t* src, uint8_t* drop, bool* planned) {
   const int nb = static_cast<int>(ceil_div(s.T, route_tile(s)));
+  if (planned) *planned = false;
+  if (static_cast<int64_t>(nb) * s.N <= kTileStats) {
+    const bool plan = idx && pos && src && drop;
+    const PlanOut po{plan ? idx : nullptr, pos, src, drop};
+    hipLaunchKernelGGL(route_stats_tiles_kernel, dim3(nb), dim3(STS), 0, st, psum, hist, nb,
+                       route_tile(s), s.T, s.N, s.k, s.capacity, s.alpha, rs, po);
+    if (planned) *planned = plan;
+    return hipGetLastError();
+  }
   const int se = stats_experts_per_block(s.N);
   const int blocks = static_cast<int>(ceil_div(s.N, se));
   hipLaunchKernelGGL(route_stats_kernel, dim3(blocks), dim3(blocks == 1 ? ST1 : ST), 0, st,
