@@ -316,10 +316,14 @@ def profiled_traffic(kernel_key):
 
 
 def expert_weight_bytes(wl):
-    """Bytes of the expert weights one layer reads (routed + shared)."""
+    """Bytes of the expert weights one layer reads (routed + shared); MXFP4
+    matrices are their codes plus block scales (4.25 bits per weight)."""
     m = 3 if wl.act == "swiglu" else 2
+    n = wl.N + (1 if wl.shared else 0)
+    if getattr(wl, "wfmt", "bf16") == "mxfp4":
+        return n * m * (wl.F * wl.d // 2 + wl.F * wl.d // 32)
     s = 2 if wl.dtype == "bf16" else 4
-    return (wl.N + (1 if wl.shared else 0)) * m * wl.F * wl.d * s
+    return n * m * wl.F * wl.d * s
 
 
 def graph_step_time(step, steps, warmup):
@@ -416,8 +420,12 @@ def sweep(steps, warmup):
     print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | GEMM down us | shared us | "
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|")
-    for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx"):
-        wl = si.WORKLOADS[name]
+    for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx", "switch_mxfp4", "deepseek_v3_mxfp4"):
+        if name.endswith("_mxfp4"):
+            # the same layer with MXFP4 expert weights
+            wl = si.WORKLOADS[name[:-len("_mxfp4")]].replace(name=name, wfmt="mxfp4")
+        else:
+            wl = si.WORKLOADS[name]
         inp = si.generate(wl)
         g = {k: _to_dev(v) for k, v in inp.items()}
         del inp
@@ -431,7 +439,7 @@ def sweep(steps, warmup):
         wgb = expert_weight_bytes(wl) / (gemm_us * 1e-6) / 1e9
         mem_us = ph[0] + ph[4]
         mgb = (rb + db + cb) / (mem_us * 1e-6) / 1e9
-        print(f"| {name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k}, F={wl.F}) | {wl.T / wall:,.0f} | "
+        print(f"| {name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k}, F={wl.F}{', MXFP4 experts' if wl.wfmt == 'mxfp4' else ''}) | {wl.T / wall:,.0f} | "
               f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | "
               f"{tf:.0f} ({100 * tf / PEAK_BF16_TFLOPS:.1f}%) | {wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) | "
               f"{mgb:.0f} ({100 * mgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)

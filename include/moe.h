@@ -87,10 +87,23 @@ typedef enum { MOE_DROP_PASSTHROUGH = 0, MOE_DROP_ZERO = 1, MOE_DROP_FALLBACK = 
  * single expert is weighted by its router probability); a token's weights sum
  * to at most 1. */
 typedef enum { MOE_GATE_SPARSE = 0, MOE_GATE_FULL = 1 } moe_gate;
+/* Storage of the expert weights (W1, W3, W2 and the shared expert's; the router
+ * W_g keeps dtype).  DEFAULT: dtype.  MXFP4 ("MoE: what it costs to train and
+ * serve" / "Memory: sparsity only helps once it fits": gpt-oss experts at about
+ * 4.25 bits per weight), read as the OCP microscaling format: each matrix
+ * [rows][K] (K the dimension the product sums over: d for W1/W3, F for W2) is
+ * rows*K/2 bytes of FP4 E2M1 codes, row-major, element 2i in the low nibble of
+ * byte i, followed by rows*K/32 E8M0 scales (2^(e-127); one per 32 elements of
+ * a row, row-major); a weight is its code's value (0, 0.5, 1, 1.5, 2, 3, 4, 6,
+ * signed) times its block's scale.  Stacked expert tensors hold N such
+ * matrices back to back.  Needs dtype bf16; the weights are widened exactly
+ * to bf16 inside the GEMMs (scale 255, NaN, is not supported, and scales
+ * above 2^125 can overflow bf16). */
+typedef enum { MOE_W_DEFAULT = 0, MOE_W_MXFP4 = 1 } moe_wfmt;
 
 /* Shape and options of one layer.  Enumerations are stored as int32_t so that
- * the struct layout is fixed: 8 + 15 * 4 = 68 bytes padded to 72, alpha at
- * offset 60, gate at offset 64. */
+ * the struct layout is fixed: 8 + 16 * 4 = 72 bytes, alpha at offset 60, gate
+ * at offset 64, wfmt at offset 68. */
 typedef struct moe_shape {
   int64_t T;             /* tokens, >= 0 */
   int32_t d;             /* hidden size */
@@ -113,6 +126,7 @@ typedef struct moe_shape {
   int32_t drop;          /* moe_drop: what a dropped slot contributes */
   float alpha;           /* L_aux coefficient ("Load balancing": typically 0.01-0.1) */
   int32_t gate;          /* moe_gate: how the selected experts are weighted */
+  int32_t wfmt;          /* moe_wfmt: storage of the expert weights */
 } moe_shape;
 
 /* Bytes of device scratch needed by moe_route, moe_dispatch and moe_experts for

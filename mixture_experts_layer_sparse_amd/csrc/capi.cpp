@@ -96,6 +96,8 @@ moe_status check_shape(const moe_shape* s) {
   }
   if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_ARG;
   if (s->gate != MOE_GATE_SPARSE && s->gate != MOE_GATE_FULL) return MOE_ERR_ARG;
+  if (s->wfmt != MOE_W_DEFAULT && s->wfmt != MOE_W_MXFP4) return MOE_ERR_ARG;
+  if (s->wfmt == MOE_W_MXFP4 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // positions and row indices are int32
   if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (s->dtype == MOE_BF16 && (s->d % 64 != 0 || s->F % 64 != 0)) return MOE_ERR_UNSUPPORTED;

@@ -69,7 +69,8 @@ struct GemmArgs {
   int n_out;               // output columns (F for up, d for down)
   const uint16_t* b0;      // [n_seg][n_out][K]  (W1 or W2)
   const uint16_t* b1;      // [n_seg][n_out][K]  (W3, SwiGLU only)
-  int64_t b_stride;        // n_out * K
+  int64_t b_stride;        // n_out * K (elements); MXFP4 B: bytes of one matrix (codes, then scales)
+  int64_t mx_scale_off;    // MXFP4 B: byte offset of the scales within a matrix (n_out * K / 2)
   uint16_t* out;           // [rows][n_out]
   int nt;                  // n-tiles of the tile list
   int split_slots;         // > 0: tail split over this many workgroup slots (see below)
@@ -185,9 +186,18 @@ __device__ __forceinline__ int swz(int row) {
 // which applies the epilogue.  The launches count the same tile list from
 // `offsets`; without split-K every output element is computed by one workgroup
 // over the whole K.
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK>
+//
+// MX: B (the weights) is MXFP4: per matrix [n_out][K], FP4 E2M1 codes (two per
+// byte, element 2i in the low nibble) then one E8M0 scale per 32 elements of
+// a row.  Register-staged pipeline only: each wave loads 32 rows x 64 K of
+// codes (16 bytes per lane, one 32-element block) and the block's scale, and
+// widens them exactly to bf16 (v_cvt_scalef32_pk_bf16_fp4) as it writes the
+// stage, so the LDS tile and the MFMA loop are those of a bf16 B.
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK,
+          bool MX = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   static_assert(!SPLITK || TAIL, "split-K is a tail mode");
+  static_assert(!MX || (REG && BN == 32 * WGM * WGN), "MXFP4 B: register staging, 32 rows per wave");
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
   constexpr int BK = 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
@@ -357,6 +367,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // the buffer return zero), B per expert matrix; per-lane B offsets
   __amdgpu_buffer_rsrc_t rsB0 = make_rsrc(g.b0, 0), rsB1 = rsB0;
   uint32_t b_off[B_PW];
+  uint32_t mx_code = 0, mx_scale = 0;            // MXFP4 B: this lane's code and scale offsets (K step 0)
   bool wave_rows = false;                        // a wave whose rows all lie past the segment end skips its MFMAs
   int wave_blocks = TMI;                         // 32-row blocks of the wave's rows inside the segment
   int a_rows = 0;                                // rows of the tile inside its segment
@@ -402,6 +413,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       a_bytes = static_cast<uint64_t>(g.rows - row0) * K * SA;
     }
     a_nrec = a_bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(a_bytes);
+    if constexpr (MX) {
+      // lane: row n = wave * 32 + lane / 2 of the B tile, the half (32 elements
+      // of the step's 64) lane % 2; the tile's rows interleave W1 and W3 in
+      // runs of WN / 2 >= 32 (gated), so a wave's rows come from one matrix
+      const uint8_t* m0 = reinterpret_cast<const uint8_t*>(g.b0) + e * g.b_stride;
+      const uint8_t* m1 = GATED ? reinterpret_cast<const uint8_t*>(g.b1) + e * g.b_stride : m0;
+      rsB0 = make_rsrc(m0, static_cast<uint64_t>(g.b_stride));
+      rsB1 = GATED ? make_rsrc(m1, static_cast<uint64_t>(g.b_stride)) : rsB0;
+      const int n = wave * 32 + (lane >> 1);
+      int f;
+      if (GATED) {
+        const int wn_ = n / WN, q = n % WN, half = WN / 2;
+        f = ntile * (BN / 2) + wn_ * half + (q % half);
+      } else {
+        f = ntile * BN + n;
+      }
+      mx_code = static_cast<uint32_t>(f) * static_cast<uint32_t>(K / 2) + (lane & 1) * 16;
+      mx_scale = static_cast<uint32_t>(g.mx_scale_off) + static_cast<uint32_t>(f) * static_cast<uint32_t>(K / 32) +
+                 (lane & 1);
+    } else {
     const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
     rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
     rsB1 = GATED ? make_rsrc(g.b1 + e * g.b_stride, b_bytes) : rsB0;
@@ -418,6 +449,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       }
       b_off[j] = static_cast<uint32_t>((f * K) * 2 + c * 16);
     }
+    }
     wave_rows = row0 + wm * WM < row_end;
     a_rows = __builtin_amdgcn_readfirstlane(row_end - row0);
     rs_a_whole = make_rsrc(a_tile, a_bytes);
@@ -431,18 +463,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // 16 bytes per lane, each landing at lane * 16 of its 1 KB block in LDS.
   // RB register buffers keep RB steps of loads in flight.
   constexpr int RB = REG ? MOE_GEMM_RBUF : 1;
-  u32x4 ra[RB][A_PW], rb[RB][B_PW];
+  u32x4 ra[RB][A_PW], rb[RB][MX ? 1 : B_PW];
+  uint32_t rsc[RB];                              // MXFP4 B: the lane's block scale (E8M0)
   auto load_regs = [&](int kt, auto Q) {
     constexpr int q = decltype(Q)::value;
     const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) ra[q][j] = buf_load16(rs_a_whole, a_off[j], ka);
+    if constexpr (MX) {
+      // gated: the wave's 32 rows are W1 rows in the first half of each WN-wide column group
+      const bool w3 = GATED && ((wave * 32) % WN) >= WN / 2;
+      const __amdgpu_buffer_rsrc_t r = w3 ? rsB1 : rsB0;
+      rb[q][0] = buf_load16(r, mx_code, static_cast<uint32_t>(kt * (BK / 2)));
+      rsc[q] = __builtin_amdgcn_raw_buffer_load_b8(r, mx_scale, static_cast<uint32_t>(kt * (BK / 32)), 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < B_PW; ++j) {
-      const int gi = wave * B_PW + j;
-      // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
-      const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
-      rb[q][j] = buf_load16(w3 ? rsB1 : rsB0, b_off[j], kb);
+      for (int j = 0; j < B_PW; ++j) {
+        const int gi = wave * B_PW + j;
+        // gated: B rows q < WN/2 of each wave column group come from W1, the rest from W3
+        const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
+        rb[q][j] = buf_load16(w3 ? rsB1 : rsB0, b_off[j], kb);
+      }
     }
   };
   auto store_regs = [&](uint8_t* stg, auto Q) {
@@ -450,9 +491,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < A_PW; ++j)
       *reinterpret_cast<u32x4*>(stg + (wave * A_PW + j) * 1024 + lane * 16) = ra[q][j];
+    if constexpr (MX) {
+      // 32 codes -> 32 bf16 (4 chunks of 16 bytes) at row n, chunks 4 * (lane % 2) ..,
+      // swizzled like every bf16 B row; scale 2^(e - 127) (e = 0: 2^-127)
+      const int n = wave * 32 + (lane >> 1);
+      const uint32_t e8 = rsc[q] & 0xFFu;
+      const float sf = __uint_as_float(e8 == 0 ? 0x00400000u : (e8 << 23));
 #pragma unroll
-    for (int j = 0; j < B_PW; ++j)
-      *reinterpret_cast<u32x4*>(stg + A_BYTES + (wave * B_PW + j) * 1024 + lane * 16) = rb[q][j];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = rb[q][0][i];
+        u32x4 o;
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 3));
+        const int c = (lane & 1) * 4 + i;
+        *reinterpret_cast<u32x4*>(stg + A_BYTES + n * ROWB + ((c ^ swz<ROWB>(n)) << 4)) = o;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j)
+        *reinterpret_cast<u32x4*>(stg + A_BYTES + (wave * B_PW + j) * 1024 + lane * 16) = rb[q][j];
+    }
   };
   auto compute = [&](const uint8_t* sA, int kk) {
     const uint8_t* sB = sA + A_BYTES;
@@ -899,14 +959,15 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------- launch --
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK = false>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK = false,
+          bool MX = false>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL, SPLITK>), dim3(grid),
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL, SPLITK, MX>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, st, g);
   return hipGetLastError();
 }
@@ -931,8 +992,8 @@ bool skinny(int64_t rows, int n_seg, int64_t nt) {
   return 2 * mt * nt <= split_slots();
 }
 
-int pick_bm(int64_t rows, int n_seg, int min_avg_256, int64_t nt, bool split) {
-  if (split && skinny(rows, n_seg, nt)) return 128;
+int pick_bm(int64_t rows, int n_seg, int min_avg_256, int64_t nt, bool split, bool mx = false) {
+  if (mx || (split && skinny(rows, n_seg, nt))) return 128;
   const int64_t avg = n_seg > 0 ? rows / n_seg : rows;
   return avg >= min_avg_256 ? 256 : 128;
 }
@@ -943,11 +1004,12 @@ int pick_bm(int64_t rows, int n_seg, int min_avg_256, int64_t nt, bool split) {
 // load path: LDS-DMA for the MFMA-bound 256-row tiles, the register-staged
 // pipeline (more bytes in flight) for the weight-streaming 128-row tiles.  The
 // 256-row tile list is tail-split; its 128x128 quarters run on 4 waves of 64x64.
-template <int EPI, bool FP8A>
+template <int EPI, bool FP8A, bool MX = false>
 hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, void* split,
                        hipStream_t st) {
   const int nt = g.nt;
-  if (bm == 256) {
+  if (MX && bm == 256) return hipErrorInvalidValue;          // (MXFP4 weights: 128-row tiles only)
+  if (!MX && bm == 256) {
     const int mtu = static_cast<int>(ceil_div(rows, 256)) + (dense ? 0 : n_seg);
     g.split_slots = split_slots();
     // the scratch header holds the tail's tile count, range count and up to S / 2 tiles' rows
@@ -982,12 +1044,12 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, 
   const bool all_split = split != nullptr && 2 * mt_most * nt <= g.split_slots;
   hipError_t err = hipSuccess;
   if (!all_split) {
-    err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false>(g, mtu * nt, st);
+    err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX>(g, mtu * nt, st);
     if (err != hipSuccess || split == nullptr) return err;
   }
   g.part_meta = static_cast<int32_t*>(split);
   g.part = reinterpret_cast<float*>(static_cast<char*>(split) + kSplitMetaBytes);
-  err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true>(g, kSplitKMax * mtu * nt, st);
+  err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true, MX>(g, kSplitKMax * mtu * nt, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gg_splitk_reduce<EPI, FP8A, 128>), dim3(g.split_slots / 2, 8), dim3(256), 0, st, g);
   return hipGetLastError();
@@ -1007,8 +1069,9 @@ size_t gemm_split_bytes(const moe_shape& s) {
   const int64_t nt_down = ceil_div(s.d, 256);
   const bool fp8 = s.buf_dtype == MOE_FP8_E4M3;
   int64_t tiles = 0;
+  const bool mx = s.wfmt == MOE_W_MXFP4;
   auto add = [&](int64_t r, int n_seg, int min_avg_256, int64_t nt) {
-    if (skinny(r, n_seg, nt) || pick_bm(r, n_seg, min_avg_256, nt, false) == 256)
+    if (skinny(r, n_seg, nt) || pick_bm(r, n_seg, min_avg_256, nt, false, mx) == 256)
       tiles = std::max(tiles, (ceil_div(r, 128) + (n_seg > 1 ? n_seg : 0)) * nt);
   };
   add(rows, s.N, fp8 ? kBm256RowsFp8 : kBm256RowsUp, nt_up);
@@ -1090,19 +1153,24 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
   g.n_out = s.F;
   g.b0 = static_cast<const uint16_t*>(w1);
   g.b1 = static_cast<const uint16_t*>(w3);
-  g.b_stride = static_cast<int64_t>(s.F) * s.d;
+  const bool mx = s.wfmt == MOE_W_MXFP4;
+  g.b_stride = mx ? static_cast<int64_t>(mxfp4_bytes(s.F, s.d)) : static_cast<int64_t>(s.F) * s.d;
+  g.mx_scale_off = static_cast<int64_t>(s.F) * s.d / 2;
   g.out = static_cast<uint16_t*>(h);
   const bool gated = s.act == MOE_ACT_SWIGLU;
   g.nt = static_cast<int>(gated ? ceil_div(s.F, 128) : ceil_div(s.F, 256));
   const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8 ? kBm256RowsFp8 : kBm256RowsUp, g.nt, sk);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, fp8 ? kBm256RowsFp8 : kBm256RowsUp, g.nt, sk, mx);
   if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
-  if (gated) return fp8 ? dispatch_up<EPI_SWIGLU, true>(bm, g, rows, n_seg, dense, split, st)
-                        : dispatch_up<EPI_SWIGLU, false>(bm, g, rows, n_seg, dense, split, st);
-  if (s.act == MOE_ACT_RELU) return fp8 ? dispatch_up<EPI_RELU, true>(bm, g, rows, n_seg, dense, split, st)
-                                        : dispatch_up<EPI_RELU, false>(bm, g, rows, n_seg, dense, split, st);
-  return fp8 ? dispatch_up<EPI_SILU, true>(bm, g, rows, n_seg, dense, split, st)
-             : dispatch_up<EPI_SILU, false>(bm, g, rows, n_seg, dense, split, st);
+#define MOE_UP(EPI_)                                                                                   \
+  return mx ? (fp8 ? dispatch_up<EPI_, true, true>(bm, g, rows, n_seg, dense, split, st)               \
+                   : dispatch_up<EPI_, false, true>(bm, g, rows, n_seg, dense, split, st))             \
+            : (fp8 ? dispatch_up<EPI_, true>(bm, g, rows, n_seg, dense, split, st)                     \
+                   : dispatch_up<EPI_, false>(bm, g, rows, n_seg, dense, split, st));
+  if (gated) MOE_UP(EPI_SWIGLU)
+  if (s.act == MOE_ACT_RELU) MOE_UP(EPI_RELU)
+  MOE_UP(EPI_SILU)
+#undef MOE_UP
 }
 
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
@@ -1127,13 +1195,16 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.n_out = s.d;
   g.b0 = static_cast<const uint16_t*>(w2);
   g.b1 = nullptr;
-  g.b_stride = static_cast<int64_t>(s.d) * s.F;
+  const bool mx = s.wfmt == MOE_W_MXFP4;
+  g.b_stride = mx ? static_cast<int64_t>(mxfp4_bytes(s.d, s.F)) : static_cast<int64_t>(s.d) * s.F;
+  g.mx_scale_off = static_cast<int64_t>(s.d) * s.F / 2;
   g.out = static_cast<uint16_t*>(out);
   g.nt = static_cast<int>(ceil_div(s.d, 256));
   const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, kBm256RowsDown, g.nt, sk);
+  const int bm = pick_bm(rows, dense ? 1 : n_seg, kBm256RowsDown, g.nt, sk, mx);
   if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
-  return dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, split, st);
+  return mx ? dispatch_up<EPI_STORE, false, true>(bm, g, rows, n_seg, dense, split, st)
+            : dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, split, st);
 }
 
 }  // namespace moe

@@ -38,6 +38,12 @@ __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) {
   return (a + b - 1) / b;
 }
 
+// Bytes of one MXFP4 matrix [rows][K]: the codes (two per byte), then one E8M0
+// scale per 32 elements of a row.
+constexpr inline size_t mxfp4_bytes(int64_t rows, int64_t K) {
+  return static_cast<size_t>(rows * K / 2 + rows * K / 32);
+}
+
 // Workspace carving: offsets (bytes) of each region for one shape.
 struct WsLayout {
   size_t route_psum;    // float   [nb_route][N]

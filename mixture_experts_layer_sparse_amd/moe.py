@@ -23,11 +23,13 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_ACT_SILU, MOE_ACT_RELU, MOE_ACT_SWIGLU = range(3)
 MOE_DROP_PASSTHROUGH, MOE_DROP_ZERO, MOE_DROP_FALLBACK = range(3)
 MOE_GATE_SPARSE, MOE_GATE_FULL = range(2)
+MOE_W_DEFAULT, MOE_W_MXFP4 = range(2)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 _ACT = {"silu": MOE_ACT_SILU, "relu": MOE_ACT_RELU, "swiglu": MOE_ACT_SWIGLU}
 _DROP = {"passthrough": MOE_DROP_PASSTHROUGH, "zero": MOE_DROP_ZERO, "fallback": MOE_DROP_FALLBACK}
 _GATE = {"sparse": MOE_GATE_SPARSE, "full": MOE_GATE_FULL}
+_WFMT = {"bf16": MOE_W_DEFAULT, "f32": MOE_W_DEFAULT, "default": MOE_W_DEFAULT, "mxfp4": MOE_W_MXFP4}
 
 
 class MoeError(RuntimeError):
@@ -42,7 +44,7 @@ class Shape(ctypes.Structure):
                 ("capacity", c_int32), ("n_groups", c_int32), ("topk_groups", c_int32),
                 ("group_score_k", c_int32), ("has_shared", c_int32), ("dtype", c_int32),
                 ("buf_dtype", c_int32), ("act", c_int32), ("drop", c_int32), ("alpha", c_float),
-                ("gate", c_int32)]
+                ("gate", c_int32), ("wfmt", c_int32)]
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -64,11 +66,16 @@ class Shape(ctypes.Structure):
 
 def make_shape(T, d, N, k, F, act="swiglu", dtype="bf16", buf=None, capacity=0,
                drop="passthrough", n_groups=0, topk_groups=0, group_score_k=2, shared=False,
-               alpha=0.01, gate="sparse") -> Shape:
+               alpha=0.01, gate="sparse", wfmt="default") -> Shape:
     return Shape(T=T, d=d, N=N, k=k, F=F, capacity=capacity, n_groups=n_groups,
                  topk_groups=topk_groups, group_score_k=group_score_k,
                  has_shared=1 if shared else 0, dtype=_DT[dtype], buf_dtype=_DT[buf or dtype],
-                 act=_ACT[act], drop=_DROP[drop], alpha=alpha, gate=_GATE[gate])
+                 act=_ACT[act], drop=_DROP[drop], alpha=alpha, gate=_GATE[gate], wfmt=_WFMT[wfmt])
+
+
+def mxfp4_bytes(rows: int, K: int) -> int:
+    """Bytes of one MXFP4 matrix [rows][K] as the library takes it: codes, then scales."""
+    return rows * K // 2 + rows * K // 32
 
 
 def shape_of(wl) -> Shape:
@@ -78,7 +85,7 @@ def shape_of(wl) -> Shape:
     return make_shape(wl.T, wl.d, wl.N, wl.k, wl.F, act=wl.act, dtype=wl.dtype, buf=wl.buf,
                       capacity=wl.capacity, drop=wl.drop, n_groups=wl.n_groups,
                       topk_groups=wl.topk_groups, group_score_k=wl.group_score_k,
-                      gate=getattr(wl, "gate", "sparse"),
+                      gate=getattr(wl, "gate", "sparse"), wfmt=getattr(wl, "wfmt", "default"),
                       shared=wl.shared, alpha=wl.alpha)
 
 
@@ -151,6 +158,17 @@ def _check(t: torch.Tensor | None, name: str, shape: tuple, dtype: torch.dtype,
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_w(t, name: str, s: Shape, n: int | None, rows: int, K: int, required: bool = True) -> None:
+    """An expert weight tensor: [n][rows][K] (or [rows][K] when n is None) in the
+    layer's type, or for MXFP4 weights [n][codes + scales] bytes."""
+    if s.wfmt == MOE_W_MXFP4:
+        shape = (mxfp4_bytes(rows, K),) if n is None else (n, mxfp4_bytes(rows, K))
+        _check(t, name, shape, torch.uint8, required)
+    else:
+        shape = (rows, K) if n is None else (n, rows, K)
+        _check(t, name, shape, s.torch_dtype, required)
 
 
 def workspace_bytes(s: Shape) -> int:
@@ -292,8 +310,8 @@ def expert_up_gather(s: Shape, a, row_scale, offsets, src, w1, w3, h=None, ws=No
     _check(a, "a", (s.T, s.d), torch.uint8 if fp8 else s.torch_dtype)
     _check(offsets, "offsets", (s.N + 1,), torch.int32)
     _check(src, "src", (R,), torch.int32)
-    _check(w1, "w1", (s.N, F, s.d), s.torch_dtype)
-    _check(w3, "w3", (s.N, F, s.d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
+    _check_w(w1, "w1", s, s.N, F, s.d)
+    _check_w(w3, "w3", s, s.N, F, s.d, required=s.act == MOE_ACT_SWIGLU)
     if h is None:
         h = torch.empty((R, F), dtype=s.torch_dtype, device=a.device)
     _call("moe_expert_up_gather", ctypes.byref(s), _ptr(a), _ptr(row_scale), _ptr(offsets), _ptr(src),
@@ -307,8 +325,8 @@ def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None, ws=None):
     R, F = s.T * s.k, s.F
     _check(x_perm, "x_perm", (R, s.d), s.buf_torch_dtype)
     _check(offsets, "offsets", (s.N + 1,), torch.int32)
-    _check(w1, "w1", (s.N, F, s.d), s.torch_dtype)
-    _check(w3, "w3", (s.N, F, s.d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
+    _check_w(w1, "w1", s, s.N, F, s.d)
+    _check_w(w3, "w3", s, s.N, F, s.d, required=s.act == MOE_ACT_SWIGLU)
     if h is None:
         h = torch.empty((R, F), dtype=s.torch_dtype, device=x_perm.device)
     _call("moe_expert_up", ctypes.byref(s), _ptr(x_perm), _ptr(row_scale), _ptr(offsets), _ptr(w1),
@@ -320,7 +338,7 @@ def expert_down(s: Shape, h, offsets, w2, out=None, ws=None):
     """ws as for expert_up."""
     R = s.T * s.k
     _check(h, "h", (R, s.F), s.torch_dtype)
-    _check(w2, "w2", (s.N, s.d, s.F), s.torch_dtype)
+    _check_w(w2, "w2", s, s.N, s.d, s.F)
     if out is None:
         out = torch.empty((R, s.d), dtype=s.torch_dtype, device=h.device)
     _call("moe_expert_down", ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(out), _ptr(ws),
@@ -330,9 +348,9 @@ def expert_down(s: Shape, h, offsets, w2, out=None, ws=None):
 
 def shared_expert(s: Shape, x, ws1, ws3, ws2, h_shared=None, out_shared=None, ws=None):
     T, d, F = s.T, s.d, s.F
-    _check(ws1, "ws1", (F, d), s.torch_dtype)
-    _check(ws3, "ws3", (F, d), s.torch_dtype, required=s.act == MOE_ACT_SWIGLU)
-    _check(ws2, "ws2", (d, F), s.torch_dtype)
+    _check_w(ws1, "ws1", s, None, F, d)
+    _check_w(ws3, "ws3", s, None, F, d, required=s.act == MOE_ACT_SWIGLU)
+    _check_w(ws2, "ws2", s, None, d, F)
     if h_shared is None:
         h_shared = torch.empty((T, F), dtype=s.torch_dtype, device=x.device)
     if out_shared is None:
@@ -384,14 +402,14 @@ class Layer:
         T, N, k, d, F = s.T, s.N, s.k, s.d, s.F
         dt = s.torch_dtype
         _check(wg, "wg", (N, d), dt)
-        _check(w1, "w1", (N, F, d), dt)
-        _check(w3, "w3", (N, F, d), dt, required=s.act == MOE_ACT_SWIGLU)
-        _check(w2, "w2", (N, d, F), dt)
+        _check_w(w1, "w1", s, N, F, d)
+        _check_w(w3, "w3", s, N, F, d, required=s.act == MOE_ACT_SWIGLU)
+        _check_w(w2, "w2", s, N, d, F)
         _check(bias, "bias", (N,), torch.float32, required=False)
         if s.has_shared:
-            _check(ws1, "ws1", (F, d), dt)
-            _check(ws3, "ws3", (F, d), dt, required=s.act == MOE_ACT_SWIGLU)
-            _check(ws2, "ws2", (d, F), dt)
+            _check_w(ws1, "ws1", s, None, F, d)
+            _check_w(ws3, "ws3", s, None, F, d, required=s.act == MOE_ACT_SWIGLU)
+            _check_w(ws2, "ws2", s, None, d, F)
         self.wg, self.w1, self.w3, self.w2, self.bias = wg, w1, w3, w2, bias
         self.ws1, self.ws3, self.ws2 = ws1, ws3, ws2
         e = dict(dtype=torch.int32, device=device)

@@ -127,12 +127,11 @@ def mxfp4_split(buf: np.ndarray, rows: int, K: int) -> tuple:
 
 def mxfp4_decode(buf: np.ndarray, rows: int, K: int) -> np.ndarray:
     """Exact float64 values of an MXFP4 matrix [rows][K]: code value times its
-    block's scale."""
+    block's scale (each code byte looked up as its two values)."""
     codes, scales = mxfp4_split(buf, rows, K)
-    el = np.empty((rows, K), np.int64)
-    el[:, 0::2] = codes & 0xF
-    el[:, 1::2] = codes >> 4
-    return fp4_e2m1_decode(el) * np.repeat(e8m0_decode(scales), MX_BLOCK, axis=1)
+    pairs = np.stack([fp4_e2m1_decode(np.arange(256) & 0xF), fp4_e2m1_decode(np.arange(256) >> 4)], axis=1)
+    vals = pairs[codes].reshape(rows, K // MX_BLOCK, MX_BLOCK)
+    return (vals * e8m0_decode(scales)[:, :, None]).reshape(rows, K)
 
 
 def as_weights(a: np.ndarray, wfmt: str, dtype: str, rows: int, K: int) -> np.ndarray:

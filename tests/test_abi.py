@@ -43,17 +43,17 @@ def test_struct_layout_matches_c(M, tmp_path):
     import subprocess
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(moe_shape),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(moe_shape),'
                    ' offsetof(moe_shape, d), offsetof(moe_shape, drop), offsetof(moe_shape, alpha),'
-                   ' offsetof(moe_shape, gate));'
+                   ' offsetof(moe_shape, gate), offsetof(moe_shape, wfmt));'
                    'return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
-    size, off_d, off_drop, off_alpha, off_gate = map(int, subprocess.run([str(exe)], capture_output=True,
-                                                               text=True, check=True).stdout.split())
+    size, off_d, off_drop, off_alpha, off_gate, off_wfmt = map(
+        int, subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split())
     assert ctypes.sizeof(M.Shape) == size == 72
-    assert (M.Shape.d.offset, M.Shape.drop.offset, M.Shape.alpha.offset, M.Shape.gate.offset) == \
-        (off_d, off_drop, off_alpha, off_gate)
+    assert (M.Shape.d.offset, M.Shape.drop.offset, M.Shape.alpha.offset, M.Shape.gate.offset,
+            M.Shape.wfmt.offset) == (off_d, off_drop, off_alpha, off_gate, off_wfmt)
 
 
 def _s(M, **kw):
@@ -85,6 +85,10 @@ def test_shape_checks(M):
     assert M.check_shape(_s(M, gate="full")) == M.MOE_OK
     assert M.check_shape(_s(M).replace(gate=2)) == M.MOE_ERR_ARG
     assert M.check_shape(_s(M).replace(drop=3)) == M.MOE_ERR_ARG
+    # MXFP4 expert weights need bf16 layers
+    assert M.check_shape(_s(M, dtype="bf16", wfmt="mxfp4")) == M.MOE_OK
+    assert M.check_shape(_s(M, wfmt="mxfp4")) == M.MOE_ERR_UNSUPPORTED
+    assert M.check_shape(_s(M).replace(wfmt=2)) == M.MOE_ERR_ARG
 
 
 def test_null_pointers_and_workspace_rejected_on_host(M):

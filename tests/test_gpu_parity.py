@@ -490,3 +490,30 @@ def test_fused_phases_equal_dispatch_buffer_phases(name):
         assert torch.equal(got["row_scale"][:R], ref["row_scale"][:R])
         assert torch.equal(got["x_codes"][got["src"][:R].long()], ref["x_perm"][:R])
     assert torch.equal(h[:R], h_ref[:R])
+
+
+# ---------------------------------------------------------- MXFP4 expert weights --
+# The OCP microscaling format the gpt-oss experts use ("MoE: what it costs to
+# train and serve" / "Memory: sparsity only helps once it fits"): the layer
+# through moe_forward against the oracle, which decodes every weight exactly,
+# and the single-phase calls and the fused layer bit for bit equal to it.
+
+MX_CASES = {
+    # ReLU, bf16 activations, capacity drops, 128-row tiles and their split-K tail
+    "switch_small": lambda: si.small("switch", wfmt="mxfp4"),
+    # SwiGLU with bf16 activations
+    "mixtral_small": lambda: si.small("mixtral", wfmt="mxfp4"),
+    # fp8 activations, groups, MXFP4 shared expert
+    "deepseek_small": lambda: si.small("deepseek_v3", wfmt="mxfp4", shared=True),
+    # one token: every GEMM split along K
+    "one_token": lambda: si.small("deepseek_v3", T=1, wfmt="mxfp4", shared=True),
+    "switch_full": lambda: si.WORKLOADS["switch"].replace(name="switch_mxfp4", wfmt="mxfp4"),
+    "deepseek_v3_full": lambda: si.WORKLOADS["deepseek_v3"].replace(name="deepseek_v3_mxfp4", wfmt="mxfp4"),
+}
+
+
+@pytest.mark.parametrize("name", list(MX_CASES))
+def test_mxfp4_layer(name):
+    wl = MX_CASES[name]()
+    print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} F={wl.F}", flush=True)
+    _forward_and_phases(wl, si.generate(wl))
