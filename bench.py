@@ -173,7 +173,8 @@ def _src_hash(path):
 
 
 def _short(name):
-    for key in ("gg_splitk_reduce", "gg_kernel", "logits_split_kernel", "route_kernel", "route_stats_kernel",
+    for key in ("gg_splitk_reduce", "gg_kernel", "logits_split_kernel", "route_kernel", "route_stats_tiles_kernel",
+                "route_stats_kernel",
                 "disp_hist_kernel", "disp_plan_tiles_kernel", "disp_plan_kernel", "disp_copy_kernel",
                 "disp_fp8_kernel", "combine_bf16_kernel", "combine_f32_kernel", "__amd_rocclr_copyBuffer"):
         if key in name:
@@ -222,7 +223,7 @@ def summarize(prof, out, steps, warmup):
         dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
         timed = dur[warmup:warmup + steps] if len(dur) >= warmup + steps else dur
         r0 = rs[0]
-        regs = (f"{r0.get('Arch_VGPR_Count', '?')}+{r0.get('Accum_VGPR_Count', '?')} / "
+        regs = (f"{r0.get('Arch_VGPR_Count', r0.get('VGPR_Count', '?'))}+{r0.get('Accum_VGPR_Count', '?')} / "
                 f"{r0.get('SGPR_Count', '?')} / {int(r0.get('LDS_Block_Size', 0) or 0) // 1024} / "
                 f"{r0.get('Scratch_Size', '?')}")
         kern[k] = {"calls": len(dur), "timed_us": sum(timed) / len(timed), "all_us": sum(dur) / len(dur),
@@ -236,6 +237,11 @@ def summarize(prof, out, steps, warmup):
     occ = counters("occ", "OccupancyPercent")
     copy_kib = (1 << 28) / 1024
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    # GRBM_GUI_ACTIVE is summed over the XCDs
+    n_xcc = 8
+    for r in rows_of("trace", "run_agent_info.csv"):
+        if r.get("Agent_Type", "").endswith("GPU") and r.get("Num_Xcc"):
+            n_xcc = int(r["Num_Xcc"])
     rows, table, table2 = {}, [], []
     for k, v in sorted(kern.items(), key=lambda kv: -kv[1]["timed_us"]):
         if k.startswith("__amd"):
@@ -247,11 +253,14 @@ def summarize(prof, out, steps, warmup):
         table.append(f"| `{k}` | {v['calls']} | {v['timed_us']:.1f} | {v['all_us']:.1f} | {fb / 2**20:.1f} | "
                      f"{wb / 2**20:.1f} |")
         # the shader clock under the profiler: active GPU cycles over the dispatch's duration
-        clk = gui.get(k, 0.0) / (v["all_us"] * 1e3) if k in gui else 0.0
+        # (only for dispatches long enough that the profiler's own active
+        # cycles around them do not count)
+        clk = gui.get(k, 0.0) / n_xcc / (v["all_us"] * 1e3) if k in gui and v["all_us"] > 200 else 0.0
+        clk_s = f"{clk:.2f}" if clk else "-"
         bf16_tflop = mops.get(k, 0.0) * 512 / 1e12
         table2.append(f"| `{k}` | {v['regs']} | {v['wg']} x {int(v['grid']) // max(int(v['wg']), 1) if str(v['grid']).isdigit() else '?'} | "
                       f"{mfma.get(k, 0.0):.1f} | {bf16_tflop:.3f} | {bankc.get(k, 0.0):.3g} | "
-                      f"{ldsact.get(k, 0.0):.3g} | {occ.get(k, 0.0):.1f} | {clk:.2f} |")
+                      f"{ldsact.get(k, 0.0):.3g} | {occ.get(k, 0.0):.1f} | {clk_s} |")
     data = {"gemm_src_sha256_16": _src_hash(GEMM_SRC), "fetch_scale": f_scale,
             "write_scale": w_scale, "timed_steps": [warmup, steps], "kernels": rows}
     text = "\n".join([
@@ -275,12 +284,12 @@ def summarize(prof, out, steps, warmup):
         "|---|---|---|---|---|---|",
         *table,
         "",
-        "Registers (arch VGPR + accumulation VGPR / SGPR), LDS KiB and scratch bytes per lane from the kernel "
+        "Registers as the trace reports them (its VGPR field + accumulation VGPRs / SGPRs; the code object of the gate/up kernel allocates 238 VGPRs), LDS KiB and scratch bytes per lane from the kernel "
         "trace; workgroup size x workgroups; MfmaUtil = MFMA-busy cycles / (active cycles x SIMDs), %; bf16 "
         "MFMA TFLOP per dispatch from SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS bank-conflict and LDS-active "
-        "cycles (summed over the SEs); OccupancyPercent; clock = GRBM_GUI_ACTIVE cycles per dispatch over the "
-        "dispatch's average duration, GHz (the counter runs are short, so their first dispatches run at a "
-        "higher clock than a long run).",
+        "cycles (summed over the SEs); OccupancyPercent; clock = GRBM_GUI_ACTIVE cycles per dispatch and XCD "
+        "over the dispatch's average duration in the trace run, GHz, for dispatches over 200 us (the counter "
+        "runs are short, so they run at a higher clock than the long trace run).",
         "",
         "| kernel | VGPR / SGPR / LDS / scratch | launch | MfmaUtil % | bf16 MFMA TFLOP | LDS bank-conflict "
         "cycles | LDS active cycles | occupancy % | clock GHz |",
