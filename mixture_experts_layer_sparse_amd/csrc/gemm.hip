@@ -30,6 +30,9 @@
 //   * fp8 activations (e4m3 codes) stay fp8 in LDS and are widened to bf16
 //     exactly as fragments are read; the per-row scale multiplies the float32
 //     accumulator;
+//   * MXFP4 weights are widened to bf16 as they are written to LDS, except
+//     with fp8 activations: then both operands stay in their codes and the
+//     scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) applies the block scales;
 //   * SwiGLU: the B tile interleaves W1 and W3 rows of the same output columns
 //     so that each wave holds both halves of its outputs; the activation runs
 //     on the accumulators and h is written once, in bf16.
@@ -40,9 +43,13 @@
 
 #include "moe_internal.h"
 
-// register buffers of staged loads: 1 or 2 K steps in flight beyond the LDS stages
+// register buffers of staged loads: K steps in flight beyond the LDS stages (bf16
+// and MXFP4 weights); 3 and 4 measured no faster than 2 on any shape
 #ifndef MOE_GEMM_RBUF
 #define MOE_GEMM_RBUF 2
+#endif
+#ifndef MOE_GEMM_RBUF_MX
+#define MOE_GEMM_RBUF_MX 2
 #endif
 // 1: each XCD owns runs of consecutive tile ids; 0: tile id = round * grid + block
 #ifndef MOE_GEMM_XCD_MAP
@@ -54,6 +61,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum Epi { EPI_STORE = 0, EPI_SILU = 1, EPI_RELU = 2, EPI_SWIGLU = 3 };
 
@@ -140,6 +148,16 @@ __device__ __forceinline__ void sched_mfma_loads(std::integer_sequence<int, Q...
   (sched_mfma_then_loads<(Q + 1) * LPW / NMM - Q * LPW / NMM>(), ...);
 }
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // f(integral_constant<int, min(n, N)>) for a wave-uniform 0 <= n: one code
 // path per count of live 32-row blocks.
 template <int N, typename F>
@@ -193,17 +211,30 @@ __device__ __forceinline__ int swz(int row) {
 // codes (16 bytes per lane, one 32-element block) and the block's scale, and
 // widens them exactly to bf16 (v_cvt_scalef32_pk_bf16_fp4) as it writes the
 // stage, so the LDS tile and the MFMA loop are those of a bf16 B.
+//
+// MXS (MXFP4 B with fp8 A, K a multiple of 128): no widening at all.  The
+// stage holds the e4m3 codes of A, the FP4 codes of B and B's E8M0 scales as
+// they are in memory, and v_mfma_scale_f32_32x32x64_f8f6f4 multiplies them
+// (A scale 1, the per-row scale on the accumulator as for every fp8 A).  In
+// that instruction a lane of the B operand holds 32 consecutive K (one MX
+// block, with its scale) and the lane half h of column n holds K 32h ..
+// 32h + 31 of the 64; the A lane half h holds K 16h .. 16h + 15 in its first
+// 16 bytes and K 32 + 16h .. 32 + 16h + 15 in the next 16.  A step is 128 K
+// (two MFMA slices).
 template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK,
-          bool MX = false>
+          bool MX = false, bool MXS = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   static_assert(!SPLITK || TAIL, "split-K is a tail mode");
   static_assert(!MX || (REG && BN == 32 * WGM * WGN), "MXFP4 B: register staging, 32 rows per wave");
+  static_assert(!MXS || (MX && FP8A), "scaled MFMA: fp8 A, MXFP4 B");
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
-  constexpr int BK = 64;
+  constexpr int BK = MXS ? 128 : 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
-  constexpr int ROWA = BK * SA, ROWB = BK * 2;     // bytes per tile row per stage
+  constexpr int ROWA = BK * SA;                    // bytes per tile row per stage: A,
+  constexpr int ROWB = MXS ? BK / 2 : BK * 2;      // B (FP4 codes with MXS, else bf16)
   constexpr int A_BYTES = BM * ROWA, B_BYTES = BN * ROWB;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int SC_BYTES = MXS ? BN * 4 : 0;       // MXS: B's 4 block scales per row and step
+  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   constexpr int A_PW = A_BYTES / 1024 / NW;        // 1 KB wave-loads per wave per stage
   constexpr int B_PW = B_BYTES / 1024 / NW;
   constexpr int LPW = A_PW + B_PW;                 // loads per wave per stage
@@ -368,6 +399,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   __amdgpu_buffer_rsrc_t rsB0 = make_rsrc(g.b0, 0), rsB1 = rsB0;
   uint32_t b_off[B_PW];
   uint32_t mx_code = 0, mx_scale = 0;            // MXFP4 B: this lane's code and scale offsets (K step 0)
+  // gated: B tile row n interleaves W1 and W3 rows in runs of WN / 2; the weight row it holds
+  auto b_row = [&](int n) {
+    if (GATED) {
+      const int wn_ = n / WN, q = n % WN, half = WN / 2;
+      return ntile * (BN / 2) + wn_ * half + (q % half);
+    }
+    return ntile * BN + n;
+  };
   bool wave_rows = false;                        // a wave whose rows all lie past the segment end skips its MFMAs
   int wave_blocks = TMI;                         // 32-row blocks of the wave's rows inside the segment
   int a_rows = 0;                                // rows of the tile inside its segment
@@ -421,17 +460,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const uint8_t* m1 = GATED ? reinterpret_cast<const uint8_t*>(g.b1) + e * g.b_stride : m0;
       rsB0 = make_rsrc(m0, static_cast<uint64_t>(g.b_stride));
       rsB1 = GATED ? make_rsrc(m1, static_cast<uint64_t>(g.b_stride)) : rsB0;
-      const int n = wave * 32 + (lane >> 1);
-      int f;
-      if (GATED) {
-        const int wn_ = n / WN, q = n % WN, half = WN / 2;
-        f = ntile * (BN / 2) + wn_ * half + (q % half);
+      if constexpr (MXS) {
+        // codes: rows wave * 32 + 16 j + lane / 4, 16-byte chunk lane % 4 of the
+        // step's 64 bytes (piece j adds 16 weight rows, as the soffset); scales:
+        // lane % 32's row, the step's 4 bytes as one word
+        const int fc = b_row(wave * 32 + (lane >> 2)), fs = b_row(wave * 32 + (lane & 31));
+        mx_code = static_cast<uint32_t>(fc) * static_cast<uint32_t>(K / 2) + (lane & 3) * 16;
+        mx_scale = static_cast<uint32_t>(g.mx_scale_off) + static_cast<uint32_t>(fs) * static_cast<uint32_t>(K / 32);
       } else {
-        f = ntile * BN + n;
+        const int f = b_row(wave * 32 + (lane >> 1));
+        mx_code = static_cast<uint32_t>(f) * static_cast<uint32_t>(K / 2) + (lane & 1) * 16;
+        mx_scale = static_cast<uint32_t>(g.mx_scale_off) + static_cast<uint32_t>(f) * static_cast<uint32_t>(K / 32) +
+                   (lane & 1);
       }
-      mx_code = static_cast<uint32_t>(f) * static_cast<uint32_t>(K / 2) + (lane & 1) * 16;
-      mx_scale = static_cast<uint32_t>(g.mx_scale_off) + static_cast<uint32_t>(f) * static_cast<uint32_t>(K / 32) +
-                 (lane & 1);
     } else {
     const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
     rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
@@ -440,14 +481,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     for (int j = 0; j < B_PW; ++j) {
       const int n = (wave * B_PW + j) * (1024 / ROWB) + lane / B_CPR;
       const int c = (lane % B_CPR) ^ swz<ROWB>(n);
-      int f;
-      if (GATED) {
-        const int wn_ = n / WN, q = n % WN, half = WN / 2;
-        f = ntile * (BN / 2) + wn_ * half + (q % half);
-      } else {
-        f = ntile * BN + n;
-      }
-      b_off[j] = static_cast<uint32_t>((f * K) * 2 + c * 16);
+      b_off[j] = static_cast<uint32_t>((b_row(n) * K) * 2 + c * 16);
     }
     }
     wave_rows = row0 + wm * WM < row_end;
@@ -462,15 +496,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // K steps of this wave's loads, staged in registers: A_PW + B_PW pieces of
   // 16 bytes per lane, each landing at lane * 16 of its 1 KB block in LDS.
   // RB register buffers keep RB steps of loads in flight.
-  constexpr int RB = REG ? MOE_GEMM_RBUF : 1;
-  u32x4 ra[RB][A_PW], rb[RB][MX ? 1 : B_PW];
-  uint32_t rsc[RB];                              // MXFP4 B: the lane's block scale (E8M0)
+  constexpr int RB = REG ? (MX ? MOE_GEMM_RBUF_MX : MOE_GEMM_RBUF) : 1;
+  static_assert(RB >= 1 && RB <= 4, "register buffers");
+  u32x4 ra[RB][A_PW], rb[RB][MX && !MXS ? 1 : B_PW];
+  uint32_t rsc[RB];                              // MXFP4 B: the lane's block scale(s) (E8M0)
   auto load_regs = [&](int kt, auto Q) {
     constexpr int q = decltype(Q)::value;
     const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) ra[q][j] = buf_load16(rs_a_whole, a_off[j], ka);
-    if constexpr (MX) {
+    if constexpr (MXS) {
+      const bool w3 = GATED && ((wave * 32) % WN) >= WN / 2;
+      const __amdgpu_buffer_rsrc_t r = w3 ? rsB1 : rsB0;
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j)
+        rb[q][j] = buf_load16(r, mx_code, static_cast<uint32_t>(kt * (BK / 2) + j * 16 * (K / 2)));
+      rsc[q] = __builtin_amdgcn_raw_buffer_load_b32(r, mx_scale, static_cast<uint32_t>(kt * (BK / 32)), 0);
+    } else if constexpr (MX) {
       // gated: the wave's 32 rows are W1 rows in the first half of each WN-wide column group
       const bool w3 = GATED && ((wave * 32) % WN) >= WN / 2;
       const __amdgpu_buffer_rsrc_t r = w3 ? rsB1 : rsB0;
@@ -491,7 +533,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < A_PW; ++j)
       *reinterpret_cast<u32x4*>(stg + (wave * A_PW + j) * 1024 + lane * 16) = ra[q][j];
-    if constexpr (MX) {
+    if constexpr (MXS) {
+      // codes as loaded (row n, chunk lane % 4, swizzled), the scale word of row wave * 32 + lane
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j) {
+        const int n = wave * 32 + j * 16 + (lane >> 2);
+        *reinterpret_cast<u32x4*>(stg + A_BYTES + n * ROWB + (((lane & 3) ^ swz<ROWB>(n)) << 4)) = rb[q][j];
+      }
+      if (lane < 32) *reinterpret_cast<uint32_t*>(stg + A_BYTES + B_BYTES + (wave * 32 + lane) * 4) = rsc[q];
+    } else if constexpr (MX) {
       // 32 codes -> 32 bf16 (4 chunks of 16 bytes) at row n, chunks 4 * (lane % 2) ..,
       // swizzled like every bf16 B row; scale 2^(e - 127) (e = 0: 2^-127)
       const int n = wave * 32 + (lane >> 1);
@@ -514,7 +564,38 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         *reinterpret_cast<u32x4*>(stg + A_BYTES + (wave * B_PW + j) * 1024 + lane * 16) = rb[q][j];
     }
   };
+  // MXS: MFMA slice kk (64 K) of the stage
+  auto compute_mxs = [&](const uint8_t* sA, int kk) {
+    const uint8_t* sB = sA + A_BYTES;
+    i32x8 af[TMI], bfr[TNI];
+    int sc[TNI];
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int r = wm * WM + i * 32 + fr;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + r * ROWA + (((kk * 4 + fk) ^ swz<ROWA>(r)) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + r * ROWA + (((kk * 4 + 2 + fk) ^ swz<ROWA>(r)) << 4));
+      af[i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+      const int n = wn * WN + j * 32 + fr;
+      const u32x4 b = *reinterpret_cast<const u32x4*>(sB + n * ROWB + (((kk * 2 + fk) ^ swz<ROWB>(n)) << 4));
+      // (FP4 B reads the first four registers of the operand)
+      bfr[j] = __builtin_bit_cast(i32x8, __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1));
+      sc[j] = sB[B_BYTES + n * 4 + kk * 2 + fk];
+    }
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0 /* A e4m3 */,
+                                                                     4 /* B e2m1 */, 0, 127, 0, sc[j]);
+  };
   auto compute = [&](const uint8_t* sA, int kk) {
+    if constexpr (MXS) {
+      compute_mxs(sA, kk);
+      return;
+    }
     const uint8_t* sB = sA + A_BYTES;
     const int cc = kk * 2 + fk;                 // 8-element k chunk of this lane
     bf16x8 af[TMI], bfr[TNI];
@@ -542,24 +623,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
-  // Register-staged pipeline: while step kt computes from one LDS stage,
+  // Register-staged pipeline (RB register buffers, 2 by default; MXFP4 weights
+  // MOE_GEMM_RBUF_MX): while step kt computes from one LDS stage,
   // registers hold the loads of the next RB steps; halfway through step kt
   // the registers of step kt + 1 are written to the other stage and refilled
   // with the loads of step kt + 1 + RB, so RB steps of global loads stay in
   // flight.  One barrier per step publishes the written stage and frees the
   // one just read.  Register buffer q holds steps congruent to q mod RB.
   using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, (RB > 1 ? 1 : 0)>;
+  constexpr int NSL = MXS ? BK / 64 : BK / 16;     // MFMA K slices per step
   auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, auto Q) {
     if (wave_rows) {
 #pragma unroll
-      for (int kk = 0; kk < BK / 32; ++kk) compute(cur, kk);
+      for (int kk = 0; kk < NSL / 2; ++kk) compute(cur, kk);
     }
     if (kt + 1 < kend) store_regs(nxt, Q);
     if (kt + 1 + RB < kend) load_regs(kt + 1 + RB, Q);
     if (wave_rows) {
 #pragma unroll
-      for (int kk = BK / 32; kk < BK / 16; ++kk) compute(cur, kk);
+      for (int kk = NSL / 2; kk < NSL; ++kk) compute(cur, kk);
     }
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
@@ -663,7 +745,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  static_assert(BK / 16 == 4, "four K slices per step");
+  static_assert(REG || BK / 16 == 4, "four K slices per step");
   // invariant at step entry: fragments of (cur, slice 0) issued into buffer 0.
   // NI = the wave's live 32-row blocks: fragment reads and MFMAs of blocks
   // wholly past the segment end are left out, so that a segment's partial
@@ -708,14 +790,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     if constexpr (REG) {
       load_regs(kbeg, I0{});
       store_regs(sm0, I0{});
-      if (kend - kbeg > 1) load_regs(kbeg + 1, I1{});
-      if (RB > 1 && kend - kbeg > 2) load_regs(kbeg + 2, I0{});
+      // steps kbeg + 1 .. kbeg + RB into buffers 1, .., RB - 1, 0
+      static_for<RB>([&](auto I) {
+        constexpr int i = decltype(I)::value + 1;
+        if (kend - kbeg > i) load_regs(kbeg + i, std::integral_constant<int, i % RB>{});
+      });
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      // step kt stores the registers of step kt + 1: buffer (kt + 1 - kbeg) % RB
-      for (int kt = kbeg; kt < kend; kt += 2) {
-        step(kt, sm0, sm1, I1{});
-        if (kt + 1 < kend) step(kt + 1, sm1, sm0, I0{});
+      // step kt stores the registers of step kt + 1: buffer (kt + 1 - kbeg) % RB;
+      // the LDS stages alternate, so the loop is unrolled by lcm(2, RB)
+      constexpr int U = RB % 2 == 0 ? RB : 2 * RB;
+      for (int kt = kbeg; kt < kend; kt += U) {
+        static_for<U>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          if (j == 0 || kt + j < kend)
+            step(kt + j, j % 2 ? sm1 : sm0, j % 2 ? sm0 : sm1, std::integral_constant<int, (j + 1) % RB>{});
+        });
       }
     } else {
       // the tile's first two steps were issued before the previous epilogue
@@ -960,14 +1050,14 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 // ------------------------------------------------------------------- launch --
 
 template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK = false,
-          bool MX = false>
+          bool MX = false, bool MXS = false>
 hipError_t launch_gg_on(const GemmArgs& g, int tiles_upper, hipStream_t st) {
   int cus = device_cu_count();
   int grid = (cus / 8) * 8;
   int want = ((tiles_upper + 7) / 8) * 8;
   if (want < grid) grid = want;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL, SPLITK, MX>), dim3(grid),
+  hipLaunchKernelGGL((gg_kernel<BM, BN, WGM, WGN, EPI, FP8A, REG, TAIL, SPLITK, MX, MXS>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, st, g);
   return hipGetLastError();
 }
@@ -1042,14 +1132,19 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, 
   const int64_t segs = dense ? 1 : (rows < n_seg ? rows : n_seg);
   const int64_t mt_most = dense ? ceil_div(rows, 128) : std::min<int64_t>(rows, (rows + 127 * segs) / 128);
   const bool all_split = split != nullptr && 2 * mt_most * nt <= g.split_slots;
+  // fp8 A with MXFP4 B: the scaled MFMA on the codes as stored (128-K steps)
+  constexpr bool MXS_OK = MX && FP8A;
+  const bool mxs = MXS_OK && g.K % 128 == 0;
   hipError_t err = hipSuccess;
   if (!all_split) {
-    err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX>(g, mtu * nt, st);
+    err = mxs ? launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX, MXS_OK>(g, mtu * nt, st)
+              : launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX>(g, mtu * nt, st);
     if (err != hipSuccess || split == nullptr) return err;
   }
   g.part_meta = static_cast<int32_t*>(split);
   g.part = reinterpret_cast<float*>(static_cast<char*>(split) + kSplitMetaBytes);
-  err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true, MX>(g, kSplitKMax * mtu * nt, st);
+  err = mxs ? launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true, MX, MXS_OK>(g, kSplitKMax * mtu * nt, st)
+            : launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, true, true, MX>(g, kSplitKMax * mtu * nt, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gg_splitk_reduce<EPI, FP8A, 128>), dim3(g.split_slots / 2, 8), dim3(256), 0, st, g);
   return hipGetLastError();

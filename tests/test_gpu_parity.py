@@ -503,8 +503,10 @@ MX_CASES = {
     "switch_small": lambda: si.small("switch", wfmt="mxfp4"),
     # SwiGLU with bf16 activations
     "mixtral_small": lambda: si.small("mixtral", wfmt="mxfp4"),
-    # fp8 activations, groups, MXFP4 shared expert
+    # fp8 activations (gate/up on the scaled fp8 x FP4 MFMA), groups, MXFP4 shared expert
     "deepseek_small": lambda: si.small("deepseek_v3", wfmt="mxfp4", shared=True),
+    # fp8 activations with d not a multiple of 128: the gate/up widens the weights to bf16
+    "deepseek_d448": lambda: si.small("deepseek_v3", d=448, wfmt="mxfp4"),
     # one token: every GEMM split along K
     "one_token": lambda: si.small("deepseek_v3", T=1, wfmt="mxfp4", shared=True),
     "switch_full": lambda: si.WORKLOADS["switch"].replace(name="switch_mxfp4", wfmt="mxfp4"),
