@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--workload", default="mixtral",
+                    help="mixtral, switch, deepseek_v3, dbrx, tiny; append _mxfp4 for MXFP4 expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time the layer with the dispatch buffer (row copy, then the up GEMM on it) "
@@ -60,6 +61,15 @@ def parse():
                          "rocprofv3 csv output")
     ap.add_argument("--out", default=None, help="summarize: markdown file to write")
     return ap.parse_args()
+
+
+def workload(name):
+    """A named workload; the suffix ``_mxfp4`` gives the same layer with MXFP4
+    expert weights."""
+    import synthetic_inputs as si
+    if name.endswith("_mxfp4"):
+        return si.WORKLOADS[name[:-len("_mxfp4")]].replace(name=name, wfmt="mxfp4")
+    return si.WORKLOADS[name]
 
 
 def alg_bytes(wl, R, fused=False):
@@ -430,11 +440,7 @@ def sweep(steps, warmup):
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|")
     for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx", "switch_mxfp4", "deepseek_v3_mxfp4"):
-        if name.endswith("_mxfp4"):
-            # the same layer with MXFP4 expert weights
-            wl = si.WORKLOADS[name[:-len("_mxfp4")]].replace(name=name, wfmt="mxfp4")
-        else:
-            wl = si.WORKLOADS[name]
+        wl = workload(name)
         inp = si.generate(wl)
         g = {k: _to_dev(v) for k, v in inp.items()}
         del inp
@@ -611,7 +617,7 @@ def main():
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 10}))
         return
 
-    wl = si.WORKLOADS[a.workload]
+    wl = workload(a.workload)
     inp = si.generate(wl)
 
     def dev(arr):

@@ -18,14 +18,17 @@
 // spread over more waves, and for wide routers (many experts times a wide d)
 // as one dense split-K GEMM; the router then adds the partials in order.
 // Selection: with at most 32 experts a token's lanes hold one expert each (one
-// lane per token under a group limit); with more, one wave handles one token.
-// Both use maximum reductions on keys (logit, ~index), so equal logits go to
-// the lower index, and nothing depends on thread timing.
+// lane per token under a group limit), with maximum reductions on keys (logit,
+// ~index); with more, one wave handles one token, each lane four consecutive
+// experts, by a float maximum over the wave and a ballot for the lowest expert
+// index holding it.  Either way equal logits go to the lower index, and nothing
+// depends on thread timing.
 #include "moe_internal.h"
 
-// k-steps of loads each wave issues before their MFMAs
+// k-steps of loads each wave issues before their MFMAs (8 spills three
+// registers under the four-waves-per-SIMD register budget)
 #ifndef MOE_ROUTE_U
-#define MOE_ROUTE_U 8
+#define MOE_ROUTE_U 7
 #endif
 
 namespace moe {
@@ -104,11 +107,6 @@ __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
 __device__ __forceinline__ float lanef(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-__device__ __forceinline__ uint64_t lane64(uint64_t v, int l) {
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 // All-reduces over aligned runs of `width` lanes (a power of two up to 64).
@@ -140,10 +138,6 @@ __device__ __forceinline__ uint64_t run_max_u64(uint64_t v, int width) {
   return v;
 }
 // Whole wave: rows by DPP, then the four row results through readlane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = run_max_u64(v, 16);
-  return umax64(umax64(lane64(v, 0), lane64(v, 16)), umax64(lane64(v, 32), lane64(v, 48)));
-}
 __device__ __forceinline__ float wave_max_f(float v) {
   v = run_max_f(v, 16);
   return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
@@ -158,8 +152,8 @@ constexpr int SMALL_N = 32;            // up to this many experts one lane selec
 
 // Logit tile [TM][ldl] in LDS, computed by the bf16 MFMA path.  The 8 waves
 // split the experts into CG column groups of 16-expert blocks and d into KS
-// slices (CG * KS = 8); each wave issues the loads of 8 k-steps before their
-// MFMAs, so that about 32 KB per wave are in flight.
+// slices (CG * KS = 8); each wave issues the loads of MOE_ROUTE_U (7) k-steps
+// before their MFMAs, so that about 28 KB per wave are in flight.
 template <int TM>
 __device__ void logits_bf16(const RouteArgs& a, int64_t t0, float* part, float* lt, int ldl) {
   const int lane = threadIdx.x & 63;
@@ -735,10 +729,17 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     return;
   }
 
-  // one wave per token
-  float psr[4] = {0.f, 0.f, 0.f, 0.f};    // this wave's sum of p over its tokens
+  // one wave per token; lane l holds experts 4l .. 4l + 3, so that a group of
+  // gsz experts (gsz a multiple of 4, gsz / 4 a power of two) is an aligned
+  // run of gsz / 4 lanes
+  float psr[4] = {0.f, 0.f, 0.f, 0.f};    // this wave's sum of p over its tokens (expert 4 lane + i)
   const int G = a.n_groups > 1 ? a.n_groups : 1;
   const int gsz = N / G;
+  const int GL = gsz / 4;
+  const bool lane_groups = G > 1 && a.gsk <= 2 && gsz % 4 == 0 && (GL & (GL - 1)) == 0;
+  int grp[4];                             // group of expert 4 lane + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) grp[i] = G > 1 && 4 * lane + i < N ? (4 * lane + i) / gsz : 0;
   for (int m = wave; m < TM; m += RW) {
     const int64_t t = t0 + m;
     if (t >= a.T) break;
@@ -747,7 +748,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     bool ok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
+      const int e = 4 * lane + i;
       ok[i] = e < N;
       v[i] = ok[i] ? row[e] : -INFINITY;
     }
@@ -764,89 +765,92 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int i = 0; i < 4; ++i) psr[i] += z[i] * rzs;
 
-    // group limit: lane g scores group g by the sum of its gsk largest logits
-    uint64_t gmask = ~0ull;
+    // group limit: a group scores the sum of its gsk largest logits, and the
+    // topk_groups best groups (equal scores: the lower group) stay allowed
+    uint64_t gsel = ~0ull;
     if (G > 1) {
-      float gs = 0.f;
-      if (a.gsk <= 2 && gsz <= 64 && (gsz & (gsz - 1)) == 0) {
-        // a group is an aligned run of gsz lanes of one of the four 64-expert
-        // slices: a butterfly over it merges (largest, second largest) pairs
-        float gsv[4];
+      bool rep;                                   // this lane holds its group's score
+      int rg;                                     // that group
+      float gs = -INFINITY;
+      if (lane_groups) {
+        // the two largest of the lane's four, then merged over the group's lanes
+        const float a0 = fmaxf(v[0], v[1]), b0 = fminf(v[0], v[1]);
+        const float a1 = fmaxf(v[2], v[3]), b1 = fminf(v[2], v[3]);
+        float t1 = fmaxf(a0, a1), t2 = fmaxf(fminf(a0, a1), fmaxf(b0, b1));
+        auto merge = [&](float o1, float o2) {
+          t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+          t1 = fmaxf(t1, o1);
+        };
+        if (GL > 1) merge(dppf<kDppXor1>(t1), dppf<kDppXor1>(t2));
+        if (GL > 2) merge(dppf<kDppXor2>(t1), dppf<kDppXor2>(t2));
+        if (GL > 4) merge(dppf<kDppHalfMirror>(t1), dppf<kDppHalfMirror>(t2));
+        if (GL > 8) merge(dppf<kDppMirror>(t1), dppf<kDppMirror>(t2));
+        if (GL > 16) merge(__shfl_xor(t1, 16), __shfl_xor(t2, 16));
+        if (GL > 32) merge(__shfl_xor(t1, 32), __shfl_xor(t2, 32));
+        rep = (lane & (GL - 1)) == 0 && lane < G * GL;
+        rg = lane / GL;
+        if (rep) gs = a.gsk == 1 ? t1 : t1 + t2;
+      } else {
+        // lane g scores group g from the logit row
+        rep = lane < G;
+        rg = lane;
+        if (rep) {
+          float top[kMaxTopK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float t1 = v[i], t2 = -INFINITY;
-          auto merge = [&](float o1, float o2) {
-            t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
-            t1 = fmaxf(t1, o1);
-          };
-          if (gsz > 1) merge(dppf<kDppXor1>(t1), dppf<kDppXor1>(t2));
-          if (gsz > 2) merge(dppf<kDppXor2>(t1), dppf<kDppXor2>(t2));
-          if (gsz > 4) merge(dppf<kDppHalfMirror>(t1), dppf<kDppHalfMirror>(t2));
-          if (gsz > 8) merge(dppf<kDppMirror>(t1), dppf<kDppMirror>(t2));
-          if (gsz > 16) merge(__shfl_xor(t1, 16), __shfl_xor(t2, 16));
-          if (gsz > 32) merge(__shfl_xor(t1, 32), __shfl_xor(t2, 32));
-          gsv[i] = a.gsk == 1 ? t1 : t1 + t2;
-        }
-        // lane g < G fetches group g's score from the group's first lane
-        const int src_i = (lane * gsz) >> 6, src_lane = (lane * gsz) & 63;
+          for (int q = 0; q < kMaxTopK; ++q) top[q] = -INFINITY;
+          for (int e = lane * gsz; e < (lane + 1) * gsz; ++e) {
+            float val = row[e];
+            // insert into the descending list top[0..gsk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float val = __shfl(gsv[i], src_lane & 63);
-          if (i == src_i) gs = val;
-        }
-        if (lane >= G) gs = 0.f;
-      } else if (lane < G) {
-        float top[kMaxTopK];
-#pragma unroll
-        for (int q = 0; q < kMaxTopK; ++q) top[q] = -INFINITY;
-        for (int e = lane * gsz; e < (lane + 1) * gsz; ++e) {
-          float val = row[e];
-          // insert into the descending list top[0..gsk)
-#pragma unroll
-          for (int q = 0; q < kMaxTopK; ++q) {
-            if (q < a.gsk && val > top[q]) {
-              const float tmp = top[q];
-              top[q] = val;
-              val = tmp;
+            for (int q = 0; q < kMaxTopK; ++q) {
+              if (q < a.gsk && val > top[q]) {
+                const float tmp = top[q];
+                top[q] = val;
+                val = tmp;
+              }
             }
           }
+          gs = 0.f;
+#pragma unroll
+          for (int q = 0; q < kMaxTopK; ++q)
+            if (q < a.gsk) gs += top[q];
         }
-#pragma unroll
-        for (int q = 0; q < kMaxTopK; ++q)
-          if (q < a.gsk) gs += top[q];
       }
-      uint64_t gkey = lane < G ? sel_key(gs, lane) : 0ull;
-      gmask = 0ull;
+      // rounds of: the best remaining score, the lowest lane holding it
+      float cand = rep ? gs + 0.0f : -INFINITY;   // (-0 as +0)
+      gsel = 0ull;
       for (int q = 0; q < a.topk_groups; ++q) {
-        // (up to 16 groups all sit in lanes 0-15: one row's reduction)
-        const uint64_t best = G <= 16 ? lane64(run_max_u64(gkey, 16), 0) : wave_max_u64(gkey);
-        int g = key_index(best);
-        g = g < G ? g : G - 1;
-        gmask |= 1ull << g;
-        if (lane == g) gkey = 0ull;
+        const float M = wave_max_f(cand);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(rep && cand == M);
+        const int L0 = hit ? __builtin_ctzll(hit) : 0;
+        const int g = __builtin_amdgcn_readlane(rg, L0);
+        gsel |= 1ull << (g < G ? g : G - 1);
+        if (lane == L0) cand = -INFINITY;
       }
     }
-    // top-k by repeated wave max over keys (logit, ~index), built once; the
-    // winner's key (unique: it holds the index) is cleared after each round
-    uint64_t key[4];
+    // top-k over the allowed experts: rounds of the largest remaining logit
+    // and the lowest expert index holding it (lowest lane, then lowest of its
+    // four), which is then removed
+    float cv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      key[i] = ok[i] && ((gmask >> (e / gsz)) & 1ull) ? sel_key(v[i], e) : 0ull;
-    }
+    for (int i = 0; i < 4; ++i) cv[i] = ok[i] && ((gsel >> grp[i]) & 1ull) ? v[i] + 0.0f : -INFINITY;
     int sel_e[kMaxTopK];
     float sel_v[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k) {
-        const uint64_t best = wave_max_u64(umax64(umax64(key[0], key[1]), umax64(key[2], key[3])));
-        int e = key_index(best);
-        e = e < N ? e : N - 1;                    // unreachable guard (k <= candidates)
-        sel_e[j] = e;
-        sel_v[j] = key_value(best);              // (the logit, with -0 read as +0)
+        const float lm = fmaxf(fmaxf(cv[0], cv[1]), fmaxf(cv[2], cv[3]));
+        const float M = wave_max_f(lm);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(lm == M);
+        const int L0 = hit ? __builtin_ctzll(hit) : 0;
+        const int fi = cv[0] == M ? 0 : (cv[1] == M ? 1 : (cv[2] == M ? 2 : 3));
+        const int i0 = __builtin_amdgcn_readlane(fi, L0);
+        const int e = 4 * L0 + i0;
+        sel_e[j] = e < N ? e : N - 1;              // (unreachable guard: k <= candidates)
+        sel_v[j] = M;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (key[i] == best) key[i] = 0ull;
+          if (lane == L0 && i == i0) cv[i] = -INFINITY;
       }
     }
     // softmax over the k selected logits, summed in slot order
@@ -868,7 +872,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   // per-block partial statistics, combined over waves in wave order
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
+    const int e = 4 * lane + i;
     if (e < N) ps[wave][e] = psr[i];
   }
   __syncthreads();
