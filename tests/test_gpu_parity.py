@@ -87,6 +87,54 @@ def test_exact_ties_go_to_lower_index():
             assert 2 in sel and sel.index(2) < sel.index(6)
 
 
+TIE_CASES = {
+    # 64 experts, groups of 8 (two lanes each), k = 8
+    "groups_of_8": (lambda: si.small("deepseek_v3", T=300),
+                    dict(same_lane=(8, 9), cross_lane=(10, 15), group=(1, 5))),
+    # 256 experts, groups of 32 (eight lanes each), k = 8
+    "groups_of_32": (lambda: si.small("deepseek_v3", T=200, N=256),
+                     dict(same_lane=(32, 33), cross_lane=(37, 60), group=(2, 6))),
+    # 128 experts, no groups, k = 2
+    "no_groups": (lambda: si.small("switch", T=500, N=128, k=2, capacity=0),
+                  dict(same_lane=(4, 5), cross_lane=(3, 70), group=None)),
+}
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_exact_ties_go_to_lower_index_many_experts(name):
+    """More than 32 experts (one wave per token, four experts per lane):
+    duplicated router rows inside one lane's four, across lanes and as whole
+    groups give bit-identical logits or group scores, and the lower expert
+    (group) must win; all-zero tokens tie every logit and take experts
+    0 .. k-1 in order.  The oracle must match without any tie-band adoption."""
+    # (the duplicated pairs lie inside one group: the group limit may keep a
+    # higher group and drop a lower one)
+    make, dup = TIE_CASES[name]
+    wl = make()
+    inp = si.generate(wl)
+    wg = inp["wg"].copy()
+    gsz = wl.N // wl.n_groups if wl.n_groups > 1 else wl.N
+    if dup["group"] is not None:
+        lo, hi = dup["group"]
+        wg[hi * gsz:(hi + 1) * gsz] = wg[lo * gsz:(lo + 1) * gsz]
+    for lo, hi in (dup["same_lane"], dup["cross_lane"]):
+        wg[hi] = wg[lo]
+    inp["wg"] = wg
+    x = inp["x"].copy()
+    zero = [0, 17, wl.T - 1]
+    x[zero] = 0
+    inp["x"] = x
+    print(f"case {name}: T={wl.T} N={wl.N} k={wl.k} groups={wl.n_groups}", flush=True)
+    gpu, _ = _forward_and_phases(wl, inp, max_adopted=0)
+    for t in zero:
+        assert list(gpu["idx"][t]) == list(range(wl.k))
+    for lo, hi in (dup["same_lane"], dup["cross_lane"]):
+        for t in range(wl.T):
+            sel = list(gpu["idx"][t])
+            if hi in sel:
+                assert lo in sel and sel.index(lo) < sel.index(hi)
+
+
 def test_zero_rows_and_k_equals_n():
     wl = si.Workload("kN", T=130, d=128, N=4, k=4, F=128, act="swiglu", dtype="bf16", buf="fp8")
     inp = si.generate(wl)
