@@ -128,6 +128,12 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)lds, 16, voff, soff, 0, 0);
 }
 
+// 4 bytes per lane from a buffer straight into LDS (lane i writes lds + 4 * i).
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                         uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)lds, 4, voff, soff, 0, 0);
+}
+
 // s_waitcnt on the LDS counter only (lgkmcnt = 0), leaving vector loads in flight.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // s_waitcnt on the vector-memory counter only (vmcnt = 0).
@@ -219,25 +225,32 @@ __device__ __forceinline__ int swz(int row) {
 // that instruction a lane of the B operand holds 32 consecutive K (one MX
 // block, with its scale) and the lane half h of column n holds K 32h ..
 // 32h + 31 of the 64; the A lane half h holds K 16h .. 16h + 15 in its first
-// 16 bytes and K 32 + 16h .. 32 + 16h + 15 in the next 16.  A step is 128 K
-// (two MFMA slices).
+// 16 bytes and K 32 + 16h .. 32 + 16h + 15 in the next 16.  Register-staged,
+// a step is 128 K (two MFMA slices); on the LDS-DMA pipeline (K a multiple of
+// 256) a step is 256 K, four MFMA slices as in the bf16 pipeline, the codes
+// and scales landing in LDS straight from memory (the scales by 4-byte loads,
+// one wave-load per 32 B rows).
 template <int BM, int BN, int WGM, int WGN, int EPI, bool FP8A, bool REG, bool TAIL, bool SPLITK,
           bool MX = false, bool MXS = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   static_assert(!SPLITK || TAIL, "split-K is a tail mode");
-  static_assert(!MX || (REG && BN == 32 * WGM * WGN), "MXFP4 B: register staging, 32 rows per wave");
+  static_assert(!MX || ((REG || MXS) && BN == 32 * WGM * WGN), "MXFP4 B: 32 B rows per wave");
   static_assert(!MXS || (MX && FP8A), "scaled MFMA: fp8 A, MXFP4 B");
+  constexpr bool MXD = MXS && !REG;                // scaled MFMA on the LDS-DMA pipeline
   constexpr int NW = WGM * WGN;                    // waves; WGM x WGN grid of wave tiles
-  constexpr int BK = MXS ? 128 : 64;
+  constexpr int BK = MXS ? (REG ? 128 : 256) : 64;
   constexpr int SA = FP8A ? 1 : 2;                 // bytes per A element
   constexpr int ROWA = BK * SA;                    // bytes per tile row per stage: A,
   constexpr int ROWB = MXS ? BK / 2 : BK * 2;      // B (FP4 codes with MXS, else bf16)
   constexpr int A_BYTES = BM * ROWA, B_BYTES = BN * ROWB;
-  constexpr int SC_BYTES = MXS ? BN * 4 : 0;       // MXS: B's 4 block scales per row and step
+  constexpr int SCR = BK / 32;                     // MXS: B's block scales per row and step
+  constexpr int SC_BYTES = MXS ? BN * SCR : 0;
   constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   constexpr int A_PW = A_BYTES / 1024 / NW;        // 1 KB wave-loads per wave per stage
   constexpr int B_PW = B_BYTES / 1024 / NW;
-  constexpr int LPW = A_PW + B_PW;                 // loads per wave per stage
+  constexpr int B_PWS = B_PW + (MXD ? 1 : 0);      // B pieces with MXD's scale load
+  constexpr int LPW = A_PW + B_PWS;                // loads per wave per stage
+  constexpr int KB_STEP = MXS ? BK / 2 : BK * 2;   // B bytes per row and step
   // LDS-DMA loads of one step in two bursts: B (weights) right after the step
   // barrier, A in the first K slice of the next step (see fstep).  Only for
   // the gate/up GEMMs, whose A (the dispatch buffer) every n-tile re-reads, so
@@ -253,6 +266,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "load split");
   static_assert(!GATED || (WN / 2) % (1024 / ROWB) == 0, "a wave-load must not straddle W1 and W3");
   static_assert(2 * STAGE <= 144 * 1024, "LDS budget");
+  static_assert(!MXD || BN * SCR == NW * 256, "MXD: one 4-byte wave-load of scales per wave");
 
   // two LDS stages, each its own array: step kt computes from one while step
   // kt + 1 is written to the other
@@ -308,7 +322,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       // few tiles (a decode step, a small dense call): all of them split
       cut = 0;
       ksplit = S_ / total < g.split_k_max ? S_ / total : g.split_k_max;
-    } else if (!REG) {
+    } else if (!REG && !MX) {
+      // (MXFP4 kernels make no cut: their split-K tail launch is register-staged)
       const int r = total % S_;
       if (r > 0 && 4 * r <= S_) {
         cut = total - r;
@@ -460,7 +475,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const uint8_t* m1 = GATED ? reinterpret_cast<const uint8_t*>(g.b1) + e * g.b_stride : m0;
       rsB0 = make_rsrc(m0, static_cast<uint64_t>(g.b_stride));
       rsB1 = GATED ? make_rsrc(m1, static_cast<uint64_t>(g.b_stride)) : rsB0;
-      if constexpr (MXS) {
+      if constexpr (MXD) {
+        // codes: as a bf16 B's wave-loads, 8 rows of 128 bytes per 1 KB; scales:
+        // row wave * 32 + lane / 2, the step's 8 bytes as two words
+#pragma unroll
+        for (int j = 0; j < B_PW; ++j) {
+          const int n = (wave * B_PW + j) * (1024 / ROWB) + lane / B_CPR;
+          const int c = (lane % B_CPR) ^ swz<ROWB>(n);
+          b_off[j] = static_cast<uint32_t>(b_row(n)) * static_cast<uint32_t>(K / 2) + static_cast<uint32_t>(c * 16);
+        }
+        mx_scale = static_cast<uint32_t>(g.mx_scale_off) +
+                   static_cast<uint32_t>(b_row(wave * 32 + (lane >> 1))) * static_cast<uint32_t>(K / 32) + (lane & 1) * 4;
+      } else if constexpr (MXS) {
         // codes: rows wave * 32 + 16 j + lane / 4, 16-byte chunk lane % 4 of the
         // step's 64 bytes (piece j adds 16 weight rows, as the soffset); scales:
         // lane % 32's row, the step's 4 bytes as one word
@@ -540,7 +566,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         const int n = wave * 32 + j * 16 + (lane >> 2);
         *reinterpret_cast<u32x4*>(stg + A_BYTES + n * ROWB + (((lane & 3) ^ swz<ROWB>(n)) << 4)) = rb[q][j];
       }
-      if (lane < 32) *reinterpret_cast<uint32_t*>(stg + A_BYTES + B_BYTES + (wave * 32 + lane) * 4) = rsc[q];
+      if (lane < 32) *reinterpret_cast<uint32_t*>(stg + A_BYTES + B_BYTES + (wave * 32 + lane) * SCR) = rsc[q];
     } else if constexpr (MX) {
       // 32 codes -> 32 bf16 (4 chunks of 16 bytes) at row n, chunks 4 * (lane % 2) ..,
       // swizzled like every bf16 B row; scale 2^(e - 127) (e = 0: 2^-127)
@@ -582,7 +608,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const u32x4 b = *reinterpret_cast<const u32x4*>(sB + n * ROWB + (((kk * 2 + fk) ^ swz<ROWB>(n)) << 4));
       // (FP4 B reads the first four registers of the operand)
       bfr[j] = __builtin_bit_cast(i32x8, __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1));
-      sc[j] = sB[B_BYTES + n * 4 + kk * 2 + fk];
+      sc[j] = sB[B_BYTES + n * SCR + kk * 2 + fk];
     }
 #pragma unroll
     for (int i = 0; i < TMI; ++i)
@@ -655,8 +681,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // loads of step kt + 2 (into the stage just freed) issued one after each
   // MFMA: a wave that issues them all at once stalls on the full load
   // queue with its MFMAs unissued.
+  // MXD: the step's scale bytes of the wave's 32 B rows (W1 or W3 as the rows)
+  auto dma_scales = [&](__amdgpu_buffer_rsrc_t r0, __amdgpu_buffer_rsrc_t r1, uint8_t* stg, uint32_t ks) {
+    const bool w3 = GATED && ((wave * 32) % WN) >= WN / 2;
+    lds_dma4(w3 ? r1 : r0, stg + A_BYTES + B_BYTES + wave * 256, mx_scale, ks);
+  };
   auto dma = [&](int kt, uint8_t* stg, bool with_a) {
-    const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * BK * 2);
+    const uint32_t ka = static_cast<uint32_t>(kt * BK * SA), kb = static_cast<uint32_t>(kt * KB_STEP);
     if (with_a) {
 #pragma unroll
       for (int j = 0; j < A_PW; ++j) lds_dma16(rs_a(j), stg + (wave * A_PW + j) * 1024, a_off[j], ka);
@@ -667,12 +698,32 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
       lds_dma16(w3 ? rsB1 : rsB0, stg + A_BYTES + gi * 1024, b_off[j], kb);
     }
+    if constexpr (MXD) dma_scales(rsB0, rsB1, stg, static_cast<uint32_t>(kt * SCR));
   };
   bf16x8 fa[2][TMI], fb[2][TNI];
+  i32x8 xa[2][TMI];                              // MXD fragments: A as the instruction's two halves,
+  u32x4 xb[2][TNI];                              // B as the lane's MX block,
+  int xs[2][TNI];                                // and its scale
   auto ldfr = [&](const uint8_t* sA, int kk, auto P, auto NI) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value, ni = decltype(NI)::value;
     if constexpr (ni == 0) return;
     const uint8_t* sB = sA + A_BYTES;
+    if constexpr (MXD) {
+#pragma unroll
+      for (int i = 0; i < ni; ++i) {
+        const int r = wm * WM + i * 32 + fr;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + r * ROWA + (((kk * 4 + fk) ^ swz<ROWA>(r)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + r * ROWA + (((kk * 4 + 2 + fk) ^ swz<ROWA>(r)) << 4));
+        xa[p][i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int j = 0; j < TNI; ++j) {
+        const int n = wn * WN + j * 32 + fr;
+        xb[p][j] = *reinterpret_cast<const u32x4*>(sB + n * ROWB + (((kk * 2 + fk) ^ swz<ROWB>(n)) << 4));
+        xs[p][j] = sB[B_BYTES + n * SCR + kk * 2 + fk];
+      }
+      return;
+    }
     const int cc = kk * 2 + fk;
 #pragma unroll
     for (int i = 0; i < ni; ++i) {
@@ -692,13 +743,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       fb[p][j] = *reinterpret_cast<const bf16x8*>(sB + n * ROWB + ((cc ^ swz<ROWB>(n)) << 4));
     }
   };
+  // one MFMA of fragment buffer p: row block i, column block j
+  auto mfma1 = [&](auto P, int i, int j) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    if constexpr (MXD) {
+      // (FP4 B reads the first four registers of the operand)
+      const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(xb[p][j], xb[p][j], 0, 1, 2, 3, -1, -1, -1, -1));
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[p][i], b, acc[i][j], 0 /* A e4m3 */,
+                                                                   4 /* B e2m1 */, 0, 127, 0, xs[p][j]);
+    } else {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+    }
+  };
   auto mm = [&](auto P, auto NI) __attribute__((always_inline)) {
-    constexpr int p = decltype(P)::value, ni = decltype(NI)::value;
+    constexpr int ni = decltype(NI)::value;
 #pragma unroll
     for (int i = 0; i < ni; ++i)
 #pragma unroll
-      for (int j = 0; j < TNI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TNI; ++j) mfma1(P, i, j);
   };
   // MFMAs of fragment buffer P (the NI live row blocks) with the loads of
   // step kt2 into stg spread between them: A and B pieces, only A (WHAT = 1)
@@ -712,20 +774,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     constexpr int NMM = decltype(NI)::value * TNI;
     constexpr int what = decltype(WHAT)::value;
     constexpr int U0 = what == 2 ? A_PW : 0;                  // first piece (A pieces first)
-    constexpr int NL = what == 1 ? A_PW : (what == 2 ? B_PW : LPW);
+    constexpr int NL = what == 1 ? A_PW : (what == 2 ? B_PWS : LPW);
     const bool live = kt2 < kend;
 
     const __amdgpu_buffer_rsrc_t rb0 = live ? rsB0 : rs_null;
     const __amdgpu_buffer_rsrc_t rb1 = live ? rsB1 : rs_null;
     const uint32_t ka = live ? static_cast<uint32_t>(kt2 * BK * SA) : 0u;
-    const uint32_t kb = live ? static_cast<uint32_t>(kt2 * BK * 2) : 0u;
+    const uint32_t kb = live ? static_cast<uint32_t>(kt2 * KB_STEP) : 0u;
     auto issue = [&](int u) {
       if (u < A_PW) {
         lds_dma16(rs_a(u, live), stg + (wave * A_PW + u) * 1024, a_off[u], ka);
-      } else {
+      } else if (u < A_PW + B_PW) {
         const int j = u - A_PW, gi = wave * B_PW + j;
         const bool w3 = GATED && ((gi * (1024 / ROWB)) % WN) >= WN / 2;
         lds_dma16(w3 ? rb1 : rb0, stg + A_BYTES + gi * 1024, b_off[j], kb);
+      } else if constexpr (MXD) {
+        dma_scales(rb0, rb1, stg, live ? static_cast<uint32_t>(kt2 * SCR) : 0u);
       }
     };
     if constexpr (NMM == 0) {
@@ -734,8 +798,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     } else {
 #pragma unroll
       for (int q = 0; q < NMM; ++q) {
-        acc[q / TNI][q % TNI] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            fa[p][q / TNI], fb[p][q % TNI], acc[q / TNI][q % TNI], 0, 0, 0);
+        mfma1(P, q / TNI, q % TNI);
 #pragma unroll
         for (int u = q * NL / NMM; u < (q + 1) * NL / NMM; ++u) issue(U0 + u);
       }
@@ -745,7 +808,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  static_assert(REG || BK / 16 == 4, "four K slices per step");
+  static_assert(REG || (MXD ? BK / 64 : BK / 16) == 4, "four K slices per step");
   // invariant at step entry: fragments of (cur, slice 0) issued into buffer 0.
   // NI = the wave's live 32-row blocks: fragment reads and MFMAs of blocks
   // wholly past the segment end are left out, so that a segment's partial
@@ -1132,13 +1195,22 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, 
   const int64_t segs = dense ? 1 : (rows < n_seg ? rows : n_seg);
   const int64_t mt_most = dense ? ceil_div(rows, 128) : std::min<int64_t>(rows, (rows + 127 * segs) / 128);
   const bool all_split = split != nullptr && 2 * mt_most * nt <= g.split_slots;
-  // fp8 A with MXFP4 B: the scaled MFMA on the codes as stored (128-K steps)
+  // fp8 A with MXFP4 B: the scaled MFMA on the codes as stored; whole tiles on
+  // the LDS-DMA pipeline (256-K steps), else register-staged (128-K steps)
   constexpr bool MXS_OK = MX && FP8A;
   const bool mxs = MXS_OK && g.K % 128 == 0;
   hipError_t err = hipSuccess;
   if (!all_split) {
-    err = mxs ? launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX, MXS_OK>(g, mtu * nt, st)
-              : launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX>(g, mtu * nt, st);
+    if constexpr (MXS_OK) {
+      if (g.K % 256 == 0)
+        err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, false, false, false, MX, true>(g, mtu * nt, st);
+      else if (mxs)
+        err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX, true>(g, mtu * nt, st);
+      else
+        err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX>(g, mtu * nt, st);
+    } else {
+      err = launch_gg_on<128, 256, 2, 4, EPI, FP8A, true, false, false, MX>(g, mtu * nt, st);
+    }
     if (err != hipSuccess || split == nullptr) return err;
   }
   g.part_meta = static_cast<int32_t*>(split);
