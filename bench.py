@@ -93,8 +93,9 @@ def layer_step(wl, L, x, h, hs):
     """One layer forward phase by phase, the kernels of moe_forward (fused or
     not, as the layer was made), with HIP events recorded between the phases
     when given: ev[0] before, ev[1] after route + dispatch (or route + plan),
-    ev[2] after the up GEMM, ev[3] after the down GEMM, ev[4] after the shared
-    expert, ev[5] after the combine."""
+    ev[2] after the up GEMM, ev[3] after the shared expert's up GEMM (none
+    without a shared expert), ev[4] after the down GEMM (with a shared expert,
+    its down GEMM in the same launch), ev[5] after the combine."""
     from mixture_experts_layer_sparse_amd import moe as M
     s = L.s
 
@@ -109,10 +110,13 @@ def layer_step(wl, L, x, h, hs):
             ev and ev[1].record()
             M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
         ev and ev[2].record()
-        M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
+        if wl.shared:
+            M.shared_expert_up(s, x, L.ws1, L.ws3, hs, ws=L.ws)
         ev and ev[3].record()
         if wl.shared:
-            M.shared_expert(s, x, L.ws1, L.ws3, L.ws2, hs, L.out_shared, ws=L.ws)
+            M.expert_down_shared(s, h, L.offsets, L.w2, hs, L.ws2, L.out, L.out_shared, ws=L.ws)
+        else:
+            M.expert_down(s, h, L.offsets, L.w2, L.out, ws=L.ws)
         ev and ev[4].record()
         L.combine(x)
         ev and ev[5].record()
@@ -380,7 +384,7 @@ def _to_dev(arr):
 
 def _phases(wl, g, x, steps, warmup, fused=True):
     """Runs the kernels of moe_forward phase by phase; returns (layer, mean
-    phase times in us [route+dispatch, up, down, shared, combine], wall time
+    phase times in us [route+dispatch, up, shared up, down (+ shared down), combine], wall time
     per step in s)."""
     import numpy as np
     import torch
@@ -436,7 +440,7 @@ def sweep(steps, warmup):
     import synthetic_inputs as si
     reports = []
 
-    print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | GEMM down us | shared us | "
+    print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | shared up us | GEMM down (+ shared) us | "
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|")
     for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx", "switch_mxfp4", "deepseek_v3_mxfp4"):
@@ -491,7 +495,7 @@ def decode(steps, warmup):
     m = 3 if base.swiglu else 2
     per_expert = m * base.F * base.d * 2
     print("| B | experts touched (uniform estimate) | us/step | us/step, graph replay | tokens/s (graph) | "
-          "route+dispatch us | GEMM up us | GEMM down us | shared us | combine us | weight bytes streamed | "
+          "route+dispatch us | GEMM up us | shared up us | GEMM down (+ shared) us | combine us | weight bytes streamed | "
           "weight GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for B in (1, 32, 128):
@@ -649,7 +653,8 @@ def main():
         step(E[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ph = {"route_dispatch": [], "gemm_up": [], "gemm_down": [], "shared": [], "combine": []}
+    # (layer_step's phase order; with a shared expert its down GEMM runs in the routed down launch)
+    ph = {"route_dispatch": [], "gemm_up": [], "shared_up": [], "gemm_down": [], "combine": []}
     for e in E:
         for j, key in enumerate(ph):
             ph[key].append(e[j].elapsed_time(e[j + 1]))
@@ -670,7 +675,7 @@ def main():
     rb, db, cb = alg_bytes(wl, R, fused)
     t_up = ph_ms["gemm_up"] * 1e-3
     achieved = up / t_up / 1e12
-    gemm_t = (ph_ms["gemm_up"] + ph_ms["gemm_down"] + ph_ms["shared"]) * 1e-3
+    gemm_t = (ph_ms["gemm_up"] + ph_ms["shared_up"] + ph_ms["gemm_down"]) * 1e-3
     mem_t = (ph_ms["route_dispatch"] + ph_ms["combine"]) * 1e-3
     out = {
         "metric": METRIC,

@@ -224,9 +224,30 @@ moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1,
                              const void* ws3, const void* ws2, void* h_shared,
                              void* out_shared, void* ws, size_t ws_bytes, void* stream);
 
-/* All experts: moe_expert_up + moe_expert_down, plus moe_shared_expert when
- * has_shared (x, ws1, ws3, ws2, out_shared required then, else ignored).  The
- * intermediates live in the workspace.  out [T*k][d], out_shared [T][d]. */
+/* The shared expert's first GEMM alone (the same passages as moe_shared_expert):
+ * h_shared = act(Ws1 x, Ws3 x).  x [T][d]; ws1, ws3 [F][d] (ws3 NULL unless
+ * SwiGLU); h_shared [T][F] out.  All dtype.  ws as for moe_shared_expert. */
+moe_status moe_shared_expert_up(const moe_shape* s, const void* x, const void* ws1,
+                                const void* ws3, void* h_shared, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* moe_expert_down and the shared expert's down GEMM (out_shared = Ws2 h_shared)
+ * in one launch of the grouped GEMM, the shared expert as one more segment after
+ * the routed ones (two launches for float32 layers).  Requires has_shared.
+ *   h, offsets, w2, out as for moe_expert_down; h_shared [T][F], ws2 [d][F] (the
+ *   layout of one of w2's matrices), out_shared [T][d] out; ws as for
+ *   moe_expert_up.  Each output element is the one moe_expert_down or
+ *   moe_shared_expert computes, up to float32 rounding order where the two
+ *   forms split K differently (few tokens). */
+moe_status moe_expert_down_shared(const moe_shape* s, const void* h, const int32_t* offsets,
+                                  const void* w2, void* out, const void* h_shared,
+                                  const void* ws2, void* out_shared, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* All experts: moe_expert_up + moe_expert_down, or with has_shared
+ * moe_expert_up + moe_shared_expert_up + moe_expert_down_shared (x, ws1, ws3,
+ * ws2, out_shared required then, else ignored).  The intermediates live in the
+ * workspace.  out [T*k][d], out_shared [T][d]. */
 moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_scale,
                        const int32_t* offsets, const void* w1, const void* w3, const void* w2,
                        const void* x, const void* ws1, const void* ws3, const void* ws2,
@@ -308,8 +329,9 @@ moe_status moe_expert_up_gather(const moe_shape* s, const void* a, const float* 
  * one stream; results equal those of the four single-phase calls.  Every
  * output buffer is required except p, f, l_aux (may be NULL) and the
  * shared-expert buffers (ignored unless has_shared).  With x_perm == NULL the
- * layer runs fused: moe_route_plan, moe_expert_up_gather, moe_expert_down,
- * the shared expert and moe_combine, with no dispatch buffer (row_scale may
+ * layer runs fused: moe_route_plan, moe_expert_up_gather, moe_expert_down
+ * (with has_shared: moe_shared_expert_up and moe_expert_down_shared) and
+ * moe_combine, with no dispatch buffer (row_scale may
  * then be NULL too; the fp8 codes and scales live in the workspace); every
  * other output is bit for bit that of the unfused call. */
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,

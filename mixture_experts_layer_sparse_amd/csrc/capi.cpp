@@ -236,6 +236,42 @@ moe_status moe_shared_expert(const moe_shape* s, const void* x, const void* ws1,
   return hip_status(e);
 }
 
+moe_status moe_shared_expert_up(const moe_shape* s, const void* x, const void* ws1, const void* ws3,
+                                void* h_shared, void* ws, size_t ws_bytes, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !ws1 || !h_shared) return MOE_ERR_ARG;
+  if (s->act == MOE_ACT_SWIGLU && !ws3) return MOE_ERR_ARG;
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
+  moe_shape sd = *s;
+  sd.buf_dtype = sd.dtype;                     // the unquantised input
+  return hip_status(moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared, split,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_down_shared(const moe_shape* s, const void* h, const int32_t* offsets,
+                                  const void* w2, void* out, const void* h_shared, const void* ws2,
+                                  void* out_shared, void* ws, size_t ws_bytes, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!s->has_shared) return MOE_ERR_ARG;
+  if (!h || !offsets || !w2 || !out || !h_shared || !ws2 || !out_shared) return MOE_ERR_ARG;
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s->dtype != MOE_BF16) {
+    // float32 layers: two launches
+    hipError_t e = moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out, split, st);
+    if (e == hipSuccess) e = moe::launch_expert_down(*s, h_shared, nullptr, s->T, 1, ws2, out_shared, split, st);
+    return hip_status(e);
+  }
+  return hip_status(moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out, split, st, h_shared,
+                                            ws2, out_shared, s->T));
+}
+
 moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_scale,
                        const int32_t* offsets, const void* w1, const void* w3, const void* w2,
                        const void* x, const void* ws1, const void* ws3, const void* ws2,
@@ -250,9 +286,12 @@ moe_status moe_experts(const moe_shape* s, const void* x_perm, const float* row_
   moe_status r = moe_expert_up(s, x_perm, row_scale, offsets, w1, w3, base + L.h, ws, ws_bytes,
                                stream);
   if (r != MOE_OK) return r;
-  r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
-  if (r != MOE_OK || !s->has_shared) return r;
-  return moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, ws, ws_bytes, stream);
+  if (!s->has_shared) return moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
+  // the shared expert's up GEMM, then its down GEMM in the routed down launch
+  r = moe_shared_expert_up(s, x, ws1, ws3, base + L.h_shared, ws, ws_bytes, stream);
+  if (r != MOE_OK) return r;
+  return moe_expert_down_shared(s, base + L.h, offsets, w2, out, base + L.h_shared, ws2, out_shared, ws,
+                                ws_bytes, stream);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* out, const void* out_shared, const void* x,
@@ -481,12 +520,15 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
   r = moe_expert_up_gather(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, ws, ws_bytes,
                            stream);
   if (r != MOE_OK) return r;
-  r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
-  if (r != MOE_OK) return r;
   if (s->has_shared) {
-    r = moe_shared_expert(s, x, ws1, ws3, ws2, base + L.h_shared, out_shared, ws, ws_bytes, stream);
+    r = moe_shared_expert_up(s, x, ws1, ws3, base + L.h_shared, ws, ws_bytes, stream);
     if (r != MOE_OK) return r;
+    r = moe_expert_down_shared(s, base + L.h, offsets, w2, out, base + L.h_shared, ws2, out_shared, ws,
+                               ws_bytes, stream);
+  } else {
+    r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
   }
+  if (r != MOE_OK) return r;
   return moe_combine(s, out, out_shared, x, pos, w, y, stream);
 }
 

@@ -85,6 +85,14 @@ struct GemmArgs {
   float* part;             // split-K tail: [units][256][256] float32 partial tiles
   int32_t* part_meta;      // split-K tail: [0] = tail tiles, then (row0, row_end, ntile) per tile
   int split_k_max;         // > 0: the tail is split along K (up to this many ranges per tile)
+  // An extra dense segment after the routed ones (the shared expert's down GEMM
+  // in the launch of the routed one): A [x_rows][K] at xa, B one matrix at xb0
+  // (laid out as one of b0's), output [x_rows][n_out] at xout.  No gather, no
+  // row scale, no gated epilogue.
+  const void* xa;
+  const uint16_t* xb0;
+  uint16_t* xout;
+  int64_t x_rows;          // 0: none
 };
 
 // silu(u) = u / (1 + e^-u) with the hardware reciprocal (about 1 ulp): the result is rounded to
@@ -309,9 +317,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     }
     if (tid == 0) mt_start[0] = 0;
     if (tid < n_seg) mt_start[tid + 1] = scan_tmp[cur][tid];
+    // the extra segment's m-tiles after the routed ones
+    if (tid == n_seg - 1) mt_start[n_seg + 1] = scan_tmp[cur][tid] + static_cast<int>((g.x_rows + MBM - 1) / MBM);
     __syncthreads();
   }
-  const int MT = __builtin_amdgcn_readfirstlane(mt_start[n_seg]);
+  const int n_all = n_seg + (g.x_rows > 0 ? 1 : 0);  // segments, the extra one included
+  const int MT = __builtin_amdgcn_readfirstlane(mt_start[n_all]);
   const int NT = g.nt;
   const int total = MT * NT;
   int cut = total;                               // main tiles [0, cut), tail tiles [cut, total)
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
 
   // segment of tile-list entry Lm: mt_start[e] * NT <= Lm < mt_start[e + 1] * NT
   auto seg_of_tile = [&](int Lm) {
-    int lo = 0, hi = n_seg;
+    int lo = 0, hi = n_all;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (mt_start[mid] * NT <= Lm) lo = mid; else hi = mid;
@@ -370,6 +381,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   // each weight n-tile back to back (one HBM read, the rest from L2); each XCD
   // takes S consecutive tile ids per round.
   int round = -1, row0 = 0, row_end = 0, ntile = 0, e = 0;
+  bool xseg = false;                             // the current tile is the extra segment's
   int kbeg = 0, kend = KT, unit = 0;             // K steps of the current tile (a range for split-K)
   auto next_tile = [&]() -> bool {
     for (;;) {
@@ -388,8 +400,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const int local = Lm - __builtin_amdgcn_readfirstlane(mt_start[e]) * NT;
       const int nt_list = local / mte;
       const int mloc = local - nt_list * mte;
-      row0 = __builtin_amdgcn_readfirstlane(seg_off[e]) + mloc * MBM + (QUARTERS ? ((L >> 1) & 1) * BM : 0);
-      row_end = __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
+      xseg = e == n_seg;
+      // (the extra segment's rows count from 0 in its own buffers)
+      row0 = (xseg ? 0 : __builtin_amdgcn_readfirstlane(seg_off[e])) + mloc * MBM +
+             (QUARTERS ? ((L >> 1) & 1) * BM : 0);
+      row_end = xseg ? static_cast<int>(g.x_rows) : __builtin_amdgcn_readfirstlane(seg_off[e + 1]);
       ntile = QUARTERS ? 2 * nt_list + (L & 1) : nt_list;
       // a tail quarter wholly past the segment end or the last column has no work
       if (QUARTERS && (row0 >= row_end || ntile * (GATED ? BN / 2 : BN) >= g.n_out)) continue;
@@ -402,7 +417,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
           int32_t* m = g.part_meta + 2 + 3 * (Lm - cut);
           m[0] = row0;
           m[1] = row_end;
-          m[2] = ntile;
+          m[2] = ntile | (xseg ? (1 << 30) : 0);
         }
       }
       return true;
@@ -463,15 +478,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
         a_off[j] = static_cast<uint32_t>(t) * static_cast<uint32_t>(K * SA) + static_cast<uint32_t>(c * 16);
       }
     } else {
-      a_tile = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(row0) * K * SA;
-      a_bytes = static_cast<uint64_t>(g.rows - row0) * K * SA;
+      a_tile = static_cast<const uint8_t*>(xseg ? g.xa : g.a) + static_cast<int64_t>(row0) * K * SA;
+      a_bytes = static_cast<uint64_t>((xseg ? g.x_rows : g.rows) - row0) * K * SA;
     }
     a_nrec = a_bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(a_bytes);
     if constexpr (MX) {
       // lane: row n = wave * 32 + lane / 2 of the B tile, the half (32 elements
       // of the step's 64) lane % 2; the tile's rows interleave W1 and W3 in
       // runs of WN / 2 >= 32 (gated), so a wave's rows come from one matrix
-      const uint8_t* m0 = reinterpret_cast<const uint8_t*>(g.b0) + e * g.b_stride;
+      const uint8_t* m0 = xseg ? reinterpret_cast<const uint8_t*>(g.xb0)
+                               : reinterpret_cast<const uint8_t*>(g.b0) + e * g.b_stride;
       const uint8_t* m1 = GATED ? reinterpret_cast<const uint8_t*>(g.b1) + e * g.b_stride : m0;
       rsB0 = make_rsrc(m0, static_cast<uint64_t>(g.b_stride));
       rsB1 = GATED ? make_rsrc(m1, static_cast<uint64_t>(g.b_stride)) : rsB0;
@@ -501,7 +517,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       }
     } else {
     const uint64_t b_bytes = static_cast<uint64_t>(g.n_out) * K * 2;
-    rsB0 = make_rsrc(g.b0 + e * g.b_stride, b_bytes);
+    rsB0 = make_rsrc(xseg ? g.xb0 : g.b0 + e * g.b_stride, b_bytes);
     rsB1 = GATED ? make_rsrc(g.b1 + e * g.b_stride, b_bytes) : rsB0;
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
@@ -893,6 +909,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     // Next tile first: its first two steps load while this tile's epilogue
     // runs (the stages are free, the epilogue does not use LDS).
     const int erow0 = row0, erow_end = row_end, entile = ntile, eunit = unit;
+    uint16_t* const eout = xseg ? g.xout : g.out;
     const bool more = next_tile();
     if (more) {
       bind_tile();
@@ -945,7 +962,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
       const int row = erow0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
       const int col = col_lane - (odd ? 1 : 0);
       if (row < erow_end && col < g.n_out)
-        *reinterpret_cast<uint32_t*>(g.out + static_cast<int64_t>(row) * g.n_out + col) = word;
+        *reinterpret_cast<uint32_t*>(eout + static_cast<int64_t>(row) * g.n_out + col) = word;
     };
 #pragma unroll
     for (int i = 0; i < TMI; ++i) {
@@ -994,7 +1011,8 @@ __global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
   const int t = blockIdx.x, ntail = g.part_meta[0], ksplit = g.part_meta[1];
   if (t >= ntail) return;
   const int32_t* m = g.part_meta + 2 + 3 * t;
-  const int row0 = m[0], row_end = m[1], ntile = m[2];
+  const int row0 = m[0], row_end = m[1], ntile = m[2] & ((1 << 30) - 1);
+  uint16_t* const outp = (m[2] >> 30) & 1 ? g.xout : g.out;   // the extra segment's tile
   // A thread owns 4 adjacent output columns (16-byte partial loads, one 8-byte
   // store): 64 threads cover a tile row (gated: 32, each reading 4 up and the
   // 4 gate columns 32 further on), and the 4 waves take every 4th of the
@@ -1041,7 +1059,7 @@ __global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
       }
       o[i] = to_bf16(v);
     }
-    uint16_t* dst = g.out + static_cast<int64_t>(row) * g.n_out + col;
+    uint16_t* dst = outp + static_cast<int64_t>(row) * g.n_out + col;
     if (vec) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
                                                   o[2] | (static_cast<uint32_t>(o[3]) << 16));
@@ -1246,6 +1264,7 @@ size_t gemm_split_bytes(const moe_shape& s) {
   if (s.has_shared) {
     add(s.T, 1, kBm256RowsUp, nt_up);
     add(s.T, 1, kBm256RowsDown, nt_down);
+    add(rows + s.T, s.N + 1, kBm256RowsDown, nt_down);   // the routed and shared down in one launch
   }
   if (tiles == 0) return 0;
   const int64_t units = std::min<int64_t>(split_slots(), kSplitKMax * tiles);
@@ -1342,7 +1361,7 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
 
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
-                              hipStream_t st) {
+                              hipStream_t st, const void* xa, const void* xw2, void* xout, int64_t x_rows) {
   if (s.dtype == MOE_F32) {
     int64_t n = rows * s.d;
     dim3 grid(static_cast<unsigned>(ceil_div(n, 256)));
@@ -1367,11 +1386,19 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.mx_scale_off = static_cast<int64_t>(s.d) * s.F / 2;
   g.out = static_cast<uint16_t*>(out);
   g.nt = static_cast<int>(ceil_div(s.d, 256));
-  const bool sk = split != nullptr && skinny(rows, dense ? 1 : n_seg, g.nt);
-  const int bm = pick_bm(rows, dense ? 1 : n_seg, kBm256RowsDown, g.nt, sk, mx);
+  // the extra dense segment (offsets given; its rows and m-tiles count in the estimates)
+  const bool extra = x_rows > 0 && !dense;
+  g.xa = extra ? xa : nullptr;
+  g.xb0 = extra ? static_cast<const uint16_t*>(xw2) : nullptr;
+  g.xout = extra ? static_cast<uint16_t*>(xout) : nullptr;
+  g.x_rows = extra ? x_rows : 0;
+  const int64_t rows_all = rows + g.x_rows;
+  const int segs_all = dense ? 1 : n_seg + (extra ? 1 : 0);
+  const bool sk = split != nullptr && skinny(rows_all, segs_all, g.nt);
+  const int bm = pick_bm(rows_all, segs_all, kBm256RowsDown, g.nt, sk, mx);
   if (bm != 256 && !sk) split = nullptr;        // (128-row tiles use the scratch only when few)
-  return mx ? dispatch_up<EPI_STORE, false, true>(bm, g, rows, n_seg, dense, split, st)
-            : dispatch_up<EPI_STORE, false>(bm, g, rows, n_seg, dense, split, st);
+  return mx ? dispatch_up<EPI_STORE, false, true>(bm, g, rows_all, segs_all, dense, split, st)
+            : dispatch_up<EPI_STORE, false>(bm, g, rows_all, segs_all, dense, split, st);
 }
 
 }  // namespace moe

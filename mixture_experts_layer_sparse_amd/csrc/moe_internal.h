@@ -135,9 +135,13 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
                             const int32_t* offsets, int64_t rows, int n_seg,
                             const void* w1, const void* w3, void* h, void* split, hipStream_t st,
                             const int32_t* gather = nullptr, int64_t a_rows = 0);
+// With x_rows > 0 (and offsets), the same launch also computes an extra dense
+// segment after the routed ones: xout [x_rows][d] = xa [x_rows][F] times the one
+// matrix xw2 (laid out as one of w2's), the shared expert's down GEMM.
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
-                              hipStream_t st);
+                              hipStream_t st, const void* xa = nullptr, const void* xw2 = nullptr,
+                              void* xout = nullptr, int64_t x_rows = 0);
 size_t gemm_split_bytes(const moe_shape& s);
 
 // Wide routers (bf16, at least 64 experts, N d >= 2^19, 512 to 16384 tokens): the logits as

@@ -103,6 +103,8 @@ _SIGS = {
     "moe_expert_up_gather": (c_int32, [POINTER(Shape)] + [_P] * 7 + [_P, c_size_t, _P]),
     "moe_expert_down": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
     "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
+    "moe_shared_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
+    "moe_expert_down_shared": (c_int32, [POINTER(Shape)] + [_P] * 7 + [_P, c_size_t, _P]),
     "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
     "moe_forward": (c_int32, [POINTER(Shape)] + [_P] * 25 + [_P, c_size_t, _P]),
@@ -358,6 +360,37 @@ def shared_expert(s: Shape, x, ws1, ws3, ws2, h_shared=None, out_shared=None, ws
     _call("moe_shared_expert", ctypes.byref(s), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(ws2),
           _ptr(h_shared), _ptr(out_shared), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     return out_shared
+
+
+def shared_expert_up(s: Shape, x, ws1, ws3, h_shared=None, ws=None):
+    """moe_shared_expert_up: h_shared = act(Ws1 x, Ws3 x)."""
+    T, d, F = s.T, s.d, s.F
+    _check(x, "x", (T, d), s.torch_dtype)
+    _check_w(ws1, "ws1", s, None, F, d)
+    _check_w(ws3, "ws3", s, None, F, d, required=s.act == MOE_ACT_SWIGLU)
+    if h_shared is None:
+        h_shared = torch.empty((T, F), dtype=s.torch_dtype, device=x.device)
+    _call("moe_shared_expert_up", ctypes.byref(s), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(h_shared),
+          _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    return h_shared
+
+
+def expert_down_shared(s: Shape, h, offsets, w2, h_shared, ws2, out=None, out_shared=None, ws=None):
+    """moe_expert_down_shared: the routed down GEMM and the shared expert's in
+    one launch.  Returns (out, out_shared)."""
+    T, d, F = s.T, s.d, s.F
+    _check(h, "h", (T * s.k, F), s.torch_dtype)
+    _check_w(w2, "w2", s, s.N, d, F)
+    _check_w(ws2, "ws2", s, None, d, F)
+    _check(h_shared, "h_shared", (T, F), s.torch_dtype)
+    if out is None:
+        out = torch.empty((T * s.k, d), dtype=s.torch_dtype, device=h.device)
+    if out_shared is None:
+        out_shared = torch.empty((T, d), dtype=s.torch_dtype, device=h.device)
+    _call("moe_expert_down_shared", ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(out),
+          _ptr(h_shared), _ptr(ws2), _ptr(out_shared), _ptr(ws), 0 if ws is None else ws.numel(),
+          _stream())
+    return out, out_shared
 
 
 def experts(s: Shape, x_perm, row_scale, offsets, w1, w3, w2, x=None, ws1=None, ws3=None,

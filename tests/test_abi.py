@@ -116,6 +116,14 @@ def test_null_pointers_and_workspace_rejected_on_host(M):
     s2 = _s(M, act="swiglu")
     st = L.moe_expert_up(ctypes.byref(s2), p, None, p, p, None, p, None, 0, None)
     assert st == M.MOE_ERR_ARG
+    # the shared expert's split entry points: no shared expert, a missing buffer, SwiGLU without Ws3
+    st = L.moe_expert_down_shared(ctypes.byref(s), p, p, p, p, p, p, p, None, 0, None)
+    assert st == M.MOE_ERR_ARG
+    ssh = _s(M, shared=True)
+    st = L.moe_expert_down_shared(ctypes.byref(ssh), p, p, p, p, None, p, p, None, 0, None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_shared_expert_up(ctypes.byref(s2), p, p, None, p, None, 0, None)
+    assert st == M.MOE_ERR_ARG
     # T == 0 is a no-op even with null buffers
     s0 = _s(M, T=0)
     st = L.moe_route(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None,
