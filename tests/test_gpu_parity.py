@@ -551,6 +551,9 @@ MX_CASES = {
     "switch_small": lambda: si.small("switch", wfmt="mxfp4"),
     # SwiGLU with bf16 activations
     "mixtral_small": lambda: si.small("mixtral", wfmt="mxfp4"),
+    # bf16 activations with enough tiles for whole-tile launches: the codes on the
+    # LDS-DMA pipeline, widened as fragments are read (K = 512 and 768)
+    "mixtral_whole_tiles": lambda: si.small("mixtral", T=3000, wfmt="mxfp4"),
     # fp8 activations (gate/up on the scaled fp8 x FP4 MFMA), groups, MXFP4 shared expert
     "deepseek_small": lambda: si.small("deepseek_v3", wfmt="mxfp4", shared=True),
     # fp8 activations with d not a multiple of 128: the gate/up widens the weights to bf16
