@@ -18,6 +18,9 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 size_t elem_size(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
 }  // namespace
 
+// (a one-tile call keeps its T <= kRouteTile token scales in the smallest region)
+static_assert(kRouteTile * 4 <= kAlign, "token scales fit any workspace region");
+
 WsLayout ws_layout(const moe_shape& s) {
   WsLayout L{};
   const size_t T = static_cast<size_t>(s.T), N = static_cast<size_t>(s.N);
@@ -440,10 +443,16 @@ moe_status moe_route_plan(const moe_shape* s, const void* x, const void* w_g, co
   double* prod = reinterpret_cast<double*>(base + L.route_prod);
   const moe::RouteStats rs{counts, kept_counts, p, f, l_aux, offsets, tbase, prod,
                            reinterpret_cast<int32_t*>(prod + s->N)};
-  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, rs, st);
-  // with few tiles x experts the statistics launch also writes the plan (not
-  // for an fp8 buffer, whose quantising pass plans its token itself)
-  bool planned = false;
+  // one router tile: the router writes the plan (and its logits kernel the
+  // fp8 codes; the token scales go to the per-tile partial sums' region, which
+  // a one-tile call does not use); with few tiles x experts the statistics
+  // launch writes it (not for an fp8 buffer, whose quantising pass plans its
+  // token itself)
+  bool planned = moe::route_plans(*s);
+  const moe::RoutePlanOut plan{pos, src, drop, fp8 ? static_cast<uint8_t*>(x_codes) : nullptr,
+                               fp8 ? row_scale : nullptr, fp8 ? psum : nullptr};
+  hipError_t e = moe::launch_route(*s, x, w_g, bias, idx, w, nullptr, psum, hist, lpart, rs, st,
+                                   planned ? &plan : nullptr);
   if (e == hipSuccess && !moe::route_folds_stats(*s)) {
     if (fp8) e = moe::launch_route_finalize(*s, psum, hist, rs, st);
     else e = moe::launch_route_finalize(*s, psum, hist, rs, st, idx, pos, src, drop, &planned);

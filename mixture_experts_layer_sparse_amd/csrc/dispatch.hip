@@ -26,6 +26,7 @@
 // the permutation is the same.
 #include <algorithm>
 
+#include "fp8_quant.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -281,33 +282,6 @@ __global__ __launch_bounds__(256) void disp_copy_kernel(const uint8_t* __restric
   if (PLANNED && part == 0 && lane == 0) plan_write(pa, k, t, pj);
 }
 
-__device__ __forceinline__ uint2 quant8(uint4 v, float inv) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16) * inv;
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * inv;
-  }
-  // two floats -> two e4m3 codes (nearest even) into the low / high half-word
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-  return make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
-}
-
-__device__ __forceinline__ float absmax8(uint4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
-    m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
-  }
-  return m;
-}
-
 // fp8 dispatch: WPT waves per token in one workgroup (the row's max |x| meets
 // in LDS), so that a token's row is read and written by 64 * WPT lanes.  Rows
 // up to 64*WPT*MAXC chunks of 8 bf16 stay in registers; longer rows are read
@@ -363,9 +337,8 @@ __global__ __launch_bounds__(256) void disp_fp8_kernel(const uint16_t* __restric
     for (int w = 0; w < WPT; ++w) amax = fmaxf(amax, wmax[wave - sub + w]);
   }
   // rows below 2^-100 (zero included) count as zero rows: 448/amax would overflow
-  const bool tiny = amax < 0x1p-100f;
-  const float inv = tiny ? 1.f : __fdiv_rn(448.0f, amax);
-  const float scale = tiny ? 1.f : __fdiv_rn(amax, 448.0f);
+  float inv, scale;
+  fp8_row_scale(amax, &inv, &scale);
   if (TOKEN_ORDER) {
     uint2* dst = reinterpret_cast<uint2*>(xp + t * d);
     if (in_regs) {

@@ -68,7 +68,8 @@ WsLayout ws_layout(const moe_shape& s);
 // With few tokens (route_split_ranges(s) > 0) the logits are first computed as
 // partial sums over that many d-ranges into lpart by a separate kernel spread
 // over the experts, so that the router weights are read about once instead of
-// once per 16-token tile; the router then adds the partials in range order.
+// once per 16-token tile; the router then adds the partials in range order
+// (one range: whole dot products, for calls of one router tile).
 int route_split_ranges(const moe_shape& s);
 // The load statistics over all router tiles.  p, f, l_aux may be null;
 // offsets (may be null): exclusive scan of the kept counts, N + 1 entries;
@@ -92,9 +93,28 @@ int route_tile(const moe_shape& s);
 // With one router tile (T <= kRouteTile) the router kernel writes the
 // statistics itself; otherwise launch_route_finalize must follow launch_route.
 bool route_folds_stats(const moe_shape& s);
+// The fused layer's plan, written by the router itself for a call of one
+// router tile with bf16 x (route_plans(s)): pos, src and drop as
+// launch_dispatch_plan_fused writes them, and with an fp8 buffer (x_codes
+// non-null) the codes of x in token order, the kept slots' row scales and the
+// token scales (tscale: T floats of scratch; with one tile the per-tile partial
+// sums' region is free, and every region holds at least 64 floats).  Such a
+// call takes its logits
+// from whole dot products, one workgroup per expert (two kernels in all).
+struct RoutePlanOut {
+  int32_t* pos;
+  int32_t* src;
+  uint8_t* drop;
+  uint8_t* x_codes;
+  float* row_scale;
+  float* tscale;
+};
+bool route_plans(const moe_shape& s);
+// plan (route_plans(s) and rs.offsets required, else hipErrorInvalidValue): see RoutePlanOut.
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        float* lpart, const RouteStats& rs, hipStream_t st);
+                        float* lpart, const RouteStats& rs, hipStream_t st,
+                        const RoutePlanOut* plan = nullptr);
 // With idx, pos, src and drop given, the statistics launch may also write
 // the plan of the fused layer (launch_dispatch_plan_fused's pos, src and
 // drop); *planned (may be null) says whether it did.

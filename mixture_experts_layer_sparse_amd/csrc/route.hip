@@ -16,13 +16,18 @@
 // waves split the experts and the d-loop and their partial sums are added in a
 // fixed order.  With few tokens the logits are first computed as partials
 // spread over more waves, and for wide routers (many experts times a wide d)
-// as one dense split-K GEMM; the router then adds the partials in order.
+// as one dense split-K GEMM; the router then adds the partials in order.  A
+// call of at most 16 tokens (one router tile, e.g. a decode step) gets its
+// logits from one workgroup per expert (whole dot products), and its router
+// workgroup then also writes the fused layer's plan (and that kernel the fp8
+// codes), so such a call is two kernels.
 // Selection: with at most 32 experts a token's lanes hold one expert each (one
 // lane per token under a group limit), with maximum reductions on keys (logit,
 // ~index); with more, one wave handles one token, each lane four consecutive
 // experts, by a float maximum over the wave and a ballot for the lowest expert
 // index holding it.  Either way equal logits go to the lower index, and nothing
 // depends on thread timing.
+#include "fp8_quant.h"
 #include "moe_internal.h"
 
 // k-steps of loads each wave issues before their MFMAs (8 spills three
@@ -38,7 +43,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRouteSplitMax = 64;     // K ranges of partial logits the router adds at most
-constexpr int kLogitsSplitMax = 64;    // d-ranges of the few-token split logits at most
+constexpr int kLogitsSplitMax = 16;    // d-ranges of the few-token split logits at most
 constexpr int kRouteSplitBatch = 16;   // ranges whose loads the router issues together
 static_assert(kSplitKMax <= kRouteSplitMax, "the router adds every K range of the logits GEMM");
 
@@ -63,6 +68,13 @@ struct RouteArgs {
   int fold;             // one tile: this kernel writes the final statistics (rs) itself
   int cap;
   float alpha;
+  // with fold: the fused layer's plan (pos non-null: pos, src, drop; with
+  // row_scale the kept slots' fp8 row scales, taken from tscale [T])
+  int32_t* pos;
+  int32_t* src;
+  uint8_t* drop;
+  float* row_scale;
+  const float* tscale;
 };
 
 // Key ordering "larger logit first, then lower expert index"; 0 = no candidate.
@@ -410,6 +422,112 @@ __global__ __launch_bounds__(256) void logits_split_kernel(const uint16_t* __res
   }
 }
 
+// x . w over 8 bf16 pairs (the products are exact in float32), added to acc in element order
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+  const uint32_t xa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(xa[i] << 16), __uint_as_float(wb[i] << 16), acc);
+    acc = fmaf(__uint_as_float(xa[i] & 0xFFFF0000u), __uint_as_float(wb[i] & 0xFFFF0000u), acc);
+  }
+  return acc;
+}
+
+// Logits of a call with at most 16 tokens: workgroup e computes x[t] . W_g[e]
+// for every token, so that each router row is read once, by one CU.  The four
+// waves split the tokens (TPW per wave) or, with fewer than four tokens, each
+// token's d into P = 2 or 4 parts added in part order; a lane sums its 16-byte
+// chunks in order and the wave adds its lanes by a fixed tree.  The result is
+// the router's logits as one range of partials ([T][N]).  With x_codes the
+// workgroups also quantise x to fp8 in token order (workgroup b: tokens b,
+// b + gridDim.x, ...), codes and scales bit for bit those of the dispatch
+// quantiser, the scales into tscale [T].
+template <int TPW>
+__global__ __launch_bounds__(256) void logits_dot_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wg,
+                                                         float* __restrict__ out, int T, int d, int N,
+                                                         uint8_t* __restrict__ x_codes,
+                                                         float* __restrict__ tscale) {
+  __shared__ float red[4][4];
+  __shared__ float wmax[4];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int P = T >= 4 ? 1 : (T >= 2 ? 2 : 4);       // d-parts per token
+  const int G = 4 / P;                               // token groups
+  const int tg = wave / P, part = wave % P;
+  const int nch = d / 8;
+  const int c0 = part * nch / P, c1 = (part + 1) * nch / P;
+  const uint4* wr = reinterpret_cast<const uint4*>(wg + static_cast<int64_t>(e) * d);
+  const uint4* xb = reinterpret_cast<const uint4*>(x);
+  int tok[TPW];
+  float acc[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    tok[j] = tg + G * j;
+    acc[j] = 0.f;
+  }
+  // U chunks per lane per pass, their loads issued together (indices clamped
+  // into range: loads under a condition were waited for one by one)
+  constexpr int U = 4;
+  for (int cb = c0 + lane; cb < c1; cb += 64 * U) {
+    uint4 wv[U], xv[U][TPW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(cb + 64 * u, c1 - 1);
+      wv[u] = wr[c];
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) xv[u][j] = xb[static_cast<int64_t>(min(tok[j], T - 1)) * nch + c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (cb + 64 * u < c1) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) acc[j] = dot8_bf16(xv[u][j], wv[u], acc[j]);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = wave_sum_f(acc[j]);
+  if (P == 1) {
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+        if (tok[j] < T) out[static_cast<int64_t>(tok[j]) * N + e] = acc[j];
+    }
+  } else {
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) red[wave][j] = acc[j];
+    }
+    __syncthreads();
+    if (part == 0 && lane == 0) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        if (tok[j] >= T) continue;
+        float v = red[wave][j];
+        for (int q = 1; q < P; ++q) v += red[wave + q][j];
+        out[static_cast<int64_t>(tok[j]) * N + e] = v;
+      }
+    }
+  }
+  if (!x_codes) return;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    const uint4* xr = xb + static_cast<int64_t>(t) * nch;
+    float am = 0.f;
+    for (int c = threadIdx.x; c < nch; c += 256) am = fmaxf(am, absmax8(xr[c]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    __syncthreads();                                // (the previous token's wmax reads are done)
+    if (lane == 0) wmax[wave] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));   // (a max is exact in any order)
+    float inv, scale;
+    fp8_row_scale(am, &inv, &scale);
+    uint2* dst = reinterpret_cast<uint2*>(x_codes + static_cast<int64_t>(t) * d);
+    for (int c = threadIdx.x; c < nch; c += 256) dst[c] = quant8(xr[c], inv);
+    if (threadIdx.x == 0) tscale[t] = scale;
+  }
+}
+
 // Logits of a 16-token tile from the partials: the d-ranges added in order.
 template <int TM>
 __device__ void logits_from_partials(const RouteArgs& a, int ks, int64_t lrange, int64_t t0, float* lt,
@@ -655,6 +773,30 @@ __device__ void tile_stats(const RouteArgs& a, int e, float sum, int cnt, int* x
   scan_experts(kv, pr, N, a.alpha, a.rs.offsets, a.rs.l_aux, xk, xp);
 }
 
+// The fused layer's plan of a one-tile call, after tile_stats (every base is
+// 0): slot j of token t goes to offsets[e] + the number of earlier tokens
+// that chose e, or is dropped once that number reaches the capacity; the
+// same positions as the dispatch plan's (token order, stable).  Writes pos,
+// drop and src, and with an fp8 buffer the kept slots' row scales.
+__device__ void tile_plan(const RouteArgs& a, int* sidx) {
+  const int nk = static_cast<int>(a.T) * a.k;      // (one tile: T <= 16)
+  __syncthreads();                                 // idx and offsets written by this workgroup
+  for (int q = threadIdx.x; q < nk; q += RW * 64) sidx[q] = a.idx[q];
+  __syncthreads();
+  for (int q = threadIdx.x; q < nk; q += RW * 64) {
+    const int e = sidx[q], t = q / a.k;
+    int r = 0;
+    for (int q2 = 0; q2 < t * a.k; ++q2) r += sidx[q2] == e ? 1 : 0;
+    const int p = (a.cap > 0 && r >= a.cap) ? -1 : a.rs.offsets[e] + r;
+    a.pos[q] = p;
+    a.drop[q] = p < 0 ? 1 : 0;
+    if (p >= 0) {
+      a.src[p] = t;
+      if (a.row_scale) a.row_scale[p] = a.tscale[t];
+    }
+  }
+}
+
 template <bool BF16, int TM>
 __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   // staging buffer of the x tile (bf16, d a multiple of 512); afterwards, and
@@ -671,7 +813,9 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ int hl[kMaxExperts];
   __shared__ int xk[RW];
   __shared__ double xp[RW];
+  __shared__ int sidx[TM * kMaxTopK];    // the tile's expert choices (one-tile plan)
   static_assert(RW * 64 >= kMaxExperts, "thread e ends expert e's statistics");
+  const bool plan = a.fold && a.pos;
   const int ldl = kMaxExperts + 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = a.N, k = a.k;
@@ -712,6 +856,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       for (int m2 = 0; m2 < TM; ++m2) sum += pl[m2][e];
     }
     tile_stats(a, e, sum, e < N ? hl[e] : 0, xk, xp);
+    if (plan) tile_plan(a, sidx);
     return;
   }
   if (N <= SMALL_N) {
@@ -730,6 +875,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     if (e < N)
       for (int m2 = 0; m2 < TM; ++m2) sum += pl[m2][e];
     tile_stats(a, e, sum, e < N ? hl[e] : 0, xk, xp);
+    if (plan) tile_plan(a, sidx);
     return;
   }
 
@@ -887,6 +1033,7 @@ __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       for (int w = 0; w < RW; ++w) sum += ps[w][e];
     tile_stats(a, e, sum, e < N ? hl[e] : 0, xk, xp);
   }
+  if (plan) tile_plan(a, sidx);
 }
 
 // Statistics over all router tiles, spread over the experts so that the
@@ -1209,12 +1356,16 @@ size_t route_lds_bytes(const moe_shape& s, int TM) {
 // route + plan: 1 token 19.1 -> 17.8 us with 64 ranges instead of 16, 128
 // tokens 37.9 -> 32.5 us with 8 instead of 4; 32 tokens measured 27.2 -> 28.2
 // us with 32 instead of 16, so it keeps 16).
+bool route_plans(const moe_shape& s) {
+  return s.dtype == MOE_BF16 && s.T > 0 && s.T <= kRouteTile && s.d % 8 == 0;
+}
+
 int route_split_ranges(const moe_shape& s) {
+  if (route_plans(s)) return 1;                  // whole dot products: one range
   if (s.dtype != MOE_BF16 || s.T <= 0 || s.T >= 512 || s.d % 32 != 0) return 0;
   const int64_t units = ceil_div(s.T, 16) * ceil_div(s.N, 16);
   int64_t ks = ceil_div(1024, units);
-  const int64_t cap = s.T <= kRouteTile ? kLogitsSplitMax : 16;
-  if (ks > cap) ks = cap;
+  if (ks > kLogitsSplitMax) ks = kLogitsSplitMax;
   if (ks > s.d / 32) ks = s.d / 32;
   return static_cast<int>(ks < 1 ? 1 : ks);
 }
@@ -1236,12 +1387,36 @@ bool route_folds_stats(const moe_shape& s) { return s.T <= kRouteTile; }
 
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wg, const float* bias,
                         int32_t* idx, float* w, float* logits, float* psum, int32_t* hist,
-                        float* lpart, const RouteStats& rs, hipStream_t st) {
+                        float* lpart, const RouteStats& rs, hipStream_t st, const RoutePlanOut* plan) {
   const int ks = route_split_ranges(s);
+  const bool planning = plan != nullptr && route_plans(s) && rs.offsets != nullptr;
+  if (plan != nullptr && !planning) return hipErrorInvalidValue;
+  const bool codes = planning && plan->x_codes != nullptr;
   RouteArgs a{x, wg, bias, idx, w, logits, psum, hist, s.T, s.d, s.N, s.k,
               s.n_groups, s.topk_groups, s.group_score_k, ks > 0 ? lpart : nullptr, ks,
-              s.T * s.N, s.N, nullptr, s.gate, rs, route_folds_stats(s) ? 1 : 0, s.capacity, s.alpha};
-  if (router_gemm(s)) {
+              s.T * s.N, s.N, nullptr, s.gate, rs, route_folds_stats(s) ? 1 : 0, s.capacity, s.alpha,
+              planning ? plan->pos : nullptr, planning ? plan->src : nullptr,
+              planning ? plan->drop : nullptr, codes ? plan->row_scale : nullptr,
+              codes ? plan->tscale : nullptr};
+  if (route_plans(s)) {
+    // tokens per wave: the waves split 4 ways over tokens (T >= 4), else 2 or 1 way
+    const int T = static_cast<int>(s.T);
+    const int groups = T >= 4 ? 4 : (T >= 2 ? 2 : 1);
+    const int tpw = (T + groups - 1) / groups;
+    const auto xs = static_cast<const uint16_t*>(x);
+    const auto ws = static_cast<const uint16_t*>(wg);
+    uint8_t* xc = codes ? plan->x_codes : nullptr;
+    float* ts = codes ? plan->tscale : nullptr;
+    const dim3 grid(static_cast<unsigned>(s.N));
+    if (tpw <= 1)
+      hipLaunchKernelGGL(logits_dot_kernel<1>, grid, dim3(256), 0, st, xs, ws, lpart, T, s.d, s.N, xc, ts);
+    else if (tpw <= 2)
+      hipLaunchKernelGGL(logits_dot_kernel<2>, grid, dim3(256), 0, st, xs, ws, lpart, T, s.d, s.N, xc, ts);
+    else
+      hipLaunchKernelGGL(logits_dot_kernel<4>, grid, dim3(256), 0, st, xs, ws, lpart, T, s.d, s.N, xc, ts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (router_gemm(s)) {
     const hipError_t e = launch_router_logits(s, x, wg, lpart, st);
     if (e != hipSuccess) return e;
     a.lmeta = reinterpret_cast<const int32_t*>(lpart);

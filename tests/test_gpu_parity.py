@@ -350,6 +350,15 @@ FORWARD_CASES = {
     "dbrx_skew": lambda: si.small("dbrx"),
     "single_token": lambda: si.small("mixtral", T=1),
     "one_tile_groups_capacity": lambda: si.Workload("otc", **ONE_TILE_CASES["t10_groups_capacity"]),
+    # one router tile with bf16 x: logits from whole dot products (the four
+    # waves split d four or two ways below four tokens, else the tokens), the
+    # plan written by the router, the fp8 codes by the logits kernel
+    "one_tile_fp8_groups_shared_t1": lambda: si.small("deepseek_v3", T=1),
+    "one_tile_fp8_groups_shared_t3": lambda: si.small("deepseek_v3", T=3),
+    "one_tile_fp8_capacity_t16": lambda: si.small("deepseek_v3", T=16, capacity=1),
+    "one_tile_fp8_fewer_experts_than_tokens": lambda: si.Workload("otf", T=16, d=256, N=8, k=2, F=128,
+                                                                  buf="fp8", capacity=3),
+    "one_tile_wave_bias_t16": lambda: si.Workload("otw", **ONE_TILE_CASES["t16_wave_bias"]),
     "many_tiles_capacity": lambda: si.Workload("mbf", T=20011, d=64, N=16, k=2, F=128,
                                                act="swiglu", dtype="bf16", buf="bf16",
                                                capacity=2300),
