@@ -1349,13 +1349,14 @@ size_t route_lds_bytes(const moe_shape& s, int TM) {
 }
 }  // namespace
 
-// Split logits below 512 tokens (fewer than 32 router tiles, each of which
-// would read all of W_g): d-ranges so that about 1024 waves (one four-wave
-// workgroup per CU) stream W_g, at most kLogitsSplitMax for one router tile and
-// 16 for more, whose every tile re-adds its tokens' ranges (DeepSeek-V3 shape,
-// route + plan: 1 token 19.1 -> 17.8 us with 64 ranges instead of 16, 128
-// tokens 37.9 -> 32.5 us with 8 instead of 4; 32 tokens measured 27.2 -> 28.2
-// us with 32 instead of 16, so it keeps 16).
+// One router tile (at most 16 tokens) with bf16 x: whole dot products, one
+// range (logits_dot_kernel), and the router writes the plan.  Above that and
+// below 512 tokens (fewer than 32 router tiles, each of which would read all
+// of W_g): d-ranges so that about 1024 waves (one four-wave workgroup per CU)
+// stream W_g, at most kLogitsSplitMax, whose every tile re-adds its tokens'
+// ranges (DeepSeek-V3 shape, route + plan: 128 tokens 37.9 -> 32.5 us with 8
+// ranges instead of 4; 32 tokens measured 27.2 -> 28.2 us with 32 instead of
+// 16, so it keeps 16).
 bool route_plans(const moe_shape& s) {
   return s.dtype == MOE_BF16 && s.T > 0 && s.T <= kRouteTile && s.d % 8 == 0;
 }
