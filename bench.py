@@ -93,9 +93,11 @@ def layer_step(wl, L, x, h, hs):
     """One layer forward phase by phase, the kernels of moe_forward (fused or
     not, as the layer was made), with HIP events recorded between the phases
     when given: ev[0] before, ev[1] after route + dispatch (or route + plan),
-    ev[2] after the up GEMM, ev[3] after the shared expert's up GEMM (none
-    without a shared expert), ev[4] after the down GEMM (with a shared expert,
-    its down GEMM in the same launch), ev[5] after the combine."""
+    ev[2] after the up GEMM (in the fused layer with a shared expert, both up
+    GEMMs in one call), ev[3] after the unfused layer's shared-expert up GEMM
+    (otherwise nothing runs between ev[2] and ev[3]), ev[4] after the down GEMM
+    (with a shared expert, its down GEMM in the same launch), ev[5] after the
+    combine."""
     from mixture_experts_layer_sparse_amd import moe as M
     s = L.s
 
@@ -104,13 +106,17 @@ def layer_step(wl, L, x, h, hs):
         if L.fused:
             L.route_plan(x)
             ev and ev[1].record()
-            L.expert_up_gather(x, h)
+            if wl.shared:
+                # (routed and shared up in one call; a decode-sized call makes it one launch)
+                L.expert_up_gather_shared(x, h, hs)
+            else:
+                L.expert_up_gather(x, h)
         else:
             L.route_dispatch(x)
             ev and ev[1].record()
             M.expert_up(s, L.x_perm, L.row_scale, L.offsets, L.w1, L.w3, h, ws=L.ws)
         ev and ev[2].record()
-        if wl.shared:
+        if wl.shared and not L.fused:
             M.shared_expert_up(s, x, L.ws1, L.ws3, hs, ws=L.ws)
         ev and ev[3].record()
         if wl.shared:
@@ -440,7 +446,7 @@ def sweep(steps, warmup):
     import synthetic_inputs as si
     reports = []
 
-    print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up us | shared up us | GEMM down (+ shared) us | "
+    print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up (+ shared) us | shared up (unfused) us | GEMM down (+ shared) us | "
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|")
     for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx", "switch_mxfp4", "deepseek_v3_mxfp4"):
@@ -495,7 +501,7 @@ def decode(steps, warmup):
     m = 3 if base.swiglu else 2
     per_expert = m * base.F * base.d * 2
     print("| B | experts touched (uniform estimate) | us/step | us/step, graph replay | tokens/s (graph) | "
-          "route+dispatch us | GEMM up us | shared up us | GEMM down (+ shared) us | combine us | weight bytes streamed | "
+          "route+dispatch us | GEMM up (+ shared) us | shared up (unfused) us | GEMM down (+ shared) us | combine us | weight bytes streamed | "
           "weight GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for B in (1, 32, 128):

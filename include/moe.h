@@ -325,13 +325,27 @@ moe_status moe_expert_up_gather(const moe_shape* s, const void* a, const float* 
                                 const int32_t* offsets, const int32_t* src, const void* w1,
                                 const void* w3, void* h, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_expert_up_gather and moe_shared_expert_up in one call (has_shared must
+ * be 1): h [T*k][F] from the routed rows of a, read through src as
+ * moe_expert_up_gather reads them, and h_shared [T][F] from x [T][d] with
+ * ws1, ws3, both bit for bit what the two calls write.  "MoE: what it costs to
+ * train and serve" / "When decoding, batch size changes the arithmetic": a
+ * decode step streams weights, and a call of at most four tokens with bf16
+ * weights reads each weight row once in a single launch for both (no tiles);
+ * otherwise the two GEMMs run one after the other.  Errors as the two calls. */
+moe_status moe_expert_up_gather_shared(const moe_shape* s, const void* a, const float* row_scale,
+                                       const int32_t* offsets, const int32_t* src, const void* w1,
+                                       const void* w3, void* h, const void* x, const void* ws1,
+                                       const void* ws3, void* h_shared, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* The whole layer: moe_route_dispatch, moe_experts, moe_combine, enqueued on
  * one stream; results equal those of the four single-phase calls.  Every
  * output buffer is required except p, f, l_aux (may be NULL) and the
  * shared-expert buffers (ignored unless has_shared).  With x_perm == NULL the
  * layer runs fused: moe_route_plan, moe_expert_up_gather, moe_expert_down
- * (with has_shared: moe_shared_expert_up and moe_expert_down_shared) and
- * moe_combine, with no dispatch buffer (row_scale may
+ * (with has_shared: moe_expert_up_gather_shared and moe_expert_down_shared)
+ * and moe_combine, with no dispatch buffer (row_scale may
  * then be NULL too; the fp8 codes and scales live in the workspace); every
  * other output is bit for bit that of the unfused call. */
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,

@@ -486,6 +486,33 @@ moe_status moe_expert_up_gather(const moe_shape* s, const void* a, const float* 
                                           split, static_cast<hipStream_t>(stream), src, s->T));
 }
 
+moe_status moe_expert_up_gather_shared(const moe_shape* s, const void* a, const float* row_scale,
+                                       const int32_t* offsets, const int32_t* src, const void* w1,
+                                       const void* w3, void* h, const void* x, const void* ws1,
+                                       const void* ws3, void* h_shared, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!s->has_shared) return MOE_ERR_ARG;
+  if (!a || !offsets || !src || !w1 || !h || !x || !ws1 || !h_shared) return MOE_ERR_ARG;
+  if (s->act == MOE_ACT_SWIGLU && (!w3 || !ws3)) return MOE_ERR_ARG;
+  if (s->buf_dtype == MOE_FP8_E4M3 && !row_scale) return MOE_ERR_ARG;
+  if (!gather_fits(*s)) return MOE_ERR_UNSUPPORTED;
+  void* split = split_scratch(*s, ws, ws_bytes, &c);
+  if (c != MOE_OK) return c;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (moe::gemv_fits(*s))
+    return hip_status(moe::launch_expert_up(*s, a, row_scale, offsets, s->T * s->k, s->N, w1, w3, h, split,
+                                            st, src, s->T, x, ws1, ws3, h_shared, s->T));
+  hipError_t e = moe::launch_expert_up(*s, a, row_scale, offsets, s->T * s->k, s->N, w1, w3, h, split, st,
+                                       src, s->T);
+  if (e != hipSuccess) return hip_status(e);
+  moe_shape sd = *s;
+  sd.buf_dtype = sd.dtype;                     // the unquantised input
+  return hip_status(moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared, split, st));
+}
+
 moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
                        const void* w1, const void* w3, const void* w2, const void* ws1,
                        const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
@@ -526,15 +553,16 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
   r = moe_route_plan(s, x, w_g, bias, idx, w, counts, kept_counts, p, f, l_aux, offsets, pos, src, drop,
                      codes, rsc, ws, ws_bytes, stream);
   if (r != MOE_OK) return r;
-  r = moe_expert_up_gather(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, ws, ws_bytes,
-                           stream);
-  if (r != MOE_OK) return r;
   if (s->has_shared) {
-    r = moe_shared_expert_up(s, x, ws1, ws3, base + L.h_shared, ws, ws_bytes, stream);
+    r = moe_expert_up_gather_shared(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, x, ws1, ws3,
+                                    base + L.h_shared, ws, ws_bytes, stream);
     if (r != MOE_OK) return r;
     r = moe_expert_down_shared(s, base + L.h, offsets, w2, out, base + L.h_shared, ws2, out_shared, ws,
                                ws_bytes, stream);
   } else {
+    r = moe_expert_up_gather(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, ws, ws_bytes,
+                             stream);
+    if (r != MOE_OK) return r;
     r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
   }
   if (r != MOE_OK) return r;

@@ -1071,6 +1071,226 @@ __global__ __launch_bounds__(256) void gg_splitk_reduce(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------- decode GEMV --
+// Calls of at most four tokens (a decode step) with bf16 weights: every
+// segment holds at most four rows, so a tile of 128 or 256 rows would be
+// nearly empty and the GEMM becomes weight streaming.  Here each weight row is
+// read once and multiplied with the segment's rows (two at a time), with no
+// tiles, no LDS staging and no split-K scratch: one work item is JB output
+// columns of one segment (for the gated up GEMM the W1 and W3 rows of each),
+// its four waves each take a quarter of K, a lane sums its 16-byte chunks in
+// order, the wave adds its lanes by a fixed tree and the quarters are added
+// in wave order.  The arithmetic (float32 sums of exact bf16 products, the
+// fp8 codes widened exactly, the row scale then the activation) is that of
+// the tiled kernels; only the order of the additions differs.  Nonempty
+// segments only: an expert no token chose costs nothing.  An extra dense
+// segment (the shared expert: its own A, weights and output) can join the
+// launch.
+struct GemvArgs {
+  const void* a;            // routed A rows (bf16, or e4m3 codes with fp8): by position, or through gather
+  const float* a_scale;     // [positions] row scales (fp8 A), else null
+  const int32_t* gather;    // position -> A row, or null
+  const int32_t* offsets;   // [n_seg + 1] segment bounds over the positions, or null: one segment
+  int64_t rows;             // positions
+  int n_seg;
+  int K, n_out;
+  const uint16_t* b0;       // segment e's matrix [n_out][K] at b0 + e * b_stride
+  const uint16_t* b1;       // (gated: the W3 matrices, same layout)
+  int64_t b_stride;
+  uint16_t* out;            // [positions][n_out]
+  const uint16_t* xa;       // the extra segment: A [x_rows][K] (bf16), B at xb0 (xb1), out [x_rows][n_out]
+  const uint16_t* xb0;
+  const uint16_t* xb1;
+  uint16_t* xout;
+  int x_rows;               // 0: none
+  int epi;                  // Epi
+  int fp8;                  // routed A are e4m3 codes (scaled by a_scale)
+};
+
+constexpr int kGemvRowsMax = 4;    // tokens of a call that takes this path
+
+// x . w over 8 bf16 pairs (exact products), added to acc in element order
+__device__ __forceinline__ float gemv_dot8(uint4 a, uint4 b, float acc) {
+  const uint32_t xa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(xa[i] << 16), __uint_as_float(wb[i] << 16), acc);
+    acc = fmaf(__uint_as_float(xa[i] & 0xFFFF0000u), __uint_as_float(wb[i] & 0xFFFF0000u), acc);
+  }
+  return acc;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float gemv_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// the sum over the wave's lanes, in a fixed order (rows of 16 by DPP, then the four rows)
+__device__ __forceinline__ float gemv_wave_sum(float v) {
+  v += gemv_dpp<0xB1>(v);     // quad_perm [1, 0, 3, 2]
+  v += gemv_dpp<0x4E>(v);     // quad_perm [2, 3, 0, 1]
+  v += gemv_dpp<0x141>(v);    // lane i <-> 7 - i within 8
+  v += gemv_dpp<0x140>(v);    // lane i <-> 15 - i within 16
+  auto ln = [](float u, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), l)); };
+  return (ln(v, 0) + ln(v, 16)) + (ln(v, 32) + ln(v, 48));
+}
+
+// One pass of an item: rows r0 .. r0 + nr - 1 (nr <= 2) of a segment times JB
+// output columns from j0 (w0 = the first column's W1 row, w1 its W3 row).
+template <int JB, int U, bool GATED, bool FP8>
+__device__ __forceinline__ void gemv_pass(const GemvArgs& g, const uint8_t* a, const int32_t* gather,
+                                          const float* a_scale, int64_t r0, int nr,
+                                          const uint16_t* w0, const uint16_t* w1, uint16_t* out,
+                                          int j0, float (*red)[JB * 2 * 2]) {
+  constexpr int MATS = GATED ? 2 : 1;
+  constexpr int R = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = g.K, nch = K / 8;
+  const int c0 = wave * nch / 4, c1 = (wave + 1) * nch / 4;
+  const size_t arow = FP8 ? static_cast<size_t>(K) : static_cast<size_t>(K) * 2;   // A row bytes
+  const uint8_t* ar[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t pos = r0 + (r < nr ? r : nr - 1);
+    ar[r] = a + static_cast<size_t>(gather ? gather[pos] : pos) * arow;
+  }
+  const uint4* wr[JB][MATS];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int col = j0 + j < g.n_out ? j0 + j : g.n_out - 1;
+    wr[j][0] = reinterpret_cast<const uint4*>(w0 + static_cast<int64_t>(col) * K);
+    if (GATED) wr[j][MATS - 1] = reinterpret_cast<const uint4*>(w1 + static_cast<int64_t>(col) * K);
+  }
+  float acc[JB][MATS][R];
+#pragma unroll
+  for (int j = 0; j < JB; ++j)
+#pragma unroll
+    for (int m = 0; m < MATS; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[j][m][r] = 0.f;
+  // U chunks per lane per round, every load of the round issued first
+  // (indices clamped into range: loads under a condition are waited for one by one)
+  for (int cb = c0 + lane; cb < c1; cb += 64 * U) {
+    uint4 wv[U][JB][MATS], av[U][R];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = cb + 64 * u < c1 ? cb + 64 * u : c1 - 1;
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int m = 0; m < MATS; ++m) wv[u][j][m] = wr[j][m][c];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (FP8) av[u][r] = fp8x8_to_bf16x8(reinterpret_cast<const uint2*>(ar[r])[c]);
+        else av[u][r] = reinterpret_cast<const uint4*>(ar[r])[c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (cb + 64 * u < c1) {
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+          for (int m = 0; m < MATS; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[j][m][r] = gemv_dot8(av[u][r], wv[u][j][m], acc[j][m][r]);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < JB; ++j)
+#pragma unroll
+    for (int m = 0; m < MATS; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = gemv_wave_sum(acc[j][m][r]);
+        if (lane == 0) red[wave][(j * MATS + m) * R + r] = v;
+      }
+  __syncthreads();
+  if (threadIdx.x < JB * R) {
+    const int j = threadIdx.x / R, r = threadIdx.x % R;
+    if (j0 + j < g.n_out && r < nr) {
+      float v[MATS];
+#pragma unroll
+      for (int m = 0; m < MATS; ++m) {
+        const int q = (j * MATS + m) * R + r;
+        v[m] = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
+      }
+      const float sc = a_scale ? a_scale[r0 + r] : 1.0f;
+      float o;
+      if (GATED) {
+        o = silu_fast(v[0] * sc) * (v[MATS - 1] * sc);
+      } else {
+        o = v[0] * sc;
+        if (g.epi == EPI_SILU) o = silu_fast(o);
+        if (g.epi == EPI_RELU) o = fmaxf(o, 0.f);
+      }
+      out[static_cast<int64_t>(r0 + r) * g.n_out + j0 + j] = to_bf16(o);
+    }
+  }
+  __syncthreads();                                // (red is read before the next pass writes it)
+}
+
+template <int JB, int U, bool GATED>
+__global__ __launch_bounds__(256, 4) void gemv_kernel(GemvArgs g) {
+  __shared__ int segs[kMaxExperts + 1];
+  __shared__ int wcnt[4];
+  __shared__ float red[4][JB * 2 * 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the nonempty segments in index order (the same list in every workgroup)
+  const int n_seg = g.offsets ? g.n_seg : 1;
+  auto bounds = [&](int e, int64_t* p0, int64_t* p1) {
+    if (!g.offsets) {
+      *p0 = 0;
+      *p1 = g.rows;
+      return;
+    }
+    int64_t a = g.offsets[e], b = g.offsets[e + 1];
+    a = a < 0 ? 0 : (a > g.rows ? g.rows : a);     // (valid offsets pass unchanged)
+    b = b < a ? a : (b > g.rows ? g.rows : b);
+    *p0 = a;
+    *p1 = b;
+  };
+  bool live = false;
+  if (tid < n_seg) {
+    int64_t p0, p1;
+    bounds(tid, &p0, &p1);
+    live = p1 > p0;
+  }
+  const uint64_t mask = __ballot(live);
+  if (lane == 0) wcnt[wave] = __popcll(mask);
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wcnt[w];
+  if (live) segs[base + __popcll(mask & ((1ull << lane) - 1))] = tid;
+  const int nsegs = (wcnt[0] + wcnt[1]) + (wcnt[2] + wcnt[3]);
+  __syncthreads();
+  const int jbs = (g.n_out + JB - 1) / JB;                    // items per segment
+  const int items = (nsegs + (g.x_rows > 0 ? 1 : 0)) * jbs;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int si = it / jbs, j0 = (it - si * jbs) * JB;
+    if (si == nsegs) {                                        // the extra segment (bf16 A, no scale)
+      for (int64_t r0 = 0; r0 < g.x_rows; r0 += 2)
+        gemv_pass<JB, U, GATED, false>(g, reinterpret_cast<const uint8_t*>(g.xa), nullptr, nullptr, r0,
+                                       g.x_rows - r0 < 2 ? static_cast<int>(g.x_rows - r0) : 2, g.xb0,
+                                       g.xb1, g.xout, j0, red);
+    } else {
+      const int e = segs[si];
+      int64_t p0, p1;
+      bounds(e, &p0, &p1);
+      const uint16_t* w0 = g.b0 + (g.offsets ? e * g.b_stride : 0);
+      const uint16_t* w1 = GATED ? g.b1 + (g.offsets ? e * g.b_stride : 0) : nullptr;
+      for (int64_t r0 = p0; r0 < p1; r0 += 2) {
+        const int nr = p1 - r0 < 2 ? static_cast<int>(p1 - r0) : 2;
+        if (g.fp8)
+          gemv_pass<JB, U, GATED, true>(g, static_cast<const uint8_t*>(g.a), g.gather, g.a_scale, r0, nr,
+                                        w0, w1, g.out, j0, red);
+        else
+          gemv_pass<JB, U, GATED, false>(g, static_cast<const uint8_t*>(g.a), g.gather, nullptr, r0, nr,
+                                         w0, w1, g.out, j0, red);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------- float32 path --
 
 __device__ __forceinline__ int seg_of(const int32_t* offsets, int n_seg, int r) {
@@ -1240,6 +1460,30 @@ hipError_t dispatch_up(int bm, GemmArgs g, int64_t rows, int n_seg, bool dense, 
   return hipGetLastError();
 }
 
+// The decode GEMV launch: four workgroups per CU (at most 128 VGPRs), each
+// lane with 8 to 16 weight loads of one round in flight: U chunks per lane
+// per round (a quarter of K in one or a few rounds) times JB columns (times
+// W1 and W3 when gated).  Measured at the DeepSeek-V3 decode shape (graph
+// replay of the whole layer, 1 / 2 / 4 tokens): against the tiled split-K
+// GEMMs 191.5 / 285.8 / 531.6 -> 168.9 / 273.1 / 523.9 us; two workgroups per
+// CU with 16-24 loads lost (194.8 us at 1 token), and so did 8 loads per
+// lane (175.3) or 6 and 8 workgroups per CU (229.1, 220.3: spills).
+template <bool GATED>
+hipError_t launch_gemv_on(const GemvArgs& g, hipStream_t st) {
+  const int cpl = static_cast<int>(ceil_div(ceil_div(g.K / 8, 4), 64));   // chunks per lane
+  const dim3 grid(static_cast<unsigned>(4 * device_cu_count())), block(256);
+  if constexpr (GATED) {
+    if (cpl >= 4) hipLaunchKernelGGL((gemv_kernel<2, 4, GATED>), grid, block, 0, st, g);
+    else if (cpl >= 2) hipLaunchKernelGGL((gemv_kernel<4, 2, GATED>), grid, block, 0, st, g);
+    else hipLaunchKernelGGL((gemv_kernel<4, 1, GATED>), grid, block, 0, st, g);
+  } else {
+    if (cpl >= 4) hipLaunchKernelGGL((gemv_kernel<3, 4, GATED>), grid, block, 0, st, g);
+    else if (cpl >= 2) hipLaunchKernelGGL((gemv_kernel<8, 2, GATED>), grid, block, 0, st, g);
+    else hipLaunchKernelGGL((gemv_kernel<8, 1, GATED>), grid, block, 0, st, g);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Scratch of the split-K tails of this shape's grouped GEMMs (routed, and the
@@ -1313,10 +1557,42 @@ hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w
       g, kSplitKMax * mtu, st);
 }
 
+bool gemv_fits(const moe_shape& s) {
+  return s.dtype == MOE_BF16 && s.wfmt != MOE_W_MXFP4 && s.T > 0 && s.T <= kGemvRowsMax && s.d % 8 == 0 &&
+         s.F % 8 == 0;
+}
+
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg, const void* w1,
                             const void* w3, void* h, void* split, hipStream_t st,
-                            const int32_t* gather, int64_t a_rows) {
+                            const int32_t* gather, int64_t a_rows, const void* xa, const void* xw1,
+                            const void* xw3, void* xout, int64_t x_rows) {
+  if (gemv_fits(s)) {
+    GemvArgs g{};
+    const bool fp8 = s.buf_dtype == MOE_FP8_E4M3 && row_scale != nullptr;
+    g.a = a;
+    g.a_scale = fp8 ? row_scale : nullptr;
+    g.gather = gather;
+    g.offsets = offsets;
+    g.rows = rows;
+    g.n_seg = n_seg;
+    g.K = s.d;
+    g.n_out = s.F;
+    g.b0 = static_cast<const uint16_t*>(w1);
+    g.b1 = static_cast<const uint16_t*>(w3);
+    g.b_stride = static_cast<int64_t>(s.F) * s.d;
+    g.out = static_cast<uint16_t*>(h);
+    const bool extra = x_rows > 0 && offsets != nullptr;
+    g.xa = extra ? static_cast<const uint16_t*>(xa) : nullptr;
+    g.xb0 = extra ? static_cast<const uint16_t*>(xw1) : nullptr;
+    g.xb1 = extra ? static_cast<const uint16_t*>(xw3) : nullptr;
+    g.xout = extra ? static_cast<uint16_t*>(xout) : nullptr;
+    g.x_rows = extra ? static_cast<int>(x_rows) : 0;
+    g.epi = s.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : (s.act == MOE_ACT_RELU ? EPI_RELU : EPI_SILU);
+    g.fp8 = fp8 ? 1 : 0;
+    return s.act == MOE_ACT_SWIGLU ? launch_gemv_on<true>(g, st) : launch_gemv_on<false>(g, st);
+  }
+  if (x_rows > 0) return hipErrorInvalidValue;       // (the tiled path takes the extra segment only for down)
   if (s.dtype == MOE_F32) {
     int64_t n = rows * s.F;
     dim3 grid(static_cast<unsigned>(ceil_div(n, 256)));
@@ -1362,6 +1638,25 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
                               hipStream_t st, const void* xa, const void* xw2, void* xout, int64_t x_rows) {
+  if (gemv_fits(s)) {
+    GemvArgs g{};
+    g.a = h;
+    g.offsets = offsets;
+    g.rows = rows;
+    g.n_seg = n_seg;
+    g.K = s.F;
+    g.n_out = s.d;
+    g.b0 = static_cast<const uint16_t*>(w2);
+    g.b_stride = static_cast<int64_t>(s.d) * s.F;
+    g.out = static_cast<uint16_t*>(out);
+    const bool extra = x_rows > 0 && offsets != nullptr;
+    g.xa = extra ? static_cast<const uint16_t*>(xa) : nullptr;
+    g.xb0 = extra ? static_cast<const uint16_t*>(xw2) : nullptr;
+    g.xout = extra ? static_cast<uint16_t*>(xout) : nullptr;
+    g.x_rows = extra ? static_cast<int>(x_rows) : 0;
+    g.epi = EPI_STORE;
+    return launch_gemv_on<false>(g, st);
+  }
   if (s.dtype == MOE_F32) {
     int64_t n = rows * s.d;
     dim3 grid(static_cast<unsigned>(ceil_div(n, 256)));

@@ -151,10 +151,18 @@ hipError_t launch_dispatch_plan_fused(const moe_shape& s, const void* x, const i
 // which then has `a_rows` rows (a_rows * d * element size < 4 GiB).
 // `split` (may be null): gemm_split_bytes(s) of scratch for a split-K tail;
 // without it a mostly idle last round runs as quarter tiles.
+// Calls of at most four tokens with bf16 weights (gemv_fits) stream each
+// weight row once with no tiles (the decode GEMV); there the up launch also
+// takes an extra dense segment (x_rows > 0, with offsets): xout [x_rows][F]
+// from xa [x_rows][d] (bf16) and xw1, xw3 (the shared expert's up GEMM);
+// elsewhere x_rows must be 0.
+bool gemv_fits(const moe_shape& s);
 hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_scale,
                             const int32_t* offsets, int64_t rows, int n_seg,
                             const void* w1, const void* w3, void* h, void* split, hipStream_t st,
-                            const int32_t* gather = nullptr, int64_t a_rows = 0);
+                            const int32_t* gather = nullptr, int64_t a_rows = 0,
+                            const void* xa = nullptr, const void* xw1 = nullptr,
+                            const void* xw3 = nullptr, void* xout = nullptr, int64_t x_rows = 0);
 // With x_rows > 0 (and offsets), the same launch also computes an extra dense
 // segment after the routed ones: xout [x_rows][d] = xa [x_rows][F] times the one
 // matrix xw2 (laid out as one of w2's), the shared expert's down GEMM.

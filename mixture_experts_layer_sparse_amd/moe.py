@@ -105,6 +105,7 @@ _SIGS = {
     "moe_shared_expert": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P, c_size_t, _P]),
     "moe_shared_expert_up": (c_int32, [POINTER(Shape)] + [_P] * 4 + [_P, c_size_t, _P]),
     "moe_expert_down_shared": (c_int32, [POINTER(Shape)] + [_P] * 7 + [_P, c_size_t, _P]),
+    "moe_expert_up_gather_shared": (c_int32, [POINTER(Shape)] + [_P] * 11 + [_P, c_size_t, _P]),
     "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
     "moe_forward": (c_int32, [POINTER(Shape)] + [_P] * 25 + [_P, c_size_t, _P]),
@@ -321,6 +322,30 @@ def expert_up_gather(s: Shape, a, row_scale, offsets, src, w1, w3, h=None, ws=No
     return h
 
 
+def expert_up_gather_shared(s: Shape, a, row_scale, offsets, src, w1, w3, x, ws1, ws3, h=None,
+                            h_shared=None, ws=None):
+    """moe_expert_up_gather_shared: expert_up_gather and shared_expert_up in one
+    call (one launch for a call of at most four tokens).  Returns (h, h_shared)."""
+    R, T, F = s.T * s.k, s.T, s.F
+    fp8 = s.buf_dtype == MOE_FP8_E4M3
+    _check(a, "a", (T, s.d), torch.uint8 if fp8 else s.torch_dtype)
+    _check(offsets, "offsets", (s.N + 1,), torch.int32)
+    _check(src, "src", (R,), torch.int32)
+    _check(x, "x", (T, s.d), s.torch_dtype)
+    _check_w(w1, "w1", s, s.N, F, s.d)
+    _check_w(w3, "w3", s, s.N, F, s.d, required=s.act == MOE_ACT_SWIGLU)
+    _check_w(ws1, "ws1", s, None, F, s.d)
+    _check_w(ws3, "ws3", s, None, F, s.d, required=s.act == MOE_ACT_SWIGLU)
+    if h is None:
+        h = torch.empty((R, F), dtype=s.torch_dtype, device=a.device)
+    if h_shared is None:
+        h_shared = torch.empty((T, F), dtype=s.torch_dtype, device=a.device)
+    _call("moe_expert_up_gather_shared", ctypes.byref(s), _ptr(a), _ptr(row_scale), _ptr(offsets),
+          _ptr(src), _ptr(w1), _ptr(w3), _ptr(h), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(h_shared), _ptr(ws),
+          0 if ws is None else ws.numel(), _stream())
+    return h, h_shared
+
+
 def expert_up(s: Shape, x_perm, row_scale, offsets, w1, w3, h=None, ws=None):
     """ws: None (a mostly idle last tile round runs as quarter tiles) or a
     workspace from alloc_workspace (that round is split along K instead)."""
@@ -496,6 +521,13 @@ class Layer:
         _call("moe_expert_up_gather", ctypes.byref(s), _ptr(a), _ptr(self.row_scale),
               _ptr(self.offsets), _ptr(self.src), _ptr(self.w1), _ptr(self.w3), _ptr(h),
               _ptr(self.ws), self.ws.numel(), _stream())
+
+    def expert_up_gather_shared(self, x, h, h_shared):
+        s = self.s
+        a = self.x_codes if self.x_codes is not None else x
+        _call("moe_expert_up_gather_shared", ctypes.byref(s), _ptr(a), _ptr(self.row_scale),
+              _ptr(self.offsets), _ptr(self.src), _ptr(self.w1), _ptr(self.w3), _ptr(h), _ptr(x),
+              _ptr(self.ws1), _ptr(self.ws3), _ptr(h_shared), _ptr(self.ws), self.ws.numel(), _stream())
 
     # forward in three calls (the same kernels): route + dispatch, experts, combine
     def route_dispatch(self, x):

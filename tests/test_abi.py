@@ -124,6 +124,13 @@ def test_null_pointers_and_workspace_rejected_on_host(M):
     assert st == M.MOE_ERR_ARG
     st = L.moe_shared_expert_up(ctypes.byref(s2), p, p, None, p, None, 0, None)
     assert st == M.MOE_ERR_ARG
+    # routed + shared up in one call: no shared expert, then a missing h_shared
+    st = L.moe_expert_up_gather_shared(ctypes.byref(s), p, None, p, p, p, None, p, p, p, None, p, None, 0,
+                                       None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_expert_up_gather_shared(ctypes.byref(ssh), p, None, p, p, p, None, p, p, p, None, None, None,
+                                       0, None)
+    assert st == M.MOE_ERR_ARG
     # T == 0 is a no-op even with null buffers
     s0 = _s(M, T=0)
     st = L.moe_route(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None,

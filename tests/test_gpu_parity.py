@@ -359,6 +359,12 @@ FORWARD_CASES = {
     "one_tile_fp8_fewer_experts_than_tokens": lambda: si.Workload("otf", T=16, d=256, N=8, k=2, F=128,
                                                                   buf="fp8", capacity=3),
     "one_tile_wave_bias_t16": lambda: si.Workload("otw", **ONE_TILE_CASES["t16_wave_bias"]),
+    # at most four tokens with bf16 weights: the decode GEMV (no tiles); segments
+    # of more than two rows take two passes; U = 1, 2, 4 chunk rounds
+    "gemv_t4_relu_capacity": lambda: si.Workload("gv4", T=4, d=256, N=4, k=2, F=256, act="relu", capacity=2),
+    "gemv_t4_silu_fp8_shared_full_segments": lambda: si.Workload("gv4s", T=4, d=384, N=2, k=2, F=192,
+                                                                 act="silu", buf="fp8", shared=True),
+    "gemv_t2_mixtral_dims": lambda: si.Workload("gvm", T=2, d=4096, N=2, k=1, F=14336),
     "many_tiles_capacity": lambda: si.Workload("mbf", T=20011, d=64, N=16, k=2, F=128,
                                                act="swiglu", dtype="bf16", buf="bf16",
                                                capacity=2300),
