@@ -146,3 +146,19 @@ def test_workspace_grows_with_h(M):
         assert b > a
         s = _s(M, T=128, dtype=dt)
         assert b >= s.T * s.k * s.F * es          # the expert intermediate h lives there
+
+
+def test_bench_roofline_kernel_is_in_the_counter_summary():
+    """bench.py fills roofline.traffic from the committed counter summary by the
+    gate/up kernel's name: that name (all template arguments, as the trace
+    prints them) must be one of the summary's kernels, so that the field is not
+    silently null."""
+    import json
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    with open(bench.COUNTER_FILE) as f:
+        text = f.read()
+    data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    assert bench.UP_KERNEL["mixtral"] in data["kernels"]
