@@ -423,6 +423,9 @@ GRAPH_CASES = {
     # the fused layer (no dispatch buffer)
     "mixtral_ragged_fused": lambda: si.small("mixtral", T=1001),
     "deepseek_v3_full_fused": lambda: si.WORKLOADS["deepseek_v3"],
+    # decode steps of the fused layer: the one-tile router and the decode GEMV
+    "decode_1_token_fused": lambda: si.decode(1),
+    "decode_4_tokens_fused": lambda: si.decode(4),
 }
 
 
