@@ -389,6 +389,13 @@ def _to_dev(arr):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
+def shared_up_runs(wl, fused):
+    """Whether layer_step launches anything between ev[2] and ev[3] (the
+    unfused layer's shared-expert up GEMM); otherwise that interval holds only
+    the two event records and counts as no GEMM time."""
+    return bool(wl.shared) and not fused
+
+
 def _phases(wl, g, x, steps, warmup, fused=True):
     """Runs the kernels of moe_forward phase by phase; returns (layer, mean
     phase times in us [route+dispatch, up, shared up, down (+ shared down), combine], wall time
@@ -460,13 +467,14 @@ def sweep(steps, warmup):
         R = int(L.offsets[-1].item())
         up, down, shared = gemm_flops(wl, R)
         rb, db, cb = alg_bytes(wl, R, fused=True)
-        gemm_us = ph[1] + ph[2] + ph[3]
+        sh = shared_up_runs(wl, True)
+        gemm_us = ph[1] + (ph[2] if sh else 0.0) + ph[3]
         tf = (up + down + shared) / (gemm_us * 1e-6) / 1e12
         wgb = expert_weight_bytes(wl) / (gemm_us * 1e-6) / 1e9
         mem_us = ph[0] + ph[4]
         mgb = (rb + db + cb) / (mem_us * 1e-6) / 1e9
         print(f"| {name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k}, F={wl.F}{', MXFP4 experts' if wl.wfmt == 'mxfp4' else ''}) | {wl.T / wall:,.0f} | "
-              f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | "
+              f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {f'{ph[2]:.1f}' if sh else '-'} | {ph[3]:.1f} | {ph[4]:.1f} | "
               f"{tf:.0f} ({100 * tf / PEAK_BF16_TFLOPS:.1f}%) | {wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) | "
               f"{mgb:.0f} ({100 * mgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
         reports.append(load_report(wl, L))
@@ -513,10 +521,11 @@ def decode(steps, warmup):
         touched = int((L.counts > 0).sum().item())
         est = base.N * (1.0 - (1.0 - base.k / base.N) ** B)
         wbytes = (touched + (1 if base.shared else 0)) * per_expert
-        gemm_us = ph[1] + ph[2] + ph[3]
+        sh = shared_up_runs(wl, True)
+        gemm_us = ph[1] + (ph[2] if sh else 0.0) + ph[3]
         wgb = wbytes / (gemm_us * 1e-6) / 1e9
         print(f"| {B} | {touched} ({est:.1f}) | {wall * 1e6:.1f} | {gwall * 1e6:.1f} | {B / gwall:,.0f} | {ph[0]:.1f} | {ph[1]:.1f} | "
-              f"{ph[2]:.1f} | {ph[3]:.1f} | {ph[4]:.1f} | {wbytes / 2**30:.2f} GiB | "
+              f"{f'{ph[2]:.1f}' if sh else '-'} | {ph[3]:.1f} | {ph[4]:.1f} | {wbytes / 2**30:.2f} GiB | "
               f"{wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
         del L, x
         torch.cuda.empty_cache()
@@ -682,6 +691,8 @@ def main():
     rb, db, cb = alg_bytes(wl, R, fused)
     t_up = ph_ms["gemm_up"] * 1e-3
     achieved = up / t_up / 1e12
+    if not shared_up_runs(wl, fused):
+        ph_ms["shared_up"] = 0.0                  # (nothing launched between those two events)
     gemm_t = (ph_ms["gemm_up"] + ph_ms["shared_up"] + ph_ms["gemm_down"]) * 1e-3
     mem_t = (ph_ms["route_dispatch"] + ph_ms["combine"]) * 1e-3
     out = {
