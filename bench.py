@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="time the layer with the dispatch buffer (row copy, then the up GEMM on it) "
                          "instead of the fused gather")
+    ap.add_argument("--scatter", action="store_true",
+                    help="time the fused layer whose down GEMM also writes y (moe_forward_scatter: "
+                         "no combine launch)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens whose expert FFNs the CPU oracle runs (0: all T)")
     ap.add_argument("--mode", choices=["bench", "copy", "summarize", "sweep", "decode", "memory"],
@@ -120,6 +123,12 @@ def layer_step(wl, L, x, h, hs):
         if wl.shared and not L.fused:
             M.shared_expert_up(s, x, L.ws1, L.ws3, hs, ws=L.ws)
         ev and ev[3].record()
+        if L.scatter:
+            # the down GEMM's tiles write y (no combine launch: nothing runs between ev[4] and ev[5])
+            L.expert_down_combine(x, h, hs)
+            ev and ev[4].record()
+            ev and ev[5].record()
+            return
         if wl.shared:
             M.expert_down_shared(s, h, L.offsets, L.w2, hs, L.ws2, L.out, L.out_shared, ws=L.ws)
         else:
@@ -396,7 +405,7 @@ def shared_up_runs(wl, fused):
     return bool(wl.shared) and not fused
 
 
-def _phases(wl, g, x, steps, warmup, fused=True):
+def _phases(wl, g, x, steps, warmup, fused=True, scatter=False):
     """Runs the kernels of moe_forward phase by phase; returns (layer, mean
     phase times in us [route+dispatch, up, shared up, down (+ shared down), combine], wall time
     per step in s)."""
@@ -405,7 +414,7 @@ def _phases(wl, g, x, steps, warmup, fused=True):
     from mixture_experts_layer_sparse_amd import moe as M
     s = M.shape_of(wl)
     L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
-                ws3=g["ws3"], ws2=g["ws2"], fused=fused)
+                ws3=g["ws3"], ws2=g["ws2"], fused=fused, scatter=scatter)
     h = torch.empty((wl.T * wl.k, wl.F), dtype=s.torch_dtype, device="cuda")
     hs = torch.empty((wl.T, wl.F), dtype=s.torch_dtype, device="cuda") if wl.shared else None
     step = layer_step(wl, L, x, h, hs)
@@ -457,27 +466,35 @@ def sweep(steps, warmup):
     print("| workload | tokens/s | ms/step | route+dispatch us | GEMM up (+ shared) us | shared up (unfused) us | GEMM down (+ shared) us | "
           "combine us | GEMM TFLOP/s (% bf16 peak) | GEMM weight GB/s (% HBM) | memory phases GB/s (% HBM) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|")
-    for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx", "switch_mxfp4", "deepseek_v3_mxfp4"):
-        wl = workload(name)
+    for name in ("tiny", "mixtral", "switch", "deepseek_v3", "dbrx", "switch_mxfp4", "deepseek_v3_mxfp4",
+                 "mixtral_scatter", "switch_scatter", "deepseek_v3_scatter", "dbrx_scatter"):
+        # (_scatter: moe_forward_scatter, the down GEMM's tiles writing y; no combine launch)
+        scatter = name.endswith("_scatter")
+        wl = workload(name[:-len("_scatter")] if scatter else name)
         inp = si.generate(wl)
         g = {k: _to_dev(v) for k, v in inp.items()}
         del inp
         x = g["x"]
-        L, ph, wall = _phases(wl, g, x, steps, warmup)
+        L, ph, wall = _phases(wl, g, x, steps, warmup, scatter=scatter)
         R = int(L.offsets[-1].item())
         up, down, shared = gemm_flops(wl, R)
         rb, db, cb = alg_bytes(wl, R, fused=True)
+        if scatter:
+            ph[4], cb = 0.0, 0                    # (the combine runs in the down GEMM)
         sh = shared_up_runs(wl, True)
         gemm_us = ph[1] + (ph[2] if sh else 0.0) + ph[3]
         tf = (up + down + shared) / (gemm_us * 1e-6) / 1e12
         wgb = expert_weight_bytes(wl) / (gemm_us * 1e-6) / 1e9
         mem_us = ph[0] + ph[4]
         mgb = (rb + db + cb) / (mem_us * 1e-6) / 1e9
-        print(f"| {name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k}, F={wl.F}{', MXFP4 experts' if wl.wfmt == 'mxfp4' else ''}) | {wl.T / wall:,.0f} | "
-              f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {f'{ph[2]:.1f}' if sh else '-'} | {ph[3]:.1f} | {ph[4]:.1f} | "
+        extra = ", MXFP4 experts" if wl.wfmt == "mxfp4" else (", combine in the down GEMM" if scatter else "")
+        print(f"| {name} (T={wl.T}, d={wl.d}, N={wl.N}, k={wl.k}, F={wl.F}{extra}) | {wl.T / wall:,.0f} | "
+              f"{wall * 1e3:.3f} | {ph[0]:.1f} | {ph[1]:.1f} | {f'{ph[2]:.1f}' if sh else '-'} | {ph[3]:.1f} | "
+              f"{'-' if scatter else f'{ph[4]:.1f}'} | "
               f"{tf:.0f} ({100 * tf / PEAK_BF16_TFLOPS:.1f}%) | {wgb:.0f} ({100 * wgb / PEAK_HBM_GBPS:.1f}%) | "
               f"{mgb:.0f} ({100 * mgb / PEAK_HBM_GBPS:.1f}%) |", flush=True)
-        reports.append(load_report(wl, L))
+        if not scatter:
+            reports.append(load_report(wl, L))
         del L, g, x
         torch.cuda.empty_cache()
     print()
@@ -650,8 +667,10 @@ def main():
     g = {k: dev(v) for k, v in inp.items()}
     s = M.shape_of(wl)
     fused = not a.unfused
+    if a.scatter and a.unfused:
+        raise SystemExit("--scatter is a form of the fused layer")
     L = M.Layer(s, g["wg"], g["w1"], g["w3"], g["w2"], bias=g["bias"], ws1=g["ws1"],
-                ws3=g["ws3"], ws2=g["ws2"], fused=fused)
+                ws3=g["ws3"], ws2=g["ws2"], fused=fused, scatter=a.scatter)
     x = g["x"]
     dt = s.torch_dtype
     h = torch.empty((wl.T * wl.k, wl.F), dtype=dt, device="cuda")
@@ -694,6 +713,10 @@ def main():
     if not shared_up_runs(wl, fused):
         ph_ms["shared_up"] = 0.0                  # (nothing launched between those two events)
     gemm_t = (ph_ms["gemm_up"] + ph_ms["shared_up"] + ph_ms["gemm_down"]) * 1e-3
+    if a.scatter:
+        # the combine runs in the down GEMM's epilogue: the memory phases are route + plan alone
+        ph_ms["combine"] = 0.0
+        cb = 0
     mem_t = (ph_ms["route_dispatch"] + ph_ms["combine"]) * 1e-3
     out = {
         "metric": METRIC,
@@ -712,7 +735,8 @@ def main():
                    "act": wl.act, "dispatch_buffer": "none (fused gather)" if fused else wl.buf,
                    "activations": wl.buf, "capacity": wl.capacity,
                    "groups": [wl.n_groups, wl.topk_groups], "shared_expert": wl.shared,
-                   "kept_rows": R},
+                   "kept_rows": R,
+                   "combine": "in the down GEMM's epilogue" if a.scatter else "combine kernel"},
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM up (gate/up + activation)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,
@@ -725,7 +749,7 @@ def main():
         "dispatch_GBps": (rb + db) / (ph_ms["route_dispatch"] * 1e-3) / 1e9,
         "dispatch_GBps_covers": ("route + plan (moe_route_plan; no dispatch copy: the up GEMM gathers x "
                                  "through src)") if fused else "route + dispatch (moe_route_dispatch)",
-        "combine_GBps": cb / (ph_ms["combine"] * 1e-3) / 1e9,
+        "combine_GBps": cb / (ph_ms["combine"] * 1e-3) / 1e9 if cb else None,
         "memory_phases": {"bytes": rb + db + cb, "us": mem_t * 1e6,
                           "GBps": (rb + db + cb) / mem_t / 1e9,
                           "frac_hbm": (rb + db + cb) / mem_t / 1e9 / PEAK_HBM_GBPS},

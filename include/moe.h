@@ -357,6 +357,43 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
                        void* x_perm, float* row_scale, void* out, void* out_shared, void* y,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* The down GEMM with the combine in its epilogue: the scatter half of a fused
+ * gather-GEMM-scatter ("MoE: what it costs to train and serve" / "In short":
+ * dispatch and combine overlap with the expert computation; "Expert
+ * parallelism and two all-to-alls": the return traffic).  Writes out (and,
+ * with has_shared, out_shared) as moe_expert_down (moe_expert_down_shared)
+ * called with ws = NULL, and y as moe_combine on those outputs, bit for bit.
+ * Each tile of the down GEMM, once its output rows are written, counts them
+ * per token and 128-column group; the tile that completes a token's group
+ * (its kept slots and its shared-expert row) writes those columns of y in the
+ * combine's order and arithmetic.  Tokens that no row reaches (every slot
+ * dropped, no shared expert) get y before the GEMM.  No float atomics: results
+ * are deterministic.  Float32 layers and calls of at most four tokens (the
+ * decode GEMV) run moe_expert_down(_shared) with ws and moe_combine instead.
+ *   h [T*k][F], offsets [N+1], src [T*k] (token of each kept row), w2, out as for
+ *   moe_expert_down; h_shared, ws2, out_shared as for moe_expert_down_shared
+ *   (required with has_shared, else ignored); x [T][d], pos [T][k], w [T][k]
+ *   float32, y [T][d] as for moe_combine; ws required (its counters, no
+ *   initialisation needed).  Errors as moe_expert_down and moe_combine. */
+moe_status moe_expert_down_combine(const moe_shape* s, const void* h, const int32_t* offsets,
+                                   const int32_t* src, const void* w2, void* out, const void* h_shared,
+                                   const void* ws2, void* out_shared, const void* x, const int32_t* pos,
+                                   const float* w, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* The fused layer of moe_forward (x_perm = NULL) with moe_expert_down_combine
+ * in place of the down GEMM and the combine: moe_route_plan, the gathering up
+ * GEMM(s), moe_expert_down_combine.  Arguments as moe_forward without x_perm;
+ * every output equals that of moe_route_plan, moe_expert_up_gather(_shared)
+ * and moe_expert_down_combine called one after the other. */
+moe_status moe_forward_scatter(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                               const void* w1, const void* w3, const void* w2,
+                               const void* ws1, const void* ws3, const void* ws2,
+                               int32_t* idx, float* w, int32_t* counts, int32_t* kept_counts,
+                               float* p, float* f, float* l_aux,
+                               int32_t* offsets, int32_t* pos, int32_t* src, uint8_t* drop,
+                               float* row_scale, void* out, void* out_shared, void* y,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status st);
 

@@ -51,6 +51,8 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align_up(off + T * static_cast<size_t>(s.k) * static_cast<size_t>(s.F) * elem_size(s.dtype));
   L.h_shared = off;
   if (s.has_shared) off = align_up(off + T * static_cast<size_t>(s.F) * elem_size(s.dtype));
+  L.sc_cnt = off;
+  if (s.dtype == MOE_BF16) off = align_up(off + T * static_cast<size_t>(ceil_div(s.d, kScatterCols)) * 4);
   L.total = off;
   return L;
 }
@@ -513,13 +515,44 @@ moe_status moe_expert_up_gather_shared(const moe_shape* s, const void* a, const 
   return hip_status(moe::launch_expert_up(sd, x, nullptr, nullptr, s->T, 1, ws1, ws3, h_shared, split, st));
 }
 
-moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
-                       const void* w1, const void* w3, const void* w2, const void* ws1,
-                       const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
-                       int32_t* kept_counts, float* p, float* f, float* l_aux, int32_t* offsets,
-                       int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm, float* row_scale,
-                       void* out, void* out_shared, void* y, void* ws, size_t ws_bytes,
-                       void* stream) {
+moe_status moe_expert_down_combine(const moe_shape* s, const void* h, const int32_t* offsets,
+                                   const int32_t* src, const void* w2, void* out, const void* h_shared,
+                                   const void* ws2, void* out_shared, const void* x, const int32_t* pos,
+                                   const float* w, void* y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status c = check_shape(s);
+  if (c != MOE_OK) return c;
+  if (s->T == 0) return MOE_OK;
+  if (!h || !offsets || !src || !w2 || !out || !x || !pos || !w || !y || !ws) return MOE_ERR_ARG;
+  if (s->has_shared && (!h_shared || !ws2 || !out_shared)) return MOE_ERR_ARG;
+  const WsLayout L = moe::ws_layout(*s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s->dtype != MOE_BF16 || moe::gemv_fits(*s)) {
+    // float32 layers and decode-sized calls (the GEMV): the down GEMM, then the combine
+    c = s->has_shared ? moe_expert_down_shared(s, h, offsets, w2, out, h_shared, ws2, out_shared, ws, ws_bytes,
+                                               stream)
+                      : moe_expert_down(s, h, offsets, w2, out, ws, ws_bytes, stream);
+    if (c != MOE_OK) return c;
+    return moe_combine(s, out, s->has_shared ? out_shared : nullptr, x, pos, w, y, stream);
+  }
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sc_cnt);
+  hipError_t e = moe::launch_scatter_init(*s, pos, w, x, cnt, y, st);
+  if (e != hipSuccess) return hip_status(e);
+  const moe::ScatterArgs sc{src, pos, w, x, y, cnt};
+  if (s->has_shared)
+    return hip_status(moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out, nullptr, st, h_shared,
+                                              ws2, out_shared, s->T, &sc));
+  return hip_status(moe::launch_expert_down(*s, h, offsets, s->T * s->k, s->N, w2, out, nullptr, st, nullptr,
+                                            nullptr, nullptr, 0, &sc));
+}
+
+static moe_status forward_impl(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                               const void* w1, const void* w3, const void* w2, const void* ws1,
+                               const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
+                               int32_t* kept_counts, float* p, float* f, float* l_aux, int32_t* offsets,
+                               int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm, float* row_scale,
+                               void* out, void* out_shared, void* y, void* ws, size_t ws_bytes,
+                               void* stream, bool scatter) {
   moe_status r = check_shape(s);
   if (r != MOE_OK) return r;
   if (s->T == 0) return MOE_OK;
@@ -557,16 +590,45 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const
     r = moe_expert_up_gather_shared(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, x, ws1, ws3,
                                     base + L.h_shared, ws, ws_bytes, stream);
     if (r != MOE_OK) return r;
+    if (scatter)
+      return moe_expert_down_combine(s, base + L.h, offsets, src, w2, out, base + L.h_shared, ws2, out_shared, x,
+                                     pos, w, y, ws, ws_bytes, stream);
     r = moe_expert_down_shared(s, base + L.h, offsets, w2, out, base + L.h_shared, ws2, out_shared, ws,
                                ws_bytes, stream);
   } else {
     r = moe_expert_up_gather(s, fp8 ? codes : x, rsc, offsets, src, w1, w3, base + L.h, ws, ws_bytes,
                              stream);
     if (r != MOE_OK) return r;
+    if (scatter)
+      return moe_expert_down_combine(s, base + L.h, offsets, src, w2, out, nullptr, nullptr, nullptr, x, pos, w,
+                                     y, ws, ws_bytes, stream);
     r = moe_expert_down(s, base + L.h, offsets, w2, out, ws, ws_bytes, stream);
   }
   if (r != MOE_OK) return r;
   return moe_combine(s, out, out_shared, x, pos, w, y, stream);
+}
+
+moe_status moe_forward(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                       const void* w1, const void* w3, const void* w2, const void* ws1,
+                       const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
+                       int32_t* kept_counts, float* p, float* f, float* l_aux, int32_t* offsets,
+                       int32_t* pos, int32_t* src, uint8_t* drop, void* x_perm, float* row_scale,
+                       void* out, void* out_shared, void* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return forward_impl(s, x, w_g, bias, w1, w3, w2, ws1, ws3, ws2, idx, w, counts, kept_counts, p, f, l_aux,
+                      offsets, pos, src, drop, x_perm, row_scale, out, out_shared, y, ws, ws_bytes, stream,
+                      false);
+}
+
+moe_status moe_forward_scatter(const moe_shape* s, const void* x, const void* w_g, const float* bias,
+                               const void* w1, const void* w3, const void* w2, const void* ws1,
+                               const void* ws3, const void* ws2, int32_t* idx, float* w, int32_t* counts,
+                               int32_t* kept_counts, float* p, float* f, float* l_aux, int32_t* offsets,
+                               int32_t* pos, int32_t* src, uint8_t* drop, float* row_scale, void* out,
+                               void* out_shared, void* y, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(s, x, w_g, bias, w1, w3, w2, ws1, ws3, ws2, idx, w, counts, kept_counts, p, f, l_aux,
+                      offsets, pos, src, drop, nullptr, row_scale, out, out_shared, y, ws, ws_bytes, stream,
+                      true);
 }
 
 }  // extern "C"

@@ -21,27 +21,12 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void acc_bf16x8(float* acc, uint4 v, float w) {
-  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[2 * i] = fmaf(w, __uint_as_float(q[i] << 16), acc[2 * i]);
-    acc[2 * i + 1] = fmaf(w, __uint_as_float(q[i] & 0xFFFF0000u), acc[2 * i + 1]);
-  }
-}
-__device__ __forceinline__ void add_bf16x8(float* acc, uint4 v) {
-  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[2 * i] += __uint_as_float(q[i] << 16);
-    acc[2 * i + 1] += __uint_as_float(q[i] & 0xFFFF0000u);
-  }
-}
+__device__ __forceinline__ void acc_bf16x8(float* acc, uint4 v, float w) { combine_fma8(acc, v, w); }
+__device__ __forceinline__ void add_bf16x8(float* acc, uint4 v) { combine_add8(acc, v); }
 __device__ __forceinline__ u32x4 pack_bf16x8(const float* acc) {
+  const uint4 p = combine_pack8(acc);
   u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+  r[0] = p.x, r[1] = p.y, r[2] = p.z, r[3] = p.w;
   return r;
 }
 
@@ -144,7 +129,46 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
   }
 }
 
+// Before the combining down GEMM: cnt[t][c] = -(kept slots of t + shared), for
+// every column group c; a token that no output row reaches (every slot dropped,
+// no shared expert) gets its y here, as the combine kernel computes it: sum of
+// w * x[t] over the slots (pass-through) or zero.  One thread per (token, group).
+__global__ __launch_bounds__(256) void scatter_init_kernel(const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ w,
+                                                           const uint16_t* __restrict__ x,
+                                                           int32_t* __restrict__ cnt,
+                                                           uint16_t* __restrict__ y, int64_t T, int k,
+                                                           int d, int G, int shared, int drop_mode) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t t = q / G;
+  if (t >= T) return;
+  const int grp = static_cast<int>(q - t * G);
+  int nk = shared;
+  for (int j = 0; j < k; ++j) nk += pos[t * k + j] >= 0 ? 1 : 0;
+  cnt[q] = -nk;
+  if (nk > 0) return;
+  const bool pass = drop_mode == MOE_DROP_PASSTHROUGH;
+  for (int col = grp * kScatterCols; col < min(d, (grp + 1) * kScatterCols); col += 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (pass) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + t * d + col);
+      for (int j = 0; j < k; ++j) combine_fma8(acc, v, w[t * k + j]);
+    }
+    *reinterpret_cast<uint4*>(y + t * d + col) = combine_pack8(acc);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_scatter_init(const moe_shape& s, const int32_t* pos, const float* w, const void* x,
+                               int32_t* cnt, void* y, hipStream_t st) {
+  const int G = static_cast<int>(ceil_div(s.d, kScatterCols));
+  const int64_t n = s.T * G;
+  hipLaunchKernelGGL(scatter_init_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, st,
+                     pos, w, static_cast<const uint16_t*>(x), cnt, static_cast<uint16_t*>(y), s.T, s.k,
+                     s.d, G, s.has_shared ? 1 : 0, s.drop);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const moe_shape& s, const void* out, const void* out_shared,
                           const void* x, const int32_t* pos, const float* w, void* y,

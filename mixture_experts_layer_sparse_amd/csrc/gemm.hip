@@ -93,6 +93,17 @@ struct GemmArgs {
   const uint16_t* xb0;
   uint16_t* xout;
   int64_t x_rows;          // 0: none
+  // Combining epilogue (EPI_STORE, not split-K; sc_cnt null: off): after a tile
+  // has written its output rows it counts them per token and kScatterCols-column
+  // group, and the tile that completes a group writes those columns of y.
+  const int32_t* sc_src;   // [rows] token of each routed row (the extra segment's row r is token r)
+  const int32_t* sc_pos;   // [T][k]
+  const float* sc_w;       // [T][k]
+  const uint16_t* sc_x;    // [T][n_out]
+  uint16_t* sc_y;          // [T][n_out]
+  int32_t* sc_cnt;         // [T][ceil(n_out / kScatterCols)], set by launch_scatter_init
+  int sc_k;
+  int sc_drop;
 };
 
 // silu(u) = u / (1 + e^-u) with the hardware reciprocal (about 1 ulp): the result is rounded to
@@ -852,6 +863,69 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     else mm_dma(P1{}, NI, kt + 2, cur, W_AB{});
   };
 
+  // Combining epilogue of tile rows [r0, r_end), n-tile nt_ (extra segment: xs).
+  // The tile's own output stores are published at agent scope first (the XCDs'
+  // L2 caches are not coherent with each other), then each (row, column group)
+  // pair adds one to its token's counter; a pair that brings the counter to zero
+  // (its token's other rows in these columns are all written and published) is
+  // queued, and after an agent-scope acquire the workgroup writes those columns
+  // of y: sum over the slots in slot order of w * (the slot's output row, or for
+  // a dropped slot x or the shared output), then the shared output, float32,
+  // one rounding, the arithmetic of the combine kernel.
+  __shared__ int sc_tok[EPI == EPI_STORE ? BM * BN / kScatterCols : 1];
+  __shared__ int sc_grp[EPI == EPI_STORE ? BM * BN / kScatterCols : 1];
+  __shared__ int sc_n;
+  auto scatter_combine = [&](int r0, int r_end, int nt_, bool xs) {
+    constexpr int CG = kScatterCols;
+    const int n_out = g.n_out;
+    const int G = (n_out + CG - 1) / CG;
+    const int c0 = nt_ * BN;
+    const int ncol = min(BN, n_out - c0);
+    const int ngrp = ncol > 0 ? (ncol + CG - 1) / CG : 0;
+    const int nrow = max(0, min(BM, r_end - r0));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (tid == 0) sc_n = 0;
+    __syncthreads();
+    for (int q = tid; q < nrow * ngrp; q += NW * 64) {
+      const int r = r0 + q / ngrp, grp = c0 / CG + q % ngrp;
+      const int t = xs ? r : g.sc_src[r];
+      const int old = __hip_atomic_fetch_add(g.sc_cnt + static_cast<int64_t>(t) * G + grp, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      if (old == -1) {
+        const int i = atomicAdd(&sc_n, 1);
+        sc_tok[i] = t;
+        sc_grp[i] = grp;
+      }
+    }
+    __syncthreads();
+    const int n_own = __builtin_amdgcn_readfirstlane(sc_n);
+    if (n_own > 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      const int k = g.sc_k;
+      const bool shared = g.x_rows > 0;
+      const bool fallback = g.sc_drop == MOE_DROP_FALLBACK && shared;
+      const bool pass = g.sc_drop == MOE_DROP_PASSTHROUGH;
+      for (int q = tid; q < n_own * (CG / 8); q += NW * 64) {
+        const int it = q / (CG / 8);
+        const int64_t t = sc_tok[it];
+        const int col = sc_grp[it] * CG + (q % (CG / 8)) * 8;
+        if (col < n_out) {
+          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < k; ++j) {
+            const int p = g.sc_pos[t * k + j];
+            const float wj = g.sc_w[t * k + j];
+            const uint16_t* row = p >= 0 ? g.out + static_cast<int64_t>(p) * n_out
+                                         : (fallback ? g.xout + t * n_out : g.sc_x + t * n_out);
+            if (p >= 0 || pass || fallback) combine_fma8(acc, *reinterpret_cast<const uint4*>(row + col), wj);
+          }
+          if (shared) combine_add8(acc, *reinterpret_cast<const uint4*>(g.xout + t * n_out + col));
+          *reinterpret_cast<uint4*>(g.sc_y + t * n_out + col) = combine_pack8(acc);
+        }
+      }
+    }
+    __syncthreads();
+  };
+
   if (!next_tile()) return;
   bind_tile();
   if constexpr (!REG) {
@@ -909,6 +983,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     // Next tile first: its first two steps load while this tile's epilogue
     // runs (the stages are free, the epilogue does not use LDS).
     const int erow0 = row0, erow_end = row_end, entile = ntile, eunit = unit;
+    const bool exseg = xseg;
     uint16_t* const eout = xseg ? g.xout : g.out;
     const bool more = next_tile();
     if (more) {
@@ -993,6 +1068,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
           }
         }
       }
+    }
+    if constexpr (EPI == EPI_STORE) {
+      if (g.sc_cnt != nullptr) scatter_combine(erow0, erow_end, entile, exseg);
     }
     if (!more) break;
   }
@@ -1637,7 +1715,10 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
 
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
-                              hipStream_t st, const void* xa, const void* xw2, void* xout, int64_t x_rows) {
+                              hipStream_t st, const void* xa, const void* xw2, void* xout, int64_t x_rows,
+                              const ScatterArgs* sc) {
+  // (the combining epilogue runs in the tiled bf16 kernels only)
+  if (sc != nullptr && (gemv_fits(s) || s.dtype != MOE_BF16)) return hipErrorInvalidValue;
   if (gemv_fits(s)) {
     GemvArgs g{};
     g.a = h;
@@ -1687,6 +1768,18 @@ hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* 
   g.xb0 = extra ? static_cast<const uint16_t*>(xw2) : nullptr;
   g.xout = extra ? static_cast<uint16_t*>(xout) : nullptr;
   g.x_rows = extra ? x_rows : 0;
+  if (sc != nullptr) {
+    // every output element from one workgroup's epilogue: no split-K tail
+    split = nullptr;
+    g.sc_src = sc->src;
+    g.sc_pos = sc->pos;
+    g.sc_w = sc->w;
+    g.sc_x = static_cast<const uint16_t*>(sc->x);
+    g.sc_y = static_cast<uint16_t*>(sc->y);
+    g.sc_cnt = sc->cnt;
+    g.sc_k = s.k;
+    g.sc_drop = s.drop;
+  }
   const int64_t rows_all = rows + g.x_rows;
   const int segs_all = dense ? 1 : n_seg + (extra ? 1 : 0);
   const bool sk = split != nullptr && skinny(rows_all, segs_all, g.nt);

@@ -34,6 +34,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// The combine's arithmetic on 8 bf16 values (the combine kernel and the
+// combining epilogue of the down GEMM use these, so that both give the same
+// bits): acc += w * v with one fused multiply-add per element, acc += v, and
+// the float32 -> bf16 rounding of the sums.
+__device__ __forceinline__ void combine_fma8(float* acc, uint4 v, float w) {
+  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = fmaf(w, __uint_as_float(q[i] << 16), acc[2 * i]);
+    acc[2 * i + 1] = fmaf(w, __uint_as_float(q[i] & 0xFFFF0000u), acc[2 * i + 1]);
+  }
+}
+__device__ __forceinline__ void combine_add8(float* acc, uint4 v) {
+  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += __uint_as_float(q[i] << 16);
+    acc[2 * i + 1] += __uint_as_float(q[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ uint4 combine_pack8(const float* acc) {
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// Columns of y per arrival counter of the combining down GEMM.
+constexpr int kScatterCols = 128;
+
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) {
   return (a + b - 1) / b;
 }
@@ -58,6 +89,7 @@ struct WsLayout {
   size_t gemm_split;    // split-K tail scratch of the grouped GEMMs (gemm_split_bytes(s))
   size_t h;             // dtype   [T*k][F]
   size_t h_shared;      // dtype   [T][F]
+  size_t sc_cnt;        // int32   [T][ceil(d / kScatterCols)] arrival counters (bf16 layers)
   size_t total;
 };
 WsLayout ws_layout(const moe_shape& s);
@@ -166,10 +198,28 @@ hipError_t launch_expert_up(const moe_shape& s, const void* a, const float* row_
 // With x_rows > 0 (and offsets), the same launch also computes an extra dense
 // segment after the routed ones: xout [x_rows][d] = xa [x_rows][F] times the one
 // matrix xw2 (laid out as one of w2's), the shared expert's down GEMM.
+//
+// With `sc` (bf16 layers, no split-K scratch), the down GEMM also combines:
+// cnt[t][c] starts at minus the number of rows of token t in the launch (its
+// kept slots, plus its shared-expert row), every tile adds one per row for
+// each kScatterCols-column group it covers after publishing its output rows,
+// and the tile that brings a counter to zero writes those columns of y[t]
+// from the token's rows as the combine kernel does (launch_scatter_init sets
+// the counters and writes y of the tokens no row reaches).
+struct ScatterArgs {
+  const int32_t* src;   // [rows] token of each routed output row
+  const int32_t* pos;   // [T][k]
+  const float* w;       // [T][k]
+  const void* x;        // [T][d] (dropped slots passed through)
+  void* y;              // [T][d]
+  int32_t* cnt;         // [T][ceil(d / kScatterCols)]
+};
 hipError_t launch_expert_down(const moe_shape& s, const void* h, const int32_t* offsets,
                               int64_t rows, int n_seg, const void* w2, void* out, void* split,
                               hipStream_t st, const void* xa = nullptr, const void* xw2 = nullptr,
-                              void* xout = nullptr, int64_t x_rows = 0);
+                              void* xout = nullptr, int64_t x_rows = 0, const ScatterArgs* sc = nullptr);
+hipError_t launch_scatter_init(const moe_shape& s, const int32_t* pos, const float* w, const void* x,
+                               int32_t* cnt, void* y, hipStream_t st);
 size_t gemm_split_bytes(const moe_shape& s);
 
 // Wide routers (bf16, at least 64 experts, N d >= 2^19, 512 to 16384 tokens): the logits as

@@ -109,6 +109,8 @@ _SIGS = {
     "moe_experts": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(Shape)] + [_P] * 6 + [_P]),
     "moe_forward": (c_int32, [POINTER(Shape)] + [_P] * 25 + [_P, c_size_t, _P]),
+    "moe_expert_down_combine": (c_int32, [POINTER(Shape)] + [_P] * 12 + [_P, c_size_t, _P]),
+    "moe_forward_scatter": (c_int32, [POINTER(Shape)] + [_P] * 24 + [_P, c_size_t, _P]),
     "moe_status_string": (ctypes.c_char_p, [c_int32]),
 }
 
@@ -433,6 +435,34 @@ def experts(s: Shape, x_perm, row_scale, offsets, w1, w3, w2, x=None, ws1=None, 
     return out, out_shared
 
 
+def expert_down_combine(s: Shape, h, offsets, src, w2, x, pos, w, h_shared=None, ws2=None, out=None,
+                        out_shared=None, y=None, ws=None):
+    """moe_expert_down_combine: the down GEMM (with has_shared, the shared
+    expert's too) whose tiles also write y.  Returns (out, out_shared, y)."""
+    T, d, F = s.T, s.d, s.F
+    dev = h.device
+    _check(h, "h", (T * s.k, F), s.torch_dtype)
+    _check_w(w2, "w2", s, s.N, d, F)
+    _check(src, "src", (T * s.k,), torch.int32)
+    _check(x, "x", (T, d), s.torch_dtype)
+    _check(pos, "pos", (T, s.k), torch.int32)
+    _check(w, "w", (T, s.k), torch.float32)
+    if s.has_shared:
+        _check(h_shared, "h_shared", (T, F), s.torch_dtype)
+        _check_w(ws2, "ws2", s, None, d, F)
+        if out_shared is None:
+            out_shared = torch.empty((T, d), dtype=s.torch_dtype, device=dev)
+    if out is None:
+        out = torch.empty((T * s.k, d), dtype=s.torch_dtype, device=dev)
+    if y is None:
+        y = torch.empty((T, d), dtype=s.torch_dtype, device=dev)
+    ws = ws if ws is not None else alloc_workspace(s, dev)
+    _call("moe_expert_down_combine", ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(src), _ptr(w2),
+          _ptr(out), _ptr(h_shared), _ptr(ws2), _ptr(out_shared), _ptr(x), _ptr(pos), _ptr(w), _ptr(y),
+          _ptr(ws), ws.numel(), _stream())
+    return out, out_shared, y
+
+
 def combine(s: Shape, out, out_shared, x, pos, w, y=None):
     T, d = s.T, s.d
     _check(out, "out", (T * s.k, d), s.torch_dtype)
@@ -452,7 +482,7 @@ class Layer:
     a captured graph needs).  Buffers are exposed as attributes."""
 
     def __init__(self, s: Shape, wg, w1, w3, w2, bias=None, ws1=None, ws3=None, ws2=None,
-                 device="cuda", fused=False):
+                 device="cuda", fused=False, scatter=False):
         st = check_shape(s)
         if st != MOE_OK:
             raise MoeError("moe_check_shape", st)
@@ -483,8 +513,12 @@ class Layer:
         self.pos = torch.empty((T, k), **e)
         self.src = torch.empty(T * k, **e)
         self.drop = torch.empty((T, k), dtype=torch.uint8, device=device)
-        # fused: no dispatch buffer (the up GEMM gathers rows of x through src)
+        # fused: no dispatch buffer (the up GEMM gathers rows of x through src);
+        # scatter (fused only): the down GEMM's tiles also write y (no combine launch)
+        if scatter and not fused:
+            raise ValueError("scatter needs fused=True")
         self.fused = fused
+        self.scatter = scatter
         self.x_perm = None if fused else torch.empty((T * k, d), dtype=s.buf_torch_dtype, device=device)
         self.row_scale = torch.empty(T * k, **f) if s.buf_dtype == MOE_FP8_E4M3 else None
         self.x_codes = (torch.empty((T, d), dtype=torch.uint8, device=device)
@@ -497,6 +531,15 @@ class Layer:
     def forward(self, x) -> torch.Tensor:
         s = self.s
         _check(x, "x", (s.T, s.d), s.torch_dtype)
+        if self.scatter:
+            _call("moe_forward_scatter", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias),
+                  _ptr(self.w1), _ptr(self.w3), _ptr(self.w2), _ptr(self.ws1), _ptr(self.ws3),
+                  _ptr(self.ws2), _ptr(self.idx), _ptr(self.w), _ptr(self.counts),
+                  _ptr(self.kept_counts), _ptr(self.p), _ptr(self.f), _ptr(self.l_aux),
+                  _ptr(self.offsets), _ptr(self.pos), _ptr(self.src), _ptr(self.drop),
+                  _ptr(self.row_scale), _ptr(self.out), _ptr(self.out_shared),
+                  _ptr(self.y), _ptr(self.ws), self.ws.numel(), _stream())
+            return self.y
         _call("moe_forward", ctypes.byref(s), _ptr(x), _ptr(self.wg), _ptr(self.bias),
               _ptr(self.w1), _ptr(self.w3), _ptr(self.w2), _ptr(self.ws1), _ptr(self.ws3),
               _ptr(self.ws2), _ptr(self.idx), _ptr(self.w), _ptr(self.counts),
@@ -528,6 +571,13 @@ class Layer:
         _call("moe_expert_up_gather_shared", ctypes.byref(s), _ptr(a), _ptr(self.row_scale),
               _ptr(self.offsets), _ptr(self.src), _ptr(self.w1), _ptr(self.w3), _ptr(h), _ptr(x),
               _ptr(self.ws1), _ptr(self.ws3), _ptr(h_shared), _ptr(self.ws), self.ws.numel(), _stream())
+
+    def expert_down_combine(self, x, h, h_shared=None):
+        """The scatter layer's last phase: down GEMM(s) writing out and y."""
+        s = self.s
+        _call("moe_expert_down_combine", ctypes.byref(s), _ptr(h), _ptr(self.offsets), _ptr(self.src),
+              _ptr(self.w2), _ptr(self.out), _ptr(h_shared), _ptr(self.ws2), _ptr(self.out_shared), _ptr(x),
+              _ptr(self.pos), _ptr(self.w), _ptr(self.y), _ptr(self.ws), self.ws.numel(), _stream())
 
     # forward in three calls (the same kernels): route + dispatch, experts, combine
     def route_dispatch(self, x):

@@ -100,19 +100,27 @@ def rows_rel_err(a, b):
     return float(np.max(num / den)) if a.size else 0.0
 
 
-def run_gpu_forward(wl, inp, g=None, fused=False):
+def run_gpu_forward(wl, inp, g=None, fused=False, scatter=False):
     """The whole layer in one call (moe_forward); host copies of its outputs
     under the same names as run_gpu.  ``g`` as for run_gpu.  ``fused``: no
-    dispatch buffer (x_perm is None), the up GEMM gathers x through src."""
+    dispatch buffer (x_perm is None), the up GEMM gathers x through src.
+    ``scatter`` (fused): moe_forward_scatter, the down GEMM writing y; the result
+    then also holds ``y_combine``, moe_combine run on the call's own expert
+    outputs, which the down GEMM's y must equal bit for bit."""
     s = M.shape_of(wl)
     g = g if g is not None else upload(wl, inp)
     L = M.Layer(s, g["wg"], g["w1"], g.get("w3"), g["w2"], bias=g.get("bias"), ws1=g.get("ws1"),
-                ws3=g.get("ws3"), ws2=g.get("ws2"), fused=fused)
+                ws3=g.get("ws3"), ws2=g.get("ws2"), fused=fused or scatter, scatter=scatter)
     L.forward(g["x"])
     torch.cuda.synchronize()
     names = ["idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "src",
              "drop", "x_perm", "row_scale", "out", "out_shared", "y"]
-    return {n: host(getattr(L, n)) for n in names}
+    res = {n: host(getattr(L, n)) for n in names}
+    if scatter:
+        yc = M.combine(s, L.out, L.out_shared, g["x"], L.pos, L.w)
+        torch.cuda.synchronize()
+        res["y_combine"] = host(yc)
+    return res
 
 
 def check_layer(wl, inp, gpu, y_tokens=None, max_adopted=None):

@@ -131,6 +131,25 @@ def test_null_pointers_and_workspace_rejected_on_host(M):
     st = L.moe_expert_up_gather_shared(ctypes.byref(ssh), p, None, p, p, p, None, p, p, p, None, None, None,
                                        0, None)
     assert st == M.MOE_ERR_ARG
+    # the combining down GEMM: missing src, missing y, shared expert without its buffers, small workspace
+    st = L.moe_expert_down_combine(ctypes.byref(s), p, p, None, p, p, None, None, None, p, p, p, p, p,
+                                   M.workspace_bytes(s), None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_expert_down_combine(ctypes.byref(s), p, p, p, p, p, None, None, None, p, p, p, None, p,
+                                   M.workspace_bytes(s), None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_expert_down_combine(ctypes.byref(ssh), p, p, p, p, p, None, p, p, p, p, p, p, p,
+                                   M.workspace_bytes(ssh), None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_expert_down_combine(ctypes.byref(s), p, p, p, p, p, None, None, None, p, p, p, p, p, 8, None)
+    assert st == M.MOE_ERR_WORKSPACE
+    # the scatter layer: missing y, then too small a workspace
+    st = L.moe_forward_scatter(ctypes.byref(s), p, p, None, p, p, p, None, None, None, p, p, p, p, None,
+                               None, None, p, p, p, p, None, p, None, None, p, M.workspace_bytes(s), None)
+    assert st == M.MOE_ERR_ARG
+    st = L.moe_forward_scatter(ctypes.byref(s), p, p, None, p, p, p, None, None, None, p, p, p, p, None,
+                               None, None, p, p, p, p, None, p, None, p, p, 8, None)
+    assert st == M.MOE_ERR_WORKSPACE
     # T == 0 is a no-op even with null buffers
     s0 = _s(M, T=0)
     st = L.moe_route(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None,

@@ -410,7 +410,35 @@ def _forward_and_phases(wl, inp, y_tokens=None, max_adopted=None):
     fu = run_gpu_forward(wl, inp, g=g, fused=True)
     assert fu["x_perm"] is None
     assert_same_results(fu, fwd, wl.buf == "fp8")
+    sc = run_gpu_forward(wl, inp, g=g, scatter=True)
+    _check_scatter(wl, fwd, sc)
+    if wl.T * wl.d <= 1 << 22:
+        # (small cases: the scatter layer against the oracle as well)
+        check_layer(wl, inp, sc, y_tokens=y_tokens, max_adopted=max_adopted)
     return fwd, errs
+
+
+def _check_scatter(wl, fwd, sc):
+    """moe_forward_scatter (the down GEMM's tiles write y): routing and plan bit
+    for bit those of moe_forward, its y bit for bit what moe_combine makes of its
+    own expert outputs, and those outputs the ones moe_forward computes (up to
+    float32 rounding order where moe_forward's down GEMM splits its last tiles
+    along K: the combining GEMM runs them whole)."""
+    from oracle import compare
+    for key in ("idx", "w", "counts", "kept_counts", "p", "f", "l_aux", "offsets", "pos", "drop"):
+        assert np.array_equal(sc[key], fwd[key]), key
+    R = int(fwd["offsets"][-1])
+    assert np.array_equal(sc["src"][:R], fwd["src"][:R]), "src"
+    assert np.array_equal(sc["y"], sc["y_combine"]), "scatter y vs moe_combine on the same outputs"
+    if R > 0:
+        e = compare.rel_l2(sc["out"][:R], fwd["out"][:R])
+        assert e <= 2e-3, f"scatter out vs moe_forward out: {e}"
+    if fwd["out_shared"] is not None:
+        e = compare.rel_l2(sc["out_shared"], fwd["out_shared"])
+        assert e <= 2e-3, f"scatter out_shared vs moe_forward: {e}"
+    e = compare.rel_l2(sc["y"], fwd["y"])
+    assert e <= 2e-3, f"scatter y vs moe_forward y: {e}"
+    print(f"  scatter: y == combine(out) bit for bit; y vs moe_forward rel-L2 {e:.2e}", flush=True)
 
 
 # ------------------------------------------------------------ graph replay --
