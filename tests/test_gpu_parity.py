@@ -454,6 +454,9 @@ GRAPH_CASES = {
     # decode steps of the fused layer: the one-tile router and the decode GEMV
     "decode_1_token_fused": lambda: si.decode(1),
     "decode_4_tokens_fused": lambda: si.decode(4),
+    # the scatter layer (the down GEMM's tiles write y; its counters are set by a kernel, not a memset)
+    "switch_capacity_scatter": lambda: si.small("switch"),
+    "deepseek_fp8_groups_shared_scatter": lambda: si.small("deepseek_v3"),
 }
 
 
@@ -469,7 +472,8 @@ def test_graph_replay_matches_eager(name):
     g = upload(wl, _inputs(wl))
     s = M.shape_of(wl)
     L = M.Layer(s, g["wg"], g["w1"], g.get("w3"), g["w2"], bias=g.get("bias"), ws1=g.get("ws1"),
-                ws3=g.get("ws3"), ws2=g.get("ws2"), fused=name.endswith("_fused"))
+                ws3=g.get("ws3"), ws2=g.get("ws2"), fused=name.endswith(("_fused", "_scatter")),
+                scatter=name.endswith("_scatter"))
     x = g["x"]
     L.forward(x)
     torch.cuda.synchronize()
