@@ -349,6 +349,8 @@ FORWARD_CASES = {
     "deepseek_fp8_groups_shared": lambda: si.small("deepseek_v3"),
     "dbrx_skew": lambda: si.small("dbrx"),
     "single_token": lambda: si.small("mixtral", T=1),
+    # float32 layer (the scatter form runs the down GEMM and the combine as two launches)
+    "tiny_f32": lambda: si.WORKLOADS["tiny"],
     "one_tile_groups_capacity": lambda: si.Workload("otc", **ONE_TILE_CASES["t10_groups_capacity"]),
     # one router tile with bf16 x: logits from whole dot products (the four
     # waves split d four or two ways below four tokens, else the tokens), the
