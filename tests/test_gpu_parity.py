@@ -351,6 +351,10 @@ FORWARD_CASES = {
     "single_token": lambda: si.small("mixtral", T=1),
     # float32 layer (the scatter form runs the down GEMM and the combine as two launches)
     "tiny_f32": lambda: si.WORKLOADS["tiny"],
+    # d = 448: the last n-tile holds 192 columns and the last 128-column group of the
+    # scatter form's counters 64; capacity drops to the shared fallback expert
+    "d448_fallback_shared": lambda: si.Workload("f448", T=600, d=448, N=8, k=2, F=256, capacity=110,
+                                                drop="fallback", shared=True),
     "one_tile_groups_capacity": lambda: si.Workload("otc", **ONE_TILE_CASES["t10_groups_capacity"]),
     # one router tile with bf16 x: logits from whole dot products (the four
     # waves split d four or two ways below four tokens, else the tokens), the
