@@ -864,14 +864,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
   };
 
   // Combining epilogue of tile rows [r0, r_end), n-tile nt_ (extra segment: xs).
-  // The tile's own output stores are published at agent scope first (the XCDs'
-  // L2 caches are not coherent with each other), then each (row, column group)
-  // pair adds one to its token's counter; a pair that brings the counter to zero
-  // (its token's other rows in these columns are all written and published) is
-  // queued, and after an agent-scope acquire the workgroup writes those columns
-  // of y: sum over the slots in slot order of w * (the slot's output row, or for
-  // a dropped slot x or the shared output), then the shared output, float32,
-  // one rounding, the arithmetic of the combine kernel.
+  // After the workgroup barrier (the tile's output stores are complete), every
+  // thread publishes them at agent scope (a release fence: the XCDs' L2 caches
+  // are not coherent with each other) before its counter updates, so each
+  // update is ordered after all of the tile's stores; each (row, column group)
+  // pair adds one to its token's counter, and a pair that brings the counter to
+  // zero (the token's other rows in these columns are all written and
+  // published) is queued.  After an agent-scope acquire the workgroup writes
+  // those columns of y: sum over the slots in slot order of w * (the slot's
+  // output row, or for a dropped slot x or the shared output), then the shared
+  // output, float32, one rounding, the arithmetic of the combine kernel.
   __shared__ int sc_tok[EPI == EPI_STORE ? BM * BN / kScatterCols : 1];
   __shared__ int sc_grp[EPI == EPI_STORE ? BM * BN / kScatterCols : 1];
   __shared__ int sc_n;
@@ -883,9 +885,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gg_kernel(GemmArgs g) {
     const int ncol = min(BN, n_out - c0);
     const int ngrp = ncol > 0 ? (ncol + CG - 1) / CG : 0;
     const int nrow = max(0, min(BM, r_end - r0));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if (tid == 0) sc_n = 0;
     __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     for (int q = tid; q < nrow * ngrp; q += NW * 64) {
       const int r = r0 + q / ngrp, grp = c0 / CG + q % ngrp;
       const int t = xs ? r : g.sc_src[r];
