@@ -626,3 +626,49 @@ def test_mxfp4_layer(name):
     wl = MX_CASES[name]()
     print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} F={wl.F}", flush=True)
     _forward_and_phases(wl, si.generate(wl))
+
+
+# ------------------------------------------------- the combining down GEMM --
+
+DOWN_COMBINE_CASES = {
+    # 256-row down tiles with their quarter-tile tail, capacity drops contributing zero
+    "mixtral_capacity_zero": lambda: si.small("mixtral", T=1500, capacity=300, drop="zero"),
+    # fp8 rows, groups, the shared expert as the extra segment of the same launch
+    "deepseek_fp8_shared": lambda: si.small("deepseek_v3"),
+    # capacity drops passed through (ReLU, 128-row tiles)
+    "switch_passthrough": lambda: si.small("switch"),
+}
+
+
+@pytest.mark.parametrize("name", list(DOWN_COMBINE_CASES))
+def test_expert_down_combine_equals_down_then_combine(name):
+    """moe_expert_down_combine called on its own: out (and out_shared) bit for
+    bit those of moe_expert_down (moe_expert_down_shared) without a workspace,
+    and y bit for bit moe_combine of them, on twice-called inputs (the counters
+    need no initialisation between calls)."""
+    from moe_gpu_util import upload
+    wl = DOWN_COMBINE_CASES[name]()
+    print(f"case {name}: T={wl.T} d={wl.d} N={wl.N} k={wl.k} cap={wl.capacity}", flush=True)
+    s = M.shape_of(wl)
+    g = upload(wl, si.generate(wl))
+    x = g["x"]
+    ws = M.alloc_workspace(s)
+    pl = M.route_plan(s, x, g["wg"], g.get("bias"), ws=ws)
+    a = pl["x_codes"] if wl.buf == "fp8" else x
+    h = M.expert_up_gather(s, a, pl["row_scale"], pl["offsets"], pl["src"], g["w1"], g.get("w3"), ws=ws)
+    hs = M.shared_expert_up(s, x, g["ws1"], g.get("ws3")) if wl.shared else None
+    if wl.shared:
+        out_ref, outs_ref = M.expert_down_shared(s, h, pl["offsets"], g["w2"], hs, g["ws2"])
+    else:
+        out_ref, outs_ref = M.expert_down(s, h, pl["offsets"], g["w2"]), None
+    y_ref = M.combine(s, out_ref, outs_ref, x, pl["pos"], pl["w"])
+    torch.cuda.synchronize()
+    R = int(pl["offsets"][-1].item())
+    for rep in range(2):
+        out, outs, y = M.expert_down_combine(s, h, pl["offsets"], pl["src"], g["w2"], x, pl["pos"], pl["w"],
+                                             h_shared=hs, ws2=g.get("ws2"), ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:R], out_ref[:R]), (rep, "out")
+        if wl.shared:
+            assert torch.equal(outs, outs_ref), (rep, "out_shared")
+        assert torch.equal(y, y_ref), (rep, "y")
